@@ -1,0 +1,257 @@
+"""Seeded synthetic inputs for the Gated DeltaNet token mixer.
+
+This module only draws random numbers and stores them in the dtypes and layouts the
+library consumes. It holds none of the method's arithmetic, so both the HIP path and the
+fp64 oracle can take their inputs from here without sharing any computation.
+
+Distributions (the workload recipe of the Qwen3-Next layer shape; model card "Qwen3-Next",
+section "Model Overview": 32 V heads, 16 QK heads, head dim 128):
+
+* q, k ~ N(0, 1), then divided by their L2 norm per token and head; q is *not* scaled here,
+  the caller passes ``scale = 128**-0.5`` to the recurrence.
+* v ~ N(0, 1).
+* beta = sigmoid(N(0, 1)), so beta lies in (0, 1).
+* g = log(alpha) = -softplus(N(0, 1)) * 0.1, so alpha lies in (0, 1).
+* initial states ~ N(0, 0.02) (0.02 is a standard deviation).
+* packed variable-length batches draw lengths uniformly from an inclusive integer range.
+
+bf16 tensors are held as ``numpy.uint16`` bit patterns, rounded from fp32 to nearest even.
+Every generator takes a seed and uses numpy's PCG64, so the same call always gives the same
+bits.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+D_HEAD = 128
+H_QK = 16
+H_V = 32
+SCALE = D_HEAD ** -0.5
+
+
+# ----------------------------------------------------------------------------------------
+# bf16 storage helpers (bit manipulation only)
+# ----------------------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (round to nearest, ties to even); returns uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    rounded = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16))
+    out = rounded.astype(np.uint16)
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0)
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to fp32 (exact)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ----------------------------------------------------------------------------------------
+# primitive draws
+# ----------------------------------------------------------------------------------------
+
+def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0,1) vectors along the last axis, divided by their L2 norm (fp32)."""
+    x = rng.standard_normal(shape, dtype=np.float32)
+    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
+    return (x / np.maximum(n, 1e-12)).astype(np.float32)
+
+
+def _beta(rng: np.random.Generator, shape) -> np.ndarray:
+    z = rng.standard_normal(shape).astype(np.float64)
+    return (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+
+
+def _log_alpha(rng: np.random.Generator, shape) -> np.ndarray:
+    z = rng.standard_normal(shape).astype(np.float64)
+    return (-np.logaddexp(0.0, z) * 0.1).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------------------
+# prefill inputs (packed variable-length sequences)
+# ----------------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class PrefillInputs:
+    q: np.ndarray               # [T][h_qk][d_k]  uint16 (bf16) or float32
+    k: np.ndarray               # [T][h_qk][d_k]
+    v: np.ndarray               # [T][h_v][d_v]
+    g: np.ndarray               # [T][h_v] float32, log alpha
+    beta: np.ndarray            # [T][h_v] float32
+    cu_seqlens: np.ndarray      # [N+1] int32
+    initial_state: Optional[np.ndarray]  # [N][h_v][d_v][d_k] float32 or None
+    scale: float
+    io_dtype: str               # "bf16" or "f32"
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def num_seqs(self) -> int:
+        return int(len(self.cu_seqlens) - 1)
+
+    @property
+    def h_qk(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def h_v(self) -> int:
+        return int(self.v.shape[1])
+
+    def as_f64(self, name: str) -> np.ndarray:
+        """The exact fp64 value of an input tensor (bf16 bits widened exactly)."""
+        a = getattr(self, name)
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return bf16_bits_to_f32(a).astype(np.float64)
+        return a.astype(np.float64)
+
+
+def make_prefill(seq_lens, h_qk=H_QK, h_v=H_V, d_k=D_HEAD, d_v=D_HEAD, io_dtype="bf16",
+                 with_initial_state=False, seed=0, scale=None, state_std=0.02) -> PrefillInputs:
+    """Packed batch of sequences with the given lengths (zero lengths allowed)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seq_lens = [int(x) for x in seq_lens]
+    T = int(sum(seq_lens))
+    cu = np.zeros(len(seq_lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(seq_lens)
+    q = _unit_rows(rng, (T, h_qk, d_k))
+    k = _unit_rows(rng, (T, h_qk, d_k))
+    v = rng.standard_normal((T, h_v, d_v), dtype=np.float32)
+    beta = _beta(rng, (T, h_v))
+    g = _log_alpha(rng, (T, h_v))
+    s0 = None
+    if with_initial_state:
+        s0 = (rng.standard_normal((len(seq_lens), h_v, d_v, d_k), dtype=np.float32)
+              * np.float32(state_std)).astype(np.float32)
+    if io_dtype == "bf16":
+        q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    elif io_dtype != "f32":
+        raise ValueError(io_dtype)
+    return PrefillInputs(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu, initial_state=s0,
+                         scale=float(SCALE if scale is None else scale), io_dtype=io_dtype)
+
+
+def config0(seed=1000) -> PrefillInputs:
+    """B=1, T=256, one QK head and one V head, d=128, fp32 everywhere, S0 = 0."""
+    return make_prefill([256], h_qk=1, h_v=1, io_dtype="f32", seed=seed)
+
+
+def config1(seed=1001) -> PrefillInputs:
+    """B=1, T=4096, 16 QK / 32 V heads, bf16 q/k/v, S0 = 0 (not passed)."""
+    return make_prefill([4096], seed=seed)
+
+
+def config2(seed=1002) -> PrefillInputs:
+    """B=1, T=32768, 16 QK / 32 V heads, bf16 q/k/v, S0 ~ N(0, 0.02)."""
+    return make_prefill([32768], with_initial_state=True, seed=seed)
+
+
+# ----------------------------------------------------------------------------------------
+# decode inputs
+# ----------------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class DecodeInputs:
+    pool: np.ndarray            # [P][h_v][d_v][d_k] float32
+    q: np.ndarray               # [R][N][h_qk][d_k] uint16 (ring of R input sets)
+    k: np.ndarray               # [R][N][h_qk][d_k]
+    v: np.ndarray               # [R][N][h_v][d_v]
+    g: np.ndarray               # [R][N][h_v] float32
+    beta: np.ndarray            # [R][N][h_v] float32
+    slots: Optional[np.ndarray]  # [N] int32 pool slot per sequence, or None (identity)
+    scale: float
+
+
+def make_decode(num_seqs=256, h_qk=H_QK, h_v=H_V, d=D_HEAD, ring=16, pool_size=None,
+                permuted_slots=False, seed=1003, state_std=0.02) -> DecodeInputs:
+    """A state pool and a ring of per-step single-token inputs."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    P = num_seqs if pool_size is None else int(pool_size)
+    pool = (rng.standard_normal((P, h_v, d, d), dtype=np.float32) * np.float32(state_std))
+    q = f32_to_bf16_bits(_unit_rows(rng, (ring, num_seqs, h_qk, d)))
+    k = f32_to_bf16_bits(_unit_rows(rng, (ring, num_seqs, h_qk, d)))
+    v = f32_to_bf16_bits(rng.standard_normal((ring, num_seqs, h_v, d), dtype=np.float32))
+    beta = _beta(rng, (ring, num_seqs, h_v))
+    g = _log_alpha(rng, (ring, num_seqs, h_v))
+    slots = None
+    if permuted_slots:
+        slots = rng.permutation(P)[:num_seqs].astype(np.int32)
+    return DecodeInputs(pool=pool, q=q, k=k, v=v, g=g, beta=beta, slots=slots, scale=SCALE)
+
+
+def config3(seed=1003) -> DecodeInputs:
+    """256 sequences x 1 token, 16 QK / 32 V heads, fp32 pool ~ N(0, 0.02), ring of 16."""
+    return make_decode(seed=seed)
+
+
+# ----------------------------------------------------------------------------------------
+# front-end inputs (mixed projected q|k|v channels + conv weights)
+# ----------------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class FrontEndInputs:
+    mixed: np.ndarray           # [T][2*h_qk*d_k + h_v*d_v] uint16 (bf16)
+    conv_weight: np.ndarray     # [channels][K] float32
+    cu_seqlens: np.ndarray      # [N+1] int32
+    g: np.ndarray               # [T][h_v] float32
+    beta: np.ndarray            # [T][h_v] float32
+    initial_state: Optional[np.ndarray]  # [N][h_v][d_v][d_k] float32
+    h_qk: int
+    h_v: int
+    d_k: int
+    d_v: int
+    q_scale: float
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def num_seqs(self) -> int:
+        return int(len(self.cu_seqlens) - 1)
+
+
+def make_frontend(seq_lens, h_qk=H_QK, h_v=H_V, d_k=D_HEAD, d_v=D_HEAD, conv_kernel=4,
+                  with_initial_state=True, seed=1004, block_rows=1 << 16) -> FrontEndInputs:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seq_lens = [int(x) for x in seq_lens]
+    T = int(sum(seq_lens))
+    cu = np.zeros(len(seq_lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(seq_lens)
+    C = 2 * h_qk * d_k + h_v * d_v
+    mixed = np.empty((T, C), dtype=np.uint16)
+    for r0 in range(0, T, block_rows):   # bounded temporaries for large batches
+        r1 = min(T, r0 + block_rows)
+        mixed[r0:r1] = f32_to_bf16_bits(rng.standard_normal((r1 - r0, C), dtype=np.float32))
+    w = (rng.standard_normal((C, conv_kernel), dtype=np.float32) * np.float32(0.1))
+    beta = _beta(rng, (T, h_v))
+    g = _log_alpha(rng, (T, h_v))
+    s0 = None
+    if with_initial_state:
+        s0 = (rng.standard_normal((len(seq_lens), h_v, d_v, d_k), dtype=np.float32)
+              * np.float32(0.02))
+    return FrontEndInputs(mixed=mixed, conv_weight=w, cu_seqlens=cu, g=g, beta=beta,
+                          initial_state=s0, h_qk=h_qk, h_v=h_v, d_k=d_k, d_v=d_v,
+                          q_scale=float(d_k ** -0.5))
+
+
+def config4_lengths(seed=1004, num_seqs=64, lo=128, hi=8192):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [int(x) for x in rng.integers(lo, hi, size=num_seqs, endpoint=True)]
+
+
+def config4(seed=1004) -> FrontEndInputs:
+    """64 sequences, lengths uniform in [128, 8192], mixed bf16 [sum T][8192], conv k=4."""
+    return make_frontend(config4_lengths(seed), seed=seed + 100)
