@@ -1,0 +1,135 @@
+/*
+ * gdn.h -- C ABI of libgdn.so, a Gated DeltaNet token mixer for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "Qwen3-Next -- How a running memory and a searchable history
+ * cooperate", section "Correcting a memory instead of adding to it"): each V head keeps a
+ * fixed d_v x d_k state S. For every token it first shrinks S by a decay alpha, then
+ * corrects what S returns for the key k toward the value v with write strength beta:
+ *
+ *     S_t = alpha_t * S_{t-1} * (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *
+ * and the layer output is o_t = scale * S_t q_t, read after the update (token loop in
+ * section "01 . GatedDeltaNet(config)" of page "Qwen3-Next 80B-A3B -- The Evolving
+ * Transformer"). alpha is passed as its logarithm g = log(alpha). The state size does not
+ * depend on the number of tokens (section "Two kinds of remembering" of the first page).
+ *
+ * Heads (model card "Qwen3-Next", section "Model Overview"): h_qk query/key heads are shared
+ * by h_v value heads; V head h reads QK head h / (h_v / h_qk). The library supports
+ * d_k = d_v = 128 (the model's head dim) and any h_qk, h_v with h_v % h_qk == 0.
+ *
+ * Conventions for every function:
+ *  - Every pointer is a DEVICE pointer (hipMalloc'd or equivalent). Layouts are row-major
+ *    and contiguous, last index fastest. bf16 is the IEEE-style 16-bit brain float.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the default
+ *    stream). The library never allocates, frees or synchronises, and keeps no global
+ *    mutable state: calls are re-entrant and thread-safe.
+ *  - The caller owns every buffer. Arguments are validated on the host before anything is
+ *    launched; on a nonzero status nothing has been written. A failed launch returns
+ *    GDN_ERR_HIP. Nothing is thrown across the ABI.
+ *  - Device-side contracts that the host cannot check without a synchronisation:
+ *    cu_seqlens is nondecreasing from 0 to total_tokens, and state_slots holds distinct
+ *    indices below the pool size. Breaking them is undefined behaviour.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,         /* a required pointer is NULL */
+    GDN_ERR_SHAPE = 2,        /* a size is negative or inconsistent */
+    GDN_ERR_UNSUPPORTED = 3,  /* valid but not implemented (head dim != 128, dtype, ...) */
+    GDN_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the query says */
+    GDN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+} gdn_status;
+
+typedef enum {
+    GDN_BF16 = 0,             /* q, k, v and o in bf16; arithmetic in fp32 */
+    GDN_F32 = 1               /* q, k, v and o in fp32; arithmetic in fp32 */
+} gdn_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* gdn_status_string(gdn_status s);
+
+/*
+ * Bytes of device workspace gdn_chunk_prefill needs for these sizes. The current kernels
+ * keep every intermediate on chip, so this returns 0; callers should still query it and
+ * pass a buffer of at least that size (NULL is accepted when the answer is 0).
+ */
+size_t gdn_chunk_prefill_workspace_bytes(int32_t total_tokens, int32_t num_seqs,
+                                         int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v);
+
+/*
+ * Prefill: runs the gated delta rule over a packed batch of variable-length sequences.
+ *
+ *   q, k          [total_tokens][h_qk][d_k]      io_dtype
+ *   v             [total_tokens][h_v][d_v]       io_dtype
+ *   g, beta       [total_tokens][h_v]            fp32; alpha = exp(g), g <= 0 expected
+ *   cu_seqlens    [num_seqs + 1]                 int32; sequence n spans tokens
+ *                                                cu_seqlens[n] .. cu_seqlens[n+1]-1
+ *   scale         multiplies the read-out (o = scale * S q)
+ *   initial_state [num_seqs][h_v][d_v][d_k] fp32, or NULL for zero states
+ *   final_state   same shape, or NULL to skip; may alias initial_state (in-place update)
+ *   o             [total_tokens][h_v][d_v]       io_dtype
+ *   workspace     at least gdn_chunk_prefill_workspace_bytes(...) bytes
+ *
+ * Zero-length sequences are allowed: their final state is their initial state.
+ * io_dtype GDN_BF16 runs the chunked kernel (chunks of 64 tokens; intra-chunk products on
+ * bf16 matrix cores with fp32 accumulation, the state carried in fp32). GDN_F32 runs a
+ * token-sequential fp32 kernel (for fp32 inputs whose products must not round to bf16).
+ */
+gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
+                             const float* g, const float* beta,
+                             const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                             int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, float scale,
+                             const float* initial_state, float* final_state,
+                             void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode: one token for each of num_seqs sequences, updating their states in place.
+ *
+ *   q, k          [num_seqs][h_qk][d_k]          io_dtype
+ *   v             [num_seqs][h_v][d_v]           io_dtype
+ *   g, beta       [num_seqs][h_v]                fp32
+ *   state_pool    [pool_size][h_v][d_v][d_k]     fp32, read and written in place
+ *   state_slots   [num_seqs] int32: sequence n uses pool entry state_slots[n]; NULL means
+ *                 entry n. Slots must be distinct.
+ *   o             [num_seqs][h_v][d_v]           io_dtype
+ */
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
+                           const float* g, const float* beta,
+                           float* state_pool, const int32_t* state_slots,
+                           int32_t num_seqs, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+                           float scale, void* o, void* stream);
+
+/*
+ * Front end: short causal depthwise convolution, SiLU, L2 normalisation of every q and k
+ * head, and a scale on q (section "01 . GatedDeltaNet(config)" of the Evolving Transformer
+ * page names the short convolution for local context and the key normalisation).
+ *
+ *   mixed_qkv     [total_tokens][C] bf16 with C = 2*h_qk*d_k + h_v*d_v, channels ordered
+ *                 q heads | k heads | v heads, each head's d channels contiguous
+ *   conv_weight   [C][conv_kernel] fp32; tap conv_kernel-1 multiplies the current token,
+ *                 tap i the token conv_kernel-1-i positions earlier. No bias. The window
+ *                 never reaches across a sequence start (zero history).
+ *   q, k          [total_tokens][h_qk][d_k] bf16: silu(y) / max(||silu(y)||_2, 1e-12),
+ *                 q further multiplied by q_scale
+ *   v             [total_tokens][h_v][d_v] bf16: silu(y)
+ * conv_kernel must be between 1 and 4.
+ */
+gdn_status gdn_conv_prep(const void* mixed_qkv, const float* conv_weight, int32_t conv_kernel,
+                         const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                         int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, float q_scale,
+                         void* q, void* k, void* v, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

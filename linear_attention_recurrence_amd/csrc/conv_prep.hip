@@ -1,0 +1,154 @@
+// conv_prep.hip -- front end of the Gated DeltaNet mixer on gfx950.
+//
+// Per token t and channel c of the projected q|k|v activations (section
+// "01 . GatedDeltaNet(config)" of page "Qwen3-Next 80B-A3B -- The Evolving Transformer":
+// a short 1-D convolution gives local context; keys are L2-normalised):
+//
+//   y[t,c] = sum_i w[c,i] * x[t-(K-1)+i, c]     (x = 0 before the sequence start)
+//   z      = y * sigmoid(y)                      (SiLU)
+//   q head = z / max(||z||_2, 1e-12) * q_scale,  k head = z / max(||z||_2, 1e-12),  v = z
+//
+// HBM-bound (16 KB read + 16 KB written per token at the model's 8192 channels). Each
+// thread owns 8 adjacent channels (one 16-byte load/store) and walks R consecutive tokens,
+// keeping the last K-1 inputs of its channels in registers, so every input row is read
+// once (plus K-1 halo rows per block). Sixteen threads cover one 128-channel head, so the
+// head norm is a 16-lane reduction. A block covers 2048 channels x R tokens.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kTokensPerBlock = 32;
+constexpr int kChanPerThread = 8;
+constexpr int kThreads = 256;
+constexpr int kChanPerBlock = kThreads * kChanPerThread;   // 2048
+
+struct ConvArgs {
+  const bf16* x;
+  const float* w;
+  const int32_t* cu;
+  bf16* q;
+  bf16* k;
+  bf16* v;
+  int K, num_seqs, total_tokens, h_qk, h_v, C;
+  float q_scale;
+};
+
+__device__ __forceinline__ void load8(const bf16* p, float (&x)[8]) {
+  const bf16x8 r = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)r[e];
+}
+
+// Largest n with cu[n] <= t < cu[n+1] (t < total_tokens, so such n exists).
+__device__ int find_sequence(const int32_t* cu, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  // zero-length sequences share their start with the next one; cu[lo] <= t holds and the
+  // search picked the last such n, whose end lies beyond t
+  return lo;
+}
+
+__global__ __launch_bounds__(kThreads) void conv_prep_kernel(ConvArgs a) {
+  const int c0 = blockIdx.x * kChanPerBlock + threadIdx.x * kChanPerThread;
+  const int t_begin = blockIdx.y * kTokensPerBlock;
+  if (t_begin >= a.total_tokens) return;
+  const int t_end = min(a.total_tokens, t_begin + kTokensPerBlock);
+  if (c0 >= a.C) return;          // whole 16-lane groups leave together (C % 128 == 0)
+
+  const int nq = a.h_qk * kHeadDim;
+  const int nv = a.h_v * kHeadDim;
+  const bool is_q = c0 < nq;
+  const bool is_k = !is_q && c0 < 2 * nq;
+
+  // taps: wt[0] multiplies the current token, wt[d] the token d positions earlier
+  float wt[4][8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      wt[d][e] = (d < a.K) ? a.w[(size_t)(c0 + e) * a.K + (a.K - 1 - d)] : 0.f;
+  }
+
+  int n = find_sequence(a.cu, a.num_seqs, t_begin);
+  int seq_start = a.cu[n], seq_end = a.cu[n + 1];
+
+  float h1[8], h2[8], h3[8];     // inputs at t-1, t-2, t-3 (zero before the sequence start)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h1[e] = h2[e] = h3[e] = 0.f;
+  if (t_begin - 1 >= seq_start) load8(a.x + (size_t)(t_begin - 1) * a.C + c0, h1);
+  if (t_begin - 2 >= seq_start) load8(a.x + (size_t)(t_begin - 2) * a.C + c0, h2);
+  if (t_begin - 3 >= seq_start) load8(a.x + (size_t)(t_begin - 3) * a.C + c0, h3);
+
+  for (int t = t_begin; t < t_end; ++t) {
+    if (t >= seq_end) {           // entering the next non-empty sequence: no history
+      while (a.cu[n + 1] <= t) ++n;
+      seq_start = a.cu[n];
+      seq_end = a.cu[n + 1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h1[e] = h2[e] = h3[e] = 0.f;
+    }
+    float x0[8];
+    load8(a.x + (size_t)t * a.C + c0, x0);
+    float z[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float y = wt[0][e] * x0[e] + wt[1][e] * h1[e] + wt[2][e] * h2[e] + wt[3][e] * h3[e];
+      z[e] = y / (1.f + __expf(-y));
+      ss += z[e] * z[e];
+    }
+    bf16x8 out;
+    if (is_q || is_k) {
+      ss += __shfl_xor(ss, 8, 16);
+      ss += __shfl_xor(ss, 4, 16);
+      ss += __shfl_xor(ss, 2, 16);
+      ss += __shfl_xor(ss, 1, 16);
+      const float f = (is_q ? a.q_scale : 1.f) / fmaxf(sqrtf(ss), 1e-12f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = to_bf16(z[e] * f);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = to_bf16(z[e]);
+    }
+    bf16* dst = is_q ? a.q + (size_t)t * nq + c0
+              : is_k ? a.k + (size_t)t * nq + (c0 - nq)
+                     : a.v + (size_t)t * nv + (c0 - 2 * nq);
+    *reinterpret_cast<bf16x8*>(dst) = out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { h3[e] = h2[e]; h2[e] = h1[e]; h1[e] = x0[e]; }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_conv_prep(const void* mixed, const float* w, int K, const int32_t* cu,
+                            int num_seqs, int total_tokens, int h_qk, int h_v, float q_scale,
+                            void* q, void* k, void* v, hipStream_t stream) {
+  if (total_tokens == 0) return hipSuccess;
+  ConvArgs a;
+  a.x = static_cast<const bf16*>(mixed);
+  a.w = w;
+  a.cu = cu;
+  a.q = static_cast<bf16*>(q);
+  a.k = static_cast<bf16*>(k);
+  a.v = static_cast<bf16*>(v);
+  a.K = K;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.h_qk = h_qk;
+  a.h_v = h_v;
+  a.C = (2 * h_qk + h_v) * kHeadDim;
+  a.q_scale = q_scale;
+  const dim3 grid((a.C + kChanPerBlock - 1) / kChanPerBlock,
+                  (total_tokens + kTokensPerBlock - 1) / kTokensPerBlock);
+  hipLaunchKernelGGL(conv_prep_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,106 @@
+// gdn_api.cpp -- the C ABI of libgdn.so: host-side validation and dispatch.
+//
+// Every entry point validates its arguments before touching the HIP runtime, so a rejected
+// call launches nothing and writes nothing. Launch errors are reported as GDN_ERR_HIP.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include "gdn_launch.h"
+
+namespace {
+
+constexpr int32_t kHead = 128;
+
+bool heads_ok(int32_t h_qk, int32_t h_v) { return h_qk > 0 && h_v > 0 && h_v % h_qk == 0; }
+
+gdn_status check_common(int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v) {
+  if (h_qk <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_SHAPE;
+  if (!heads_ok(h_qk, h_v)) return GDN_ERR_SHAPE;
+  if (d_k != kHead || d_v != kHead) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: a size is negative or inconsistent";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: valid but not implemented";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown gdn_status";
+}
+
+size_t gdn_chunk_prefill_workspace_bytes(int32_t total_tokens, int32_t num_seqs, int32_t h_qk,
+                                         int32_t h_v, int32_t d_k, int32_t d_v) {
+  (void)total_tokens; (void)num_seqs; (void)h_qk; (void)h_v; (void)d_k; (void)d_v;
+  return 0;
+}
+
+gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
+                             const float* g, const float* beta,
+                             const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                             int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, float scale,
+                             const float* initial_state, float* final_state,
+                             void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || total_tokens < 0) return GDN_ERR_SHAPE;
+  const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
+  if (!cu_seqlens) return GDN_ERR_NULL;
+  if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+  const size_t need = gdn_chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v, d_k, d_v);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
+  if (!final_state && total_tokens == 0) return GDN_OK;   // nothing observable to do
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (io_dtype == GDN_F32)
+    return from_hip(gdn::launch_recurrent_prefill(q, k, v, false, g, beta, cu_seqlens, num_seqs,
+                                                  h_qk, h_v, scale, initial_state, final_state,
+                                                  o, s));
+  return from_hip(gdn::launch_chunk_prefill(q, k, v, g, beta, cu_seqlens, num_seqs, h_qk, h_v,
+                                            scale, initial_state, final_state, o, s));
+}
+
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
+                           const float* g, const float* beta,
+                           float* state_pool, const int32_t* state_slots,
+                           int32_t num_seqs, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+                           float scale, void* o, void* stream) {
+  if (num_seqs < 0) return GDN_ERR_SHAPE;
+  const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return GDN_OK;
+  if (!q || !k || !v || !g || !beta || !state_pool || !o) return GDN_ERR_NULL;
+  return from_hip(gdn::launch_decode(q, k, v, io_dtype == GDN_BF16, g, beta, state_pool,
+                                     state_slots, num_seqs, h_qk, h_v, scale, o,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_conv_prep(const void* mixed_qkv, const float* conv_weight, int32_t conv_kernel,
+                         const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                         int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, float q_scale,
+                         void* q, void* k, void* v, void* stream) {
+  if (num_seqs < 0 || total_tokens < 0) return GDN_ERR_SHAPE;
+  const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  if (conv_kernel < 1) return GDN_ERR_SHAPE;
+  if (conv_kernel > 4) return GDN_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
+  if (total_tokens == 0) return GDN_OK;
+  if (!mixed_qkv || !conv_weight || !cu_seqlens || !q || !k || !v) return GDN_ERR_NULL;
+  return from_hip(gdn::launch_conv_prep(mixed_qkv, conv_weight, conv_kernel, cu_seqlens, num_seqs,
+                                        total_tokens, h_qk, h_v, q_scale, q, k, v,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// gdn_launch.h -- internal launchers behind the C ABI (arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// One decode step over an fp32 state pool, in place (recurrent.hip).
+hipError_t launch_decode(const void* q, const void* k, const void* v, bool io_bf16,
+                         const float* g, const float* beta, float* pool, const int32_t* slots,
+                         int num_seqs, int h_qk, int h_v, float scale, void* o,
+                         hipStream_t stream);
+
+// Token-sequential prefill with the state on chip (recurrent.hip); used for fp32 I/O.
+hipError_t launch_recurrent_prefill(const void* q, const void* k, const void* v, bool io_bf16,
+                                    const float* g, const float* beta, const int32_t* cu_seqlens,
+                                    int num_seqs, int h_qk, int h_v, float scale,
+                                    const float* s0, float* s_final, void* o, hipStream_t stream);
+
+// Chunked bf16 prefill on the matrix cores (chunk_prefill.hip).
+hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const int32_t* cu_seqlens, int num_seqs,
+                                int h_qk, int h_v, float scale, const float* s0,
+                                float* s_final, void* o, hipStream_t stream);
+
+// Causal depthwise conv + SiLU + q/k L2 norm + q scale (conv_prep.hip).
+hipError_t launch_conv_prep(const void* mixed, const float* w, int K, const int32_t* cu,
+                            int num_seqs, int total_tokens, int h_qk, int h_v, float q_scale,
+                            void* q, void* k, void* v, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,172 @@
+// recurrent.hip -- token-sequential gated delta rule on gfx950, no matrix cores.
+//
+// One workgroup of 256 threads owns one (sequence, V head) state of 128 x 128 fp32 (64 KB)
+// and keeps it in registers: thread (wave w, lane l) holds columns 4*(l%32) .. +3 of the
+// 16 rows i*8 + 2*w + l/32, i = 0..15, so each load or store instruction of a wave covers
+// two whole rows (1 KB, fully coalesced). Per token (page "Qwen3-Next -- How a running
+// memory and a searchable history cooperate", section "Correcting a memory instead of
+// adding to it", with the read-out after the update of the "01 . GatedDeltaNet(config)"
+// token loop on page "Qwen3-Next 80B-A3B -- The Evolving Transformer"):
+//
+//   u = S k,  r = S q                      (row dot products, reduced over 32 lanes)
+//   c = beta * (v - alpha * u)             (the correction of the decayed memory)
+//   S <- alpha * S + c k^T
+//   o = scale * S q = scale * (alpha * r + c * (k . q))
+//
+// Two uses:
+//  * decode: one token per sequence, the state streamed from and back to an fp32 pool in
+//    HBM (64 KB read + 64 KB written per head; the kernel is bound by HBM bandwidth);
+//  * fp32 prefill: all tokens of a sequence with the state held on chip between tokens.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kRowsPerThread = 16;   // 128 rows / (4 waves * 2 half-waves)
+
+struct RecArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const int32_t* cu_seqlens;   // prefill: sequence spans; decode: unused
+  const int32_t* slots;        // decode: pool entry per sequence (NULL = identity)
+  const float* s_in;           // prefill: initial states or NULL; decode: the pool
+  float* s_out;                // prefill: final states or NULL; decode: the pool
+  void* o;
+  int num_seqs, h_qk, h_v;
+  float scale;
+};
+
+// Reduce-scatter of 32 partial sums over the 32 lanes of a half-wave: afterwards
+// vals[0] of lane c holds the half-wave total of index c. 31 exchanges instead of 160.
+__device__ __forceinline__ float reduce_scatter32(float (&vals)[32], int lane32) {
+#pragma unroll
+  for (int m = 16, n = 32; m >= 1; m >>= 1, n >>= 1) {
+    const bool upper = (lane32 & m) != 0;
+#pragma unroll
+    for (int idx = 0; idx < n / 2; ++idx) {
+      const float send = upper ? vals[idx] : vals[idx + n / 2];
+      const float keep = upper ? vals[idx + n / 2] : vals[idx];
+      vals[idx] = keep + __shfl_xor(send, m, 32);
+    }
+  }
+  return vals[0];
+}
+
+template <typename IO, bool kDecode>
+__global__ __launch_bounds__(256) void recurrent_kernel(RecArgs a) {
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int c4 = lane & 31;                 // this thread's 4 columns: 4*c4 .. 4*c4+3
+  const int n = blockIdx.x / a.h_v;
+  const int h = blockIdx.x % a.h_v;
+  const int j = h / (a.h_v / a.h_qk);       // QK head read by V head h
+  const IO* q = static_cast<const IO*>(a.q);
+  const IO* k = static_cast<const IO*>(a.k);
+  const IO* v = static_cast<const IO*>(a.v);
+  IO* o = static_cast<IO*>(a.o);
+
+  int t0, t1;
+  size_t state_in, state_out;
+  if (kDecode) {
+    t0 = n;
+    t1 = n + 1;
+    const int slot = a.slots ? a.slots[n] : n;
+    state_in = state_out = ((size_t)slot * a.h_v + h) * kHeadDim * kHeadDim;
+  } else {
+    t0 = a.cu_seqlens[n];
+    t1 = a.cu_seqlens[n + 1];
+    state_in = state_out = ((size_t)n * a.h_v + h) * kHeadDim * kHeadDim;
+  }
+  const int row_base = w * 2 + half;        // rows row_base + 8*i
+
+  f32x4 S[kRowsPerThread];
+  if (a.s_in) {
+    const float* src = a.s_in + state_in + (size_t)row_base * kHeadDim + 4 * c4;
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i)
+      S[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (size_t)i * 8 * kHeadDim));
+  } else {
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Lane c4 of each half-wave finishes row slot c4/2 (even lane: u, odd lane: r).
+  const int my_slot = c4 >> 1;
+  const int my_row = row_base + 8 * my_slot;
+  const bool my_is_r = (c4 & 1) != 0;
+
+  for (int t = t0; t < t1; ++t) {
+    const size_t qk_off = ((size_t)t * a.h_qk + j) * kHeadDim + 4 * c4;
+    const f32x4 k4 = load4(k + qk_off);
+    const f32x4 q4 = load4(q + qk_off);
+    const float alpha = __expf(a.g[(size_t)t * a.h_v + h]);
+    const float beta = a.beta[(size_t)t * a.h_v + h];
+    const float vrow = load1(v + ((size_t)t * a.h_v + h) * kHeadDim + my_row);
+
+    float vals[32];
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      vals[2 * i] = S[i][0] * k4[0] + S[i][1] * k4[1] + S[i][2] * k4[2] + S[i][3] * k4[3];
+      vals[2 * i + 1] = S[i][0] * q4[0] + S[i][1] * q4[1] + S[i][2] * q4[2] + S[i][3] * q4[3];
+    }
+    const float mine = reduce_scatter32(vals, c4);
+    const float other = __shfl_xor(mine, 1, 32);
+    const float u = my_is_r ? other : mine;
+    const float r = my_is_r ? mine : other;
+    const float kq = half_wave_sum(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
+    const float c = beta * (vrow - alpha * u);
+    if (my_is_r) store1(o + ((size_t)t * a.h_v + h) * kHeadDim + my_row, a.scale * (alpha * r + c * kq));
+
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const float ci = __shfl(c, 2 * i, 32);
+      S[i][0] = alpha * S[i][0] + ci * k4[0];
+      S[i][1] = alpha * S[i][1] + ci * k4[1];
+      S[i][2] = alpha * S[i][2] + ci * k4[2];
+      S[i][3] = alpha * S[i][3] + ci * k4[3];
+    }
+  }
+
+  if (a.s_out) {
+    float* dst = a.s_out + state_out + (size_t)row_base * kHeadDim + 4 * c4;
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i)
+      __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(dst + (size_t)i * 8 * kHeadDim));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, bool io_bf16,
+                         const float* g, const float* beta, float* pool, const int32_t* slots,
+                         int num_seqs, int h_qk, int h_v, float scale, void* o,
+                         hipStream_t stream) {
+  RecArgs a{q, k, v, g, beta, nullptr, slots, pool, pool, o, num_seqs, h_qk, h_v, scale};
+  const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(256);
+  if (io_bf16)
+    hipLaunchKernelGGL((recurrent_kernel<bf16, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((recurrent_kernel<float, true>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_recurrent_prefill(const void* q, const void* k, const void* v, bool io_bf16,
+                                    const float* g, const float* beta, const int32_t* cu_seqlens,
+                                    int num_seqs, int h_qk, int h_v, float scale,
+                                    const float* s0, float* s_final, void* o, hipStream_t stream) {
+  RecArgs a{q, k, v, g, beta, cu_seqlens, nullptr, s0, s_final, o, num_seqs, h_qk, h_v, scale};
+  const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(256);
+  if (io_bf16)
+    hipLaunchKernelGGL((recurrent_kernel<bf16, false>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((recurrent_kernel<float, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

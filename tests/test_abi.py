@@ -1,0 +1,133 @@
+"""The C ABI on the CPU: libgdn.so loads, exports what include/gdn.h declares, and rejects
+bad arguments on the host before any launch (no GPU needed: validation happens first)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from linear_attention_recurrence_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libgdn.so is not built; run __graft_entry__.build()")
+    return L.load(), L
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted(["gdn_status_string", "gdn_chunk_prefill_workspace_bytes",
+                                            "gdn_chunk_prefill", "gdn_decode_step", "gdn_conv_prep"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib, L = _lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(L.EXPORTED) == set(_declared_functions())
+
+
+def test_status_strings():
+    lib, L = _lib()
+    for s in range(6):
+        assert lib.gdn_status_string(s).decode().startswith("GDN_")
+    assert lib.gdn_status_string(99) == b"unknown gdn_status"
+
+
+def test_workspace_query():
+    lib, _ = _lib()
+    assert lib.gdn_chunk_prefill_workspace_bytes(4096, 1, 16, 32, 128, 128) == 0
+
+
+def _fake(n=1):
+    # addresses are never dereferenced: every call below fails validation first
+    return ctypes.c_void_p(0x1000 * n)
+
+
+def test_decode_validation():
+    lib, L = _lib()
+    f = lib.gdn_decode_step
+    P = _fake
+    ok = dict(q=P(1), k=P(2), v=P(3), dt=L.GDN_BF16, g=P(4), b=P(5), pool=P(6), slots=None,
+              n=4, hqk=16, hv=32, dk=128, dv=128, sc=1.0, o=P(7), st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["dt"], a["g"], a["b"], a["pool"], a["slots"], a["n"],
+                 a["hqk"], a["hv"], a["dk"], a["dv"], a["sc"], a["o"], a["st"])
+
+    assert call(q=None) == L.GDN_ERR_NULL
+    assert call(pool=None) == L.GDN_ERR_NULL
+    assert call(o=None) == L.GDN_ERR_NULL
+    assert call(n=-1) == L.GDN_ERR_SHAPE
+    assert call(hv=30) == L.GDN_ERR_SHAPE
+    assert call(hqk=0) == L.GDN_ERR_SHAPE
+    assert call(dk=64) == L.GDN_ERR_UNSUPPORTED
+    assert call(dv=256) == L.GDN_ERR_UNSUPPORTED
+    assert call(dt=7) == L.GDN_ERR_UNSUPPORTED
+    assert call(n=0, q=None, pool=None) == L.GDN_OK     # nothing to do, nothing launched
+
+
+def test_prefill_validation():
+    lib, L = _lib()
+    f = lib.gdn_chunk_prefill
+    P = _fake
+    ok = dict(q=P(1), k=P(2), v=P(3), dt=L.GDN_BF16, g=P(4), b=P(5), cu=P(6), n=2, T=100,
+              hqk=16, hv=32, dk=128, dv=128, sc=0.1, s0=None, sf=None, o=P(7), ws=None, wsb=0,
+              st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["dt"], a["g"], a["b"], a["cu"], a["n"], a["T"],
+                 a["hqk"], a["hv"], a["dk"], a["dv"], a["sc"], a["s0"], a["sf"], a["o"], a["ws"],
+                 a["wsb"], a["st"])
+
+    assert call(cu=None) == L.GDN_ERR_NULL
+    assert call(k=None) == L.GDN_ERR_NULL
+    assert call(b=None) == L.GDN_ERR_NULL
+    assert call(T=-5) == L.GDN_ERR_SHAPE
+    assert call(n=-1) == L.GDN_ERR_SHAPE
+    assert call(n=0, T=10) == L.GDN_ERR_SHAPE
+    assert call(hqk=3, hv=32) == L.GDN_ERR_SHAPE
+    assert call(dk=96) == L.GDN_ERR_UNSUPPORTED
+    assert call(dt=2) == L.GDN_ERR_UNSUPPORTED
+    assert call(n=0, T=0) == L.GDN_OK
+
+
+def test_conv_prep_validation():
+    lib, L = _lib()
+    f = lib.gdn_conv_prep
+    P = _fake
+    ok = dict(x=P(1), w=P(2), K=4, cu=P(3), n=2, T=10, hqk=16, hv=32, dk=128, dv=128, qs=0.1,
+              q=P(4), k=P(5), v=P(6), st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["x"], a["w"], a["K"], a["cu"], a["n"], a["T"], a["hqk"], a["hv"], a["dk"],
+                 a["dv"], a["qs"], a["q"], a["k"], a["v"], a["st"])
+
+    assert call(x=None) == L.GDN_ERR_NULL
+    assert call(w=None) == L.GDN_ERR_NULL
+    assert call(v=None) == L.GDN_ERR_NULL
+    assert call(K=0) == L.GDN_ERR_SHAPE
+    assert call(K=5) == L.GDN_ERR_UNSUPPORTED
+    assert call(dv=64) == L.GDN_ERR_UNSUPPORTED
+    assert call(T=-1) == L.GDN_ERR_SHAPE
+    assert call(T=0) == L.GDN_OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    from linear_attention_recurrence_amd import _lib as L
+    with pytest.raises(RuntimeError, match="not built"):
+        L.load(str(tmp_path / "missing.so"))

@@ -1,0 +1,142 @@
+"""Prefill parity: libgdn's gdn_chunk_prefill against the fp64 oracle (GPU)."""
+
+import numpy as np
+import pytest
+
+import workloads
+from tests._util import (check_outputs, check_state, oracle_prefill, prefill_to_dev,
+                         to_host_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x, with_final=True, alias=False):
+    import torch
+    import linear_attention_recurrence_amd as gdn
+    d = prefill_to_dev(x)
+    N = x.num_seqs
+    fin = None
+    if alias:
+        fin = d["s0"]
+    elif with_final:
+        fin = torch.full((N, x.h_v, 128, 128), float("nan"), dtype=torch.float32, device="cuda")
+    o = gdn.gdn_chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], x.scale,
+                              initial_state=d["s0"], final_state=fin)
+    torch.cuda.synchronize()
+    return to_host_f64(o), (None if fin is None else to_host_f64(fin))
+
+
+def _compare(x, o, fin, heads=None, seqs=None, label=""):
+    ref = oracle_prefill(x, heads=heads, seqs=seqs)
+    o_sel, r_sel, s_sel, rs_sel = [], [], [], []
+    for (n, h), (o_ref, s_ref) in ref.items():
+        t0, t1 = int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1])
+        o_sel.append(o[t0:t1, h])
+        r_sel.append(o_ref)
+        if fin is not None:
+            s_sel.append(fin[n, h])
+            rs_sel.append(s_ref)
+    res = check_outputs(np.concatenate(o_sel), np.concatenate(r_sel), label)
+    if fin is not None:
+        res = res + (check_state(np.stack(s_sel), np.stack(rs_sel), label),)
+    print(label, "max|do| %.2e relF(o) %.2e" % res[:2], ("relF(S) %.2e" % res[2]) if len(res) > 2 else "")
+    return res
+
+
+@pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 128, 200])
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_prefill_small_shapes(T, with_s0):
+    x = workloads.make_prefill([T], h_qk=2, h_v=4, with_initial_state=with_s0, seed=100 + T)
+    o, fin = _run(x)
+    _compare(x, o, fin, label="T=%d s0=%s" % (T, with_s0))
+
+
+def test_prefill_varlen_with_empty_sequences():
+    lens = [0, 130, 0, 7, 64, 1, 191]
+    x = workloads.make_prefill(lens, h_qk=2, h_v=4, with_initial_state=True, seed=7)
+    o, fin = _run(x)
+    _compare(x, o, fin, label="varlen")
+    # empty sequences return their initial state unchanged
+    for n in (0, 2):
+        np.testing.assert_array_equal(fin[n], x.initial_state[n].astype(np.float64))
+
+
+def test_prefill_varlen_equals_separate_calls():
+    lens = [70, 3, 129]
+    x = workloads.make_prefill(lens, h_qk=2, h_v=4, with_initial_state=True, seed=8)
+    o, fin = _run(x)
+    for n, L in enumerate(lens):
+        t0 = int(x.cu_seqlens[n])
+        sub = workloads.PrefillInputs(
+            q=x.q[t0:t0 + L], k=x.k[t0:t0 + L], v=x.v[t0:t0 + L], g=x.g[t0:t0 + L],
+            beta=x.beta[t0:t0 + L], cu_seqlens=np.array([0, L], dtype=np.int32),
+            initial_state=x.initial_state[n:n + 1], scale=x.scale, io_dtype="bf16")
+        o1, f1 = _run(sub)
+        np.testing.assert_array_equal(o1, o[t0:t0 + L])
+        np.testing.assert_array_equal(f1[0], fin[n])
+
+
+def test_prefill_in_place_state_and_no_final():
+    x = workloads.make_prefill([100, 37], h_qk=2, h_v=4, with_initial_state=True, seed=9)
+    o_ref, fin_ref = _run(x)
+    o2, fin2 = _run(x, alias=True)
+    np.testing.assert_array_equal(o2, o_ref)
+    np.testing.assert_array_equal(fin2, fin_ref)
+    o3, _ = _run(x, with_final=False)
+    np.testing.assert_array_equal(o3, o_ref)
+
+
+def test_prefill_deterministic():
+    x = workloads.make_prefill([333], h_qk=2, h_v=4, with_initial_state=True, seed=10)
+    a = _run(x)
+    b = _run(x)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_prefill_chaining_matches_whole():
+    """prefill(T1) -> state -> prefill(T2) equals prefill(T1 + T2) (both on the GPU)."""
+    T1, T2 = 100, 157
+    x = workloads.make_prefill([T1 + T2], h_qk=2, h_v=4, with_initial_state=True, seed=11)
+    o, fin = _run(x)
+    sl = lambda a, s: a[s]
+    p1 = workloads.PrefillInputs(q=x.q[:T1], k=x.k[:T1], v=x.v[:T1], g=x.g[:T1], beta=x.beta[:T1],
+                                 cu_seqlens=np.array([0, T1], np.int32),
+                                 initial_state=x.initial_state, scale=x.scale, io_dtype="bf16")
+    o1, f1 = _run(p1)
+    p2 = workloads.PrefillInputs(q=x.q[T1:], k=x.k[T1:], v=x.v[T1:], g=x.g[T1:], beta=x.beta[T1:],
+                                 cu_seqlens=np.array([0, T2], np.int32),
+                                 initial_state=f1.astype(np.float32), scale=x.scale, io_dtype="bf16")
+    o2, f2 = _run(p2)
+    check_outputs(np.concatenate([o1, o2]), o, "chain")
+    check_state(f2, fin, "chain")
+
+
+def test_config0_fp32():
+    """B=1, T=256, 1 QK + 1 V head, fp32 I/O (token-sequential fp32 kernel)."""
+    x = workloads.config0()
+    o, fin = _run(x)
+    res = _compare(x, o, fin, label="config0")
+    assert res[1] < 1e-5 and res[2] < 1e-5     # fp32 end to end
+
+
+def test_prefill_fp32_varlen():
+    x = workloads.make_prefill([0, 5, 77], h_qk=2, h_v=4, io_dtype="f32", with_initial_state=True,
+                               seed=12)
+    o, fin = _run(x)
+    res = _compare(x, o, fin, label="f32 varlen")
+    assert res[1] < 1e-5 and res[2] < 1e-5
+
+
+def test_config1_full():
+    """B=1, T=4096, 16 QK / 32 V heads, bf16, S0 = 0: every head against the oracle."""
+    x = workloads.config1()
+    o, fin = _run(x)
+    _compare(x, o, fin, label="config1")
+
+
+def test_config2_sampled_heads():
+    """B=1, T=32768, S0 ~ N(0, 0.02): the full launch, four V heads checked by the oracle."""
+    x = workloads.config2()
+    o, fin = _run(x)
+    _compare(x, o, fin, heads=[0, 11], label="config2 heads 0,1,22,23")

@@ -9,6 +9,11 @@ section "Model Overview": 32 V heads, 16 QK heads, head dim 128):
 
 * q, k ~ N(0, 1), then divided by their L2 norm per token and head; q is *not* scaled here,
   the caller passes ``scale = 128**-0.5`` to the recurrence.
+* Large N(0, 1) tensors are drawn by inverse-transform sampling: each value is the standard
+  normal quantile at the midpoint of one of 65536 equiprobable cells, picked by a 16-bit
+  uniform from PCG64's raw output, and held at bf16 precision. This is a discretised
+  N(0, 1) (tails cut at about 4.3 sigma) that is several times faster to draw than
+  numpy's ziggurat, which matters for the 2.3-billion-element packed batch.
 * v ~ N(0, 1).
 * beta = sigmoid(N(0, 1)), so beta lies in (0, 1).
 * g = log(alpha) = -softplus(N(0, 1)) * 0.1, so alpha lies in (0, 1).
@@ -59,11 +64,38 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 # primitive draws
 # ----------------------------------------------------------------------------------------
 
+_NORMAL_TABLE = None
+
+
+def _normal_table() -> np.ndarray:
+    """bf16 bits of the N(0,1) quantiles at the midpoints of 65536 equiprobable cells."""
+    global _NORMAL_TABLE
+    if _NORMAL_TABLE is None:
+        from statistics import NormalDist
+        inv = NormalDist().inv_cdf
+        q = np.array([inv((i + 0.5) / 65536.0) for i in range(65536)], dtype=np.float32)
+        _NORMAL_TABLE = f32_to_bf16_bits(q)
+    return _NORMAL_TABLE
+
+
+def normal_bf16_bits(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0, 1) draws (inverse-transform, 16-bit cells) as bf16 bit patterns."""
+    shape = tuple(int(s) for s in np.atleast_1d(shape)) if not isinstance(shape, tuple) else shape
+    n = int(np.prod(shape)) if len(shape) else 1
+    words = rng.bit_generator.random_raw((n + 3) // 4)
+    idx = words.view(np.uint16)[:n]
+    return _normal_table()[idx].reshape(shape)
+
+
+def normal_f32(rng: np.random.Generator, shape) -> np.ndarray:
+    return bf16_bits_to_f32(normal_bf16_bits(rng, shape))
+
+
 def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
     """N(0,1) vectors along the last axis, divided by their L2 norm (fp32)."""
-    x = rng.standard_normal(shape, dtype=np.float32)
-    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
-    return (x / np.maximum(n, 1e-12)).astype(np.float32)
+    x = normal_f32(rng, shape)
+    n = np.sqrt(np.einsum("...i,...i->...", x, x, dtype=np.float32))[..., None]
+    return (x / np.maximum(n, np.float32(1e-12))).astype(np.float32)
 
 
 def _beta(rng: np.random.Generator, shape) -> np.ndarray:
@@ -128,13 +160,12 @@ def make_prefill(seq_lens, h_qk=H_QK, h_v=H_V, d_k=D_HEAD, d_v=D_HEAD, io_dtype=
     cu[1:] = np.cumsum(seq_lens)
     q = _unit_rows(rng, (T, h_qk, d_k))
     k = _unit_rows(rng, (T, h_qk, d_k))
-    v = rng.standard_normal((T, h_v, d_v), dtype=np.float32)
+    v = normal_f32(rng, (T, h_v, d_v))
     beta = _beta(rng, (T, h_v))
     g = _log_alpha(rng, (T, h_v))
     s0 = None
     if with_initial_state:
-        s0 = (rng.standard_normal((len(seq_lens), h_v, d_v, d_k), dtype=np.float32)
-              * np.float32(state_std)).astype(np.float32)
+        s0 = normal_f32(rng, (len(seq_lens), h_v, d_v, d_k)) * np.float32(state_std)
     if io_dtype == "bf16":
         q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
     elif io_dtype != "f32":
@@ -179,10 +210,10 @@ def make_decode(num_seqs=256, h_qk=H_QK, h_v=H_V, d=D_HEAD, ring=16, pool_size=N
     """A state pool and a ring of per-step single-token inputs."""
     rng = np.random.Generator(np.random.PCG64(seed))
     P = num_seqs if pool_size is None else int(pool_size)
-    pool = (rng.standard_normal((P, h_v, d, d), dtype=np.float32) * np.float32(state_std))
+    pool = normal_f32(rng, (P, h_v, d, d)) * np.float32(state_std)
     q = f32_to_bf16_bits(_unit_rows(rng, (ring, num_seqs, h_qk, d)))
     k = f32_to_bf16_bits(_unit_rows(rng, (ring, num_seqs, h_qk, d)))
-    v = f32_to_bf16_bits(rng.standard_normal((ring, num_seqs, h_v, d), dtype=np.float32))
+    v = normal_bf16_bits(rng, (ring, num_seqs, h_v, d))
     beta = _beta(rng, (ring, num_seqs, h_v))
     g = _log_alpha(rng, (ring, num_seqs, h_v))
     slots = None
@@ -234,14 +265,13 @@ def make_frontend(seq_lens, h_qk=H_QK, h_v=H_V, d_k=D_HEAD, d_v=D_HEAD, conv_ker
     mixed = np.empty((T, C), dtype=np.uint16)
     for r0 in range(0, T, block_rows):   # bounded temporaries for large batches
         r1 = min(T, r0 + block_rows)
-        mixed[r0:r1] = f32_to_bf16_bits(rng.standard_normal((r1 - r0, C), dtype=np.float32))
+        mixed[r0:r1] = normal_bf16_bits(rng, (r1 - r0, C))
     w = (rng.standard_normal((C, conv_kernel), dtype=np.float32) * np.float32(0.1))
     beta = _beta(rng, (T, h_v))
     g = _log_alpha(rng, (T, h_v))
     s0 = None
     if with_initial_state:
-        s0 = (rng.standard_normal((len(seq_lens), h_v, d_v, d_k), dtype=np.float32)
-              * np.float32(0.02))
+        s0 = normal_f32(rng, (len(seq_lens), h_v, d_v, d_k)) * np.float32(0.02)
     return FrontEndInputs(mixed=mixed, conv_weight=w, cu_seqlens=cu, g=g, beta=beta,
                           initial_state=s0, h_qk=h_qk, h_v=h_v, d_k=d_k, d_v=d_v,
                           q_scale=float(d_k ** -0.5))
