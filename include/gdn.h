@@ -58,9 +58,12 @@ typedef enum {
 const char* gdn_status_string(gdn_status s);
 
 /*
- * Bytes of device workspace gdn_chunk_prefill needs for these sizes. The current kernels
- * keep every intermediate on chip, so this returns 0; callers should still query it and
- * pass a buffer of at least that size (NULL is accepted when the answer is 0).
+ * Bytes of device workspace gdn_chunk_prefill needs (io_dtype GDN_BF16) for these sizes: for
+ * every 64-token chunk, 57856 bytes per V head (-W, the masked and decayed Q K^T, decay
+ * factors and U~ = T diag(beta) V in fp32) and 16384 bytes per QK head (K^T), sized for
+ * ceil(total_tokens / 64) + num_seqs chunks so no host read of cu_seqlens is needed.
+ * Returns 0 for invalid sizes. The contents are scratch: nothing persists between calls,
+ * and calls sharing a workspace must not overlap.
  */
 size_t gdn_chunk_prefill_workspace_bytes(int32_t total_tokens, int32_t num_seqs,
                                          int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v);
@@ -77,7 +80,8 @@ size_t gdn_chunk_prefill_workspace_bytes(int32_t total_tokens, int32_t num_seqs,
  *   initial_state [num_seqs][h_v][d_v][d_k] fp32, or NULL for zero states
  *   final_state   same shape, or NULL to skip; may alias initial_state (in-place update)
  *   o             [total_tokens][h_v][d_v]       io_dtype
- *   workspace     at least gdn_chunk_prefill_workspace_bytes(...) bytes
+ *   workspace     at least gdn_chunk_prefill_workspace_bytes(...) bytes (unused, may be
+ *                 NULL, for GDN_F32)
  *
  * Zero-length sequences are allowed: their final state is their initial state.
  * io_dtype GDN_BF16 runs the chunked kernel (chunks of 64 tokens; intra-chunk products on

@@ -41,8 +41,8 @@ const char* gdn_status_string(gdn_status s) {
 
 size_t gdn_chunk_prefill_workspace_bytes(int32_t total_tokens, int32_t num_seqs, int32_t h_qk,
                                          int32_t h_v, int32_t d_k, int32_t d_v) {
-  (void)total_tokens; (void)num_seqs; (void)h_qk; (void)h_v; (void)d_k; (void)d_v;
-  return 0;
+  if (total_tokens < 0 || num_seqs <= 0 || check_common(h_qk, h_v, d_k, d_v) != GDN_OK) return 0;
+  return gdn::chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v);
 }
 
 gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
@@ -58,16 +58,17 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dt
   if (num_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
   if (!cu_seqlens) return GDN_ERR_NULL;
   if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
-  const size_t need = gdn_chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v, d_k, d_v);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
   if (!final_state && total_tokens == 0) return GDN_OK;   // nothing observable to do
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (io_dtype == GDN_F32)
     return from_hip(gdn::launch_recurrent_prefill(q, k, v, false, g, beta, cu_seqlens, num_seqs,
                                                   h_qk, h_v, scale, initial_state, final_state,
                                                   o, s));
-  return from_hip(gdn::launch_chunk_prefill(q, k, v, g, beta, cu_seqlens, num_seqs, h_qk, h_v,
-                                            scale, initial_state, final_state, o, s));
+  const size_t need = gdn_chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v, d_k, d_v);
+  if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  return from_hip(gdn::launch_chunk_prefill(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
+                                            h_qk, h_v, scale, initial_state, final_state, o,
+                                            workspace, s));
 }
 
 gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtype io_dtype,

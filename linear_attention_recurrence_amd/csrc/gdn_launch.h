@@ -18,11 +18,14 @@ hipError_t launch_recurrent_prefill(const void* q, const void* k, const void* v,
                                     int num_seqs, int h_qk, int h_v, float scale,
                                     const float* s0, float* s_final, void* o, hipStream_t stream);
 
-// Chunked bf16 prefill on the matrix cores (chunk_prefill.hip).
+// Chunked bf16 prefill on the matrix cores (chunk_prefill.hip): a chunk table, a
+// chunk-parallel prep launch and the sequential state pass, all on `stream`.
+size_t chunk_prefill_workspace_bytes(int total_tokens, int num_seqs, int h_qk, int h_v);
 hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const int32_t* cu_seqlens, int num_seqs,
-                                int h_qk, int h_v, float scale, const float* s0,
-                                float* s_final, void* o, hipStream_t stream);
+                                int total_tokens, int h_qk, int h_v, float scale,
+                                const float* s0, float* s_final, void* o, void* workspace,
+                                hipStream_t stream);
 
 // Causal depthwise conv + SiLU + q/k L2 norm + q scale (conv_prep.hip).
 hipError_t launch_conv_prep(const void* mixed, const float* w, int K, const int32_t* cu,

@@ -43,8 +43,16 @@ def test_status_strings():
 
 
 def test_workspace_query():
+    """The documented size: per chunk 57856 B per V head and 16384 B per QK head, for
+    ceil(T / 64) + N chunks."""
     lib, _ = _lib()
-    assert lib.gdn_chunk_prefill_workspace_bytes(4096, 1, 16, 32, 128, 128) == 0
+    for T, N in ((4096, 1), (32768, 1), (276989, 64), (0, 3), (65, 2)):
+        chunks = -(-T // 64) + N
+        expect = chunks * (32 * 57856 + 16 * 16384)
+        assert lib.gdn_chunk_prefill_workspace_bytes(T, N, 16, 32, 128, 128) == expect
+    assert lib.gdn_chunk_prefill_workspace_bytes(-1, 1, 16, 32, 128, 128) == 0
+    assert lib.gdn_chunk_prefill_workspace_bytes(10, 1, 16, 30, 128, 128) == 0
+    assert lib.gdn_chunk_prefill_workspace_bytes(10, 1, 16, 32, 64, 128) == 0
 
 
 def _fake(n=1):
@@ -101,6 +109,8 @@ def test_prefill_validation():
     assert call(hqk=3, hv=32) == L.GDN_ERR_SHAPE
     assert call(dk=96) == L.GDN_ERR_UNSUPPORTED
     assert call(dt=2) == L.GDN_ERR_UNSUPPORTED
+    assert call(ws=None) == L.GDN_ERR_WORKSPACE
+    assert call(ws=P(8), wsb=1000) == L.GDN_ERR_WORKSPACE
     assert call(n=0, T=0) == L.GDN_OK
 
 
