@@ -20,13 +20,13 @@
 //    on the bf16 matrix cores, the prefix sums, the unit-lower-triangular inverse T in fp32
 //    (16 x 16 diagonal blocks by substitution, off-diagonal blocks on the fp32 matrix
 //    cores), then U~ (T diag(beta) split into hi + lo bf16) and -W on the bf16 matrix cores.
-//    Writes -W, U~ (fp32, in the accumulator layout of the state pass),
-//    P = scale (Q K^T o Gam o lower-incl), gam, gam_C / gam and K^T.
-//  * state_kernel, one workgroup per (sequence, V head, 64 value rows), walking the
-//    sequence's chunks in order with its slice of S in fp32 registers (value rows evolve
-//    independently). Per chunk: U = U~ - W S^T, Q S^T, O = scale gam (Q S^T) + P U and the
-//    state update on the bf16 matrix cores. The next chunk's -W, Q, K^T, P and U~ stream
-//    into a second LDS buffer with direct global-to-LDS loads while the current chunk
+//    Writes -W^T, P^T with P = scale (Q K^T o Gam o lower-incl), U~ (fp32, in the
+//    accumulator layout of the state pass), gam and gam_C / gam.
+//  * state_kernel, walking each sequence's chunks in order with S in fp32 registers, 16
+//    value rows per wave (value rows evolve independently): one workgroup of 8 waves per
+//    (sequence, V head), or two of 4 waves each when there are few heads. Per chunk: U = U~ - W S^T, (Q S^T)^T, O^T = scale gam (Q S^T)^T + U^T P^T
+//    and the state update on the bf16 matrix cores. The next chunk's -W^T, Q, K, P^T and U~
+//    stream into a second LDS buffer with direct global-to-LDS loads while the current chunk
 //    computes.
 //
 // Precision: every product keeps one exact bf16 operand (K, Q, V as given); T diag(beta)
@@ -36,10 +36,15 @@
 // Matrix-core layout (v_mfma_f32_16x16x32_bf16): lane l holds A[l%16][8*(l/16)+s],
 // B[8*(l/16)+s][l%16] for s = 0..7, and C[4*(l/16)+i][l%16] for i = 0..3. A product is
 // unchanged when the same permutation is applied to the K index of A and B, so a
-// C-layout accumulator pair covering K rows k0..k0+15 and k0+16..k0+31 is a valid B
-// operand once its A partner reads K entries {4g..4g+3, 16+4g..16+4g+3} (g = l/16).
-// The fp32 16x16x4 instruction has lane l holding A[l%16][l/16], B[l/16][l%16] and the
-// same C layout; the same permutation argument lets a C-layout tile feed it as B.
+// C-layout accumulator pair covering K rows k0..k0+15 and k0+16..k0+31 is a valid
+// operand once its partner reads K entries {4g..4g+3, 16+4g..16+4g+3} (g = l/16); the
+// products below use that K order. The fp32 16x16x4 instruction has lane l holding
+// A[l%16][l/16], B[l/16][l%16] and the same C layout.
+//
+// Operands whose K index runs down the rows of a row-major LDS image (K and V contracted
+// over tokens, -W^T, P^T) are read with ds_read_b64_tr_b16: within each group of 16 lanes,
+// when lane i points at row k0 + i/4, columns n0 + 4(i%4) .. +3, lane j receives rows
+// k0 .. k0+3 of column n0 + j.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -49,18 +54,18 @@ namespace {
 constexpr int kC = 64;          // chunk length
 constexpr int kD = 128;         // head dim
 constexpr int kThreads = 256;
-constexpr int kTokPad = kC + 8;     // [x][token] LDS rows, bf16
-constexpr int kRowPad = kD + 8;     // [token][d_k] LDS rows, bf16
-constexpr int kF32Pad = kC + 4;     // [token][token] LDS rows, fp32
+constexpr size_t kStateCus = 256;   // compute units of the chip
+constexpr int kTokPad = kC + 8;     // [token][token] bf16 LDS rows
+constexpr int kTokPad4 = kC + 4;    // [token][token] bf16 LDS rows, tight
+constexpr int kF32Pad = kC + 4;     // [token][token] fp32 LDS rows
 
-// Workspace: one block per (chunk, V head), then K^T per (chunk, QK head).
-constexpr size_t kWsW = 0;                          // bf16 [64][128]: -W
-constexpr size_t kWsP = kWsW + kC * kD * 2;         // bf16 [64][64]: P
+// Workspace: one block per (chunk, V head).
+constexpr size_t kWsW = 0;                          // bf16 [128][64]: -W^T
+constexpr size_t kWsP = kWsW + kC * kD * 2;         // bf16 [64][64]: P^T
 constexpr size_t kWsGam = kWsP + kC * kC * 2;       // fp32 [64]: gam_r
 constexpr size_t kWsLam = kWsGam + kC * 4;          // fp32 [64]: gam_C / gam_r
-constexpr size_t kWsU = kWsLam + kC * 4;            // fp32 U~ in C layout: [8 col tiles][4 row tiles][64 lanes][4]
+constexpr size_t kWsU = kWsLam + kC * 4;            // fp32 U~: [8 col tiles][4 row tiles][64 lanes][4]
 constexpr size_t kWsHead = kWsU + kC * kD * 4;      // 57856 bytes
-constexpr size_t kWsKT = kD * kC * 2;               // bf16 [128][64] per (chunk, QK head)
 
 __host__ __device__ inline size_t max_chunks(int total_tokens, int num_seqs) {
   return (size_t)(total_tokens + kC - 1) / kC + (size_t)num_seqs;
@@ -76,18 +81,53 @@ struct PrefillArgs {
   const float* s0;
   float* s_final;
   bf16* o;
-  uint8_t* ws_heads;        // per (chunk, V head) blocks
-  uint8_t* ws_kt;           // per (chunk, QK head) K^T
+  uint8_t* ws;              // per (chunk, V head) blocks
   int num_seqs, h_qk, h_v, group, n_chunks_max;
   float scale;
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __bf16 bf16x4_gcc __attribute__((__vector_size__(8)));
+typedef __attribute__((address_space(3))) bf16x4_gcc* lds_bf16x4_ptr;
 
 __device__ __forceinline__ bf16x8 lds8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ bf16x4 lds4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x4 lds_tr4(const bf16* p) {
+  const bf16x4_gcc r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// ---- LDS images: unpadded rows, 16-byte pieces XOR-swizzled so that the row reads, the
+// permuted-K reads and the transpose reads below all hit distinct banks.
+// 256-byte rows ([64][128] bf16): piece p of row r at slot p ^ 2(r & 7) ^ ((r >> 3) & 1).
+__device__ __forceinline__ int sw256(int r, int col) {
+  const int p = col >> 3;
+  return r * 128 + ((p ^ ((r & 7) << 1) ^ ((r >> 3) & 1)) << 3) + (col & 7);
+}
+// 128-byte rows ([R][64] bf16): piece p of row r at slot p ^ 2((r >> 1) & 3).
+__device__ __forceinline__ int sw128(int r, int col) {
+  const int p = col >> 3;
+  return r * 64 + ((p ^ (((r >> 1) & 3) << 1)) << 3) + (col & 7);
+}
+// Operand in the permuted K order with K along the image row r (the lane's M/N index).
+__device__ __forceinline__ bf16x8 perm_row256(const bf16* img, int r, int k0, int g4) {
+  return join8(lds4(img + sw256(r, k0 + 4 * g4)), lds4(img + sw256(r, k0 + 16 + 4 * g4)));
+}
+__device__ __forceinline__ bf16x8 perm_rowpad(const bf16* rowp, int k0, int g4) {
+  return join8(lds4(rowp + k0 + 4 * g4), lds4(rowp + k0 + 16 + 4 * g4));
+}
+// Operand in the permuted K order with K down the image columns (transpose reads):
+// lane (l16, g4) gets image rows {k0 + 4 g4 .. +3, k0 + 16 + 4 g4 .. +3} of column n0 + l16.
+__device__ __forceinline__ bf16x8 perm_tr256(const bf16* img, int k0, int n0, int g4, int l16) {
+  const int r = k0 + 4 * g4 + (l16 >> 2), c = n0 + 4 * (l16 & 3);
+  return join8(lds_tr4(img + sw256(r, c)), lds_tr4(img + sw256(r + 16, c)));
+}
+__device__ __forceinline__ bf16x8 perm_tr128(const bf16* img, int k0, int n0, int g4, int l16) {
+  const int r = k0 + 4 * g4 + (l16 >> 2), c = n0 + 4 * (l16 & 3);
+  return join8(lds_tr4(img + sw128(r, c)), lds_tr4(img + sw128(r + 16, c)));
 }
 
 // Chunks of a sequence: ceil(len / 64).
@@ -140,23 +180,51 @@ __device__ int first_chunk(const int32_t* cu, int n, int lane) {
   return base;
 }
 
+// Direct global -> LDS copy of rows of a [rows][128] bf16 matrix (256-byte rows) into a
+// swizzled image: instruction i of wave w fills image rows 4(4w + i) .. +3. Image row r comes
+// from source row min(r, nv - 1) at `src + row * stride`: rows past the chunk end repeat the
+// last valid row and only feed results that are discarded or multiplied by zero.
+__device__ __forceinline__ void dma_rows256(const bf16* src, size_t stride, int nv, bf16* img,
+                                            int i, int w, int lane) {
+  const int r = 4 * (4 * w + i) + (lane >> 4);
+  const int slot = lane & 15;
+  const int piece = slot ^ ((r & 7) << 1) ^ ((r >> 3) & 1);
+  const int rs = min(r, nv - 1);
+  __builtin_amdgcn_global_load_lds(src + (size_t)rs * stride + piece * 8,
+                                   (lds_void_ptr)(img + (16 * w + 4 * i) * kD), 16, 0, 0);
+}
+// Same for a contiguous [rows][64] bf16 matrix (128-byte rows): instruction i of wave w
+// fills image rows 8(nw w + i) .. +7.
+__device__ __forceinline__ void dma_rows128(const bf16* src, bf16* img, int i, int w, int nw, int lane) {
+  const int r = 8 * (nw * w + i) + (lane >> 3);
+  const int slot = lane & 7;
+  const int piece = slot ^ (((r >> 1) & 3) << 1);
+  __builtin_amdgcn_global_load_lds(src + r * kC + piece * 8, (lds_void_ptr)(img + 8 * (nw * w + i) * kC), 16, 0, 0);
+}
+
 // ------------------------------------------------------------------------------------------
 // prep_kernel: one workgroup per (chunk, V head)
 // ------------------------------------------------------------------------------------------
 struct PrepSmem {
-  bf16 KT[kD][kTokPad];         // K^T of the chunk
-  bf16 VT[kD][kTokPad];         // V^T of the chunk for this V head; later stages -W
+  bf16 K[kC * kD];              // swizzled 256-byte rows
+  bf16 V[kC * kD];              // this V head's values, swizzled
+  union {
+    bf16 Q[kC * kD];            // loads and Q K^T only; then A; then T diag(beta)
+    float A[kC][kF32Pad];
+    struct {
+      bf16 Th[kC][kTokPad4];    // T diag(beta), hi
+      bf16 Tl[kC][kTokPad4];    // T diag(beta), lo
+    } t;
+  } r1;
   union {
     struct {
-      float A[kC][kF32Pad];
       float T[kC][kF32Pad];     // T = (I + A)^-1
     } s;
     struct {
-      bf16 Th[kC][kTokPad];     // T diag(beta), hi
-      bf16 Tl[kC][kTokPad];     // T diag(beta), lo
       bf16 Tbg[kC][kTokPad];    // -T diag(beta gam)
+      bf16 pad[kC * kF32Pad * 2 - kC * kTokPad];
     } o;
-  } u;
+  } r2;
   float G[kC];
   float beta[kC];
   float gam[kC];
@@ -183,23 +251,16 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
   const int h = j * a.group + gi;
   const int t0 = a.cu[n] + local * kC;
   const int nv = min(kC, a.cu[n + 1] - t0);
-  uint8_t* wsh = a.ws_heads + ((size_t)c * a.h_v + h) * kWsHead;
+  uint8_t* wsh = a.ws + ((size_t)c * a.h_v + h) * kWsHead;
 
-  // ---- loads: K^T and V^T into LDS, g, beta ----
+  // ---- loads: K, Q, V rows straight into swizzled LDS images; g, beta ----
+  const size_t qk_stride = (size_t)a.h_qk * kD;
+  const size_t v_stride = (size_t)a.h_v * kD;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int pc = tid + kThreads * i;          // 1024 pieces of 8 bf16
-    const int row = pc >> 4, cb = pc & 15;
-    bf16x8 kv = {}, vv = {};
-    if (row < nv) {
-      kv = *reinterpret_cast<const bf16x8*>(a.k + ((size_t)(t0 + row) * a.h_qk + j) * kD + cb * 8);
-      vv = *reinterpret_cast<const bf16x8*>(a.v + ((size_t)(t0 + row) * a.h_v + h) * kD + cb * 8);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sm.KT[cb * 8 + e][row] = kv[e];
-      sm.VT[cb * 8 + e][row] = vv[e];
-    }
+    dma_rows256(a.k + (size_t)t0 * qk_stride + (size_t)j * kD, qk_stride, nv, sm.K, i, w, lane);
+    dma_rows256(a.q + (size_t)t0 * qk_stride + (size_t)j * kD, qk_stride, nv, sm.r1.Q, i, w, lane);
+    dma_rows256(a.v + (size_t)t0 * v_stride + (size_t)h * kD, v_stride, nv, sm.V, i, w, lane);
   }
   if (tid < kC) {
     float gg = 0.f, bb = 0.f;
@@ -210,16 +271,9 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
     sm.G[tid] = gg;
     sm.beta[tid] = bb;
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (gi == 0) {   // K^T for the state pass, rows of 64 tokens
-    uint8_t* kt = a.ws_kt + ((size_t)c * a.h_qk + j) * kWsKT;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pc = tid + kThreads * i;        // 1024 pieces: row = d_k, 8 tokens each
-      const int row = pc >> 3, cb = pc & 7;
-      *reinterpret_cast<bf16x8*>(kt + ((size_t)row * kC + cb * 8) * 2) = lds8(&sm.KT[row][cb * 8]);
-    }
-  }
+
   // ---- prefix sum of log-decays ----
   if (w == 0) {
     float x = sm.G[lane];
@@ -235,62 +289,75 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
     reinterpret_cast<float*>(wsh + kWsGam)[lane] = gm;
     reinterpret_cast<float*>(wsh + kWsLam)[lane] = __expf(GC - x);
   }
-  __syncthreads();
 
-  // ---- K K^T -> A, Q K^T -> P: 10 lower tiles each, operands straight from memory ----
-  bf16* P = reinterpret_cast<bf16*>(wsh + kWsP);
-  for (int job = w; job < 20; job += 4) {
+  // ---- K K^T and Q K^T: the 10 lower tiles of each, 5 per wave, held in registers ----
+  f32x4 acc[5];
+#pragma unroll
+  for (int jj = 0; jj < 5; ++jj) {
+    const int job = w + 4 * jj;
     const bool isq = job >= 10;
     const int t = isq ? job - 10 : job;
     const int rt = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
     const int ct = t - rt * (rt + 1) / 2;
-    const int ra = 16 * rt + l16, rb = 16 * ct + l16;
-    const bf16* arow = (isq ? a.q : a.k) + ((size_t)(t0 + ra) * a.h_qk + j) * kD;
-    const bf16* brow = a.k + ((size_t)(t0 + rb) * a.h_qk + j) * kD;
-    bf16x8 av[4], bv[4];
+    const bf16* Am = isq ? sm.r1.Q : sm.K;
+    acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      av[ks] = ra < nv ? lds8(arow + 32 * ks + 8 * g4) : bf16x8{};
-      bv[ks] = rb < nv ? lds8(brow + 32 * ks + 8 * g4) : bf16x8{};
-    }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < 4; ++ks)
+      acc[jj] = mfma16x16x32(lds8(Am + sw256(16 * rt + l16, 32 * ks + 8 * g4)),
+                             lds8(sm.K + sw256(16 * ct + l16, 32 * ks + 8 * g4)), acc[jj]);
+  }
+  __syncthreads();   // Q is consumed (its space becomes A) and G is ready
+  bf16* Pt = reinterpret_cast<bf16*>(wsh + kWsP);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(av[ks], bv[ks], acc);
+  for (int jj = 0; jj < 5; ++jj) {
+    const int job = w + 4 * jj;
+    const bool isq = job >= 10;
+    const int t = isq ? job - 10 : job;
+    const int rt = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+    const int ct = t - rt * (rt + 1) / 2;
     const int s = 16 * ct + l16;
+    f32x4 val;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rt + 4 * g4 + i;
       const float decay = __expf(fminf(sm.G[r] - sm.G[s], 0.f));
-      if (isq) P[r * kC + s] = to_bf16(s <= r ? a.scale * decay * acc[i] : 0.f);
-      else sm.u.s.A[r][s] = s < r ? sm.beta[r] * decay * acc[i] : 0.f;
+      if (isq) val[i] = s <= r ? a.scale * decay * acc[jj][i] : 0.f;
+      else sm.r1.A[r][s] = s < r ? sm.beta[r] * decay * acc[jj][i] : 0.f;
+    }
+    if (isq) {   // P^T row s, tokens 16 rt + 4 g4 .. +3: one 8-byte store
+      bf16x4 pv;
+      pv[0] = to_bf16(val[0]); pv[1] = to_bf16(val[1]); pv[2] = to_bf16(val[2]); pv[3] = to_bf16(val[3]);
+      *reinterpret_cast<bf16x4*>(Pt + s * kC + 16 * rt + 4 * g4) = pv;
     }
   }
-  for (int e = tid; e < 6 * 256; e += kThreads) {   // strictly upper tiles are zero
+  for (int e = tid; e < 6 * 64; e += kThreads) {    // strictly upper tiles of P are zero
+    const int t = e >> 6, ln = e & 63;
+    const int rt = t < 3 ? 0 : t < 5 ? 1 : 2;
+    const int ct = t < 3 ? t + 1 : t < 5 ? t - 1 : 3;
+    *reinterpret_cast<bf16x4*>(Pt + (16 * ct + (ln & 15)) * kC + 16 * rt + 4 * (ln >> 4)) = bf16x4{};
+  }
+  for (int e = tid; e < 6 * 256; e += kThreads) {   // ... and of T
     const int t = e >> 8;
     const int rt = t < 3 ? 0 : t < 5 ? 1 : 2;
     const int ct = t < 3 ? t + 1 : t < 5 ? t - 1 : 3;
-    const int r = 16 * rt + ((e & 255) >> 4), s = 16 * ct + (e & 15);
-    P[r * kC + s] = to_bf16(0.f);
-    sm.u.s.T[r][s] = 0.f;
+    sm.r2.s.T[16 * rt + ((e & 255) >> 4)][16 * ct + (e & 15)] = 0.f;
   }
   __syncthreads();
 
   // ---- T = (I + A)^-1 --------------------------------------------------------------------
-  // diagonal 16 x 16 blocks: wave b inverts block b by forward substitution, lane = column
+  // diagonal 16 x 16 blocks: wave b inverts block b, lane = column, one column of A at a time
   if (lane < 16) {
     const int b0 = 16 * w, col = lane;
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.f : 0.f;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) {
-      float s = 0.f;
+    for (int m = 0; m < 15; ++m) {
 #pragma unroll
-      for (int m = 0; m < r; ++m) s += sm.u.s.A[b0 + r][b0 + m] * x[m];
-      if (r > col) x[r] = -s;
+      for (int r = m + 1; r < 16; ++r) x[r] -= sm.r1.A[b0 + r][b0 + m] * x[m];
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sm.u.s.T[b0 + r][b0 + col] = x[r];
+    for (int r = 0; r < 16; ++r) sm.r2.s.T[b0 + r][b0 + col] = x[r];
   }
   __syncthreads();
   // off-diagonal block (i, b), i = b + d:  T_ib = -T_ii * sum_{k=b}^{i-1} A_ik T_kb,
@@ -303,246 +370,311 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
       for (int kb = b; kb < i; ++kb) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          X = mfma_f32(sm.u.s.A[16 * i + l16][16 * kb + 4 * ks + g4],
-                       sm.u.s.T[16 * kb + 4 * ks + g4][16 * b + l16], X);
+          X = mfma_f32(sm.r1.A[16 * i + l16][16 * kb + 4 * ks + g4],
+                       sm.r2.s.T[16 * kb + 4 * ks + g4][16 * b + l16], X);
       }
       // X in the C layout feeds the next product as B with K order {4g + ks}
       f32x4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) Y = mfma_f32(-sm.u.s.T[16 * i + l16][16 * i + 4 * g4 + ks], X[ks], Y);
+      for (int ks = 0; ks < 4; ++ks) Y = mfma_f32(-sm.r2.s.T[16 * i + l16][16 * i + 4 * g4 + ks], X[ks], Y);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.u.s.T[16 * i + 4 * g4 + r][16 * b + l16] = Y[r];
+      for (int r = 0; r < 4; ++r) sm.r2.s.T[16 * i + 4 * g4 + r][16 * b + l16] = Y[r];
     }
     __syncthreads();
   }
 
-  // ---- operands from T: T diag(beta) as hi + lo, -T diag(beta gam) ---------------------------
-  bf16x8 hv[2], lv[2], gv[2];
+  // ---- operands from T: T diag(beta) as hi + lo (into A's space; A is consumed), and
+  // -T diag(beta gam) (into T's space once every wave has read T) --------------------------
+  bf16x8 gv[2];
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int pc = tid + kThreads * it;         // 512 pieces of 8 elements
     const int r = pc >> 3, s0 = (pc & 7) * 8;
+    bf16x8 hv, lv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float tb = sm.u.s.T[r][s0 + e] * sm.beta[s0 + e];
+      const float tb = sm.r2.s.T[r][s0 + e] * sm.beta[s0 + e];
       const bf16 hh = to_bf16(tb);
-      hv[it][e] = hh;
-      lv[it][e] = to_bf16(tb - (float)hh);
+      hv[e] = hh;
+      lv[e] = to_bf16(tb - (float)hh);
       gv[it][e] = to_bf16(-tb * sm.gam[s0 + e]);
     }
+    *reinterpret_cast<bf16x4*>(&sm.r1.t.Th[r][s0]) = bf16x4{hv[0], hv[1], hv[2], hv[3]};
+    *reinterpret_cast<bf16x4*>(&sm.r1.t.Th[r][s0 + 4]) = bf16x4{hv[4], hv[5], hv[6], hv[7]};
+    *reinterpret_cast<bf16x4*>(&sm.r1.t.Tl[r][s0]) = bf16x4{lv[0], lv[1], lv[2], lv[3]};
+    *reinterpret_cast<bf16x4*>(&sm.r1.t.Tl[r][s0 + 4]) = bf16x4{lv[4], lv[5], lv[6], lv[7]};
   }
-  __syncthreads();   // T is read; its space now holds the bf16 operands
+  __syncthreads();   // T is read; its space now holds -T diag(beta gam)
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int pc = tid + kThreads * it;
     const int r = pc >> 3, s0 = (pc & 7) * 8;
-    *reinterpret_cast<bf16x8*>(&sm.u.o.Th[r][s0]) = hv[it];
-    *reinterpret_cast<bf16x8*>(&sm.u.o.Tl[r][s0]) = lv[it];
-    *reinterpret_cast<bf16x8*>(&sm.u.o.Tbg[r][s0]) = gv[it];
+    *reinterpret_cast<bf16x8*>(&sm.r2.o.Tbg[r][s0]) = gv[it];
   }
   __syncthreads();
 
-  // ---- U~ = T diag(beta) V (hi + lo); wave w: column tiles 2w, 2w+1 -------------------------
+  // ---- U~ = T diag(beta) V (hi + lo) and -W = -T diag(beta gam) K; wave w: column tiles
+  // 2w, 2w+1. U~ goes out in the accumulator layout, -W transposed as 8-byte pieces.
   f32x4* Uw = reinterpret_cast<f32x4*>(wsh + kWsU);
+  bf16* Wt = reinterpret_cast<bf16*>(wsh + kWsW);
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc) {
     const int ct = 2 * w + cc;
+    bf16x8 bv[2], bk[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bv[ks] = perm_tr256(sm.V, 32 * ks, 16 * ct, g4, l16);
+      bk[ks] = perm_tr256(sm.K, 32 * ks, 16 * ct, g4, l16);
+    }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 au = {0.f, 0.f, 0.f, 0.f}, aw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks <= rt / 2; ++ks) {   // T is lower triangular
-        const bf16x8 bv = lds8(&sm.VT[16 * ct + l16][32 * ks + 8 * g4]);
-        acc = mfma16x16x32(lds8(&sm.u.o.Th[16 * rt + l16][32 * ks + 8 * g4]), bv, acc);
-        acc = mfma16x16x32(lds8(&sm.u.o.Tl[16 * rt + l16][32 * ks + 8 * g4]), bv, acc);
+        au = mfma16x16x32(perm_rowpad(&sm.r1.t.Th[16 * rt + l16][0], 32 * ks, g4), bv[ks], au);
+        au = mfma16x16x32(perm_rowpad(&sm.r1.t.Tl[16 * rt + l16][0], 32 * ks, g4), bv[ks], au);
+        aw = mfma16x16x32(perm_rowpad(&sm.r2.o.Tbg[16 * rt + l16][0], 32 * ks, g4), bk[ks], aw);
       }
-      Uw[(ct * 4 + rt) * 64 + lane] = acc;      // the state pass loads this lane's tile as is
+      Uw[(ct * 4 + rt) * 64 + lane] = au;
+      bf16x4 wv;
+      wv[0] = to_bf16(aw[0]); wv[1] = to_bf16(aw[1]); wv[2] = to_bf16(aw[2]); wv[3] = to_bf16(aw[3]);
+      *reinterpret_cast<bf16x4*>(Wt + (16 * ct + l16) * kC + 16 * rt + 4 * g4) = wv;
     }
   }
-  __syncthreads();   // V^T is read; its space now stages -W
+}
 
-  // ---- -W = (-T diag(beta gam)) K; wave w: column tiles 2w, 2w+1 ----------------------------
-  bf16(*Wst)[kRowPad] = reinterpret_cast<bf16(*)[kRowPad]>(&sm.VT[0][0]);
+// ------------------------------------------------------------------------------------------
+// state_kernel<NW>: NW waves of 16 value rows each per workgroup. NW = 8 covers a whole
+// (sequence, V head) with two waves per SIMD; NW = 4 covers half of one, so two workgroups
+// (on the same XCD) share a head and twice as many CUs work when there are few heads.
+// ------------------------------------------------------------------------------------------
+
+// LDS of the state pass: the shared per-chunk operands, double buffered as two separate
+// objects (so the compiler can tell that reads of one never wait for direct loads into
+// the other), and each wave's U~ tiles, single buffered.
+struct StateBuf {
+  bf16 Wt[kD * kC];      // -W^T, 128-byte rows
+  bf16 Pt[kC * kC];      // P^T, 128-byte rows
+  bf16 Q[kC * kD];       // 256-byte rows
+  bf16 K[kC * kD];       // 256-byte rows
+  float gl[2 * kC];      // gam, then gam_C / gam
+};
+
+// Per-lane LDS element offsets, computed once (the swizzles keep K-steps, row tiles, the
+// second half of a permuted operand and the buffer index out of the lane-dependent part).
+struct LaneOffsets {
+  int q[4][2];      // Q row reads: K-step ks, half
+  int t128[4];      // -W^T and P^T transpose reads: column tile
+  int k[8];         // K transpose reads: column tile
+};
+
+__device__ __forceinline__ void lane_offsets(LaneOffsets& o, int g4, int l16) {
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc) {
-    const int ct = 2 * w + cc;
+  for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int hf = 0; hf < 2; ++hf) o.q[ks][hf] = sw256(l16, 32 * ks + 16 * hf + 4 * g4);
+  const int rr = 4 * g4 + (l16 >> 2), cc = 4 * (l16 & 3);
 #pragma unroll
-      for (int ks = 0; ks <= rt / 2; ++ks)
-        acc = mfma16x16x32(lds8(&sm.u.o.Tbg[16 * rt + l16][32 * ks + 8 * g4]),
-                           lds8(&sm.KT[16 * ct + l16][32 * ks + 8 * g4]), acc);
+  for (int x = 0; x < 4; ++x) o.t128[x] = sw128(rr, 16 * x + cc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Wst[16 * rt + 4 * g4 + i][16 * ct + l16] = to_bf16(acc[i]);
-    }
+  for (int x = 0; x < 8; ++x) o.k[x] = sw256(rr, 16 * x + cc);
+}
+
+// This wave's share of the direct loads of one chunk. The NW waves of a workgroup split
+// the sixteen 1 KB instructions of each 16 KB image (-W^T, Q, K) and the eight of P^T;
+// every wave brings its own 4 KB of U~. `ni` = 16 / NW instructions per image.
+struct DmaPlan {
+  int wt[8];        // -W^T source offsets (elements)
+  int pt[4];        // P^T source offsets (elements)
+  int qk_row[8];    // Q / K source rows within the chunk
+  int qk_piece[8];  // Q / K source element offsets within the row
+  int ni;
+};
+
+__device__ __forceinline__ void dma_plan(DmaPlan& d, int ni, int w, int lane) {
+  d.ni = ni;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * (ni * w + i) + (lane >> 3);
+    d.wt[i] = r * kC + ((lane & 7) ^ (((r >> 1) & 3) << 1)) * 8;
+    const int rq = 4 * (ni * w + i) + (lane >> 4);
+    d.qk_row[i] = rq;
+    d.qk_piece[i] = ((lane & 15) ^ ((rq & 7) << 1) ^ ((rq >> 3) & 1)) * 8;
   }
-  __syncthreads();
-  bf16* Wg = reinterpret_cast<bf16*>(wsh + kWsW);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int pc = tid + kThreads * i;          // 1024 pieces of 8
-    const int row = pc >> 4, cb = pc & 15;
-    *reinterpret_cast<bf16x8*>(Wg + row * kD + cb * 8) = lds8(&Wst[row][cb * 8]);
+    const int rp = 8 * ((ni / 2) * w + i) + (lane >> 3);
+    d.pt[i] = rp * kC + ((lane & 7) ^ (((rp >> 1) & 3) << 1)) * 8;
   }
 }
 
-// ------------------------------------------------------------------------------------------
-// state_kernel: one workgroup per (sequence, V head, 64 * NT value rows)
-// ------------------------------------------------------------------------------------------
-// LDS image of one chunk's shared operands. Rows are unpadded; 16-byte pieces are XOR
-// swizzled so the operand reads below hit distinct banks: in a 256-byte row (W, Q) piece p
-// of row r sits at slot p ^ (r & 15); in a 128-byte row (K^T, P) at slot p ^ ((r >> 1) & 7).
-struct StateBuf {
-  bf16 W[kC * kD];      // -W
-  bf16 Q[kC * kD];
-  bf16 KT[kD * kC];
-  bf16 P[kC * kC];
-  f32x4 U[4][4][64];    // U~ of the 64 value rows: [wave's column tile][row tile][lane]
-  float gam[kC];
-  float lam[kC];
+// Sources and destinations of one chunk's direct loads.
+struct DmaChunk {
+  const bf16* wt;
+  const bf16* pt;
+  const bf16* qb;       // row 0 of the chunk, this QK head
+  const bf16* kb;
+  const f32x4* u;       // this wave's U~ tiles
+  const float* gl;
+  bf16* d_wt;           // LDS destinations
+  bf16* d_pt;
+  bf16* d_q;
+  bf16* d_k;
+  f32x4* d_u;
+  float* d_gl;
+  int nv;               // valid rows of the chunk
 };
 
-__device__ __forceinline__ int sw256(int r, int piece) { return r * 128 + ((piece ^ (r & 15)) << 3); }
-__device__ __forceinline__ int sw128(int r, int piece) { return r * 64 + ((piece ^ ((r >> 1) & 7)) << 3); }
+// Number of direct-load instructions per wave per chunk: U~, the three 16 KB images, P^T,
+// and the decay factors.
+__device__ __forceinline__ constexpr int dma_pieces(int ni) { return 4 + 3 * ni + ni / 2 + 1; }
 
-// A operand, K order {4g..4g+3, 16+4g..16+4g+3} + k0, from a swizzled 256-byte-row image
-__device__ __forceinline__ bf16x8 perm256(const bf16* img, int r, int k0, int g4) {
-  const int k1 = k0 + 4 * g4, k2 = k1 + 16;
-  return join8(lds4(img + sw256(r, k1 >> 3) + (k1 & 7)), lds4(img + sw256(r, k2 >> 3) + (k2 & 7)));
+// Issues direct-load instruction p (0 <= p < dma_pieces) of a chunk. p is a constant once
+// the callers' loops unroll, so each call folds to one instruction.
+__device__ __forceinline__ void dma_piece(int p, const DmaChunk& d, const DmaPlan& dp, int qk_stride,
+                                          int w, int lane) {
+  const int ni = dp.ni;
+  if (p < 4) {
+    __builtin_amdgcn_global_load_lds(d.u + p * 64 + lane, (lds_void_ptr)(d.d_u + p * 64), 16, 0, 0);
+    return;
+  }
+  p -= 4;
+  if (p < 3 * ni) {
+    const int i = p / 3, which = p % 3;
+    if (which == 0) {
+      __builtin_amdgcn_global_load_lds(d.wt + dp.wt[i], (lds_void_ptr)(d.d_wt + 8 * (ni * w + i) * kC), 16, 0, 0);
+    } else {
+      // rows past the chunk end repeat the last valid row and only feed discarded results
+      const int row = dp.qk_row[i] < d.nv ? dp.qk_row[i] : d.nv - 1;
+      const int off = row * qk_stride + dp.qk_piece[i];
+      if (which == 1)
+        __builtin_amdgcn_global_load_lds(d.qb + off, (lds_void_ptr)(d.d_q + 4 * (ni * w + i) * kD), 16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(d.kb + off, (lds_void_ptr)(d.d_k + 4 * (ni * w + i) * kD), 16, 0, 0);
+    }
+    return;
+  }
+  p -= 3 * ni;
+  if (p < ni / 2) {
+    __builtin_amdgcn_global_load_lds(d.pt + dp.pt[p], (lds_void_ptr)(d.d_pt + 8 * ((ni / 2) * w + p) * kC), 16, 0, 0);
+    return;
+  }
+  if (w == 0 && lane < 32)   // gam then lam, 512 contiguous bytes
+    __builtin_amdgcn_global_load_lds(d.gl + lane * 4, (lds_void_ptr)d.d_gl, 16, 0, 0);
 }
-__device__ __forceinline__ bf16x8 perm128(const bf16* img, int r, int k0, int g4) {
-  const int k1 = k0 + 4 * g4, k2 = k1 + 16;
-  return join8(lds4(img + sw128(r, k1 >> 3) + (k1 & 7)), lds4(img + sw128(r, k2 >> 3) + (k2 & 7)));
+
+// Direct loads of chunk slot s of the twelve slots a chunk's compute offers (one per
+// K-step of U, per read-out tile and per pair of state tiles), spread evenly.
+template <int NI>
+__device__ __forceinline__ void dma_slot(int s, bool on, const DmaChunk& d, const DmaPlan& dp,
+                                         int qk_stride, int w, int lane) {
+  constexpr int P = dma_pieces(NI);
+  if (!on) return;
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (p * 12 / P == s) dma_piece(p, d, dp, qk_stride, w, lane);
 }
 
-// Direct global -> LDS loads of chunk c's operands into `buf`; every wave issues its share,
-// in four parts (part 0..3) so they can be spread over the math of the current chunk.
-struct DmaSrc {
-  const bf16* W;
-  const bf16* P;
-  const float* G;
-  const bf16* K;
-  const f32x4* U;
-  int t0, nv;
-};
-
-__device__ __forceinline__ DmaSrc dma_src(const PrefillArgs& a, int c, int t0, int nv, int h, int j,
-                                          int dvb, int w) {
-  const uint8_t* head = a.ws_heads + ((size_t)c * a.h_v + h) * kWsHead;
-  DmaSrc d;
-  d.W = reinterpret_cast<const bf16*>(head + kWsW);
-  d.P = reinterpret_cast<const bf16*>(head + kWsP);
-  d.G = reinterpret_cast<const float*>(head + kWsGam);
-  d.U = reinterpret_cast<const f32x4*>(head + kWsU) + (size_t)(4 * dvb + w) * 4 * 64;
-  d.K = reinterpret_cast<const bf16*>(a.ws_kt + ((size_t)c * a.h_qk + j) * kWsKT);
-  d.t0 = t0;
-  d.nv = nv;
+__device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& dst, f32x4* dst_u, int c,
+                                              int t0, int t_seq1, int h, int j, int col0) {
+  DmaChunk d;
+  const uint8_t* head = a.ws + ((size_t)c * a.h_v + h) * kWsHead;
+  const size_t qk_stride = (size_t)a.h_qk * kD;
+  d.wt = reinterpret_cast<const bf16*>(head + kWsW);
+  d.pt = reinterpret_cast<const bf16*>(head + kWsP);
+  d.qb = a.q + (size_t)t0 * qk_stride + (size_t)j * kD;
+  d.kb = a.k + (size_t)t0 * qk_stride + (size_t)j * kD;
+  d.u = reinterpret_cast<const f32x4*>(head + kWsU) + (size_t)(col0 >> 4) * 4 * 64;
+  d.gl = reinterpret_cast<const float*>(head + kWsGam);
+  d.d_wt = dst.Wt;
+  d.d_pt = dst.Pt;
+  d.d_q = dst.Q;
+  d.d_k = dst.K;
+  d.d_u = dst_u;
+  d.d_gl = dst.gl;
+  d.nv = min(kC, t_seq1 - t0);
   return d;
 }
 
-__device__ __forceinline__ void dma_part(const PrefillArgs& a, const DmaSrc& d, StateBuf& buf, int part,
-                                         int j, int w, int lane) {
-  // part i: W and Q rows of instruction i, K^T rows of instruction i, P (parts 0-1) or U~
-  // (parts 2-3), and gam/lam with part 0
-  const int i = part;
-  {
-    // 256-byte rows: one instruction fills 4 rows
-    const int r = 4 * (4 * w + i) + (lane >> 4), slot = lane & 15, piece = slot ^ (r & 15);
-    __builtin_amdgcn_global_load_lds(d.W + r * kD + piece * 8, (lds_void_ptr)&buf.W[16 * kD * w + 4 * kD * i], 16, 0, 0);
-    const int rq = min(r, d.nv - 1);   // rows past the chunk end only feed unstored outputs
-    __builtin_amdgcn_global_load_lds(a.q + ((size_t)(d.t0 + rq) * a.h_qk + j) * kD + piece * 8,
-                                     (lds_void_ptr)&buf.Q[16 * kD * w + 4 * kD * i], 16, 0, 0);
-    // 128-byte rows: one instruction fills 8 rows
-    const int rk = 8 * (4 * w + i) + (lane >> 3), sk = lane & 7, pk = sk ^ ((rk >> 1) & 7);
-    __builtin_amdgcn_global_load_lds(d.K + rk * kC + pk * 8, (lds_void_ptr)&buf.KT[32 * kC * w + 8 * kC * i], 16, 0, 0);
-  }
-  if (i < 2) {
-    const int rp = 8 * (2 * w + i) + (lane >> 3), sp = lane & 7, pp = sp ^ ((rp >> 1) & 7);
-    __builtin_amdgcn_global_load_lds(d.P + rp * kC + pp * 8, (lds_void_ptr)&buf.P[16 * kC * w + 8 * kC * i], 16, 0, 0);
-  } else {
-    // this wave's U~ column tile: 4 row tiles of 64 lanes x 16 bytes, already in lane order
-    const int rt = 2 * (i - 2);
-    __builtin_amdgcn_global_load_lds(d.U + rt * 64 + lane, (lds_void_ptr)&buf.U[w][rt][0], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(d.U + (rt + 1) * 64 + lane, (lds_void_ptr)&buf.U[w][rt + 1][0], 16, 0, 0);
-  }
-  if (i == 0 && w == 0 && lane < 32)   // gam then lam, 512 contiguous bytes
-    __builtin_amdgcn_global_load_lds(d.G + lane * 4, (lds_void_ptr)&buf.gam[0], 16, 0, 0);
-}
-
-__device__ __forceinline__ void dma_chunk(const PrefillArgs& a, StateBuf& buf, int c, int t0, int nv,
-                                          int h, int j, int dvb, int w, int lane) {
-  const DmaSrc d = dma_src(a, c, t0, nv, h, j, dvb, w);
-#pragma unroll
-  for (int part = 0; part < 4; ++part) dma_part(a, d, buf, part, j, w, lane);
-}
-
-// One chunk of the state pass for this wave's 16 value rows, reading `B` and streaming the
-// next chunk into `Bn`. The outputs are formed transposed (value rows x tokens) so each lane
-// ends up with four adjacent value rows of one token: 8-byte stores.
-__device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf& B, StateBuf& Bn,
-                                            f32x4 (&St)[8], int c, int t0, int nv, int t_seq1,
-                                            bool has_next, int h, int j, int dvb, int col0, int w,
-                                            int lane) {
+// One chunk of the state pass for this wave's 16 value rows, reading LDS buffer `cur` while
+// the next chunk (`nx`, if `has_next`) streams into the other one; its loads are spread
+// over the compute so the vector-memory unit works in the background. The read-out is
+// formed transposed (value rows x tokens) so each lane ends up with four adjacent value
+// rows of one token.
+template <int NW>
+__device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf& cur, const f32x4* my_u,
+                                            const LaneOffsets& lo, const DmaPlan& dp, f32x4 (&St)[8],
+                                            const DmaChunk& nx, bool has_next, int t0, int nv, int h,
+                                            int col0, int w, int lane) {
+  constexpr int NI = 16 / NW;
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
+  const int qk_stride = a.h_qk * kD;
   __builtin_amdgcn_s_waitcnt(0);   // this chunk's direct loads have landed (own share)
   __syncthreads();                 // ... everyone's; and the other buffer is free
-  DmaSrc dn;
-  if (has_next) dn = dma_src(a, c + 1, t0 + kC, min(kC, t_seq1 - t0 - kC), h, j, dvb, w);
 
-  // S^T as bf16 operands (B operand of U, A operand of the transposed read-out)
-  bf16x8 Sb[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) Sb[ks] = pack8(St[2 * ks], St[2 * ks + 1]);
-  // U = U~ - W S^T  (token rows x value rows);  QSt = (Q S^T)^T (value rows x tokens)
+  // U = U~ - W S^T  (tokens x value rows), starting from U~
   f32x4 U[4], QSt[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    U[rt] = B.U[w][rt][lane];
+    U[rt] = my_u[rt * 64 + lane];
     QSt[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): U~ is in registers before its refill
+  __builtin_amdgcn_sched_barrier(0);
+
+  // S^T as bf16 operands (B of U, A of the transposed read-out)
+  bf16x8 Sb[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) Sb[ks] = pack8(St[2 * ks], St[2 * ks + 1]);
+  const bf16* Wt = cur.Wt;
+  const bf16* Q = cur.Q;
+  // U -= W S^T ;  QSt = (Q S^T)^T (value rows x tokens)
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
+    dma_slot<NI>(ks, has_next, nx, dp, qk_stride, w, lane);
     bf16x8 aw[4], aq[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      aw[rt] = perm256(B.W, 16 * rt + l16, 32 * ks, g4);
-      aq[rt] = perm256(B.Q, 16 * rt + l16, 32 * ks, g4);
+      aw[rt] = join8(lds_tr4(Wt + lo.t128[rt] + 2048 * ks), lds_tr4(Wt + lo.t128[rt] + 2048 * ks + 1024));
+      aq[rt] = join8(lds4(Q + lo.q[ks][0] + 2048 * rt), lds4(Q + lo.q[ks][1] + 2048 * rt));
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       U[rt] = mfma16x16x32(aw[rt], Sb[ks], U[rt]);
       QSt[rt] = mfma16x16x32(Sb[ks], aq[rt], QSt[rt]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (has_next) dma_part(a, dn, Bn, ks, j, w, lane);   // spread the next chunk's loads
-    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);   // keep each K-step's loads next to its products
   }
   // U as bf16 for the read-out; the decayed U as a hi + lo pair for the state update
+  const float* gam = &cur.gl[0];
+  const float* lam = &cur.gl[kC];
   bf16x8 Ub[2], Bh[2], Bl[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     Ub[ks] = pack8(U[2 * ks], U[2 * ks + 1]);
-    f32x4 hi[2], lo[2];
+    f32x4 hi[2], lw[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float u = U[2 * ks + hh][i] * B.lam[16 * (2 * ks + hh) + 4 * g4 + i];
+        const float u = U[2 * ks + hh][i] * lam[16 * (2 * ks + hh) + 4 * g4 + i];
         const float uh = (float)to_bf16(u);
         hi[hh][i] = uh;
-        lo[hh][i] = u - uh;
+        lw[hh][i] = u - uh;
       }
     Bh[ks] = pack8(hi[0], hi[1]);
-    Bl[ks] = pack8(lo[0], lo[1]);
+    Bl[ks] = pack8(lw[0], lw[1]);
   }
-  // O^T = scale gam (Q S^T)^T + (P U)^T = ... + U^T P^T, stored as 8-byte pieces
+  // O^T = scale gam (Q S^T)^T + U^T P^T, stored as 8-byte pieces
+  const bf16* Pt = cur.Pt;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    f32x4 acc = QSt[nt] * (a.scale * B.gam[16 * nt + l16]);
+    dma_slot<NI>(4 + nt, has_next, nx, dp, qk_stride, w, lane);
+    f32x4 acc = QSt[nt] * (a.scale * gam[16 * nt + l16]);
 #pragma unroll
-    for (int ks = 0; ks <= nt / 2; ++ks) acc = mfma16x16x32(Ub[ks], perm128(B.P, 16 * nt + l16, 32 * ks, g4), acc);
+    for (int ks = 0; ks <= nt / 2; ++ks)
+      acc = mfma16x16x32(Ub[ks], join8(lds_tr4(Pt + lo.t128[nt] + 2048 * ks), lds_tr4(Pt + lo.t128[nt] + 2048 * ks + 1024)), acc);
     const int tok = 16 * nt + l16;
     if (tok < nv) {
       bf16x4 ov;
@@ -551,62 +683,82 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
     }
   }
   // S^T <- gam_C S^T + K^T (diag(gam_C / gam) U)
-  const float gC = B.gam[kC - 1];
+  const float gC = gam[kC - 1];
+  const bf16* K = cur.K;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
-    const bf16x8 ak0 = perm128(B.KT, 16 * mt + l16, 0, g4);
-    const bf16x8 ak1 = perm128(B.KT, 16 * mt + l16, 32, g4);
+    if (!(mt & 1)) dma_slot<NI>(8 + mt / 2, has_next, nx, dp, qk_stride, w, lane);
+    const bf16x8 ak0 = join8(lds_tr4(K + lo.k[mt]), lds_tr4(K + lo.k[mt] + 2048));
+    const bf16x8 ak1 = join8(lds_tr4(K + lo.k[mt] + 4096), lds_tr4(K + lo.k[mt] + 6144));
     f32x4 s = St[mt] * gC;
     s = mfma16x16x32(ak0, Bh[0], s);
     s = mfma16x16x32(ak0, Bl[0], s);
     s = mfma16x16x32(ak1, Bh[1], s);
     St[mt] = mfma16x16x32(ak1, Bl[1], s);
+    if (mt & 1) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// One workgroup per (sequence, V head, 64 value rows); wave w owns 16 of them.
-__global__ __launch_bounds__(kThreads) void state_kernel(PrefillArgs a) {
-  // two separately declared buffers so each half of the loop reads one while the other fills
+template <int NW>
+__global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
   __shared__ StateBuf buf0;
   __shared__ StateBuf buf1;
+  __shared__ f32x4 utiles[NW][4][64];
+  constexpr int kBlocks = 8 / NW;             // workgroups per (sequence, V head)
+  constexpr int NI = 16 / NW;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int lane = tid & 63;
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
 
-  // the two value-row blocks of one (sequence, V head) sit on the same XCD (blockIdx % 8)
+  // the workgroups of the V heads sharing one QK head (same Q and K) sit on one XCD
+  const int per = 8 * a.group * kBlocks;
   const int bid = blockIdx.x;
-  const int grp = bid / 16, rem = bid % 16;
-  const int pair = grp * 8 + rem % 8;
-  const int dvb = rem / 8;
-  if (pair >= a.num_seqs * a.h_v) return;
-  const int n = pair / a.h_v, h = pair % a.h_v;
-  const int j = h / a.group;
-  const int col0 = dvb * 64 + 16 * w;              // this wave's first value row
-  const int col = col0 + l16;                      // this lane's value row in S
+  const int grp = bid / per, rem = bid % per;
+  const int p = grp * 8 + rem % 8;            // (sequence, QK head) pair
+  if (p >= a.num_seqs * a.h_qk) return;
+  const int sub = rem / 8;                    // V head within the group, value-row block
+  const int n = p / a.h_qk, j = p % a.h_qk;
+  const int h = j * a.group + sub / kBlocks;
+  const int col0 = (sub % kBlocks) * (16 * NW) + 16 * w;   // this wave's first value row
+  const int col = col0 + l16;                               // this lane's value row in S
   const int t_seq0 = a.cu[n], t_seq1 = a.cu[n + 1];
   const int n_chunks = (t_seq1 - t_seq0 + kC - 1) / kC;
   const int c_begin = first_chunk(a.cu, n, lane);
   const size_t state_off = (((size_t)n * a.h_v + h) * kD + col) * kD;
+  const int qk_stride = a.h_qk * kD;
+
+  LaneOffsets lo;
+  lane_offsets(lo, g4, l16);
+  DmaPlan dp;
+  dma_plan(dp, NI, w, lane);
 
   // St[mt][i] = S[col][16 mt + 4 g4 + i]
   f32x4 St[8];
+  if (a.s0) {
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    if (a.s0) St[mt] = *reinterpret_cast<const f32x4*>(a.s0 + state_off + 16 * mt + 4 * g4);
-    else St[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 8; ++mt) St[mt] = *reinterpret_cast<const f32x4*>(a.s0 + state_off + 16 * mt + 4 * g4);
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) St[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (n_chunks > 0) dma_chunk(a, buf0, c_begin, t_seq0, min(kC, t_seq1 - t_seq0), h, j, dvb, w, lane);
+  f32x4* my_u = &utiles[w][0][0];
+  if (n_chunks > 0) {
+    const DmaChunk d0 = dma_chunk(a, buf0, my_u, c_begin, t_seq0, t_seq1, h, j, col0);
+#pragma unroll
+    for (int s = 0; s < 12; ++s) dma_slot<NI>(s, true, d0, dp, qk_stride, w, lane);
+  }
+  // chunks alternate between the two LDS buffers
   for (int ci = 0; ci < n_chunks; ci += 2) {
     const int t0 = t_seq0 + ci * kC;
-    state_chunk(a, buf0, buf1, St, c_begin + ci, t0, min(kC, t_seq1 - t0), t_seq1,
-                ci + 1 < n_chunks, h, j, dvb, col0, w, lane);
+    const DmaChunk d1 = dma_chunk(a, buf1, my_u, c_begin + ci + 1, t0 + kC, t_seq1, h, j, col0);
+    state_chunk<NW>(a, buf0, my_u, lo, dp, St, d1, ci + 1 < n_chunks, t0, min(kC, t_seq1 - t0), h, col0, w, lane);
     if (ci + 1 < n_chunks) {
       const int t1 = t0 + kC;
-      state_chunk(a, buf1, buf0, St, c_begin + ci + 1, t1, min(kC, t_seq1 - t1), t_seq1,
-                  ci + 2 < n_chunks, h, j, dvb, col0, w, lane);
+      const DmaChunk d2 = dma_chunk(a, buf0, my_u, c_begin + ci + 2, t1 + kC, t_seq1, h, j, col0);
+      state_chunk<NW>(a, buf1, my_u, lo, dp, St, d2, ci + 2 < n_chunks, t1, min(kC, t_seq1 - t1), h, col0, w, lane);
     }
   }
 
@@ -620,8 +772,8 @@ __global__ __launch_bounds__(kThreads) void state_kernel(PrefillArgs a) {
 }  // namespace
 
 size_t chunk_prefill_workspace_bytes(int total_tokens, int num_seqs, int h_qk, int h_v) {
-  const size_t nc = max_chunks(total_tokens, num_seqs);
-  return nc * (size_t)h_v * kWsHead + nc * (size_t)h_qk * kWsKT;
+  (void)h_qk;
+  return max_chunks(total_tokens, num_seqs) * (size_t)h_v * kWsHead;
 }
 
 hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
@@ -639,10 +791,8 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
   a.s0 = s0;
   a.s_final = s_final;
   a.o = static_cast<bf16*>(o);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.ws = static_cast<uint8_t*>(workspace);
   const size_t nc = max_chunks(total_tokens, num_seqs);
-  a.ws_heads = ws;
-  a.ws_kt = ws + nc * (size_t)h_v * kWsHead;
   a.num_seqs = num_seqs;
   a.h_qk = h_qk;
   a.h_v = h_v;
@@ -655,9 +805,17 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
     const size_t prep_blocks = (pairs + 7) / 8 * 8 * (size_t)a.group;
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(kThreads), 0, stream, a);
   }
-  const size_t pairs = (size_t)num_seqs * h_v;
-  const size_t state_blocks = (pairs + 7) / 8 * 16;
-  hipLaunchKernelGGL(state_kernel, dim3((unsigned)state_blocks), dim3(kThreads), 0, stream, a);
+  // 8 / NW workgroups of NW waves per (sequence, V head): two of 4 waves spread a few
+  // heads over twice the CUs; once the heads fill the chip, one of 8 waves avoids the
+  // operand traffic that every workgroup repeats.
+  const size_t seq_pairs = (size_t)num_seqs * h_qk;
+  const size_t groups = (seq_pairs + 7) / 8 * 8 * (size_t)a.group;
+  const size_t heads = (size_t)num_seqs * h_v;
+  if (heads * 2 <= kStateCus) {
+    hipLaunchKernelGGL(state_kernel<4>, dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(state_kernel<8>, dim3((unsigned)groups), dim3(8 * kWave), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -76,6 +76,25 @@ def test_prefill_varlen_equals_separate_calls():
         np.testing.assert_array_equal(f1[0], fin[n])
 
 
+def test_prefill_many_sequences_full_heads():
+    """Enough (sequence, V head) pairs for the one-workgroup-per-head geometry of the state
+    pass; each sequence run alone takes the two-workgroups-per-head geometry, and the two
+    must agree bit for bit (same per-row arithmetic)."""
+    lens = [0, 1, 64, 65, 200, 17, 128, 0, 311, 63, 90, 5]
+    x = workloads.make_prefill(lens, h_qk=16, h_v=32, with_initial_state=True, seed=13)
+    o, fin = _run(x)
+    _compare(x, o, fin, label="12 seqs, 32 V heads")
+    for n in (4, 8):
+        L, t0 = lens[n], int(x.cu_seqlens[n])
+        sub = workloads.PrefillInputs(
+            q=x.q[t0:t0 + L], k=x.k[t0:t0 + L], v=x.v[t0:t0 + L], g=x.g[t0:t0 + L],
+            beta=x.beta[t0:t0 + L], cu_seqlens=np.array([0, L], dtype=np.int32),
+            initial_state=x.initial_state[n:n + 1], scale=x.scale, io_dtype="bf16")
+        o1, f1 = _run(sub)
+        np.testing.assert_array_equal(o1, o[t0:t0 + L])
+        np.testing.assert_array_equal(f1[0], fin[n])
+
+
 def test_prefill_in_place_state_and_no_final():
     x = workloads.make_prefill([100, 37], h_qk=2, h_v=4, with_initial_state=True, seed=9)
     o_ref, fin_ref = _run(x)
