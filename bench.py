@@ -1,19 +1,30 @@
 """Benchmark of the Gated DeltaNet mixer on one MI355X.
 
 Headline: chunked prefill throughput (tokens/s) on the Qwen3-Next layer shape, B=1, T=4096,
-16 QK heads shared by 32 V heads, head dim 128, bf16 q/k/v, S0 = 0, fp32 final states. A
-step is one gdn_chunk_prefill call over the whole batch (every step of the chunked method
-runs inside it). Alongside: decode-step HBM bandwidth on a 256-sequence fp32 state pool,
+16 QK heads shared by 32 V heads, head dim 128, bf16 q/k/v/o, S0 = 0, fp32 final states. A
+step is one gdn_chunk_prefill call over the whole batch: its two launches (the
+chunk-parallel prep and the sequential state pass) run every step of the chunked method.
+Alongside: the decode step on a 256-sequence fp32 state pool (HBM-bound, no matrix cores)
 and the packed variable-length front end + prefill. The fp64 oracle is timed on the host
 cores on the headline workload as a CPU baseline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline]
-Prints one JSON line.
+Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps K2]
+                  [--workload prefill,decode,frontend] [--no-cpu-baseline]
+      prints one JSON line
+  python bench.py --workload copy
+      a plain 1 GiB device copy, the calibration run for hardware byte counters
+  python bench.py --pmc-summary DIR
+      per-kernel averages of the counters in rocprofv3 --pmc output under DIR
 """
 
 from __future__ import annotations
 
 import argparse
+import collections
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +43,39 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
 D = 128
 C = 64
 H_QK, H_V = 16, 32
+CSRC = os.path.join(ROOT, "linear_attention_recurrence_amd", "csrc")
+
+# Hardware byte counters of one launch, from two rocprofv3 --pmc runs (FETCH_SIZE, then
+# WRITE_SIZE) of `python bench.py --workload prefill,decode,copy --steps 5 --warmup 1
+# --no-cpu-baseline`, in KiB per dispatch, scaled by what the same counters read for a
+# plain 1 GiB device copy. `sources` fingerprints the kernel sources the figures were taken
+# on: once they change, the figures no longer describe the kernel and traffic is reported
+# as null. Filled from the summaries kept under profiles/.
+COUNTER_TRAFFIC = {
+    "prefill": {"bytes": 382167363, "sources": "6762a2ebf2a156b8"},
+    "decode": {"bytes": 1083839827, "sources": "f2a9a710ebc63b27"},
+}
+
+
+def _sources_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+PREFILL_SOURCES = ("chunk_prefill.hip", "gdn_device.h")
+DECODE_SOURCES = ("recurrent.hip", "gdn_device.h")
+
+
+def counter_traffic(name, sources):
+    """Counter-measured HBM bytes per call for `name`, or None when not measured on these
+    kernel sources."""
+    rec = COUNTER_TRAFFIC.get(name)
+    if rec is None or rec["sources"] != _sources_sha(sources):
+        return None
+    return rec["bytes"]
 
 
 # ---------------------------------------------------------------------------------------
@@ -62,6 +106,7 @@ def decode_bytes(num_seqs: int, h_qk=H_QK, h_v=H_V) -> float:
 
 
 def conv_prep_bytes(tokens: int, h_qk=H_QK, h_v=H_V) -> float:
+    """HBM bytes of the front end: the mixed input read and q, k, v written (bf16)."""
     ch = 2 * h_qk * D + h_v * D
     return float(tokens) * ch * 2 * 2
 
@@ -77,28 +122,36 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def _time_launches(fn, n_launches, warmup):
-    """Runs fn(i) warmup times, then n_launches times between HIP events on torch's current
-    stream (the stream libgdn launches on). Returns (total_ms, per-launch ms list)."""
+def _timed(fn, steps, warmup):
+    """W untimed calls, then exactly `steps` calls between two device synchronisations.
+    HIP events around every call, recorded on torch's current stream (the stream the
+    binding launches on), give the per-call device durations. Returns (wall seconds of the
+    timed region, mean per-call device ms)."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_launches)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_launches)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(n_launches):
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
         starts[i].record()
         fn(i)
         ends[i].record()
-    t1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1), [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, float(np.mean(per))
 
 
-def bench_prefill_config1(steps, warmup, copies=4):
+def _workspace(total_tokens, num_seqs):
+    import torch
+    import linear_attention_recurrence_amd as gdn
+    need = gdn.gdn_chunk_prefill_workspace_bytes(total_tokens, num_seqs, H_QK, H_V, D, D)
+    return torch.empty(need, dtype=torch.uint8, device="cuda")
+
+
+def bench_prefill(steps, warmup, copies=4):
     """B=1, T=4096 prefill; `copies` input sets rotate so the 256 MB last-level cache cannot
     hold the working set across steps."""
     import torch
@@ -111,18 +164,18 @@ def bench_prefill_config1(steps, warmup, copies=4):
                          cu=_dev(x.cu_seqlens),
                          o=torch.empty((4096, H_V, D), dtype=torch.bfloat16, device="cuda"),
                          fin=torch.empty((1, H_V, D, D), dtype=torch.float32, device="cuda")))
+    ws = _workspace(4096, 1)
     scale = D ** -0.5
 
     def step(i):
         s = sets[i % copies]
         gdn.gdn_chunk_prefill(s["q"], s["k"], s["v"], s["g"], s["b"], s["cu"], scale,
-                              final_state=s["fin"], o=s["o"])
+                              final_state=s["fin"], o=s["o"], workspace=ws)
 
-    total_ms, per = _time_launches(step, steps, warmup)
-    return total_ms, per
+    return _timed(step, steps, warmup)
 
 
-def bench_decode_config3(steps, warmup):
+def bench_decode(steps, warmup):
     """256 sequences x 1 token over the 512 MiB fp32 pool, ring of 16 input sets."""
     import torch
     import linear_attention_recurrence_amd as gdn
@@ -136,11 +189,10 @@ def bench_decode_config3(steps, warmup):
         r = i % 16
         gdn.gdn_decode_step(q[r], k[r], v[r], g[r], b[r], pool, d.scale, o=o)
 
-    total_ms, per = _time_launches(step, steps, warmup)
-    return total_ms, per
+    return _timed(step, steps, warmup)
 
 
-def bench_frontend_config4(reps, warmup):
+def bench_frontend(reps, warmup):
     """64 packed sequences (lengths uniform in [128, 8192]): gdn_conv_prep then
     gdn_chunk_prefill with per-sequence initial and final states."""
     import torch
@@ -156,30 +208,67 @@ def bench_frontend_config4(reps, warmup):
     v = torch.empty((T, H_V, D), dtype=torch.bfloat16, device="cuda")
     o = torch.empty_like(v)
     fin = torch.empty_like(s0)
+    ws = _workspace(T, N)
 
     def conv(i):
         gdn.gdn_conv_prep(mixed, w, cu, H_QK, H_V, D, D, fe.q_scale, q=q, k=k, v=v)
 
     def prefill(i):
-        gdn.gdn_chunk_prefill(q, k, v, g, b, cu, 1.0, initial_state=s0, final_state=fin, o=o)
+        gdn.gdn_chunk_prefill(q, k, v, g, b, cu, 1.0, initial_state=s0, final_state=fin, o=o,
+                              workspace=ws)
 
-    conv_ms, _ = _time_launches(conv, reps, warmup)
-    pre_ms, _ = _time_launches(prefill, reps, warmup)
-    return T, N, conv_ms / reps, pre_ms / reps
+    _, conv_ms = _timed(conv, reps, warmup)
+    _, pre_ms = _timed(prefill, reps, warmup)
+    return T, N, conv_ms, pre_ms
 
 
-def cpu_baseline():
-    """The fp64 oracle, as it stands, on the headline workload (all 32 heads, T = 4096)."""
+def bench_copy(steps, warmup, nbytes=1 << 30):
+    """A plain device-to-device copy of `nbytes`: reads and writes exactly nbytes each."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    wall, ms = _timed(lambda i: dst.copy_(src), steps, warmup)
+    return nbytes, ms
+
+
+def cpu_baseline(min_core_seconds=10.0):
+    """The fp64 oracle, as it stands, on the headline workload (B=1, T=4096, all 32 heads),
+    run whole and repeated until about `min_core_seconds` of CPU work has been done."""
     import oracle
     import workloads
     x = workloads.config1()
     args = [x.as_f64(n) for n in ("q", "k", "v", "g", "beta")]
     threads = oracle.default_threads()
-    t = time.perf_counter()
-    oracle.recurrence(*args, x.cu_seqlens, x.scale, n_threads=threads)
-    dt = time.perf_counter() - t
-    return {"value": x.total_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "whole workload: B=1, T=4096, 32 V heads, fp64 token loop, %.2f s wall" % dt}
+    reps, t = 0, time.perf_counter()
+    while True:
+        oracle.recurrence(*args, x.cu_seqlens, x.scale, n_threads=threads)
+        reps += 1
+        dt = time.perf_counter() - t
+        if dt * threads >= min_core_seconds:
+            break
+    return {"value": reps * x.total_tokens / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "the whole headline workload (B=1, T=4096, 32 V heads, fp64 token loop) "
+                      "run %d times, %.2f s wall on %d threads" % (reps, dt, threads)}
+
+
+def pmc_summary(root):
+    """Per-kernel average counter values per dispatch from rocprofv3 --pmc CSV output."""
+    lines = []
+    for f in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)):
+        agg = collections.defaultdict(lambda: collections.defaultdict(float))
+        disp = collections.defaultdict(set)
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                k = r.get("Kernel_Name", "")
+                agg[k][r["Counter_Name"]] += float(r["Counter_Value"])
+                disp[k].add(r.get("Dispatch_Id", ""))
+        lines.append("== %s" % os.path.relpath(f, root))
+        for k, d in agg.items():
+            nd = max(1, len(disp[k]))
+            lines.append("  %-60s dispatches=%-4d %s" % (
+                k[:60], nd, " ".join("%s=%.6g" % (c, v / nd) for c, v in sorted(d.items()))))
+    return "\n".join(lines)
 
 
 def main():
@@ -187,60 +276,74 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--no-extras", action="store_true", help="headline prefill only")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--workload", default="prefill,decode,frontend",
+                    help="comma list of prefill, decode, frontend, copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-summary", metavar="DIR")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary))
+        return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU only: the Gated DeltaNet path here has no multi-GPU "
+              "mode (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    work = [w.strip() for w in args.workload.split(",") if w.strip()]
     import torch
     torch.cuda.set_device(0)
+    out = {}
 
-    total_ms, per = bench_prefill_config1(args.steps, args.warmup)
-    kernel_ms = float(np.mean(per))
-    tokens = 4096
-    value = tokens * args.steps / (total_ms / 1e3)
-    flops = prefill_flops(tokens)
-    nbytes = prefill_bytes(tokens, 1, with_s0=False)
-    achieved_gbs = nbytes / (kernel_ms / 1e3) / 1e9
-    achieved_tf = flops / (kernel_ms / 1e3) / 1e12
-    out = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": total_ms / args.steps,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "gated delta rule chunked prefill, B=1, T=4096, 16 QK / 32 V heads, "
-                               "d=128, chunk 64, bf16 q/k/v/o, fp32 state, S0=0, final state out",
-                   "global_batch": 1, "seq_len": tokens, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "chunk_prefill_kernel", "kernel_ms": kernel_ms,
-                     "algorithmic_bytes": nbytes},
-        "roofline_mfma": {"achieved": achieved_tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "frac": achieved_tf / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": flops},
-    }
-    if not args.no_extras:
-        dsteps = 1000
-        dtot, dper = bench_decode_config3(dsteps, 20)
-        dms = float(np.mean(dper))
+    if "prefill" in work:
+        wall, call_ms = bench_prefill(args.steps, args.warmup)
+        tokens = 4096
+        flops = prefill_flops(tokens)
+        nbytes = prefill_bytes(tokens, 1, with_s0=False)
+        achieved = nbytes / (call_ms / 1e3) / 1e9
+        traffic = counter_traffic("prefill", PREFILL_SOURCES)
+        out.update({
+            "metric": METRIC,
+            "value": tokens * args.steps / wall,
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": wall * 1e3 / args.steps,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "gated delta rule chunked prefill, B=1, T=4096, 16 QK / 32 V "
+                                   "heads, d=128, chunk 64, bf16 q/k/v/o, fp32 state, S0=0, "
+                                   "final state out",
+                       "global_batch": 1, "seq_len": tokens, "parallelism": "none (1 GPU)"},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                         "kernel": "gdn_chunk_prefill call: prep_kernel + state_kernel<4>",
+                         "call_ms": call_ms, "algorithmic_bytes": nbytes},
+            "roofline_mfma": {"achieved": flops / (call_ms / 1e3) / 1e12,
+                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": flops / (call_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                              "algorithmic_flops": flops},
+        })
+    if "decode" in work:
+        dsteps = args.decode_steps
+        wall, dms = bench_decode(dsteps, args.warmup)
         dbytes = decode_bytes(256)
-        out["decode"] = {"workload": "decode step, 256 sequences x 1 token, 16 QK / 32 V heads, "
-                                     "fp32 state pool 512 MiB in place, 1000 steps",
-                         "ms_per_step": dtot / dsteps, "kernel_ms": dms,
-                         "tokens_per_s": 256 * dsteps / (dtot / 1e3),
-                         "achieved_GBs": dbytes / (dms / 1e3) / 1e9,
-                         "frac_of_hbm_peak": dbytes / (dms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                         "algorithmic_bytes": dbytes}
-        T4, N4, conv_ms, pre_ms = bench_frontend_config4(10, 2)
+        achieved = dbytes / (dms / 1e3) / 1e9
+        out["decode"] = {
+            "workload": "decode step, 256 sequences x 1 token, 16 QK / 32 V heads, fp32 state "
+                        "pool 512 MiB updated in place, ring of 16 input sets",
+            "steps": dsteps, "ms_per_step": wall * 1e3 / dsteps,
+            "tokens_per_s": 256 * dsteps / wall,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": counter_traffic("decode", DECODE_SOURCES),
+                         "kernel": "recurrent_kernel<bf16, decode>", "kernel_ms": dms,
+                         "algorithmic_bytes": dbytes}}
+    if "frontend" in work:
+        T4, N4, conv_ms, pre_ms = bench_frontend(10, 2)
         out["frontend_prefill"] = {
             "workload": "64 packed sequences, lengths uniform in [128, 8192], conv k=4 front end "
                         "then prefill with S0 and final states",
@@ -250,9 +353,12 @@ def main():
             "conv_prep_GBs": conv_prep_bytes(T4) / (conv_ms / 1e3) / 1e9,
             "prefill_GBs": prefill_bytes(T4, N4, True) / (pre_ms / 1e3) / 1e9,
             "prefill_TFLOPs": prefill_flops(T4) / (pre_ms / 1e3) / 1e12}
-    if not args.no_cpu_baseline:
+    if "copy" in work:
+        nb, cms = bench_copy(max(5, args.steps), args.warmup)
+        out["copy"] = {"bytes_each_way": nb, "ms": cms, "GBs_read_plus_write": 2 * nb / (cms / 1e3) / 1e9}
+    if "prefill" in work and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
-    print(json.dumps(out))
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":
