@@ -20,12 +20,12 @@
 //    on the bf16 matrix cores, the prefix sums, the unit-lower-triangular inverse T in fp32
 //    (16 x 16 diagonal blocks by substitution, off-diagonal blocks on the fp32 matrix
 //    cores), then U~ (T diag(beta) split into hi + lo bf16) and -W on the bf16 matrix cores.
-//    Writes -W^T, P^T with P = scale (Q K^T o Gam o lower-incl), U~ (fp32, in the
+//    Writes -W, P^T with P = scale (Q K^T o Gam o lower-incl), U~ (fp32, in the
 //    accumulator layout of the state pass), gam and gam_C / gam.
 //  * state_kernel, walking each sequence's chunks in order with S in fp32 registers, 16
 //    value rows per wave (value rows evolve independently): one workgroup of 8 waves per
-//    (sequence, V head), or two of 4 waves each when there are few heads. Per chunk: U = U~ - W S^T, (Q S^T)^T, O^T = scale gam (Q S^T)^T + U^T P^T
-//    and the state update on the bf16 matrix cores. The next chunk's -W^T, Q, K, P^T and U~
+//    (sequence, V head), or two of 4 or four of 2 waves each when there are few heads. Per chunk: U = U~ - W S^T, (Q S^T)^T, O^T = scale gam (Q S^T)^T + U^T P^T
+//    and the state update on the bf16 matrix cores. The next chunk's -W, Q, K, P^T and U~
 //    stream into a second LDS buffer with direct global-to-LDS loads while the current chunk
 //    computes.
 //
@@ -42,7 +42,7 @@
 // A[l%16][l/16], B[l/16][l%16] and the same C layout.
 //
 // Operands whose K index runs down the rows of a row-major LDS image (K and V contracted
-// over tokens, -W^T, P^T) are read with ds_read_b64_tr_b16: within each group of 16 lanes,
+// over tokens, P^T) are read with ds_read_b64_tr_b16: within each group of 16 lanes,
 // when lane i points at row k0 + i/4, columns n0 + 4(i%4) .. +3, lane j receives rows
 // k0 .. k0+3 of column n0 + j.
 #include "gdn_device.h"
@@ -60,7 +60,7 @@ constexpr int kTokPad4 = kC + 4;    // [token][token] bf16 LDS rows, tight
 constexpr int kF32Pad = kC + 4;     // [token][token] fp32 LDS rows
 
 // Workspace: one block per (chunk, V head).
-constexpr size_t kWsW = 0;                          // bf16 [128][64]: -W^T
+constexpr size_t kWsW = 0;                          // bf16 [64][128]: -W
 constexpr size_t kWsP = kWsW + kC * kD * 2;         // bf16 [64][64]: P^T
 constexpr size_t kWsGam = kWsP + kC * kC * 2;       // fp32 [64]: gam_r
 constexpr size_t kWsLam = kWsGam + kC * 4;          // fp32 [64]: gam_C / gam_r
@@ -414,9 +414,11 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
   __syncthreads();
 
   // ---- U~ = T diag(beta) V (hi + lo) and -W = -T diag(beta gam) K; wave w: column tiles
-  // 2w, 2w+1. U~ goes out in the accumulator layout, -W transposed as 8-byte pieces.
+  // 2w, 2w+1. U~ goes out in the accumulator layout; -W is formed transposed (K^T times
+  // the transposed operand: the same registers with the roles swapped) so each lane holds
+  // four adjacent columns of one -W row, stored as 8-byte pieces.
   f32x4* Uw = reinterpret_cast<f32x4*>(wsh + kWsU);
-  bf16* Wt = reinterpret_cast<bf16*>(wsh + kWsW);
+  bf16* Wg = reinterpret_cast<bf16*>(wsh + kWsW);
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc) {
     const int ct = 2 * w + cc;
@@ -433,73 +435,74 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
       for (int ks = 0; ks <= rt / 2; ++ks) {   // T is lower triangular
         au = mfma16x16x32(perm_rowpad(&sm.r1.t.Th[16 * rt + l16][0], 32 * ks, g4), bv[ks], au);
         au = mfma16x16x32(perm_rowpad(&sm.r1.t.Tl[16 * rt + l16][0], 32 * ks, g4), bv[ks], au);
-        aw = mfma16x16x32(perm_rowpad(&sm.r2.o.Tbg[16 * rt + l16][0], 32 * ks, g4), bk[ks], aw);
+        aw = mfma16x16x32(bk[ks], perm_rowpad(&sm.r2.o.Tbg[16 * rt + l16][0], 32 * ks, g4), aw);
       }
       Uw[(ct * 4 + rt) * 64 + lane] = au;
       bf16x4 wv;
       wv[0] = to_bf16(aw[0]); wv[1] = to_bf16(aw[1]); wv[2] = to_bf16(aw[2]); wv[3] = to_bf16(aw[3]);
-      *reinterpret_cast<bf16x4*>(Wt + (16 * ct + l16) * kC + 16 * rt + 4 * g4) = wv;
+      *reinterpret_cast<bf16x4*>(Wg + (16 * rt + l16) * kD + 16 * ct + 4 * g4) = wv;
     }
   }
 }
 
 // ------------------------------------------------------------------------------------------
 // state_kernel<NW>: NW waves of 16 value rows each per workgroup. NW = 8 covers a whole
-// (sequence, V head) with two waves per SIMD; NW = 4 covers half of one, so two workgroups
-// (on the same XCD) share a head and twice as many CUs work when there are few heads.
+// (sequence, V head) with two waves per SIMD; NW = 4 and NW = 2 cover a half and a quarter
+// of one, so two or four workgroups (on the same XCD) share a head and more CUs work when
+// there are few heads.
 // ------------------------------------------------------------------------------------------
 
 // LDS of the state pass: the shared per-chunk operands, double buffered as two separate
 // objects (so the compiler can tell that reads of one never wait for direct loads into
 // the other), and each wave's U~ tiles, single buffered.
 struct StateBuf {
-  bf16 Wt[kD * kC];      // -W^T, 128-byte rows
+  bf16 W[kC * kD];       // -W, 256-byte rows
   bf16 Pt[kC * kC];      // P^T, 128-byte rows
   bf16 Q[kC * kD];       // 256-byte rows
   bf16 K[kC * kD];       // 256-byte rows
-  float gl[2 * kC];      // gam, then gam_C / gam
+  float gl[4 * kC];      // gam, then gam_C / gam, then a copy of both (see dma_piece)
 };
 
-// Per-lane LDS element offsets, computed once (the swizzles keep K-steps, row tiles, the
-// second half of a permuted operand and the buffer index out of the lane-dependent part).
+// Per-lane LDS element offsets, computed once (the swizzles keep K-steps, row tiles and the
+// buffer out of the lane-dependent part).
+//
+// S is held in K order: St[2 ks + h][i] = S[col][32 ks + 8 g4 + 4 h + i], so the packed
+// operand of K-step ks holds S[col][32 ks + 8 g4 .. + 7] and its partners (-W and Q rows)
+// are single 16-byte row reads. The state update produces that order by reading K^T
+// columns 32 ks + 8 a + 4 h .. + 3 for output rows 4 a .. 4 a + 3.
 struct LaneOffsets {
-  int q[4][2];      // Q row reads: K-step ks, half
-  int t128[4];      // -W^T and P^T transpose reads: column tile
-  int k[8];         // K transpose reads: column tile
+  int row[4];       // -W and Q row reads: K-step ks (add 2048 per row tile)
+  int t128[4];      // P^T transpose reads: column tile
+  int k[8];         // K transpose reads: state tile
 };
 
 __device__ __forceinline__ void lane_offsets(LaneOffsets& o, int g4, int l16) {
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) o.q[ks][hf] = sw256(l16, 32 * ks + 16 * hf + 4 * g4);
+  for (int ks = 0; ks < 4; ++ks) o.row[ks] = sw256(l16, 32 * ks + 8 * g4);
   const int rr = 4 * g4 + (l16 >> 2), cc = 4 * (l16 & 3);
 #pragma unroll
   for (int x = 0; x < 4; ++x) o.t128[x] = sw128(rr, 16 * x + cc);
 #pragma unroll
-  for (int x = 0; x < 8; ++x) o.k[x] = sw256(rr, 16 * x + cc);
+  for (int x = 0; x < 8; ++x) o.k[x] = sw256(rr, 32 * (x >> 1) + 8 * (l16 & 3) + 4 * (x & 1));
 }
 
 // This wave's share of the direct loads of one chunk. The NW waves of a workgroup split
-// the sixteen 1 KB instructions of each 16 KB image (-W^T, Q, K) and the eight of P^T;
+// the sixteen 1 KB instructions of each 16 KB image (-W, Q, K) and the eight of P^T;
 // every wave brings its own 4 KB of U~. `ni` = 16 / NW instructions per image.
 struct DmaPlan {
-  int wt[8];        // -W^T source offsets (elements)
   int pt[4];        // P^T source offsets (elements)
-  int qk_row[8];    // Q / K source rows within the chunk
-  int qk_piece[8];  // Q / K source element offsets within the row
-  int ni;
+  int row[8];       // -W / Q / K source rows within the chunk
+  int piece[8];     // -W / Q / K source element offsets within the row
+  int ni;           // 16 / NW, at most 8
 };
 
 __device__ __forceinline__ void dma_plan(DmaPlan& d, int ni, int w, int lane) {
   d.ni = ni;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int r = 8 * (ni * w + i) + (lane >> 3);
-    d.wt[i] = r * kC + ((lane & 7) ^ (((r >> 1) & 3) << 1)) * 8;
     const int rq = 4 * (ni * w + i) + (lane >> 4);
-    d.qk_row[i] = rq;
-    d.qk_piece[i] = ((lane & 15) ^ ((rq & 7) << 1) ^ ((rq >> 3) & 1)) * 8;
+    d.row[i] = rq;
+    d.piece[i] = ((lane & 15) ^ ((rq & 7) << 1) ^ ((rq >> 3) & 1)) * 8;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -510,13 +513,13 @@ __device__ __forceinline__ void dma_plan(DmaPlan& d, int ni, int w, int lane) {
 
 // Sources and destinations of one chunk's direct loads.
 struct DmaChunk {
-  const bf16* wt;
+  const bf16* w;
   const bf16* pt;
   const bf16* qb;       // row 0 of the chunk, this QK head
   const bf16* kb;
   const f32x4* u;       // this wave's U~ tiles
   const float* gl;
-  bf16* d_wt;           // LDS destinations
+  bf16* d_w;            // LDS destinations
   bf16* d_pt;
   bf16* d_q;
   bf16* d_k;
@@ -542,11 +545,11 @@ __device__ __forceinline__ void dma_piece(int p, const DmaChunk& d, const DmaPla
   if (p < 3 * ni) {
     const int i = p / 3, which = p % 3;
     if (which == 0) {
-      __builtin_amdgcn_global_load_lds(d.wt + dp.wt[i], (lds_void_ptr)(d.d_wt + 8 * (ni * w + i) * kC), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(d.w + dp.row[i] * kD + dp.piece[i], (lds_void_ptr)(d.d_w + 4 * (ni * w + i) * kD), 16, 0, 0);
     } else {
       // rows past the chunk end repeat the last valid row and only feed discarded results
-      const int row = dp.qk_row[i] < d.nv ? dp.qk_row[i] : d.nv - 1;
-      const int off = row * qk_stride + dp.qk_piece[i];
+      const int row = dp.row[i] < d.nv ? dp.row[i] : d.nv - 1;
+      const int off = row * qk_stride + dp.piece[i];
       if (which == 1)
         __builtin_amdgcn_global_load_lds(d.qb + off, (lds_void_ptr)(d.d_q + 4 * (ni * w + i) * kD), 16, 0, 0);
       else
@@ -559,17 +562,18 @@ __device__ __forceinline__ void dma_piece(int p, const DmaChunk& d, const DmaPla
     __builtin_amdgcn_global_load_lds(d.pt + dp.pt[p], (lds_void_ptr)(d.d_pt + 8 * ((ni / 2) * w + p) * kC), 16, 0, 0);
     return;
   }
-  if (w == 0 && lane < 32)   // gam then lam, 512 contiguous bytes
-    __builtin_amdgcn_global_load_lds(d.gl + lane * 4, (lds_void_ptr)d.d_gl, 16, 0, 0);
+  // gam then lam, 512 contiguous bytes. Every wave issues it (identical data, so the
+  // overlapping writes agree) and the upper 32 lanes repeat the lower ones: no branch,
+  // which would split the scheduling regions around it.
+  __builtin_amdgcn_global_load_lds(d.gl + (lane & 31) * 4, (lds_void_ptr)d.d_gl, 16, 0, 0);
 }
 
 // Direct loads of chunk slot s of the twelve slots a chunk's compute offers (one per
 // K-step of U, per read-out tile and per pair of state tiles), spread evenly.
 template <int NI>
-__device__ __forceinline__ void dma_slot(int s, bool on, const DmaChunk& d, const DmaPlan& dp,
-                                         int qk_stride, int w, int lane) {
+__device__ __forceinline__ void dma_slot(int s, const DmaChunk& d, const DmaPlan& dp, int qk_stride,
+                                         int w, int lane) {
   constexpr int P = dma_pieces(NI);
-  if (!on) return;
 #pragma unroll
   for (int p = 0; p < P; ++p)
     if (p * 12 / P == s) dma_piece(p, d, dp, qk_stride, w, lane);
@@ -580,13 +584,13 @@ __device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& ds
   DmaChunk d;
   const uint8_t* head = a.ws + ((size_t)c * a.h_v + h) * kWsHead;
   const size_t qk_stride = (size_t)a.h_qk * kD;
-  d.wt = reinterpret_cast<const bf16*>(head + kWsW);
+  d.w = reinterpret_cast<const bf16*>(head + kWsW);
   d.pt = reinterpret_cast<const bf16*>(head + kWsP);
   d.qb = a.q + (size_t)t0 * qk_stride + (size_t)j * kD;
   d.kb = a.k + (size_t)t0 * qk_stride + (size_t)j * kD;
   d.u = reinterpret_cast<const f32x4*>(head + kWsU) + (size_t)(col0 >> 4) * 4 * 64;
   d.gl = reinterpret_cast<const float*>(head + kWsGam);
-  d.d_wt = dst.Wt;
+  d.d_w = dst.W;
   d.d_pt = dst.Pt;
   d.d_q = dst.Q;
   d.d_k = dst.K;
@@ -597,15 +601,17 @@ __device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& ds
 }
 
 // One chunk of the state pass for this wave's 16 value rows, reading LDS buffer `cur` while
-// the next chunk (`nx`, if `has_next`) streams into the other one; its loads are spread
-// over the compute so the vector-memory unit works in the background. The read-out is
-// formed transposed (value rows x tokens) so each lane ends up with four adjacent value
-// rows of one token.
+// the next chunk (`nx`) streams into the other one; its loads are spread over the compute
+// so the vector-memory unit works in the background. After a sequence's last chunk `nx`
+// names the following block of the workspace and the sequence's last rows: in bounds, and
+// never read. The code has no branches, so the scheduler sees each chunk whole. The
+// read-out is formed transposed (value rows x tokens) so each lane ends up with four
+// adjacent value rows of one token.
 template <int NW>
 __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf& cur, const f32x4* my_u,
                                             const LaneOffsets& lo, const DmaPlan& dp, f32x4 (&St)[8],
-                                            const DmaChunk& nx, bool has_next, int t0, int nv, int h,
-                                            int col0, int w, int lane) {
+                                            const DmaChunk& nx, int t0, int nv, int h, int col0, int w,
+                                            int lane) {
   constexpr int NI = 16 / NW;
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
@@ -627,24 +633,32 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
   bf16x8 Sb[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) Sb[ks] = pack8(St[2 * ks], St[2 * ks + 1]);
-  const bf16* Wt = cur.Wt;
+  const bf16* Wl = cur.W;
   const bf16* Q = cur.Q;
-  // U -= W S^T ;  QSt = (Q S^T)^T (value rows x tokens)
+  // U -= W S^T ;  QSt = (Q S^T)^T (value rows x tokens). Operands of K-step ks + 1 are read
+  // while the products of K-step ks run.
+  bf16x8 aw[2][4], aq[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    aw[0][rt] = lds8(Wl + lo.row[0] + 2048 * rt);
+    aq[0][rt] = lds8(Q + lo.row[0] + 2048 * rt);
+  }
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    dma_slot<NI>(ks, has_next, nx, dp, qk_stride, w, lane);
-    bf16x8 aw[4], aq[4];
+    const int cb = ks & 1;
+    if (ks + 1 < 4) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        aw[cb ^ 1][rt] = lds8(Wl + lo.row[ks + 1] + 2048 * rt);
+        aq[cb ^ 1][rt] = lds8(Q + lo.row[ks + 1] + 2048 * rt);
+      }
+    }
+    dma_slot<NI>(ks, nx, dp, qk_stride, w, lane);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      aw[rt] = join8(lds_tr4(Wt + lo.t128[rt] + 2048 * ks), lds_tr4(Wt + lo.t128[rt] + 2048 * ks + 1024));
-      aq[rt] = join8(lds4(Q + lo.q[ks][0] + 2048 * rt), lds4(Q + lo.q[ks][1] + 2048 * rt));
+      U[rt] = mfma16x16x32(aw[cb][rt], Sb[ks], U[rt]);
+      QSt[rt] = mfma16x16x32(Sb[ks], aq[cb][rt], QSt[rt]);
     }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      U[rt] = mfma16x16x32(aw[rt], Sb[ks], U[rt]);
-      QSt[rt] = mfma16x16x32(Sb[ks], aq[rt], QSt[rt]);
-    }
-    __builtin_amdgcn_sched_barrier(0);   // keep each K-step's loads next to its products
   }
   // U as bf16 for the read-out; the decayed U as a hi + lo pair for the state update
   const float* gam = &cur.gl[0];
@@ -666,28 +680,31 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
     Bh[ks] = pack8(hi[0], hi[1]);
     Bl[ks] = pack8(lw[0], lw[1]);
   }
-  // O^T = scale gam (Q S^T)^T + U^T P^T, stored as 8-byte pieces
+  // O^T = scale gam (Q S^T)^T + U^T P^T, stored as 8-byte pieces through a buffer resource
+  // that ends at the chunk's last valid token, so stores past it are dropped by the
+  // hardware range check instead of a branch
   const bf16* Pt = cur.Pt;
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      a.o + ((size_t)t0 * a.h_v + h) * kD, (short)0, nv * a.h_v * kD * 2, 0x00020000);
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    dma_slot<NI>(4 + nt, has_next, nx, dp, qk_stride, w, lane);
+    dma_slot<NI>(4 + nt, nx, dp, qk_stride, w, lane);
     f32x4 acc = QSt[nt] * (a.scale * gam[16 * nt + l16]);
 #pragma unroll
     for (int ks = 0; ks <= nt / 2; ++ks)
       acc = mfma16x16x32(Ub[ks], join8(lds_tr4(Pt + lo.t128[nt] + 2048 * ks), lds_tr4(Pt + lo.t128[nt] + 2048 * ks + 1024)), acc);
     const int tok = 16 * nt + l16;
-    if (tok < nv) {
-      bf16x4 ov;
-      ov[0] = to_bf16(acc[0]); ov[1] = to_bf16(acc[1]); ov[2] = to_bf16(acc[2]); ov[3] = to_bf16(acc[3]);
-      *reinterpret_cast<bf16x4*>(a.o + ((size_t)(t0 + tok) * a.h_v + h) * kD + col0 + 4 * g4) = ov;
-    }
+    bf16x4 ov;
+    ov[0] = to_bf16(acc[0]); ov[1] = to_bf16(acc[1]); ov[2] = to_bf16(acc[2]); ov[3] = to_bf16(acc[3]);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov), orsrc,
+                                          (tok * a.h_v * kD + col0 + 4 * g4) * 2, 0, 0);
   }
   // S^T <- gam_C S^T + K^T (diag(gam_C / gam) U)
   const float gC = gam[kC - 1];
   const bf16* K = cur.K;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
-    if (!(mt & 1)) dma_slot<NI>(8 + mt / 2, has_next, nx, dp, qk_stride, w, lane);
+    if (!(mt & 1)) dma_slot<NI>(8 + mt / 2, nx, dp, qk_stride, w, lane);
     const bf16x8 ak0 = join8(lds_tr4(K + lo.k[mt]), lds_tr4(K + lo.k[mt] + 2048));
     const bf16x8 ak1 = join8(lds_tr4(K + lo.k[mt] + 4096), lds_tr4(K + lo.k[mt] + 6144));
     f32x4 s = St[mt] * gC;
@@ -695,7 +712,6 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
     s = mfma16x16x32(ak0, Bl[0], s);
     s = mfma16x16x32(ak1, Bh[1], s);
     St[mt] = mfma16x16x32(ak1, Bl[1], s);
-    if (mt & 1) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -734,11 +750,12 @@ __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
   DmaPlan dp;
   dma_plan(dp, NI, w, lane);
 
-  // St[mt][i] = S[col][16 mt + 4 g4 + i]
+  // St[mt][i] = S[col][32 (mt / 2) + 8 g4 + 4 (mt % 2) + i]
   f32x4 St[8];
   if (a.s0) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) St[mt] = *reinterpret_cast<const f32x4*>(a.s0 + state_off + 16 * mt + 4 * g4);
+    for (int mt = 0; mt < 8; ++mt)
+      St[mt] = *reinterpret_cast<const f32x4*>(a.s0 + state_off + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1));
   } else {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) St[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -748,24 +765,25 @@ __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
   if (n_chunks > 0) {
     const DmaChunk d0 = dma_chunk(a, buf0, my_u, c_begin, t_seq0, t_seq1, h, j, col0);
 #pragma unroll
-    for (int s = 0; s < 12; ++s) dma_slot<NI>(s, true, d0, dp, qk_stride, w, lane);
+    for (int s = 0; s < 12; ++s) dma_slot<NI>(s, d0, dp, qk_stride, w, lane);
   }
   // chunks alternate between the two LDS buffers
   for (int ci = 0; ci < n_chunks; ci += 2) {
     const int t0 = t_seq0 + ci * kC;
     const DmaChunk d1 = dma_chunk(a, buf1, my_u, c_begin + ci + 1, t0 + kC, t_seq1, h, j, col0);
-    state_chunk<NW>(a, buf0, my_u, lo, dp, St, d1, ci + 1 < n_chunks, t0, min(kC, t_seq1 - t0), h, col0, w, lane);
+    state_chunk<NW>(a, buf0, my_u, lo, dp, St, d1, t0, min(kC, t_seq1 - t0), h, col0, w, lane);
     if (ci + 1 < n_chunks) {
       const int t1 = t0 + kC;
       const DmaChunk d2 = dma_chunk(a, buf0, my_u, c_begin + ci + 2, t1 + kC, t_seq1, h, j, col0);
-      state_chunk<NW>(a, buf1, my_u, lo, dp, St, d2, ci + 2 < n_chunks, t1, min(kC, t_seq1 - t1), h, col0, w, lane);
+      state_chunk<NW>(a, buf1, my_u, lo, dp, St, d2, t1, min(kC, t_seq1 - t1), h, col0, w, lane);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);   // the last (unused) direct loads land before LDS is released
 
   if (a.s_final) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
-      *reinterpret_cast<f32x4*>(a.s_final + state_off + 16 * mt + 4 * g4) = St[mt];
+      *reinterpret_cast<f32x4*>(a.s_final + state_off + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1)) = St[mt];
   }
 }
 
@@ -805,13 +823,15 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
     const size_t prep_blocks = (pairs + 7) / 8 * 8 * (size_t)a.group;
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(kThreads), 0, stream, a);
   }
-  // 8 / NW workgroups of NW waves per (sequence, V head): two of 4 waves spread a few
-  // heads over twice the CUs; once the heads fill the chip, one of 8 waves avoids the
-  // operand traffic that every workgroup repeats.
+  // 8 / NW workgroups of NW waves per (sequence, V head). With few heads, small workgroups
+  // spread each head over more CUs (every CU's LDS then serves fewer waves); once the heads
+  // fill the chip, larger ones avoid the operand traffic that every workgroup repeats.
   const size_t seq_pairs = (size_t)num_seqs * h_qk;
   const size_t groups = (seq_pairs + 7) / 8 * 8 * (size_t)a.group;
   const size_t heads = (size_t)num_seqs * h_v;
-  if (heads * 2 <= kStateCus) {
+  if (heads * 4 <= kStateCus) {
+    hipLaunchKernelGGL(state_kernel<2>, dim3((unsigned)(groups * 4)), dim3(2 * kWave), 0, stream, a);
+  } else if (heads * 2 <= kStateCus) {
     hipLaunchKernelGGL(state_kernel<4>, dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
   } else {
     hipLaunchKernelGGL(state_kernel<8>, dim3((unsigned)groups), dim3(8 * kWave), 0, stream, a);

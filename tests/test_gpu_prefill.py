@@ -76,22 +76,33 @@ def test_prefill_varlen_equals_separate_calls():
         np.testing.assert_array_equal(f1[0], fin[n])
 
 
+def _sub_batch(x, first, last):
+    """Sequences first..last-1 of a packed batch as a batch of their own."""
+    t0, t1 = int(x.cu_seqlens[first]), int(x.cu_seqlens[last])
+    return workloads.PrefillInputs(
+        q=x.q[t0:t1], k=x.k[t0:t1], v=x.v[t0:t1], g=x.g[t0:t1], beta=x.beta[t0:t1],
+        cu_seqlens=(x.cu_seqlens[first:last + 1] - t0).astype(np.int32),
+        initial_state=x.initial_state[first:last], scale=x.scale, io_dtype="bf16")
+
+
 def test_prefill_many_sequences_full_heads():
-    """Enough (sequence, V head) pairs for the one-workgroup-per-head geometry of the state
-    pass; each sequence run alone takes the two-workgroups-per-head geometry, and the two
-    must agree bit for bit (same per-row arithmetic)."""
+    """The state pass picks its workgroup shape from the number of (sequence, V head) pairs:
+    12 sequences x 32 V heads take one 8-wave workgroup per head, 4 sequences two 4-wave
+    workgroups, 1 sequence four 2-wave workgroups. Per-row arithmetic is the same in all
+    three, so the results must agree bit for bit."""
     lens = [0, 1, 64, 65, 200, 17, 128, 0, 311, 63, 90, 5]
     x = workloads.make_prefill(lens, h_qk=16, h_v=32, with_initial_state=True, seed=13)
     o, fin = _run(x)
     _compare(x, o, fin, label="12 seqs, 32 V heads")
+    sub = _sub_batch(x, 4, 8)
+    o4, f4 = _run(sub)
+    t0, t1 = int(x.cu_seqlens[4]), int(x.cu_seqlens[8])
+    np.testing.assert_array_equal(o4, o[t0:t1])
+    np.testing.assert_array_equal(f4, fin[4:8])
     for n in (4, 8):
-        L, t0 = lens[n], int(x.cu_seqlens[n])
-        sub = workloads.PrefillInputs(
-            q=x.q[t0:t0 + L], k=x.k[t0:t0 + L], v=x.v[t0:t0 + L], g=x.g[t0:t0 + L],
-            beta=x.beta[t0:t0 + L], cu_seqlens=np.array([0, L], dtype=np.int32),
-            initial_state=x.initial_state[n:n + 1], scale=x.scale, io_dtype="bf16")
-        o1, f1 = _run(sub)
-        np.testing.assert_array_equal(o1, o[t0:t0 + L])
+        o1, f1 = _run(_sub_batch(x, n, n + 1))
+        t0, t1 = int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1])
+        np.testing.assert_array_equal(o1, o[t0:t1])
         np.testing.assert_array_equal(f1[0], fin[n])
 
 
