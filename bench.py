@@ -340,7 +340,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS,
                          "traffic": counter_traffic("decode", DECODE_SOURCES),
-                         "kernel": "recurrent_kernel<bf16, decode>", "kernel_ms": dms,
+                         "kernel": "decode_kernel<bf16>", "kernel_ms": dms,
                          "algorithmic_bytes": dbytes}}
     if "frontend" in work:
         T4, N4, conv_ms, pre_ms = bench_frontend(10, 2)

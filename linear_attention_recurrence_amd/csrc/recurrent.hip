@@ -13,10 +13,12 @@
 //   S <- alpha * S + c k^T
 //   o = scale * S q = scale * (alpha * r + c * (k . q))
 //
-// Two uses:
-//  * decode: one token per sequence, the state streamed from and back to an fp32 pool in
-//    HBM (64 KB read + 64 KB written per head; the kernel is bound by HBM bandwidth);
-//  * fp32 prefill: all tokens of a sequence with the state held on chip between tokens.
+// Two kernels:
+//  * decode_kernel: one token per sequence, the state streamed from and back to an fp32
+//    pool in HBM (64 KB read + 64 KB written per head; bound by HBM bandwidth). 512 threads
+//    per head, 8 rows each: the layout that streams fastest on this chip.
+//  * recurrent_kernel: fp32 prefill, all tokens of a sequence with the state held on chip
+//    between tokens (256 threads, 16 rows each).
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -56,7 +58,88 @@ __device__ __forceinline__ float reduce_scatter32(float (&vals)[32], int lane32)
   return vals[0];
 }
 
-template <typename IO, bool kDecode>
+// Reduce-scatter of 16 partial sums over the 32 lanes of a half-wave: afterwards lanes
+// 2c and 2c + 1 both hold the half-wave total of index c.
+__device__ __forceinline__ float reduce_scatter16(float (&vals)[16], int lane32) {
+#pragma unroll
+  for (int m = 16, n = 16; m >= 2; m >>= 1, n >>= 1) {
+    const bool upper = (lane32 & m) != 0;
+#pragma unroll
+    for (int idx = 0; idx < n / 2; ++idx) {
+      const float send = upper ? vals[idx] : vals[idx + n / 2];
+      const float keep = upper ? vals[idx + n / 2] : vals[idx];
+      vals[idx] = keep + __shfl_xor(send, m, 32);
+    }
+  }
+  return vals[0] + __shfl_xor(vals[0], 1, 32);
+}
+
+// One decode step. Thread (wave w of 8, lane l) holds columns 4*(l%32) .. +3 of the 8 rows
+// i*16 + 2*w + l/32, i = 0..7: each load or store instruction of a wave covers two whole
+// rows (1 KB). Same arithmetic as recurrent_kernel for one token.
+template <typename IO>
+__global__ __launch_bounds__(512) void decode_kernel(RecArgs a) {
+  constexpr int kRows = 8;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int c4 = lane & 31;
+  const int n = blockIdx.x / a.h_v;
+  const int h = blockIdx.x % a.h_v;
+  const int j = h / (a.h_v / a.h_qk);
+  const IO* q = static_cast<const IO*>(a.q);
+  const IO* k = static_cast<const IO*>(a.k);
+  const IO* v = static_cast<const IO*>(a.v);
+  IO* o = static_cast<IO*>(a.o);
+  const int slot = a.slots ? a.slots[n] : n;
+  const size_t state = ((size_t)slot * a.h_v + h) * kHeadDim * kHeadDim;
+  const int row_base = w * 2 + half;        // rows row_base + 16*i
+
+  float* sp = a.s_out + state + (size_t)row_base * kHeadDim + 4 * c4;
+  f32x4 S[kRows];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i)
+    S[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)i * 16 * kHeadDim));
+
+  // lanes 4i, 4i+1 finish u of row slot i; lanes 4i+2, 4i+3 finish r
+  const int my_slot = c4 >> 2;
+  const int my_row = row_base + 16 * my_slot;
+  const bool my_is_r = (c4 & 2) != 0;
+
+  const size_t qk_off = ((size_t)n * a.h_qk + j) * kHeadDim + 4 * c4;
+  const f32x4 k4 = load4(k + qk_off);
+  const f32x4 q4 = load4(q + qk_off);
+  const float alpha = __expf(a.g[(size_t)n * a.h_v + h]);
+  const float beta = a.beta[(size_t)n * a.h_v + h];
+  const float vrow = load1(v + ((size_t)n * a.h_v + h) * kHeadDim + my_row);
+
+  float vals[16];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    vals[2 * i] = S[i][0] * k4[0] + S[i][1] * k4[1] + S[i][2] * k4[2] + S[i][3] * k4[3];
+    vals[2 * i + 1] = S[i][0] * q4[0] + S[i][1] * q4[1] + S[i][2] * q4[2] + S[i][3] * q4[3];
+  }
+  const float mine = reduce_scatter16(vals, c4);
+  const float other = __shfl_xor(mine, 2, 32);
+  const float u = my_is_r ? other : mine;
+  const float r = my_is_r ? mine : other;
+  const float kq = half_wave_sum(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
+  const float c = beta * (vrow - alpha * u);
+  if ((c4 & 3) == 2) store1(o + ((size_t)n * a.h_v + h) * kHeadDim + my_row, a.scale * (alpha * r + c * kq));
+
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const float ci = __shfl(c, 4 * i, 32);
+    S[i][0] = alpha * S[i][0] + ci * k4[0];
+    S[i][1] = alpha * S[i][1] + ci * k4[1];
+    S[i][2] = alpha * S[i][2] + ci * k4[2];
+    S[i][3] = alpha * S[i][3] + ci * k4[3];
+    __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(sp + (size_t)i * 16 * kHeadDim));
+  }
+}
+
+template <typename IO>
 __global__ __launch_bounds__(256) void recurrent_kernel(RecArgs a) {
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -71,18 +154,10 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecArgs a) {
   const IO* v = static_cast<const IO*>(a.v);
   IO* o = static_cast<IO*>(a.o);
 
-  int t0, t1;
-  size_t state_in, state_out;
-  if (kDecode) {
-    t0 = n;
-    t1 = n + 1;
-    const int slot = a.slots ? a.slots[n] : n;
-    state_in = state_out = ((size_t)slot * a.h_v + h) * kHeadDim * kHeadDim;
-  } else {
-    t0 = a.cu_seqlens[n];
-    t1 = a.cu_seqlens[n + 1];
-    state_in = state_out = ((size_t)n * a.h_v + h) * kHeadDim * kHeadDim;
-  }
+  const int t0 = a.cu_seqlens[n];
+  const int t1 = a.cu_seqlens[n + 1];
+  const size_t state_in = ((size_t)n * a.h_v + h) * kHeadDim * kHeadDim;
+  const size_t state_out = state_in;
   const int row_base = w * 2 + half;        // rows row_base + 8*i
 
   f32x4 S[kRowsPerThread];
@@ -148,11 +223,11 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool io_bf
                          int num_seqs, int h_qk, int h_v, float scale, void* o,
                          hipStream_t stream) {
   RecArgs a{q, k, v, g, beta, nullptr, slots, pool, pool, o, num_seqs, h_qk, h_v, scale};
-  const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(256);
+  const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(512);
   if (io_bf16)
-    hipLaunchKernelGGL((recurrent_kernel<bf16, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<bf16>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((recurrent_kernel<float, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<float>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -163,9 +238,9 @@ hipError_t launch_recurrent_prefill(const void* q, const void* k, const void* v,
   RecArgs a{q, k, v, g, beta, cu_seqlens, nullptr, s0, s_final, o, num_seqs, h_qk, h_v, scale};
   const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(256);
   if (io_bf16)
-    hipLaunchKernelGGL((recurrent_kernel<bf16, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((recurrent_kernel<bf16>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((recurrent_kernel<float, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((recurrent_kernel<float>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
