@@ -11,8 +11,10 @@
 // HBM-bound (16 KB read + 16 KB written per token at the model's 8192 channels). Each
 // thread owns 8 adjacent channels (one 16-byte load/store) and walks R consecutive tokens,
 // keeping the last K-1 inputs of its channels in registers, so every input row is read
-// once (plus K-1 halo rows per block). Sixteen threads cover one 128-channel head, so the
-// head norm is a 16-lane reduction. A block covers 2048 channels x R tokens.
+// once (plus K-1 halo rows per block). The rows are loaded in groups of 8 tokens, the next
+// group in flight while the current one is computed, so each thread keeps up to 16 loads
+// outstanding. Sixteen threads cover one 128-channel head, so the head norm is a 16-lane
+// reduction. A block covers 2048 channels x R tokens.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -20,6 +22,7 @@ namespace gdn {
 namespace {
 
 constexpr int kTokensPerBlock = 32;
+constexpr int kGroup = 8;                                   // tokens per load group
 constexpr int kChanPerThread = 8;
 constexpr int kThreads = 256;
 constexpr int kChanPerBlock = kThreads * kChanPerThread;   // 2048
@@ -39,6 +42,14 @@ __device__ __forceinline__ void load8(const bf16* p, float (&x)[8]) {
   const bf16x8 r = *reinterpret_cast<const bf16x8*>(p);
 #pragma unroll
   for (int e = 0; e < 8; ++e) x[e] = (float)r[e];
+}
+
+// Rows t0 .. t0 + kGroup - 1 of this thread's channels (rows at or past t_end read as 0).
+__device__ __forceinline__ void load_group(const bf16* x, size_t C, int t0, int t_end,
+                                           bf16x8 (&raw)[kGroup]) {
+#pragma unroll
+  for (int u = 0; u < kGroup; ++u)
+    raw[u] = (t0 + u < t_end) ? *reinterpret_cast<const bf16x8*>(x + (size_t)(t0 + u) * C) : bf16x8{};
 }
 
 // Largest n with cu[n] <= t < cu[n+1] (t < total_tokens, so such n exists).
@@ -85,43 +96,56 @@ __global__ __launch_bounds__(kThreads) void conv_prep_kernel(ConvArgs a) {
   if (t_begin - 2 >= seq_start) load8(a.x + (size_t)(t_begin - 2) * a.C + c0, h2);
   if (t_begin - 3 >= seq_start) load8(a.x + (size_t)(t_begin - 3) * a.C + c0, h3);
 
-  for (int t = t_begin; t < t_end; ++t) {
-    if (t >= seq_end) {           // entering the next non-empty sequence: no history
-      while (a.cu[n + 1] <= t) ++n;
-      seq_start = a.cu[n];
-      seq_end = a.cu[n + 1];
+  const bf16* xc = a.x + c0;
+  bf16x8 raw[2][kGroup];
+  load_group(xc, a.C, t_begin, t_end, raw[0]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) h1[e] = h2[e] = h3[e] = 0.f;
+  for (int gi = 0; gi < kTokensPerBlock / kGroup; ++gi) {
+    const int tg = t_begin + gi * kGroup;
+    if (gi + 1 < kTokensPerBlock / kGroup) load_group(xc, a.C, tg + kGroup, t_end, raw[(gi + 1) & 1]);
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      const int t = tg + u;
+      if (t >= t_end) break;
+      if (t >= seq_end) {           // entering the next non-empty sequence: no history
+        while (a.cu[n + 1] <= t) ++n;
+        seq_start = a.cu[n];
+        seq_end = a.cu[n + 1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h1[e] = h2[e] = h3[e] = 0.f;
+      }
+      float x0[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x0[e] = (float)raw[gi & 1][u][e];
+      float z[8];
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = wt[0][e] * x0[e] + wt[1][e] * h1[e] + wt[2][e] * h2[e] + wt[3][e] * h3[e];
+        z[e] = y * __builtin_amdgcn_rcpf(1.f + __expf(-y));   // hardware 1-ulp reciprocal
+        ss += z[e] * z[e];
+      }
+      bf16x8 out;
+      if (is_q || is_k) {
+        ss += __shfl_xor(ss, 8, 16);
+        ss += __shfl_xor(ss, 4, 16);
+        ss += __shfl_xor(ss, 2, 16);
+        ss += __shfl_xor(ss, 1, 16);
+        // 1 / max(||z||, 1e-12) = rsqrt(max(||z||^2, 1e-24)), hardware 1-ulp rsqrt
+        const float f = (is_q ? a.q_scale : 1.f) * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = to_bf16(z[e] * f);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = to_bf16(z[e]);
+      }
+      bf16* dst = is_q ? a.q + (size_t)t * nq + c0
+                : is_k ? a.k + (size_t)t * nq + (c0 - nq)
+                       : a.v + (size_t)t * nv + (c0 - 2 * nq);
+      *reinterpret_cast<bf16x8*>(dst) = out;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { h3[e] = h2[e]; h2[e] = h1[e]; h1[e] = x0[e]; }
     }
-    float x0[8];
-    load8(a.x + (size_t)t * a.C + c0, x0);
-    float z[8];
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float y = wt[0][e] * x0[e] + wt[1][e] * h1[e] + wt[2][e] * h2[e] + wt[3][e] * h3[e];
-      z[e] = y / (1.f + __expf(-y));
-      ss += z[e] * z[e];
-    }
-    bf16x8 out;
-    if (is_q || is_k) {
-      ss += __shfl_xor(ss, 8, 16);
-      ss += __shfl_xor(ss, 4, 16);
-      ss += __shfl_xor(ss, 2, 16);
-      ss += __shfl_xor(ss, 1, 16);
-      const float f = (is_q ? a.q_scale : 1.f) / fmaxf(sqrtf(ss), 1e-12f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = to_bf16(z[e] * f);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = to_bf16(z[e]);
-    }
-    bf16* dst = is_q ? a.q + (size_t)t * nq + c0
-              : is_k ? a.k + (size_t)t * nq + (c0 - nq)
-                     : a.v + (size_t)t * nv + (c0 - 2 * nq);
-    *reinterpret_cast<bf16x8*>(dst) = out;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) { h3[e] = h2[e]; h2[e] = h1[e]; h1[e] = x0[e]; }
   }
 }
 
