@@ -225,15 +225,72 @@ struct PrepSmem {
       bf16 pad[kC * kF32Pad * 2 - kC * kTokPad];
     } o;
   } r2;
-  float G[kC];
-  float beta[kC];
-  float gam[kC];
+  alignas(16) float G[kC];
+  alignas(16) float beta[kC];
+  alignas(16) float gam[kC];
 };
+
+// Lower 16 x 16 tile t (0..9, row-major over the lower triangle) of a 64 x 64 product.
+__device__ __forceinline__ constexpr int tile_row(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
+__device__ __forceinline__ constexpr int tile_col(int t) { return t - tile_row(t) * (tile_row(t) + 1) / 2; }
+
+// Tiles PAR, PAR + 2, ..., PAR + 8 of K K^T (ISQ = false) or Q K^T (ISQ = true).
+template <bool ISQ, int PAR>
+__device__ __forceinline__ void gram_tiles(const PrepSmem& sm, f32x4 (&acc)[5], int g4, int l16) {
+  const bf16* Am = ISQ ? sm.r1.Q : sm.K;
+#pragma unroll
+  for (int jj = 0; jj < 5; ++jj) {
+    const int t = PAR + 2 * jj;
+    const int rt = tile_row(t), ct = tile_col(t);
+    acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc[jj] = mfma16x16x32(lds8(Am + sw256(16 * rt + l16, 32 * ks + 8 * g4)),
+                             lds8(sm.K + sw256(16 * ct + l16, 32 * ks + 8 * g4)), acc[jj]);
+  }
+}
+
+// Masked and decayed tiles: A = strictly-lower(beta_r Gam_rs (K K^T)_rs) into LDS, or
+// P = scale lower-incl(Gam_rs (Q K^T)_rs), stored transposed to the workspace (8 bytes per
+// lane: four adjacent query tokens of one key token).
+template <bool ISQ, int PAR>
+__device__ __forceinline__ void gram_epilogue(PrepSmem& sm, const f32x4 (&acc)[5], bf16* Pt, float scale,
+                                              int g4, int l16) {
+  f32x4 Gr[5], Br[5];
+  float Gs[5];
+#pragma unroll
+  for (int jj = 0; jj < 5; ++jj) {   // every LDS read first: the stores into A would order them
+    const int t = PAR + 2 * jj;
+    const int rt = tile_row(t), ct = tile_col(t);
+    Gr[jj] = *reinterpret_cast<const f32x4*>(&sm.G[16 * rt + 4 * g4]);
+    if (!ISQ) Br[jj] = *reinterpret_cast<const f32x4*>(&sm.beta[16 * rt + 4 * g4]);
+    Gs[jj] = sm.G[16 * ct + l16];
+  }
+#pragma unroll
+  for (int jj = 0; jj < 5; ++jj) {
+    const int t = PAR + 2 * jj;
+    const int rt = tile_row(t), ct = tile_col(t);
+    const int s = 16 * ct + l16;
+    f32x4 val;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rt + 4 * g4 + i;
+      const float decay = __expf(fminf(Gr[jj][i] - Gs[jj], 0.f));
+      if (ISQ) val[i] = s <= r ? scale * decay * acc[jj][i] : 0.f;
+      else sm.r1.A[r][s] = s < r ? Br[jj][i] * decay * acc[jj][i] : 0.f;
+    }
+    if (ISQ) {
+      bf16x4 pv;
+      pv[0] = to_bf16(val[0]); pv[1] = to_bf16(val[1]); pv[2] = to_bf16(val[2]); pv[3] = to_bf16(val[3]);
+      *reinterpret_cast<bf16x4*>(Pt + s * kC + 16 * rt + 4 * g4) = pv;
+    }
+  }
+}
 
 __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
   __shared__ PrepSmem sm;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int lane = tid & 63;
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
@@ -290,57 +347,22 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
     reinterpret_cast<float*>(wsh + kWsLam)[lane] = __expf(GC - x);
   }
 
-  // ---- K K^T and Q K^T: the 10 lower tiles of each, 5 per wave, held in registers ----
+  // ---- K K^T and Q K^T: the 10 lower tiles of each; waves 0, 1 take K K^T, waves 2, 3
+  // Q K^T, alternate tiles each, held in registers ----
   f32x4 acc[5];
-#pragma unroll
-  for (int jj = 0; jj < 5; ++jj) {
-    const int job = w + 4 * jj;
-    const bool isq = job >= 10;
-    const int t = isq ? job - 10 : job;
-    const int rt = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-    const int ct = t - rt * (rt + 1) / 2;
-    const bf16* Am = isq ? sm.r1.Q : sm.K;
-    acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc[jj] = mfma16x16x32(lds8(Am + sw256(16 * rt + l16, 32 * ks + 8 * g4)),
-                             lds8(sm.K + sw256(16 * ct + l16, 32 * ks + 8 * g4)), acc[jj]);
-  }
+  if (w == 0) gram_tiles<false, 0>(sm, acc, g4, l16);
+  else if (w == 1) gram_tiles<false, 1>(sm, acc, g4, l16);
+  else if (w == 2) gram_tiles<true, 0>(sm, acc, g4, l16);
+  else gram_tiles<true, 1>(sm, acc, g4, l16);
   __syncthreads();   // Q is consumed (its space becomes A) and G is ready
   bf16* Pt = reinterpret_cast<bf16*>(wsh + kWsP);
-#pragma unroll
-  for (int jj = 0; jj < 5; ++jj) {
-    const int job = w + 4 * jj;
-    const bool isq = job >= 10;
-    const int t = isq ? job - 10 : job;
-    const int rt = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-    const int ct = t - rt * (rt + 1) / 2;
-    const int s = 16 * ct + l16;
-    f32x4 val;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rt + 4 * g4 + i;
-      const float decay = __expf(fminf(sm.G[r] - sm.G[s], 0.f));
-      if (isq) val[i] = s <= r ? a.scale * decay * acc[jj][i] : 0.f;
-      else sm.r1.A[r][s] = s < r ? sm.beta[r] * decay * acc[jj][i] : 0.f;
-    }
-    if (isq) {   // P^T row s, tokens 16 rt + 4 g4 .. +3: one 8-byte store
-      bf16x4 pv;
-      pv[0] = to_bf16(val[0]); pv[1] = to_bf16(val[1]); pv[2] = to_bf16(val[2]); pv[3] = to_bf16(val[3]);
-      *reinterpret_cast<bf16x4*>(Pt + s * kC + 16 * rt + 4 * g4) = pv;
-    }
-  }
-  for (int e = tid; e < 6 * 64; e += kThreads) {    // strictly upper tiles of P are zero
-    const int t = e >> 6, ln = e & 63;
-    const int rt = t < 3 ? 0 : t < 5 ? 1 : 2;
-    const int ct = t < 3 ? t + 1 : t < 5 ? t - 1 : 3;
-    *reinterpret_cast<bf16x4*>(Pt + (16 * ct + (ln & 15)) * kC + 16 * rt + 4 * (ln >> 4)) = bf16x4{};
-  }
-  for (int e = tid; e < 6 * 256; e += kThreads) {   // ... and of T
-    const int t = e >> 8;
-    const int rt = t < 3 ? 0 : t < 5 ? 1 : 2;
-    const int ct = t < 3 ? t + 1 : t < 5 ? t - 1 : 3;
-    sm.r2.s.T[16 * rt + ((e & 255) >> 4)][16 * ct + (e & 15)] = 0.f;
+  if (w == 0) gram_epilogue<false, 0>(sm, acc, Pt, a.scale, g4, l16);
+  else if (w == 1) gram_epilogue<false, 1>(sm, acc, Pt, a.scale, g4, l16);
+  else if (w == 2) gram_epilogue<true, 0>(sm, acc, Pt, a.scale, g4, l16);
+  else gram_epilogue<true, 1>(sm, acc, Pt, a.scale, g4, l16);
+  if (tid < 128) {   // the strictly upper tiles of P that the read-out's 32-token K-steps see
+    const int rt = (tid >> 6) * 2, ln = tid & 63;
+    *reinterpret_cast<bf16x4*>(Pt + (16 * (rt + 1) + (ln & 15)) * kC + 16 * rt + 4 * (ln >> 4)) = bf16x4{};
   }
   __syncthreads();
 
@@ -386,18 +408,31 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
   // ---- operands from T: T diag(beta) as hi + lo (into A's space; A is consumed), and
   // -T diag(beta gam) (into T's space once every wave has read T) --------------------------
   bf16x8 gv[2];
+  f32x4 Tv[2][2], bv[2][2], gmv[2][2];   // every LDS read first (see the epilogue above)
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int pc = tid + kThreads * it;         // 512 pieces of 8 elements
     const int r = pc >> 3, s0 = (pc & 7) * 8;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      Tv[it][hh] = *reinterpret_cast<const f32x4*>(&sm.r2.s.T[r][s0 + 4 * hh]);
+      bv[it][hh] = *reinterpret_cast<const f32x4*>(&sm.beta[s0 + 4 * hh]);
+      gmv[it][hh] = *reinterpret_cast<const f32x4*>(&sm.gam[s0 + 4 * hh]);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int pc = tid + kThreads * it;
+    const int r = pc >> 3, s0 = (pc & 7) * 8;
     bf16x8 hv, lv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float tb = sm.r2.s.T[r][s0 + e] * sm.beta[s0 + e];
+      // T is lower triangular; its strict upper part is never written
+      const float tb = (s0 + e <= r) ? Tv[it][e >> 2][e & 3] * bv[it][e >> 2][e & 3] : 0.f;
       const bf16 hh = to_bf16(tb);
       hv[e] = hh;
       lv[e] = to_bf16(tb - (float)hh);
-      gv[it][e] = to_bf16(-tb * sm.gam[s0 + e]);
+      gv[it][e] = to_bf16(-tb * gmv[it][e >> 2][e & 3]);
     }
     *reinterpret_cast<bf16x4*>(&sm.r1.t.Th[r][s0]) = bf16x4{hv[0], hv[1], hv[2], hv[3]};
     *reinterpret_cast<bf16x4*>(&sm.r1.t.Th[r][s0 + 4]) = bf16x4{hv[4], hv[5], hv[6], hv[7]};
