@@ -22,9 +22,9 @@
 //    cores), then U~ (T diag(beta) split into hi + lo bf16) and -W on the bf16 matrix cores.
 //    Writes -W, P^T with P = scale (Q K^T o Gam o lower-incl), U~ (fp32, in the
 //    accumulator layout of the state pass), gam and gam_C / gam.
-//  * state_kernel, walking each sequence's chunks in order with S in fp32 registers, 16
-//    value rows per wave (value rows evolve independently): one workgroup of 8 waves per
-//    (sequence, V head), or two of 4 or four of 2 waves each when there are few heads. Per chunk: U = U~ - W S^T, (Q S^T)^T, O^T = scale gam (Q S^T)^T + U^T P^T
+//  * state_kernel, walking each sequence's chunks in order with S in fp32 registers, 16 or
+//    32 value rows per wave (value rows evolve independently), one to four workgroups per
+//    (sequence, V head) depending on how many heads there are. Per chunk: U = U~ - W S^T, (Q S^T)^T, O^T = scale gam (Q S^T)^T + U^T P^T
 //    and the state update on the bf16 matrix cores. The next chunk's -W, Q, K, P^T and U~
 //    stream into a second LDS buffer with direct global-to-LDS loads while the current chunk
 //    computes.
@@ -481,10 +481,13 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// state_kernel<NW>: NW waves of 16 value rows each per workgroup. NW = 8 covers a whole
-// (sequence, V head) with two waves per SIMD; NW = 4 and NW = 2 cover a half and a quarter
-// of one, so two or four workgroups (on the same XCD) share a head and more CUs work when
-// there are few heads.
+// state_kernel<NW, NT>: NW waves of NT 16-row value tiles each per workgroup, so
+// 8 / (NW NT) workgroups per (sequence, V head), placed on one XCD. Every wave reads the
+// chunk's shared operands (-W, Q, K, P^T) from LDS once for all of its tiles: NT = 2 halves
+// the LDS traffic per value row, NT = 1 halves the dependent work per wave. With few heads
+// the pass is bound by each wave's chain of dependent steps (NT = 1, small workgroups on
+// many CUs); once the heads fill the chip it is bound by LDS traffic (NT = 2, one
+// workgroup per head).
 // ------------------------------------------------------------------------------------------
 
 // LDS of the state pass: the shared per-chunk operands, double buffered as two separate
@@ -501,10 +504,10 @@ struct StateBuf {
 // Per-lane LDS element offsets, computed once (the swizzles keep K-steps, row tiles and the
 // buffer out of the lane-dependent part).
 //
-// S is held in K order: St[2 ks + h][i] = S[col][32 ks + 8 g4 + 4 h + i], so the packed
-// operand of K-step ks holds S[col][32 ks + 8 g4 .. + 7] and its partners (-W and Q rows)
-// are single 16-byte row reads. The state update produces that order by reading K^T
-// columns 32 ks + 8 a + 4 h .. + 3 for output rows 4 a .. 4 a + 3.
+// S is held in K order: St[c][2 ks + h][i] = S[row][32 ks + 8 g4 + 4 h + i] for the lane's
+// value row of tile c, so the packed operand of K-step ks holds S[row][32 ks + 8 g4 .. + 7]
+// and its partners (-W and Q rows) are single 16-byte row reads. The state update produces
+// that order by reading K^T columns 32 ks + 8 a + 4 h .. + 3 for output rows 4 a .. 4 a + 3.
 struct LaneOffsets {
   int row[4];       // -W and Q row reads: K-step ks (add 2048 per row tile)
   int t128[4];      // P^T transpose reads: column tile
@@ -523,24 +526,25 @@ __device__ __forceinline__ void lane_offsets(LaneOffsets& o, int g4, int l16) {
 
 // This wave's share of the direct loads of one chunk. The NW waves of a workgroup split
 // the sixteen 1 KB instructions of each 16 KB image (-W, Q, K) and the eight of P^T;
-// every wave brings its own 4 KB of U~. `ni` = 16 / NW instructions per image.
+// every wave brings its own 4 KB of U~ per value tile. `ni` = 16 / NW instructions per
+// image.
 struct DmaPlan {
-  int pt[4];        // P^T source offsets (elements)
-  int row[8];       // -W / Q / K source rows within the chunk
-  int piece[8];     // -W / Q / K source element offsets within the row
-  int ni;           // 16 / NW, at most 8
+  int pt[8];        // P^T source offsets (elements)
+  int row[16];      // -W / Q / K source rows within the chunk
+  int piece[16];    // -W / Q / K source element offsets within the row
+  int ni;
 };
 
 __device__ __forceinline__ void dma_plan(DmaPlan& d, int ni, int w, int lane) {
   d.ni = ni;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 16; ++i) {
     const int rq = 4 * (ni * w + i) + (lane >> 4);
     d.row[i] = rq;
     d.piece[i] = ((lane & 15) ^ ((rq & 7) << 1) ^ ((rq >> 3) & 1)) * 8;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int rp = 8 * ((ni / 2) * w + i) + (lane >> 3);
     d.pt[i] = rp * kC + ((lane & 7) ^ (((rp >> 1) & 3) << 1)) * 8;
   }
@@ -563,20 +567,20 @@ struct DmaChunk {
   int nv;               // valid rows of the chunk
 };
 
-// Number of direct-load instructions per wave per chunk: U~, the three 16 KB images, P^T,
-// and the decay factors.
-__device__ __forceinline__ constexpr int dma_pieces(int ni) { return 4 + 3 * ni + ni / 2 + 1; }
+// Number of direct-load instructions per wave per chunk: U~ (nt tiles), the three 16 KB
+// images, P^T, and the decay factors.
+__device__ __forceinline__ constexpr int dma_pieces(int ni, int nt) { return 4 * nt + 3 * ni + ni / 2 + 1; }
 
 // Issues direct-load instruction p (0 <= p < dma_pieces) of a chunk. p is a constant once
 // the callers' loops unroll, so each call folds to one instruction.
-__device__ __forceinline__ void dma_piece(int p, const DmaChunk& d, const DmaPlan& dp, int qk_stride,
-                                          int w, int lane) {
+__device__ __forceinline__ void dma_piece(int p, int nt, const DmaChunk& d, const DmaPlan& dp,
+                                          int qk_stride, int w, int lane) {
   const int ni = dp.ni;
-  if (p < 4) {
+  if (p < 4 * nt) {
     __builtin_amdgcn_global_load_lds(d.u + p * 64 + lane, (lds_void_ptr)(d.d_u + p * 64), 16, 0, 0);
     return;
   }
-  p -= 4;
+  p -= 4 * nt;
   if (p < 3 * ni) {
     const int i = p / 3, which = p % 3;
     if (which == 0) {
@@ -605,13 +609,13 @@ __device__ __forceinline__ void dma_piece(int p, const DmaChunk& d, const DmaPla
 
 // Direct loads of chunk slot s of the twelve slots a chunk's compute offers (one per
 // K-step of U, per read-out tile and per pair of state tiles), spread evenly.
-template <int NI>
+template <int NI, int NT>
 __device__ __forceinline__ void dma_slot(int s, const DmaChunk& d, const DmaPlan& dp, int qk_stride,
                                          int w, int lane) {
-  constexpr int P = dma_pieces(NI);
+  constexpr int P = dma_pieces(NI, NT);
 #pragma unroll
   for (int p = 0; p < P; ++p)
-    if (p * 12 / P == s) dma_piece(p, d, dp, qk_stride, w, lane);
+    if (p * 12 / P == s) dma_piece(p, NT, d, dp, qk_stride, w, lane);
 }
 
 __device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& dst, f32x4* dst_u, int c,
@@ -635,16 +639,16 @@ __device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& ds
   return d;
 }
 
-// One chunk of the state pass for this wave's 16 value rows, reading LDS buffer `cur` while
-// the next chunk (`nx`) streams into the other one; its loads are spread over the compute
-// so the vector-memory unit works in the background. After a sequence's last chunk `nx`
-// names the following block of the workspace and the sequence's last rows: in bounds, and
-// never read. The code has no branches, so the scheduler sees each chunk whole. The
-// read-out is formed transposed (value rows x tokens) so each lane ends up with four
-// adjacent value rows of one token.
-template <int NW>
+// One chunk of the state pass for this wave's 16 NT value rows (tiles c at col0 + 16 c),
+// reading LDS buffer `cur` while the next chunk (`nx`) streams into the other
+// one; its loads are spread over the compute so the vector-memory unit works in the
+// background. After a sequence's last chunk `nx` names the following block of the
+// workspace and the sequence's last rows: in bounds, and never read. The code has no
+// branches, so the scheduler sees each chunk whole. The read-out is formed transposed
+// (value rows x tokens) so each lane ends up with four adjacent value rows of one token.
+template <int NW, int NT>
 __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf& cur, const f32x4* my_u,
-                                            const LaneOffsets& lo, const DmaPlan& dp, f32x4 (&St)[8],
+                                            const LaneOffsets& lo, const DmaPlan& dp, f32x4 (&St)[NT][8],
                                             const DmaChunk& nx, int t0, int nv, int h, int col0, int w,
                                             int lane) {
   constexpr int NI = 16 / NW;
@@ -655,23 +659,27 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
   __syncthreads();                 // ... everyone's; and the other buffer is free
 
   // U = U~ - W S^T  (tokens x value rows), starting from U~
-  f32x4 U[4], QSt[4];
+  f32x4 U[NT][4], QSt[NT][4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    U[rt] = my_u[rt * 64 + lane];
-    QSt[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int c = 0; c < NT; ++c)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      U[c][rt] = my_u[(4 * c + rt) * 64 + lane];
+      QSt[c][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): U~ is in registers before its refill
   __builtin_amdgcn_sched_barrier(0);
 
   // S^T as bf16 operands (B of U, A of the transposed read-out)
-  bf16x8 Sb[4];
+  bf16x8 Sb[NT][4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) Sb[ks] = pack8(St[2 * ks], St[2 * ks + 1]);
+  for (int c = 0; c < NT; ++c)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) Sb[c][ks] = pack8(St[c][2 * ks], St[c][2 * ks + 1]);
   const bf16* Wl = cur.W;
   const bf16* Q = cur.Q;
   // U -= W S^T ;  QSt = (Q S^T)^T (value rows x tokens). Operands of K-step ks + 1 are read
-  // while the products of K-step ks run.
+  // while the products of K-step ks run; each operand serves both value tiles.
   bf16x8 aw[2][4], aq[2][4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
@@ -688,33 +696,37 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
         aq[cb ^ 1][rt] = lds8(Q + lo.row[ks + 1] + 2048 * rt);
       }
     }
-    dma_slot<NI>(ks, nx, dp, qk_stride, w, lane);
+    dma_slot<NI, NT>(ks, nx, dp, qk_stride, w, lane);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      U[rt] = mfma16x16x32(aw[cb][rt], Sb[ks], U[rt]);
-      QSt[rt] = mfma16x16x32(Sb[ks], aq[cb][rt], QSt[rt]);
-    }
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        U[c][rt] = mfma16x16x32(aw[cb][rt], Sb[c][ks], U[c][rt]);
+        QSt[c][rt] = mfma16x16x32(Sb[c][ks], aq[cb][rt], QSt[c][rt]);
+      }
   }
   // U as bf16 for the read-out; the decayed U as a hi + lo pair for the state update
   const float* gam = &cur.gl[0];
   const float* lam = &cur.gl[kC];
-  bf16x8 Ub[2], Bh[2], Bl[2];
+  bf16x8 Ub[NT][2], Bh[NT][2], Bl[NT][2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    Ub[ks] = pack8(U[2 * ks], U[2 * ks + 1]);
-    f32x4 hi[2], lw[2];
+  for (int c = 0; c < NT; ++c)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    for (int ks = 0; ks < 2; ++ks) {
+      Ub[c][ks] = pack8(U[c][2 * ks], U[c][2 * ks + 1]);
+      f32x4 hi[2], lw[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float u = U[2 * ks + hh][i] * lam[16 * (2 * ks + hh) + 4 * g4 + i];
-        const float uh = (float)to_bf16(u);
-        hi[hh][i] = uh;
-        lw[hh][i] = u - uh;
-      }
-    Bh[ks] = pack8(hi[0], hi[1]);
-    Bl[ks] = pack8(lw[0], lw[1]);
-  }
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float u = U[c][2 * ks + hh][i] * lam[16 * (2 * ks + hh) + 4 * g4 + i];
+          const float uh = (float)to_bf16(u);
+          hi[hh][i] = uh;
+          lw[hh][i] = u - uh;
+        }
+      Bh[c][ks] = pack8(hi[0], hi[1]);
+      Bl[c][ks] = pack8(lw[0], lw[1]);
+    }
   // O^T = scale gam (Q S^T)^T + U^T P^T, stored as 8-byte pieces through a buffer resource
   // that ends at the chunk's last valid token, so stores past it are dropped by the
   // hardware range check instead of a branch
@@ -723,39 +735,49 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
       a.o + ((size_t)t0 * a.h_v + h) * kD, (short)0, nv * a.h_v * kD * 2, 0x00020000);
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    dma_slot<NI>(4 + nt, nx, dp, qk_stride, w, lane);
-    f32x4 acc = QSt[nt] * (a.scale * gam[16 * nt + l16]);
+    dma_slot<NI, NT>(4 + nt, nx, dp, qk_stride, w, lane);
+    bf16x8 bp[2];
 #pragma unroll
     for (int ks = 0; ks <= nt / 2; ++ks)
-      acc = mfma16x16x32(Ub[ks], join8(lds_tr4(Pt + lo.t128[nt] + 2048 * ks), lds_tr4(Pt + lo.t128[nt] + 2048 * ks + 1024)), acc);
+      bp[ks] = join8(lds_tr4(Pt + lo.t128[nt] + 2048 * ks), lds_tr4(Pt + lo.t128[nt] + 2048 * ks + 1024));
+    const float gs = a.scale * gam[16 * nt + l16];
     const int tok = 16 * nt + l16;
-    bf16x4 ov;
-    ov[0] = to_bf16(acc[0]); ov[1] = to_bf16(acc[1]); ov[2] = to_bf16(acc[2]); ov[3] = to_bf16(acc[3]);
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov), orsrc,
-                                          (tok * a.h_v * kD + col0 + 4 * g4) * 2, 0, 0);
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      f32x4 acc = QSt[c][nt] * gs;
+#pragma unroll
+      for (int ks = 0; ks <= nt / 2; ++ks) acc = mfma16x16x32(Ub[c][ks], bp[ks], acc);
+      bf16x4 ov;
+      ov[0] = to_bf16(acc[0]); ov[1] = to_bf16(acc[1]); ov[2] = to_bf16(acc[2]); ov[3] = to_bf16(acc[3]);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov), orsrc,
+                                            (tok * a.h_v * kD + col0 + 16 * c + 4 * g4) * 2, 0, 0);
+    }
   }
   // S^T <- gam_C S^T + K^T (diag(gam_C / gam) U)
   const float gC = gam[kC - 1];
   const bf16* K = cur.K;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
-    if (!(mt & 1)) dma_slot<NI>(8 + mt / 2, nx, dp, qk_stride, w, lane);
+    if (!(mt & 1)) dma_slot<NI, NT>(8 + mt / 2, nx, dp, qk_stride, w, lane);
     const bf16x8 ak0 = join8(lds_tr4(K + lo.k[mt]), lds_tr4(K + lo.k[mt] + 2048));
     const bf16x8 ak1 = join8(lds_tr4(K + lo.k[mt] + 4096), lds_tr4(K + lo.k[mt] + 6144));
-    f32x4 s = St[mt] * gC;
-    s = mfma16x16x32(ak0, Bh[0], s);
-    s = mfma16x16x32(ak0, Bl[0], s);
-    s = mfma16x16x32(ak1, Bh[1], s);
-    St[mt] = mfma16x16x32(ak1, Bl[1], s);
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      f32x4 s = St[c][mt] * gC;
+      s = mfma16x16x32(ak0, Bh[c][0], s);
+      s = mfma16x16x32(ak0, Bl[c][0], s);
+      s = mfma16x16x32(ak1, Bh[c][1], s);
+      St[c][mt] = mfma16x16x32(ak1, Bl[c][1], s);
+    }
   }
 }
 
-template <int NW>
+template <int NW, int NT>
 __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
   __shared__ StateBuf buf0;
   __shared__ StateBuf buf1;
-  __shared__ f32x4 utiles[NW][4][64];
-  constexpr int kBlocks = 8 / NW;             // workgroups per (sequence, V head)
+  __shared__ f32x4 utiles[NW][4 * NT][64];
+  constexpr int kBlocks = 8 / (NW * NT);      // workgroups per (sequence, V head)
   constexpr int NI = 16 / NW;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
@@ -772,12 +794,10 @@ __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
   const int sub = rem / 8;                    // V head within the group, value-row block
   const int n = p / a.h_qk, j = p % a.h_qk;
   const int h = j * a.group + sub / kBlocks;
-  const int col0 = (sub % kBlocks) * (16 * NW) + 16 * w;   // this wave's first value row
-  const int col = col0 + l16;                               // this lane's value row in S
+  const int col0 = (sub % kBlocks) * (16 * NT * NW) + 16 * NT * w;   // this wave's first value row
   const int t_seq0 = a.cu[n], t_seq1 = a.cu[n + 1];
   const int n_chunks = (t_seq1 - t_seq0 + kC - 1) / kC;
   const int c_begin = first_chunk(a.cu, n, lane);
-  const size_t state_off = (((size_t)n * a.h_v + h) * kD + col) * kD;
   const int qk_stride = a.h_qk * kD;
 
   LaneOffsets lo;
@@ -785,40 +805,44 @@ __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
   DmaPlan dp;
   dma_plan(dp, NI, w, lane);
 
-  // St[mt][i] = S[col][32 (mt / 2) + 8 g4 + 4 (mt % 2) + i]
-  f32x4 St[8];
-  if (a.s0) {
+  // St[c][mt][i] = S[col0 + 16 c + l16][32 (mt / 2) + 8 g4 + 4 (mt % 2) + i]
+  f32x4 St[NT][8];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    const size_t state_off = (((size_t)n * a.h_v + h) * kD + col0 + 16 * c + l16) * kD;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
-      St[mt] = *reinterpret_cast<const f32x4*>(a.s0 + state_off + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1));
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) St[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      St[c][mt] = a.s0 ? *reinterpret_cast<const f32x4*>(a.s0 + state_off + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1))
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   f32x4* my_u = &utiles[w][0][0];
   if (n_chunks > 0) {
     const DmaChunk d0 = dma_chunk(a, buf0, my_u, c_begin, t_seq0, t_seq1, h, j, col0);
 #pragma unroll
-    for (int s = 0; s < 12; ++s) dma_slot<NI>(s, d0, dp, qk_stride, w, lane);
+    for (int s = 0; s < 12; ++s) dma_slot<NI, NT>(s, d0, dp, qk_stride, w, lane);
   }
   // chunks alternate between the two LDS buffers
   for (int ci = 0; ci < n_chunks; ci += 2) {
     const int t0 = t_seq0 + ci * kC;
     const DmaChunk d1 = dma_chunk(a, buf1, my_u, c_begin + ci + 1, t0 + kC, t_seq1, h, j, col0);
-    state_chunk<NW>(a, buf0, my_u, lo, dp, St, d1, t0, min(kC, t_seq1 - t0), h, col0, w, lane);
+    state_chunk<NW, NT>(a, buf0, my_u, lo, dp, St, d1, t0, min(kC, t_seq1 - t0), h, col0, w, lane);
     if (ci + 1 < n_chunks) {
       const int t1 = t0 + kC;
       const DmaChunk d2 = dma_chunk(a, buf0, my_u, c_begin + ci + 2, t1 + kC, t_seq1, h, j, col0);
-      state_chunk<NW>(a, buf1, my_u, lo, dp, St, d2, t1, min(kC, t_seq1 - t1), h, col0, w, lane);
+      state_chunk<NW, NT>(a, buf1, my_u, lo, dp, St, d2, t1, min(kC, t_seq1 - t1), h, col0, w, lane);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);   // the last (unused) direct loads land before LDS is released
 
   if (a.s_final) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-      *reinterpret_cast<f32x4*>(a.s_final + state_off + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1)) = St[mt];
+    for (int c = 0; c < NT; ++c) {
+      const size_t state_off = (((size_t)n * a.h_v + h) * kD + col0 + 16 * c + l16) * kD;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        *reinterpret_cast<f32x4*>(a.s_final + state_off + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1)) = St[c][mt];
+    }
   }
 }
 
@@ -858,18 +882,18 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
     const size_t prep_blocks = (pairs + 7) / 8 * 8 * (size_t)a.group;
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(kThreads), 0, stream, a);
   }
-  // 8 / NW workgroups of NW waves per (sequence, V head). With few heads, small workgroups
-  // spread each head over more CUs (every CU's LDS then serves fewer waves); once the heads
-  // fill the chip, larger ones avoid the operand traffic that every workgroup repeats.
+  // With few heads, 2-wave workgroups of one tile per wave, four per head, spread the heads
+  // over many CUs; once the heads fill the chip, one 4-wave workgroup of two tiles per wave
+  // per head avoids the operand traffic that every workgroup repeats.
   const size_t seq_pairs = (size_t)num_seqs * h_qk;
   const size_t groups = (seq_pairs + 7) / 8 * 8 * (size_t)a.group;
   const size_t heads = (size_t)num_seqs * h_v;
   if (heads * 4 <= kStateCus) {
-    hipLaunchKernelGGL(state_kernel<2>, dim3((unsigned)(groups * 4)), dim3(2 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<2, 1>), dim3((unsigned)(groups * 4)), dim3(2 * kWave), 0, stream, a);
   } else if (heads * 2 <= kStateCus) {
-    hipLaunchKernelGGL(state_kernel<4>, dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<4, 1>), dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(state_kernel<8>, dim3((unsigned)groups), dim3(8 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<4, 2>), dim3((unsigned)groups), dim3(4 * kWave), 0, stream, a);
   }
   return hipGetLastError();
 }
