@@ -607,15 +607,17 @@ __device__ __forceinline__ void dma_piece(int p, int nt, const DmaChunk& d, cons
   __builtin_amdgcn_global_load_lds(d.gl + (lane & 31) * 4, (lds_void_ptr)d.d_gl, 16, 0, 0);
 }
 
-// Direct loads of chunk slot s of the twelve slots a chunk's compute offers (one per
-// K-step of U, per read-out tile and per pair of state tiles), spread evenly.
+// Direct loads of chunk slot s of the slots a chunk's compute offers, spread evenly: one
+// per state tile of the update (off the chain that leads from U to the next state) and,
+// with two value tiles per wave (more compute to hide them behind), one per K-step of U.
+__device__ __forceinline__ constexpr int dma_slots(int nt) { return nt == 2 ? 12 : 8; }
 template <int NI, int NT>
 __device__ __forceinline__ void dma_slot(int s, const DmaChunk& d, const DmaPlan& dp, int qk_stride,
                                          int w, int lane) {
   constexpr int P = dma_pieces(NI, NT);
 #pragma unroll
   for (int p = 0; p < P; ++p)
-    if (p * 12 / P == s) dma_piece(p, NT, d, dp, qk_stride, w, lane);
+    if (p * dma_slots(NT) / P == s) dma_piece(p, NT, d, dp, qk_stride, w, lane);
 }
 
 __device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& dst, f32x4* dst_u, int c,
@@ -646,7 +648,7 @@ __device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& ds
 // workspace and the sequence's last rows: in bounds, and never read. The code has no
 // branches, so the scheduler sees each chunk whole. The read-out is formed transposed
 // (value rows x tokens) so each lane ends up with four adjacent value rows of one token.
-template <int NW, int NT>
+template <int NW, int NT, bool DW>
 __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf& cur, const f32x4* my_u,
                                             const LaneOffsets& lo, const DmaPlan& dp, f32x4 (&St)[NT][8],
                                             const DmaChunk& nx, int t0, int nv, int h, int col0, int w,
@@ -667,8 +669,16 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
       U[c][rt] = my_u[(4 * c + rt) * 64 + lane];
       QSt[c][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): U~ is in registers before its refill
-  __builtin_amdgcn_sched_barrier(0);
+  // the decay factors this lane uses, read now so their latency hides behind the products:
+  // lam4[q] = gam_C / gam of tokens 16 q + 4 g4 .. + 3, gs[nt] = scale gam of token 16 nt + l16
+  f32x4 lam4[4];
+  float gs[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    lam4[q] = *reinterpret_cast<const f32x4*>(&cur.gl[kC + 16 * q + 4 * g4]);
+    gs[q] = cur.gl[16 * q + l16];
+  }
+  const float gC = cur.gl[kC - 1];
 
   // S^T as bf16 operands (B of U, A of the transposed read-out)
   bf16x8 Sb[NT][4];
@@ -678,36 +688,23 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
     for (int ks = 0; ks < 4; ++ks) Sb[c][ks] = pack8(St[c][2 * ks], St[c][2 * ks + 1]);
   const bf16* Wl = cur.W;
   const bf16* Q = cur.Q;
-  // U -= W S^T ;  QSt = (Q S^T)^T (value rows x tokens). Operands of K-step ks + 1 are read
-  // while the products of K-step ks run; each operand serves both value tiles.
-  bf16x8 aw[2][4], aq[2][4];
+  const bf16* K = cur.K;
+  // U -= W S^T first: it is the head of the chain that leads to the next state. All of
+  // -W is read at once (one LDS latency); each operand serves every value tile.
+  bf16x8 aw[4][4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    aw[0][rt] = lds8(Wl + lo.row[0] + 2048 * rt);
-    aq[0][rt] = lds8(Q + lo.row[0] + 2048 * rt);
-  }
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) aw[ks][rt] = lds8(Wl + lo.row[ks] + 2048 * rt);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const int cb = ks & 1;
-    if (ks + 1 < 4) {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        aw[cb ^ 1][rt] = lds8(Wl + lo.row[ks + 1] + 2048 * rt);
-        aq[cb ^ 1][rt] = lds8(Q + lo.row[ks + 1] + 2048 * rt);
-      }
-    }
-    dma_slot<NI, NT>(ks, nx, dp, qk_stride, w, lane);
+    if (!DW && NT == 2) dma_slot<NI, NT>(ks, nx, dp, qk_stride, w, lane);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        U[c][rt] = mfma16x16x32(aw[cb][rt], Sb[c][ks], U[c][rt]);
-        QSt[c][rt] = mfma16x16x32(Sb[c][ks], aq[cb][rt], QSt[c][rt]);
-      }
+      for (int c = 0; c < NT; ++c) U[c][rt] = mfma16x16x32(aw[ks][rt], Sb[c][ks], U[c][rt]);
   }
   // U as bf16 for the read-out; the decayed U as a hi + lo pair for the state update
-  const float* gam = &cur.gl[0];
-  const float* lam = &cur.gl[kC];
   bf16x8 Ub[NT][2], Bh[NT][2], Bl[NT][2];
 #pragma unroll
   for (int c = 0; c < NT; ++c)
@@ -719,7 +716,7 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float u = U[c][2 * ks + hh][i] * lam[16 * (2 * ks + hh) + 4 * g4 + i];
+          const float u = U[c][2 * ks + hh][i] * lam4[2 * ks + hh][i];
           const float uh = (float)to_bf16(u);
           hi[hh][i] = uh;
           lw[hh][i] = u - uh;
@@ -727,56 +724,96 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
       Bh[c][ks] = pack8(hi[0], hi[1]);
       Bl[c][ks] = pack8(lw[0], lw[1]);
     }
-  // O^T = scale gam (Q S^T)^T + U^T P^T, stored as 8-byte pieces through a buffer resource
-  // that ends at the chunk's last valid token, so stores past it are dropped by the
-  // hardware range check instead of a branch
+  // S^T <- gam_C S^T + K^T (diag(gam_C / gam) U), with the read-out in between (off the
+  // chain to the next state): step mt updates state tile mt and adds K-steps 2 (mt % 2),
+  // 2 (mt % 2) + 1 to QSt = (Q S^T)^T tile mt / 2 (value rows x tokens); after its second
+  // step, read-out tile nt = mt / 2, O^T = scale gam (Q S^T)^T + U^T P^T, is stored as
+  // 8-byte pieces through a buffer resource that ends at the chunk's last valid token (so
+  // stores past it are dropped by the hardware range check instead of a branch). Operands
+  // of step mt + 1 are read while the products of step mt run.
   const bf16* Pt = cur.Pt;
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
       a.o + ((size_t)t0 * a.h_v + h) * kD, (short)0, nv * a.h_v * kD * 2, 0x00020000);
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    dma_slot<NI, NT>(4 + nt, nx, dp, qk_stride, w, lane);
-    bf16x8 bp[2];
-#pragma unroll
-    for (int ks = 0; ks <= nt / 2; ++ks)
-      bp[ks] = join8(lds_tr4(Pt + lo.t128[nt] + 2048 * ks), lds_tr4(Pt + lo.t128[nt] + 2048 * ks + 1024));
-    const float gs = a.scale * gam[16 * nt + l16];
-    const int tok = 16 * nt + l16;
-#pragma unroll
-    for (int c = 0; c < NT; ++c) {
-      f32x4 acc = QSt[c][nt] * gs;
-#pragma unroll
-      for (int ks = 0; ks <= nt / 2; ++ks) acc = mfma16x16x32(Ub[c][ks], bp[ks], acc);
-      bf16x4 ov;
-      ov[0] = to_bf16(acc[0]); ov[1] = to_bf16(acc[1]); ov[2] = to_bf16(acc[2]); ov[3] = to_bf16(acc[3]);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov), orsrc,
-                                            (tok * a.h_v * kD + col0 + 16 * c + 4 * g4) * 2, 0, 0);
-    }
-  }
-  // S^T <- gam_C S^T + K^T (diag(gam_C / gam) U)
-  const float gC = gam[kC - 1];
-  const bf16* K = cur.K;
+  bf16x8 ak[2][2], aq[2][2];
+  ak[0][0] = join8(lds_tr4(K + lo.k[0]), lds_tr4(K + lo.k[0] + 2048));
+  ak[0][1] = join8(lds_tr4(K + lo.k[0] + 4096), lds_tr4(K + lo.k[0] + 6144));
+  aq[0][0] = lds8(Q + lo.row[0]);
+  aq[0][1] = lds8(Q + lo.row[1]);
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
-    if (!(mt & 1)) dma_slot<NI, NT>(8 + mt / 2, nx, dp, qk_stride, w, lane);
-    const bf16x8 ak0 = join8(lds_tr4(K + lo.k[mt]), lds_tr4(K + lo.k[mt] + 2048));
-    const bf16x8 ak1 = join8(lds_tr4(K + lo.k[mt] + 4096), lds_tr4(K + lo.k[mt] + 6144));
+    const int cb = mt & 1;
+    if (mt + 1 < 8) {
+      const int m1 = mt + 1;
+      ak[cb ^ 1][0] = join8(lds_tr4(K + lo.k[m1]), lds_tr4(K + lo.k[m1] + 2048));
+      ak[cb ^ 1][1] = join8(lds_tr4(K + lo.k[m1] + 4096), lds_tr4(K + lo.k[m1] + 6144));
+      aq[cb ^ 1][0] = lds8(Q + lo.row[2 * (m1 & 1)] + 2048 * (m1 >> 1));
+      aq[cb ^ 1][1] = lds8(Q + lo.row[2 * (m1 & 1) + 1] + 2048 * (m1 >> 1));
+    }
+    if (!DW) dma_slot<NI, NT>((NT == 2 ? 4 : 0) + mt, nx, dp, qk_stride, w, lane);
+    const int nt = mt >> 1;
+    bf16x8 bp[2];
+    if (mt & 1) {
+#pragma unroll
+      for (int ks = 0; ks <= nt / 2; ++ks)
+        bp[ks] = join8(lds_tr4(Pt + lo.t128[nt] + 2048 * ks), lds_tr4(Pt + lo.t128[nt] + 2048 * ks + 1024));
+    }
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
       f32x4 s = St[c][mt] * gC;
-      s = mfma16x16x32(ak0, Bh[c][0], s);
-      s = mfma16x16x32(ak0, Bl[c][0], s);
-      s = mfma16x16x32(ak1, Bh[c][1], s);
-      St[c][mt] = mfma16x16x32(ak1, Bl[c][1], s);
+      s = mfma16x16x32(ak[cb][0], Bh[c][0], s);
+      s = mfma16x16x32(ak[cb][0], Bl[c][0], s);
+      s = mfma16x16x32(ak[cb][1], Bh[c][1], s);
+      St[c][mt] = mfma16x16x32(ak[cb][1], Bl[c][1], s);
+      const int k0 = 2 * (mt & 1);
+      QSt[c][nt] = mfma16x16x32(Sb[c][k0], aq[cb][0], QSt[c][nt]);
+      QSt[c][nt] = mfma16x16x32(Sb[c][k0 + 1], aq[cb][1], QSt[c][nt]);
+    }
+    if (mt & 1) {
+      const float gsn = a.scale * gs[nt];
+      const int tok = 16 * nt + l16;
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        f32x4 acc = QSt[c][nt] * gsn;
+#pragma unroll
+        for (int ks = 0; ks <= nt / 2; ++ks) acc = mfma16x16x32(Ub[c][ks], bp[ks], acc);
+        bf16x4 ov;
+        ov[0] = to_bf16(acc[0]); ov[1] = to_bf16(acc[1]); ov[2] = to_bf16(acc[2]); ov[3] = to_bf16(acc[3]);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov), orsrc,
+                                              (tok * a.h_v * kD + col0 + 16 * c + 4 * g4) * 2, 0, 0);
+      }
     }
   }
 }
 
+// All direct loads of one chunk, issued by one wave (the loading wave of a DW workgroup):
+// the three 16 KB images, P^T, the decay factors, and the U~ tiles of each of the NW
+// compute waves (wave v's tiles start at value row col_base + 16 NT v).
 template <int NW, int NT>
-__global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
+__device__ __forceinline__ void dma_all(const PrefillArgs& a, StateBuf& dst, f32x4 (*dst_u)[4 * NT][64],
+                                        const DmaPlan& dp, int c, int t0, int t_seq1, int h, int j,
+                                        int col_base, int lane) {
+  const int qk_stride = a.h_qk * kD;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const DmaChunk d = dma_chunk(a, dst, &dst_u[v][0][0], c, t0, t_seq1, h, j, col_base + 16 * NT * v);
+    if (v == 0) {
+#pragma unroll
+      for (int p = 0; p < dma_pieces(16, NT); ++p) dma_piece(p, NT, d, dp, qk_stride, 0, lane);
+    } else {
+#pragma unroll
+      for (int p = 0; p < 4 * NT; ++p) dma_piece(p, NT, d, dp, qk_stride, 0, lane);
+    }
+  }
+}
+
+// DW = true adds a loading wave (wave NW) that issues every direct load of the next chunk
+// right after each chunk's barrier and then waits for them, so the NW compute waves never
+// stall on issuing loads. Its U~ tiles need their own double buffer.
+template <int NW, int NT, bool DW>
+__global__ __launch_bounds__((NW + DW) * kWave) void state_kernel(PrefillArgs a) {
   __shared__ StateBuf buf0;
   __shared__ StateBuf buf1;
-  __shared__ f32x4 utiles[NW][4 * NT][64];
+  __shared__ f32x4 utiles[DW ? 2 : 1][NW][4 * NT][64];
   constexpr int kBlocks = 8 / (NW * NT);      // workgroups per (sequence, V head)
   constexpr int NI = 16 / NW;
   const int tid = threadIdx.x;
@@ -794,12 +831,29 @@ __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
   const int sub = rem / 8;                    // V head within the group, value-row block
   const int n = p / a.h_qk, j = p % a.h_qk;
   const int h = j * a.group + sub / kBlocks;
-  const int col0 = (sub % kBlocks) * (16 * NT * NW) + 16 * NT * w;   // this wave's first value row
+  const int col_base = (sub % kBlocks) * (16 * NT * NW);   // the workgroup's first value row
   const int t_seq0 = a.cu[n], t_seq1 = a.cu[n + 1];
   const int n_chunks = (t_seq1 - t_seq0 + kC - 1) / kC;
   const int c_begin = first_chunk(a.cu, n, lane);
   const int qk_stride = a.h_qk * kD;
 
+  if (DW && w == NW) {   // the loading wave: one barrier per chunk, like the compute waves
+    DmaPlan dpl;
+    dma_plan(dpl, 16, 0, lane);
+    if (n_chunks > 0) dma_all<NW, NT>(a, buf0, utiles[0], dpl, c_begin, t_seq0, t_seq1, h, j, col_base, lane);
+    for (int ci = 0; ci < n_chunks; ++ci) {
+      __builtin_amdgcn_s_waitcnt(0);   // chunk ci has landed
+      __syncthreads();                 // ... and the other buffers are free
+      if (ci + 1 < n_chunks) {
+        const int t1 = t_seq0 + (ci + 1) * kC;
+        if (ci & 1) dma_all<NW, NT>(a, buf0, utiles[0], dpl, c_begin + ci + 1, t1, t_seq1, h, j, col_base, lane);
+        else dma_all<NW, NT>(a, buf1, utiles[DW ? 1 : 0], dpl, c_begin + ci + 1, t1, t_seq1, h, j, col_base, lane);
+      }
+    }
+    return;
+  }
+
+  const int col0 = col_base + 16 * NT * w;    // this wave's first value row
   LaneOffsets lo;
   lane_offsets(lo, g4, l16);
   DmaPlan dp;
@@ -816,21 +870,22 @@ __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
                        : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  f32x4* my_u = &utiles[w][0][0];
-  if (n_chunks > 0) {
-    const DmaChunk d0 = dma_chunk(a, buf0, my_u, c_begin, t_seq0, t_seq1, h, j, col0);
+  f32x4* my_u0 = &utiles[0][w][0][0];
+  f32x4* my_u1 = &utiles[DW ? 1 : 0][w][0][0];
+  if (!DW && n_chunks > 0) {
+    const DmaChunk d0 = dma_chunk(a, buf0, my_u0, c_begin, t_seq0, t_seq1, h, j, col0);
 #pragma unroll
-    for (int s = 0; s < 12; ++s) dma_slot<NI, NT>(s, d0, dp, qk_stride, w, lane);
+    for (int s = 0; s < dma_slots(NT); ++s) dma_slot<NI, NT>(s, d0, dp, qk_stride, w, lane);
   }
   // chunks alternate between the two LDS buffers
   for (int ci = 0; ci < n_chunks; ci += 2) {
     const int t0 = t_seq0 + ci * kC;
-    const DmaChunk d1 = dma_chunk(a, buf1, my_u, c_begin + ci + 1, t0 + kC, t_seq1, h, j, col0);
-    state_chunk<NW, NT>(a, buf0, my_u, lo, dp, St, d1, t0, min(kC, t_seq1 - t0), h, col0, w, lane);
+    const DmaChunk d1 = dma_chunk(a, buf1, my_u1, c_begin + ci + 1, t0 + kC, t_seq1, h, j, col0);
+    state_chunk<NW, NT, DW>(a, buf0, my_u0, lo, dp, St, d1, t0, min(kC, t_seq1 - t0), h, col0, w, lane);
     if (ci + 1 < n_chunks) {
       const int t1 = t0 + kC;
-      const DmaChunk d2 = dma_chunk(a, buf0, my_u, c_begin + ci + 2, t1 + kC, t_seq1, h, j, col0);
-      state_chunk<NW, NT>(a, buf1, my_u, lo, dp, St, d2, t1, min(kC, t_seq1 - t1), h, col0, w, lane);
+      const DmaChunk d2 = dma_chunk(a, buf0, my_u0, c_begin + ci + 2, t1 + kC, t_seq1, h, j, col0);
+      state_chunk<NW, NT, DW>(a, buf1, my_u1, lo, dp, St, d2, t1, min(kC, t_seq1 - t1), h, col0, w, lane);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);   // the last (unused) direct loads land before LDS is released
@@ -882,18 +937,19 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
     const size_t prep_blocks = (pairs + 7) / 8 * 8 * (size_t)a.group;
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(kThreads), 0, stream, a);
   }
-  // With few heads, 2-wave workgroups of one tile per wave, four per head, spread the heads
-  // over many CUs; once the heads fill the chip, one 4-wave workgroup of two tiles per wave
-  // per head avoids the operand traffic that every workgroup repeats.
+  // With few heads, four workgroups per head of two compute waves (one tile each) and a
+  // loading wave spread the heads over many CUs; once the heads fill the chip, one 4-wave
+  // workgroup of two tiles per wave per head avoids the operand traffic that every
+  // workgroup repeats.
   const size_t seq_pairs = (size_t)num_seqs * h_qk;
   const size_t groups = (seq_pairs + 7) / 8 * 8 * (size_t)a.group;
   const size_t heads = (size_t)num_seqs * h_v;
   if (heads * 4 <= kStateCus) {
-    hipLaunchKernelGGL((state_kernel<2, 1>), dim3((unsigned)(groups * 4)), dim3(2 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<2, 1, true>), dim3((unsigned)(groups * 4)), dim3(3 * kWave), 0, stream, a);
   } else if (heads * 2 <= kStateCus) {
-    hipLaunchKernelGGL((state_kernel<4, 1>), dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<4, 1, false>), dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((state_kernel<4, 2>), dim3((unsigned)groups), dim3(4 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<4, 2, false>), dim3((unsigned)groups), dim3(4 * kWave), 0, stream, a);
   }
   return hipGetLastError();
 }
