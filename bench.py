@@ -52,8 +52,8 @@ CSRC = os.path.join(ROOT, "linear_attention_recurrence_amd", "csrc")
 # on: once they change, the figures no longer describe the kernel and traffic is reported
 # as null. Filled from the summaries kept under profiles/.
 COUNTER_TRAFFIC = {
-    "prefill": {"bytes": 382167363, "sources": "6762a2ebf2a156b8"},
-    "decode": {"bytes": 1083839827, "sources": "f2a9a710ebc63b27"},
+    "prefill": {"bytes": 378087142, "sources": "f351d1e92f3d652b"},
+    "decode": {"bytes": 1083392512, "sources": "cdfecddd07ed50cc"},
 }
 
 
@@ -320,7 +320,7 @@ def main():
                        "global_batch": 1, "seq_len": tokens, "parallelism": "none (1 GPU)"},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                         "kernel": "gdn_chunk_prefill call: prep_kernel + state_kernel<4>",
+                         "kernel": "gdn_chunk_prefill call: prep_kernel + state_kernel<2, 1, true>",
                          "call_ms": call_ms, "algorithmic_bytes": nbytes},
             "roofline_mfma": {"achieved": flops / (call_ms / 1e3) / 1e12,
                               "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
