@@ -18,8 +18,11 @@ SOURCES = ["recurrent.hip", "conv_prep.hip", "chunk_prefill.hip", "gdn_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
-# Packed fp32 instructions stay off: ordinary float code only.
-DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 instructions stay off: ordinary float code only. Matrix-core accumulators
+# are kept in the ordinary vector registers when they fit, so the vector code that scales
+# and packs them needs no copies from the accumulation registers.
+DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def _compile(src: str) -> str:

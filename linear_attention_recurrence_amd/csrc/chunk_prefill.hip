@@ -689,20 +689,24 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
   const bf16* Wl = cur.W;
   const bf16* Q = cur.Q;
   const bf16* K = cur.K;
-  // U -= W S^T first: it is the head of the chain that leads to the next state. All of
-  // -W is read at once (one LDS latency); each operand serves every value tile.
-  bf16x8 aw[4][4];
+  // U -= W S^T first: it is the head of the chain that leads to the next state. Operands
+  // of K-step ks + 1 are read while the products of K-step ks run; each operand serves
+  // every value tile.
+  bf16x8 aw[2][4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) aw[ks][rt] = lds8(Wl + lo.row[ks] + 2048 * rt);
+  for (int rt = 0; rt < 4; ++rt) aw[0][rt] = lds8(Wl + lo.row[0] + 2048 * rt);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
+    const int cb = ks & 1;
+    if (ks + 1 < 4) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) aw[cb ^ 1][rt] = lds8(Wl + lo.row[ks + 1] + 2048 * rt);
+    }
     if (!DW && NT == 2) dma_slot<NI, NT>(ks, nx, dp, qk_stride, w, lane);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int c = 0; c < NT; ++c) U[c][rt] = mfma16x16x32(aw[ks][rt], Sb[c][ks], U[c][rt]);
+      for (int c = 0; c < NT; ++c) U[c][rt] = mfma16x16x32(aw[cb][rt], Sb[c][ks], U[c][rt]);
   }
   // U as bf16 for the read-out; the decayed U as a hi + lo pair for the state update
   bf16x8 Ub[NT][2], Bh[NT][2], Bl[NT][2];
