@@ -941,14 +941,16 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
     const size_t prep_blocks = (pairs + 7) / 8 * 8 * (size_t)a.group;
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(kThreads), 0, stream, a);
   }
-  // With few heads, four workgroups per head of two compute waves (one tile each) and a
-  // loading wave spread the heads over many CUs; once the heads fill the chip, one 4-wave
-  // workgroup of two tiles per wave per head avoids the operand traffic that every
-  // workgroup repeats.
+  // With few heads, eight or four workgroups per head of one or two compute waves (one
+  // tile each) and a loading wave spread the heads over many CUs; once the heads fill the
+  // chip, one 4-wave workgroup of two tiles per wave per head avoids the operand traffic
+  // that every workgroup repeats.
   const size_t seq_pairs = (size_t)num_seqs * h_qk;
   const size_t groups = (seq_pairs + 7) / 8 * 8 * (size_t)a.group;
   const size_t heads = (size_t)num_seqs * h_v;
-  if (heads * 4 <= kStateCus) {
+  if (heads * 8 <= kStateCus) {
+    hipLaunchKernelGGL((state_kernel<1, 1, true>), dim3((unsigned)(groups * 8)), dim3(2 * kWave), 0, stream, a);
+  } else if (heads * 4 <= kStateCus) {
     hipLaunchKernelGGL((state_kernel<2, 1, true>), dim3((unsigned)(groups * 4)), dim3(3 * kWave), 0, stream, a);
   } else if (heads * 2 <= kStateCus) {
     hipLaunchKernelGGL((state_kernel<4, 1, false>), dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);

@@ -87,23 +87,19 @@ def _sub_batch(x, first, last):
 
 def test_prefill_many_sequences_full_heads():
     """The state pass picks its workgroup shape from the number of (sequence, V head) pairs:
-    12 sequences x 32 V heads take one 8-wave workgroup per head, 4 sequences two 4-wave
-    workgroups, 1 sequence four 2-wave workgroups. Per-row arithmetic is the same in all
-    three, so the results must agree bit for bit."""
+    12 sequences x 32 V heads take one workgroup of two value tiles per wave per head, 4
+    sequences two workgroups of one tile per wave, 2 sequences four and 1 sequence eight
+    workgroups with a loading wave. Per-row arithmetic is the same in all of them, so the
+    results must agree bit for bit."""
     lens = [0, 1, 64, 65, 200, 17, 128, 0, 311, 63, 90, 5]
     x = workloads.make_prefill(lens, h_qk=16, h_v=32, with_initial_state=True, seed=13)
     o, fin = _run(x)
     _compare(x, o, fin, label="12 seqs, 32 V heads")
-    sub = _sub_batch(x, 4, 8)
-    o4, f4 = _run(sub)
-    t0, t1 = int(x.cu_seqlens[4]), int(x.cu_seqlens[8])
-    np.testing.assert_array_equal(o4, o[t0:t1])
-    np.testing.assert_array_equal(f4, fin[4:8])
-    for n in (4, 8):
-        o1, f1 = _run(_sub_batch(x, n, n + 1))
-        t0, t1 = int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1])
-        np.testing.assert_array_equal(o1, o[t0:t1])
-        np.testing.assert_array_equal(f1[0], fin[n])
+    for first, last in ((4, 8), (8, 10), (4, 5), (8, 9)):
+        ob, fb = _run(_sub_batch(x, first, last))
+        t0, t1 = int(x.cu_seqlens[first]), int(x.cu_seqlens[last])
+        np.testing.assert_array_equal(ob, o[t0:t1])
+        np.testing.assert_array_equal(fb, fin[first:last])
 
 
 def test_prefill_in_place_state_and_no_final():
