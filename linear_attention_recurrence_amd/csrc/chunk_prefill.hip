@@ -708,6 +708,18 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
 #pragma unroll
       for (int c = 0; c < NT; ++c) U[c][rt] = mfma16x16x32(aw[cb][rt], Sb[c][ks], U[c][rt]);
   }
+  // QSt = (Q S^T)^T (value rows x tokens) next: it does not depend on the hi/lo split
+  // below, so its products fill the matrix cores while that vector work runs
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    bf16x8 aq[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) aq[rt] = lds8(Q + lo.row[ks] + 2048 * rt);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int c = 0; c < NT; ++c) QSt[c][rt] = mfma16x16x32(Sb[c][ks], aq[rt], QSt[c][rt]);
+  }
   // U as bf16 for the read-out; the decayed U as a hi + lo pair for the state update
   bf16x8 Ub[NT][2], Bh[NT][2], Bl[NT][2];
 #pragma unroll
@@ -729,20 +741,17 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
       Bl[c][ks] = pack8(lw[0], lw[1]);
     }
   // S^T <- gam_C S^T + K^T (diag(gam_C / gam) U), with the read-out in between (off the
-  // chain to the next state): step mt updates state tile mt and adds K-steps 2 (mt % 2),
-  // 2 (mt % 2) + 1 to QSt = (Q S^T)^T tile mt / 2 (value rows x tokens); after its second
-  // step, read-out tile nt = mt / 2, O^T = scale gam (Q S^T)^T + U^T P^T, is stored as
-  // 8-byte pieces through a buffer resource that ends at the chunk's last valid token (so
-  // stores past it are dropped by the hardware range check instead of a branch). Operands
-  // of step mt + 1 are read while the products of step mt run.
+  // chain to the next state): after state tiles 2 nt and 2 nt + 1, read-out tile nt,
+  // O^T = scale gam (Q S^T)^T + U^T P^T, is stored as 8-byte pieces through a buffer
+  // resource that ends at the chunk's last valid token (so stores past it are dropped by
+  // the hardware range check instead of a branch). Operands of step mt + 1 are read while
+  // the products of step mt run.
   const bf16* Pt = cur.Pt;
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
       a.o + ((size_t)t0 * a.h_v + h) * kD, (short)0, nv * a.h_v * kD * 2, 0x00020000);
-  bf16x8 ak[2][2], aq[2][2];
+  bf16x8 ak[2][2];
   ak[0][0] = join8(lds_tr4(K + lo.k[0]), lds_tr4(K + lo.k[0] + 2048));
   ak[0][1] = join8(lds_tr4(K + lo.k[0] + 4096), lds_tr4(K + lo.k[0] + 6144));
-  aq[0][0] = lds8(Q + lo.row[0]);
-  aq[0][1] = lds8(Q + lo.row[1]);
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
     const int cb = mt & 1;
@@ -750,8 +759,6 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
       const int m1 = mt + 1;
       ak[cb ^ 1][0] = join8(lds_tr4(K + lo.k[m1]), lds_tr4(K + lo.k[m1] + 2048));
       ak[cb ^ 1][1] = join8(lds_tr4(K + lo.k[m1] + 4096), lds_tr4(K + lo.k[m1] + 6144));
-      aq[cb ^ 1][0] = lds8(Q + lo.row[2 * (m1 & 1)] + 2048 * (m1 >> 1));
-      aq[cb ^ 1][1] = lds8(Q + lo.row[2 * (m1 & 1) + 1] + 2048 * (m1 >> 1));
     }
     if (!DW) dma_slot<NI, NT>((NT == 2 ? 4 : 0) + mt, nx, dp, qk_stride, w, lane);
     const int nt = mt >> 1;
@@ -768,9 +775,6 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
       s = mfma16x16x32(ak[cb][0], Bl[c][0], s);
       s = mfma16x16x32(ak[cb][1], Bh[c][1], s);
       St[c][mt] = mfma16x16x32(ak[cb][1], Bl[c][1], s);
-      const int k0 = 2 * (mt & 1);
-      QSt[c][nt] = mfma16x16x32(Sb[c][k0], aq[cb][0], QSt[c][nt]);
-      QSt[c][nt] = mfma16x16x32(Sb[c][k0 + 1], aq[cb][1], QSt[c][nt]);
     }
     if (mt & 1) {
       const float gsn = a.scale * gs[nt];
