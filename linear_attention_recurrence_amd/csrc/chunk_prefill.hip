@@ -657,7 +657,9 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
   const int qk_stride = a.h_qk * kD;
-  __builtin_amdgcn_s_waitcnt(0);   // this chunk's direct loads have landed (own share)
+  // this chunk's direct loads have landed (own share; with a loading wave there are none,
+  // and the read-out stores need not complete) ...
+  if (!DW) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();                 // ... everyone's; and the other buffer is free
 
   // U = U~ - W S^T  (tokens x value rows), starting from U~

@@ -102,6 +102,29 @@ def test_prefill_many_sequences_full_heads():
         np.testing.assert_array_equal(fb, fin[first:last])
 
 
+@pytest.mark.parametrize("h_qk,h_v", [(1, 1), (4, 4), (2, 8), (1, 32)])
+def test_prefill_head_groupings(h_qk, h_v):
+    """V heads per QK head from 1 to 32 (the mapping h -> h / (h_v / h_qk))."""
+    x = workloads.make_prefill([90, 0, 150], h_qk=h_qk, h_v=h_v, with_initial_state=True,
+                               seed=20 + h_v)
+    o, fin = _run(x)
+    _compare(x, o, fin, label="h_qk=%d h_v=%d" % (h_qk, h_v))
+
+
+def test_prefill_all_sequences_empty():
+    """Zero tokens: every final state is its initial state, and nothing else is written."""
+    x = workloads.make_prefill([0, 0, 0], h_qk=2, h_v=4, with_initial_state=True, seed=21)
+    import torch
+    import linear_attention_recurrence_amd as gdn
+    d = prefill_to_dev(x)
+    fin = torch.full((3, 4, 128, 128), float("nan"), dtype=torch.float32, device="cuda")
+    o = gdn.gdn_chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], x.scale,
+                              initial_state=d["s0"], final_state=fin)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0
+    np.testing.assert_array_equal(to_host_f64(fin), x.initial_state.astype(np.float64))
+
+
 def test_prefill_in_place_state_and_no_final():
     x = workloads.make_prefill([100, 37], h_qk=2, h_v=4, with_initial_state=True, seed=9)
     o_ref, fin_ref = _run(x)
