@@ -19,15 +19,16 @@
 //  * prep_kernel, one workgroup per (chunk, V head), all chunks in parallel: K K^T and Q K^T
 //    on the bf16 matrix cores, the prefix sums, the unit-lower-triangular inverse T in fp32
 //    (16 x 16 diagonal blocks by substitution, off-diagonal blocks on the fp32 matrix
-//    cores), then U~ (T diag(beta) split into hi + lo bf16) and -W on the bf16 matrix cores.
-//    Writes -W, P^T with P = scale (Q K^T o Gam o lower-incl), U~ (fp32, in the
-//    accumulator layout of the state pass), gam and gam_C / gam.
+//    cores), then -W on the bf16 matrix cores. Writes -W, P^T with
+//    P = scale (Q K^T o Gam o lower-incl), gam, gam_C / gam, and T diag(beta) as a hi + lo
+//    bf16 pair in the operand order of the state pass.
 //  * state_kernel, walking each sequence's chunks in order with S in fp32 registers, 16 or
-//    32 value rows per wave (value rows evolve independently), one to four workgroups per
-//    (sequence, V head) depending on how many heads there are. Per chunk: U = U~ - W S^T, (Q S^T)^T, O^T = scale gam (Q S^T)^T + U^T P^T
-//    and the state update on the bf16 matrix cores. The next chunk's -W, Q, K, P^T and U~
-//    stream into a second LDS buffer with direct global-to-LDS loads while the current chunk
-//    computes.
+//    32 value rows per wave (value rows evolve independently), one to eight workgroups per
+//    (sequence, V head) depending on how many heads there are. Per chunk:
+//    U~ = T diag(beta) V (by a loading wave when there is one), U = U~ - W S^T,
+//    (Q S^T)^T, O^T = scale gam (Q S^T)^T + U^T P^T and the state update on the bf16
+//    matrix cores. The next chunk's -W, Q, K, P^T, T diag(beta) and values stream into LDS
+//    with direct global-to-LDS loads while the current chunk computes.
 //
 // Precision: every product keeps one exact bf16 operand (K, Q, V as given); T diag(beta)
 // and the decayed U that feeds the state are split into hi + lo bf16 pairs so they keep
@@ -64,8 +65,18 @@ constexpr size_t kWsW = 0;                          // bf16 [64][128]: -W
 constexpr size_t kWsP = kWsW + kC * kD * 2;         // bf16 [64][64]: P^T
 constexpr size_t kWsGam = kWsP + kC * kC * 2;       // fp32 [64]: gam_r
 constexpr size_t kWsLam = kWsGam + kC * 4;          // fp32 [64]: gam_C / gam_r
-constexpr size_t kWsU = kWsLam + kC * 4;            // fp32 U~: [8 col tiles][4 row tiles][64 lanes][4]
-constexpr size_t kWsHead = kWsU + kC * kD * 4;      // 57856 bytes
+constexpr size_t kWsTh = kWsLam + kC * 4;          // bf16 T diag(beta), hi, operand order (below)
+constexpr size_t kWsTl = kWsTh + kC * kC * 2;       // bf16 T diag(beta), lo, operand order
+constexpr size_t kWsHead = kWsTl + kC * kC * 2;     // 41472 bytes
+
+// T diag(beta) is stored in the order the state pass reads it as the A operand of
+// U~ = T diag(beta) V: fragment 2 rt + ks (row tile rt, K-step ks) holds, for lane
+// l = l16 + 16 g4, the eight entries T[16 rt + l16][32 ks + 16 h + 4 g4 + i] (h, i = 0, 1 /
+// 0..3, element 4 h + i), so one 16-byte read per lane fetches an operand. Element offset of
+// entry (r, s) for s a multiple of 4:
+__device__ __forceinline__ int tb_frag_off(int r, int s) {
+  return ((2 * (r >> 4) + (s >> 5)) * 64 + (r & 15) + 16 * ((s >> 2) & 3)) * 8 + 4 * ((s >> 4) & 1);
+}
 
 __host__ __device__ inline size_t max_chunks(int total_tokens, int num_seqs) {
   return (size_t)(total_tokens + kC - 1) / kC + (size_t)num_seqs;
@@ -207,24 +218,12 @@ __device__ __forceinline__ void dma_rows128(const bf16* src, bf16* img, int i, i
 // ------------------------------------------------------------------------------------------
 struct PrepSmem {
   bf16 K[kC * kD];              // swizzled 256-byte rows
-  bf16 V[kC * kD];              // this V head's values, swizzled
   union {
-    bf16 Q[kC * kD];            // loads and Q K^T only; then A; then T diag(beta)
+    bf16 Q[kC * kD];            // loads and Q K^T only; then A; then -T diag(beta gam)
     float A[kC][kF32Pad];
-    struct {
-      bf16 Th[kC][kTokPad4];    // T diag(beta), hi
-      bf16 Tl[kC][kTokPad4];    // T diag(beta), lo
-    } t;
+    bf16 Tbg[kC][kTokPad];
   } r1;
-  union {
-    struct {
-      float T[kC][kF32Pad];     // T = (I + A)^-1
-    } s;
-    struct {
-      bf16 Tbg[kC][kTokPad];    // -T diag(beta gam)
-      bf16 pad[kC * kF32Pad * 2 - kC * kTokPad];
-    } o;
-  } r2;
+  float T[kC][kF32Pad];         // T = (I + A)^-1
   alignas(16) float G[kC];
   alignas(16) float beta[kC];
   alignas(16) float gam[kC];
@@ -287,7 +286,7 @@ __device__ __forceinline__ void gram_epilogue(PrepSmem& sm, const f32x4 (&acc)[5
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillArgs a) {
   __shared__ PrepSmem sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
@@ -310,14 +309,12 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
   const int nv = min(kC, a.cu[n + 1] - t0);
   uint8_t* wsh = a.ws + ((size_t)c * a.h_v + h) * kWsHead;
 
-  // ---- loads: K, Q, V rows straight into swizzled LDS images; g, beta ----
+  // ---- loads: K, Q rows straight into swizzled LDS images; g, beta ----
   const size_t qk_stride = (size_t)a.h_qk * kD;
-  const size_t v_stride = (size_t)a.h_v * kD;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     dma_rows256(a.k + (size_t)t0 * qk_stride + (size_t)j * kD, qk_stride, nv, sm.K, i, w, lane);
     dma_rows256(a.q + (size_t)t0 * qk_stride + (size_t)j * kD, qk_stride, nv, sm.r1.Q, i, w, lane);
-    dma_rows256(a.v + (size_t)t0 * v_stride + (size_t)h * kD, v_stride, nv, sm.V, i, w, lane);
   }
   if (tid < kC) {
     float gg = 0.f, bb = 0.f;
@@ -379,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
       for (int r = m + 1; r < 16; ++r) x[r] -= sm.r1.A[b0 + r][b0 + m] * x[m];
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sm.r2.s.T[b0 + r][b0 + col] = x[r];
+    for (int r = 0; r < 16; ++r) sm.T[b0 + r][b0 + col] = x[r];
   }
   __syncthreads();
   // off-diagonal block (i, b), i = b + d:  T_ib = -T_ii * sum_{k=b}^{i-1} A_ik T_kb,
@@ -393,21 +390,22 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
           X = mfma_f32(sm.r1.A[16 * i + l16][16 * kb + 4 * ks + g4],
-                       sm.r2.s.T[16 * kb + 4 * ks + g4][16 * b + l16], X);
+                       sm.T[16 * kb + 4 * ks + g4][16 * b + l16], X);
       }
       // X in the C layout feeds the next product as B with K order {4g + ks}
       f32x4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) Y = mfma_f32(-sm.r2.s.T[16 * i + l16][16 * i + 4 * g4 + ks], X[ks], Y);
+      for (int ks = 0; ks < 4; ++ks) Y = mfma_f32(-sm.T[16 * i + l16][16 * i + 4 * g4 + ks], X[ks], Y);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.r2.s.T[16 * i + 4 * g4 + r][16 * b + l16] = Y[r];
+      for (int r = 0; r < 4; ++r) sm.T[16 * i + 4 * g4 + r][16 * b + l16] = Y[r];
     }
     __syncthreads();
   }
 
-  // ---- operands from T: T diag(beta) as hi + lo (into A's space; A is consumed), and
-  // -T diag(beta gam) (into T's space once every wave has read T) --------------------------
-  bf16x8 gv[2];
+  // ---- operands from T: T diag(beta) as a hi + lo bf16 pair, straight to the workspace
+  // in operand order, and -T diag(beta gam) into A's space (A is consumed) ------------------
+  bf16* Thg = reinterpret_cast<bf16*>(wsh + kWsTh);
+  bf16* Tlg = reinterpret_cast<bf16*>(wsh + kWsTl);
   f32x4 Tv[2][2], bv[2][2], gmv[2][2];   // every LDS read first (see the epilogue above)
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
@@ -415,7 +413,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
     const int r = pc >> 3, s0 = (pc & 7) * 8;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      Tv[it][hh] = *reinterpret_cast<const f32x4*>(&sm.r2.s.T[r][s0 + 4 * hh]);
+      Tv[it][hh] = *reinterpret_cast<const f32x4*>(&sm.T[r][s0 + 4 * hh]);
       bv[it][hh] = *reinterpret_cast<const f32x4*>(&sm.beta[s0 + 4 * hh]);
       gmv[it][hh] = *reinterpret_cast<const f32x4*>(&sm.gam[s0 + 4 * hh]);
     }
@@ -424,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
   for (int it = 0; it < 2; ++it) {
     const int pc = tid + kThreads * it;
     const int r = pc >> 3, s0 = (pc & 7) * 8;
-    bf16x8 hv, lv;
+    bf16x8 hv, lv, gv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       // T is lower triangular; its strict upper part is never written
@@ -432,47 +430,34 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
       const bf16 hh = to_bf16(tb);
       hv[e] = hh;
       lv[e] = to_bf16(tb - (float)hh);
-      gv[it][e] = to_bf16(-tb * gmv[it][e >> 2][e & 3]);
+      gv[e] = to_bf16(-tb * gmv[it][e >> 2][e & 3]);
     }
-    *reinterpret_cast<bf16x4*>(&sm.r1.t.Th[r][s0]) = bf16x4{hv[0], hv[1], hv[2], hv[3]};
-    *reinterpret_cast<bf16x4*>(&sm.r1.t.Th[r][s0 + 4]) = bf16x4{hv[4], hv[5], hv[6], hv[7]};
-    *reinterpret_cast<bf16x4*>(&sm.r1.t.Tl[r][s0]) = bf16x4{lv[0], lv[1], lv[2], lv[3]};
-    *reinterpret_cast<bf16x4*>(&sm.r1.t.Tl[r][s0 + 4]) = bf16x4{lv[4], lv[5], lv[6], lv[7]};
-  }
-  __syncthreads();   // T is read; its space now holds -T diag(beta gam)
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int pc = tid + kThreads * it;
-    const int r = pc >> 3, s0 = (pc & 7) * 8;
-    *reinterpret_cast<bf16x8*>(&sm.r2.o.Tbg[r][s0]) = gv[it];
+    for (int hh = 0; hh < 2; ++hh) {
+      const int off = tb_frag_off(r, s0 + 4 * hh);
+      *reinterpret_cast<bf16x4*>(Thg + off) = bf16x4{hv[4 * hh], hv[4 * hh + 1], hv[4 * hh + 2], hv[4 * hh + 3]};
+      *reinterpret_cast<bf16x4*>(Tlg + off) = bf16x4{lv[4 * hh], lv[4 * hh + 1], lv[4 * hh + 2], lv[4 * hh + 3]};
+    }
+    *reinterpret_cast<bf16x8*>(&sm.r1.Tbg[r][s0]) = gv;
   }
   __syncthreads();
 
-  // ---- U~ = T diag(beta) V (hi + lo) and -W = -T diag(beta gam) K; wave w: column tiles
-  // 2w, 2w+1. U~ goes out in the accumulator layout; -W is formed transposed (K^T times
-  // the transposed operand: the same registers with the roles swapped) so each lane holds
-  // four adjacent columns of one -W row, stored as 8-byte pieces.
-  f32x4* Uw = reinterpret_cast<f32x4*>(wsh + kWsU);
+  // ---- -W = -T diag(beta gam) K; wave w: column tiles 2w, 2w+1. -W is formed transposed
+  // (K^T times the transposed operand: the same registers with the roles swapped) so each
+  // lane holds four adjacent columns of one -W row, stored as 8-byte pieces.
   bf16* Wg = reinterpret_cast<bf16*>(wsh + kWsW);
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc) {
     const int ct = 2 * w + cc;
-    bf16x8 bv[2], bk[2];
+    bf16x8 bk[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bv[ks] = perm_tr256(sm.V, 32 * ks, 16 * ct, g4, l16);
-      bk[ks] = perm_tr256(sm.K, 32 * ks, 16 * ct, g4, l16);
-    }
+    for (int ks = 0; ks < 2; ++ks) bk[ks] = perm_tr256(sm.K, 32 * ks, 16 * ct, g4, l16);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      f32x4 au = {0.f, 0.f, 0.f, 0.f}, aw = {0.f, 0.f, 0.f, 0.f};
+      f32x4 aw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks <= rt / 2; ++ks) {   // T is lower triangular
-        au = mfma16x16x32(perm_rowpad(&sm.r1.t.Th[16 * rt + l16][0], 32 * ks, g4), bv[ks], au);
-        au = mfma16x16x32(perm_rowpad(&sm.r1.t.Tl[16 * rt + l16][0], 32 * ks, g4), bv[ks], au);
-        aw = mfma16x16x32(bk[ks], perm_rowpad(&sm.r2.o.Tbg[16 * rt + l16][0], 32 * ks, g4), aw);
-      }
-      Uw[(ct * 4 + rt) * 64 + lane] = au;
+      for (int ks = 0; ks <= rt / 2; ++ks)   // T is lower triangular
+        aw = mfma16x16x32(bk[ks], perm_rowpad(&sm.r1.Tbg[16 * rt + l16][0], 32 * ks, g4), aw);
       bf16x4 wv;
       wv[0] = to_bf16(aw[0]); wv[1] = to_bf16(aw[1]); wv[2] = to_bf16(aw[2]); wv[3] = to_bf16(aw[3]);
       *reinterpret_cast<bf16x4*>(Wg + (16 * rt + l16) * kD + 16 * ct + 4 * g4) = wv;
@@ -492,13 +477,22 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrefillArgs a) {
 
 // LDS of the state pass: the shared per-chunk operands, double buffered as two separate
 // objects (so the compiler can tell that reads of one never wait for direct loads into
-// the other), and each wave's U~ tiles, single buffered.
+// the other).
 struct StateBuf {
   bf16 W[kC * kD];       // -W, 256-byte rows
   bf16 Pt[kC * kC];      // P^T, 128-byte rows
   bf16 Q[kC * kD];       // 256-byte rows
   bf16 K[kC * kD];       // 256-byte rows
   float gl[4 * kC];      // gam, then gam_C / gam, then a copy of both (see dma_piece)
+};
+
+// The inputs of U~ = T diag(beta) V, single buffered: T diag(beta) hi and lo in operand
+// order, and the workgroup's NTILE value tiles, [tile][token][16] bf16 (32-byte rows).
+template <int NTILE>
+struct TvBuf {
+  bf16 th[kC * kC];
+  bf16 tl[kC * kC];
+  bf16 v[NTILE][kC * 16];
 };
 
 // Per-lane LDS element offsets, computed once (the swizzles keep K-steps, row tiles and the
@@ -524,10 +518,37 @@ __device__ __forceinline__ void lane_offsets(LaneOffsets& o, int g4, int l16) {
   for (int x = 0; x < 8; ++x) o.k[x] = sw256(rr, 32 * (x >> 1) + 8 * (l16 & 3) + 4 * (x & 1));
 }
 
-// This wave's share of the direct loads of one chunk. The NW waves of a workgroup split
-// the sixteen 1 KB instructions of each 16 KB image (-W, Q, K) and the eight of P^T;
-// every wave brings its own 4 KB of U~ per value tile. `ni` = 16 / NW instructions per
-// image.
+// U~ = T diag(beta) V for one 16-row value tile (tokens x value rows, accumulator layout).
+// T diag(beta) = hi + lo is lower triangular, so row tile rt needs K-steps 0 .. rt / 2. The
+// value operand is read transposed: lane (l16, g4) gets tokens {32 ks + 4 g4 .. +3,
+// 32 ks + 16 + 4 g4 .. +3} of value row l16, the K order of the stored T fragments.
+__device__ __forceinline__ void utilde_tile(const bf16* th, const bf16* tl, const bf16* vt, f32x4 (&u)[4],
+                                            int g4, int l16, int lane) {
+  const int vo = (4 * g4 + (l16 >> 2)) * 16 + 4 * (l16 & 3);
+  bf16x8 bv[2], ah[8], al[8];   // every LDS read first, then the products
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) bv[ks] = join8(lds_tr4(vt + vo + 512 * ks), lds_tr4(vt + vo + 512 * ks + 256));
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+    if ((f & 1) > (f >> 1) / 2) continue;   // fragments above the diagonal are zero
+    ah[f] = lds8(th + (f * 64 + lane) * 8);
+    al[f] = lds8(tl + (f * 64 + lane) * 8);
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks <= rt / 2; ++ks) {
+      acc = mfma16x16x32(ah[2 * rt + ks], bv[ks], acc);
+      acc = mfma16x16x32(al[2 * rt + ks], bv[ks], acc);
+    }
+    u[rt] = acc;
+  }
+}
+
+// This wave's share of the direct loads of one chunk's shared operands. The NW waves of a
+// workgroup split the sixteen 1 KB instructions of each 16 KB image (-W, Q, K) and the
+// eight of P^T. `ni` = 16 / NW instructions per image.
 struct DmaPlan {
   int pt[8];        // P^T source offsets (elements)
   int row[16];      // -W / Q / K source rows within the chunk
@@ -556,31 +577,27 @@ struct DmaChunk {
   const bf16* pt;
   const bf16* qb;       // row 0 of the chunk, this QK head
   const bf16* kb;
-  const f32x4* u;       // this wave's U~ tiles
   const float* gl;
+  const bf16* th;       // T diag(beta) hi, lo (operand order)
+  const bf16* tl;
+  const bf16* vb;       // row 0 of the chunk, this V head, the workgroup's first value row
   bf16* d_w;            // LDS destinations
   bf16* d_pt;
   bf16* d_q;
   bf16* d_k;
-  f32x4* d_u;
   float* d_gl;
   int nv;               // valid rows of the chunk
 };
 
-// Number of direct-load instructions per wave per chunk: U~ (nt tiles), the three 16 KB
-// images, P^T, and the decay factors.
-__device__ __forceinline__ constexpr int dma_pieces(int ni, int nt) { return 4 * nt + 3 * ni + ni / 2 + 1; }
+// Number of direct-load instructions per wave per chunk for the shared operands: the three
+// 16 KB images, P^T, and the decay factors.
+__device__ __forceinline__ constexpr int dma_pieces(int ni) { return 3 * ni + ni / 2 + 1; }
 
-// Issues direct-load instruction p (0 <= p < dma_pieces) of a chunk. p is a constant once
-// the callers' loops unroll, so each call folds to one instruction.
-__device__ __forceinline__ void dma_piece(int p, int nt, const DmaChunk& d, const DmaPlan& dp,
-                                          int qk_stride, int w, int lane) {
+// Issues shared-operand load p (0 <= p < dma_pieces) of a chunk. p is a constant once the
+// callers' loops unroll, so each call folds to one instruction.
+__device__ __forceinline__ void dma_piece(int p, const DmaChunk& d, const DmaPlan& dp, int qk_stride,
+                                          int w, int lane) {
   const int ni = dp.ni;
-  if (p < 4 * nt) {
-    __builtin_amdgcn_global_load_lds(d.u + p * 64 + lane, (lds_void_ptr)(d.d_u + p * 64), 16, 0, 0);
-    return;
-  }
-  p -= 4 * nt;
   if (p < 3 * ni) {
     const int i = p / 3, which = p % 3;
     if (which == 0) {
@@ -607,21 +624,41 @@ __device__ __forceinline__ void dma_piece(int p, int nt, const DmaChunk& d, cons
   __builtin_amdgcn_global_load_lds(d.gl + (lane & 31) * 4, (lds_void_ptr)d.d_gl, 16, 0, 0);
 }
 
-// Direct loads of chunk slot s of the slots a chunk's compute offers, spread evenly: one
-// per state tile of the update (off the chain that leads from U to the next state) and,
-// with two value tiles per wave (more compute to hide them behind), one per K-step of U.
+// Direct load of T diag(beta) fragment f (0..7 hi, 8..15 lo): a straight 1 KB copy.
+template <int NTILE>
+__device__ __forceinline__ void dma_tb(int f, const DmaChunk& d, TvBuf<NTILE>& tv, int lane) {
+  const bf16* src = (f < 8 ? d.th : d.tl) + 512 * (f & 7) + 8 * lane;
+  bf16* dst = (f < 8 ? tv.th : tv.tl) + 512 * (f & 7);
+  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
+}
+
+// Direct load of tokens 32 i .. 32 i + 31 of value tile t of the workgroup (two lanes per
+// token); rows past the chunk end repeat the last valid row (T diag(beta) is zero there).
+template <int NTILE>
+__device__ __forceinline__ void dma_v(int t, int i, const DmaChunk& d, TvBuf<NTILE>& tv, int v_stride,
+                                      int lane) {
+  const int r = 32 * i + (lane >> 1);
+  const int row = r < d.nv ? r : d.nv - 1;
+  __builtin_amdgcn_global_load_lds(d.vb + row * v_stride + 16 * t + 8 * (lane & 1),
+                                   (lds_void_ptr)(tv.v[t] + 512 * i), 16, 0, 0);
+}
+
+// Shared-operand loads of chunk slot s of the slots a chunk's compute offers, spread
+// evenly: one per state tile of the update (off the chain that leads from U to the next
+// state) and, with two value tiles per wave (more compute to hide them behind), one per
+// K-step of U.
 __device__ __forceinline__ constexpr int dma_slots(int nt) { return nt == 2 ? 12 : 8; }
 template <int NI, int NT>
 __device__ __forceinline__ void dma_slot(int s, const DmaChunk& d, const DmaPlan& dp, int qk_stride,
                                          int w, int lane) {
-  constexpr int P = dma_pieces(NI, NT);
+  constexpr int P = dma_pieces(NI);
 #pragma unroll
   for (int p = 0; p < P; ++p)
-    if (p * dma_slots(NT) / P == s) dma_piece(p, NT, d, dp, qk_stride, w, lane);
+    if (p * dma_slots(NT) / P == s) dma_piece(p, d, dp, qk_stride, w, lane);
 }
 
-__device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& dst, f32x4* dst_u, int c,
-                                              int t0, int t_seq1, int h, int j, int col0) {
+__device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& dst, int c, int t0, int t_seq1,
+                                              int h, int j, int col_base) {
   DmaChunk d;
   const uint8_t* head = a.ws + ((size_t)c * a.h_v + h) * kWsHead;
   const size_t qk_stride = (size_t)a.h_qk * kD;
@@ -629,16 +666,30 @@ __device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& ds
   d.pt = reinterpret_cast<const bf16*>(head + kWsP);
   d.qb = a.q + (size_t)t0 * qk_stride + (size_t)j * kD;
   d.kb = a.k + (size_t)t0 * qk_stride + (size_t)j * kD;
-  d.u = reinterpret_cast<const f32x4*>(head + kWsU) + (size_t)(col0 >> 4) * 4 * 64;
   d.gl = reinterpret_cast<const float*>(head + kWsGam);
+  d.th = reinterpret_cast<const bf16*>(head + kWsTh);
+  d.tl = reinterpret_cast<const bf16*>(head + kWsTl);
+  d.vb = a.v + ((size_t)t0 * a.h_v + h) * kD + col_base;
   d.d_w = dst.W;
   d.d_pt = dst.Pt;
   d.d_q = dst.Q;
   d.d_k = dst.K;
-  d.d_u = dst_u;
   d.d_gl = dst.gl;
   d.nv = min(kC, t_seq1 - t0);
   return d;
+}
+
+// This wave's loads of the U~ inputs of chunk `d` without a loading wave: a share of the
+// T diag(beta) fragments and its own value tiles.
+template <int NW, int NT>
+__device__ __forceinline__ void dma_tv_share(const DmaChunk& d, TvBuf<NW * NT>& tv, int v_stride, int w,
+                                             int lane) {
+#pragma unroll
+  for (int f = 0; f < 16 / NW; ++f) dma_tb(f + (16 / NW) * w, d, tv, lane);
+#pragma unroll
+  for (int c = 0; c < NT; ++c)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma_v(NT * w + c, i, d, tv, v_stride, lane);
 }
 
 // One chunk of the state pass for this wave's 16 NT value rows (tiles c at col0 + 16 c),
@@ -648,11 +699,15 @@ __device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& ds
 // workspace and the sequence's last rows: in bounds, and never read. The code has no
 // branches, so the scheduler sees each chunk whole. The read-out is formed transposed
 // (value rows x tokens) so each lane ends up with four adjacent value rows of one token.
+//
+// U~ comes either from the loading wave (DW: `my_u`, in the accumulator layout) or, without
+// one, from this wave's own products over `tv`, after which a second barrier frees `tv` for
+// the next chunk's T diag(beta) and values.
 template <int NW, int NT, bool DW>
 __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf& cur, const f32x4* my_u,
-                                            const LaneOffsets& lo, const DmaPlan& dp, f32x4 (&St)[NT][8],
-                                            const DmaChunk& nx, int t0, int nv, int h, int col0, int w,
-                                            int lane) {
+                                            TvBuf<NW * NT>& tv, const LaneOffsets& lo, const DmaPlan& dp,
+                                            f32x4 (&St)[NT][8], const DmaChunk& nx, int t0, int nv, int h,
+                                            int col0, int w, int lane) {
   constexpr int NI = 16 / NW;
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
@@ -664,13 +719,21 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
 
   // U = U~ - W S^T  (tokens x value rows), starting from U~
   f32x4 U[NT][4], QSt[NT][4];
+  if (DW) {
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) U[c][rt] = my_u[(4 * c + rt) * 64 + lane];
+  } else {
+#pragma unroll
+    for (int c = 0; c < NT; ++c) utilde_tile(tv.th, tv.tl, tv.v[NT * w + c], U[c], g4, l16, lane);
+    __syncthreads();               // every wave has read tv
+    dma_tv_share<NW, NT>(nx, tv, a.h_v * kD, w, lane);
+  }
 #pragma unroll
   for (int c = 0; c < NT; ++c)
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      U[c][rt] = my_u[(4 * c + rt) * 64 + lane];
-      QSt[c][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int rt = 0; rt < 4; ++rt) QSt[c][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // the decay factors this lane uses, read now so their latency hides behind the products:
   // lam4[q] = gam_C / gam of tokens 16 q + 4 g4 .. + 3, gs[nt] = scale gam of token 16 nt + l16
   f32x4 lam4[4];
@@ -795,35 +858,72 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
   }
 }
 
-// All direct loads of one chunk, issued by one wave (the loading wave of a DW workgroup):
-// the three 16 KB images, P^T, the decay factors, and the U~ tiles of each of the NW
-// compute waves (wave v's tiles start at value row col_base + 16 NT v).
-template <int NW, int NT>
-__device__ __forceinline__ void dma_all(const PrefillArgs& a, StateBuf& dst, f32x4 (*dst_u)[4 * NT][64],
-                                        const DmaPlan& dp, int c, int t0, int t_seq1, int h, int j,
-                                        int col_base, int lane) {
-  const int qk_stride = a.h_qk * kD;
+// The shared-operand loads of one chunk, issued by one wave (the loading wave of a DW
+// workgroup): the three 16 KB images, P^T and the decay factors.
+__device__ __forceinline__ void dma_all(const DmaChunk& d, const DmaPlan& dp, int qk_stride, int lane) {
 #pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    const DmaChunk d = dma_chunk(a, dst, &dst_u[v][0][0], c, t0, t_seq1, h, j, col_base + 16 * NT * v);
-    if (v == 0) {
-#pragma unroll
-      for (int p = 0; p < dma_pieces(16, NT); ++p) dma_piece(p, NT, d, dp, qk_stride, 0, lane);
-    } else {
-#pragma unroll
-      for (int p = 0; p < 4 * NT; ++p) dma_piece(p, NT, d, dp, qk_stride, 0, lane);
-    }
-  }
+  for (int p = 0; p < dma_pieces(16); ++p) dma_piece(p, d, dp, qk_stride, 0, lane);
 }
 
-// DW = true adds a loading wave (wave NW) that issues every direct load of the next chunk
-// right after each chunk's barrier and then waits for them, so the NW compute waves never
-// stall on issuing loads. Its U~ tiles need their own double buffer.
-template <int NW, int NT, bool DW>
-__global__ __launch_bounds__((NW + DW) * kWave) void state_kernel(PrefillArgs a) {
+// The U~ inputs of one chunk, issued by one wave (the U~ wave of a DW workgroup): T diag(beta)
+// hi and lo and the workgroup's value tiles.
+template <int NTILE>
+__device__ __forceinline__ constexpr int dma_tv_pieces() { return 16 + 2 * NTILE; }
+template <int NTILE>
+__device__ __forceinline__ void dma_tv_all(const DmaChunk& d, TvBuf<NTILE>& tv, int v_stride, int lane) {
+#pragma unroll
+  for (int f = 0; f < 16; ++f) dma_tb(f, d, tv, lane);
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma_v(t, i, d, tv, v_stride, lane);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
+// (vmcnt split over bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Workgroup barrier for the U~ wave: its LDS reads and writes complete first (lgkmcnt(0)),
+// but not its direct loads still in flight, which only it reads, after its own wait. The
+// empty asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The U~ wave's products for every tile of the workgroup from landed inputs: into the compute
+// waves' tile buffers, in the accumulator layout.
+template <int NW, int NT>
+__device__ __forceinline__ void utilde_all(const TvBuf<NW * NT>& tv, f32x4 (*dst_u)[4 * NT][64], int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int v = 0; v < NW; ++v)
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      f32x4 u[4];
+      utilde_tile(tv.th, tv.tl, tv.v[NT * v + c], u, g4, l16, lane);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) dst_u[v][4 * c + rt][lane] = u[rt];
+    }
+}
+
+// DW = true adds two helper waves. The loading wave (wave NW) issues the shared-operand
+// loads of the next chunk right after each chunk's barrier and waits for them, so the NW
+// compute waves never stall on issuing loads. The U~ wave (wave NW + 1) forms the next
+// chunk's U~ for all compute waves into a double buffer of tiles; with TVB = 2 buffers of
+// U~ inputs it loads them two chunks ahead, so their latency overlaps its products.
+template <int NW, int NT, bool DW, int TVB>
+__global__ __launch_bounds__((NW + 2 * DW) * kWave) void state_kernel(PrefillArgs a) {
+  static_assert(DW || TVB == 1, "without helper waves U~ inputs are single buffered");
   __shared__ StateBuf buf0;
   __shared__ StateBuf buf1;
-  __shared__ f32x4 utiles[DW ? 2 : 1][NW][4 * NT][64];
+  // U~ inputs: one or two buffers, separate objects so reads of one never wait for loads
+  // into the other
+  __shared__ TvBuf<NW * NT> tv;
+  __shared__ std::conditional_t<TVB == 2, TvBuf<NW * NT>, char> tv_b;
+  __shared__ f32x4 utiles[DW ? 2 : 1][DW ? NW : 1][DW ? 4 * NT : 1][64];
   constexpr int kBlocks = 8 / (NW * NT);      // workgroups per (sequence, V head)
   constexpr int NI = 16 / NW;
   const int tid = threadIdx.x;
@@ -846,21 +946,86 @@ __global__ __launch_bounds__((NW + DW) * kWave) void state_kernel(PrefillArgs a)
   const int n_chunks = (t_seq1 - t_seq0 + kC - 1) / kC;
   const int c_begin = first_chunk(a.cu, n, lane);
   const int qk_stride = a.h_qk * kD;
+  const int v_stride = a.h_v * kD;
 
-  if (DW && w == NW) {   // the loading wave: one barrier per chunk, like the compute waves
-    DmaPlan dpl;
-    dma_plan(dpl, 16, 0, lane);
-    if (n_chunks > 0) dma_all<NW, NT>(a, buf0, utiles[0], dpl, c_begin, t_seq0, t_seq1, h, j, col_base, lane);
-    for (int ci = 0; ci < n_chunks; ++ci) {
-      __builtin_amdgcn_s_waitcnt(0);   // chunk ci has landed
-      __syncthreads();                 // ... and the other buffers are free
-      if (ci + 1 < n_chunks) {
-        const int t1 = t_seq0 + (ci + 1) * kC;
-        if (ci & 1) dma_all<NW, NT>(a, buf0, utiles[0], dpl, c_begin + ci + 1, t1, t_seq1, h, j, col_base, lane);
-        else dma_all<NW, NT>(a, buf1, utiles[DW ? 1 : 0], dpl, c_begin + ci + 1, t1, t_seq1, h, j, col_base, lane);
+  if constexpr (DW) {
+    if (w == NW) {   // the loading wave: one barrier per chunk, like the compute waves
+      DmaPlan dpl;
+      dma_plan(dpl, 16, 0, lane);
+      auto issue = [&](int ci, StateBuf& dst) {
+        dma_all(dma_chunk(a, dst, c_begin + ci, t_seq0 + ci * kC, t_seq1, h, j, col_base), dpl, qk_stride, lane);
+      };
+      // even chunks into buf0, odd ones into buf1 (fixed destinations, so the addresses fold)
+      if (n_chunks > 0) issue(0, buf0);
+      for (int ci = 0; ci < n_chunks; ci += 2) {
+        __builtin_amdgcn_s_waitcnt(0);   // chunk ci has landed
+        __syncthreads();                 // ... and buf1 is free
+        if (ci + 1 < n_chunks) {
+          issue(ci + 1, buf1);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+          if (ci + 2 < n_chunks) issue(ci + 2, buf0);
+        }
       }
+      return;
     }
-    return;
+    if (w == NW + 1) {   // the U~ wave: chunk ci + 1's U~ during chunk ci
+      constexpr int kTv = dma_tv_pieces<NW * NT>();
+      auto issue = [&](int ci, TvBuf<NW * NT>& dst) {   // U~ inputs of chunk ci
+        dma_tv_all(dma_chunk(a, buf0, c_begin + ci, t_seq0 + ci * kC, t_seq1, h, j, col_base), dst, v_stride, lane);
+      };
+      if constexpr (TVB == 2) {
+        // even chunks' inputs in tv, odd chunks' in tv_b: chunk ci + 2's are issued while
+        // chunk ci + 1's (issued a chunk earlier) are used
+        if (n_chunks > 0) {
+          issue(0, tv);
+          if (n_chunks > 1) {
+            issue(1, tv_b);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTv));
+          } else {
+            __builtin_amdgcn_s_waitcnt(0);
+          }
+          utilde_all<NW, NT>(tv, utiles[0], lane);
+        }
+        for (int ci = 0; ci < n_chunks; ci += 2) {
+          barrier_lds_only();
+          if (ci + 1 < n_chunks) {
+            if (ci + 2 < n_chunks) {
+              issue(ci + 2, tv);
+              __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTv));
+            } else {
+              __builtin_amdgcn_s_waitcnt(0);
+            }
+            utilde_all<NW, NT>(tv_b, utiles[1], lane);
+            barrier_lds_only();
+            if (ci + 2 < n_chunks) {
+              if (ci + 3 < n_chunks) {
+                issue(ci + 3, tv_b);
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTv));
+              } else {
+                __builtin_amdgcn_s_waitcnt(0);
+              }
+              utilde_all<NW, NT>(tv, utiles[0], lane);
+            }
+          }
+        }
+      } else {
+        if (n_chunks > 0) {
+          issue(0, tv);
+          __builtin_amdgcn_s_waitcnt(0);
+          utilde_all<NW, NT>(tv, utiles[0], lane);
+        }
+        for (int ci = 0; ci < n_chunks; ++ci) {
+          barrier_lds_only();
+          if (ci + 1 < n_chunks) {
+            issue(ci + 1, tv);
+            __builtin_amdgcn_s_waitcnt(0);
+            utilde_all<NW, NT>(tv, utiles[(ci + 1) & 1], lane);
+          }
+        }
+      }
+      return;
+    }
   }
 
   const int col0 = col_base + 16 * NT * w;    // this wave's first value row
@@ -880,22 +1045,23 @@ __global__ __launch_bounds__((NW + DW) * kWave) void state_kernel(PrefillArgs a)
                        : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  f32x4* my_u0 = &utiles[0][w][0][0];
-  f32x4* my_u1 = &utiles[DW ? 1 : 0][w][0][0];
+  const f32x4* my_u0 = &utiles[0][DW ? w : 0][0][0];
+  const f32x4* my_u1 = &utiles[DW ? 1 : 0][DW ? w : 0][0][0];
   if (!DW && n_chunks > 0) {
-    const DmaChunk d0 = dma_chunk(a, buf0, my_u0, c_begin, t_seq0, t_seq1, h, j, col0);
+    const DmaChunk d0 = dma_chunk(a, buf0, c_begin, t_seq0, t_seq1, h, j, col_base);
+    dma_tv_share<NW, NT>(d0, tv, v_stride, w, lane);
 #pragma unroll
     for (int s = 0; s < dma_slots(NT); ++s) dma_slot<NI, NT>(s, d0, dp, qk_stride, w, lane);
   }
   // chunks alternate between the two LDS buffers
   for (int ci = 0; ci < n_chunks; ci += 2) {
     const int t0 = t_seq0 + ci * kC;
-    const DmaChunk d1 = dma_chunk(a, buf1, my_u1, c_begin + ci + 1, t0 + kC, t_seq1, h, j, col0);
-    state_chunk<NW, NT, DW>(a, buf0, my_u0, lo, dp, St, d1, t0, min(kC, t_seq1 - t0), h, col0, w, lane);
+    const DmaChunk d1 = dma_chunk(a, buf1, c_begin + ci + 1, t0 + kC, t_seq1, h, j, col_base);
+    state_chunk<NW, NT, DW>(a, buf0, my_u0, tv, lo, dp, St, d1, t0, min(kC, t_seq1 - t0), h, col0, w, lane);
     if (ci + 1 < n_chunks) {
       const int t1 = t0 + kC;
-      const DmaChunk d2 = dma_chunk(a, buf0, my_u0, c_begin + ci + 2, t1 + kC, t_seq1, h, j, col0);
-      state_chunk<NW, NT, DW>(a, buf1, my_u1, lo, dp, St, d2, t1, min(kC, t_seq1 - t1), h, col0, w, lane);
+      const DmaChunk d2 = dma_chunk(a, buf0, c_begin + ci + 2, t1 + kC, t_seq1, h, j, col_base);
+      state_chunk<NW, NT, DW>(a, buf1, my_u1, tv, lo, dp, St, d2, t1, min(kC, t_seq1 - t1), h, col0, w, lane);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);   // the last (unused) direct loads land before LDS is released
@@ -955,13 +1121,13 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
   const size_t groups = (seq_pairs + 7) / 8 * 8 * (size_t)a.group;
   const size_t heads = (size_t)num_seqs * h_v;
   if (heads * 8 <= kStateCus) {
-    hipLaunchKernelGGL((state_kernel<1, 1, true>), dim3((unsigned)(groups * 8)), dim3(2 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<1, 1, true, 2>), dim3((unsigned)(groups * 8)), dim3(3 * kWave), 0, stream, a);
   } else if (heads * 4 <= kStateCus) {
-    hipLaunchKernelGGL((state_kernel<2, 1, true>), dim3((unsigned)(groups * 4)), dim3(3 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<2, 1, true, 1>), dim3((unsigned)(groups * 4)), dim3(4 * kWave), 0, stream, a);
   } else if (heads * 2 <= kStateCus) {
-    hipLaunchKernelGGL((state_kernel<4, 1, false>), dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<4, 1, false, 1>), dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((state_kernel<4, 2, false>), dim3((unsigned)groups), dim3(4 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<4, 2, false, 1>), dim3((unsigned)groups), dim3(4 * kWave), 0, stream, a);
   }
   return hipGetLastError();
 }
