@@ -219,11 +219,10 @@ __device__ __forceinline__ void dma_rows128(const bf16* src, bf16* img, int i, i
 struct PrepSmem {
   bf16 K[kC * kD];              // swizzled 256-byte rows
   union {
-    bf16 Q[kC * kD];            // loads and Q K^T only; then A; then -T diag(beta gam)
-    float A[kC][kF32Pad];
+    bf16 Q[kC * kD];            // loads and Q K^T only; then A with T; then -T diag(beta gam)
+    float A[kC][kF32Pad];       // A in the strict lower triangle, T transposed in the upper one
     bf16 Tbg[kC][kTokPad];
   } r1;
-  float T[kC][kF32Pad];         // T = (I + A)^-1
   alignas(16) float G[kC];
   alignas(16) float beta[kC];
   alignas(16) float gam[kC];
@@ -286,7 +285,7 @@ __device__ __forceinline__ void gram_epilogue(PrepSmem& sm, const f32x4 (&acc)[5
   }
 }
 
-__global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
   __shared__ PrepSmem sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
@@ -364,19 +363,24 @@ __global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillArgs a) {
   __syncthreads();
 
   // ---- T = (I + A)^-1 --------------------------------------------------------------------
+  // T is unit lower triangular and A strictly lower triangular, so they share one array: A
+  // keeps the strict lower triangle and T[r][c] (r >= c) goes to the mirror position [c][r].
+  float (&M)[kC][kF32Pad] = sm.r1.A;
   // diagonal 16 x 16 blocks: wave b inverts block b, lane = column, one column of A at a time
   if (lane < 16) {
     const int b0 = 16 * w, col = lane;
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) {   // row r of the block: x_r = e_r - sum_{m < r} A_rm x_m
+      f32x4 ar[4];
 #pragma unroll
-    for (int m = 0; m < 15; ++m) {
+      for (int q = 0; q < (r + 3) / 4; ++q) ar[q] = *reinterpret_cast<const f32x4*>(&M[b0 + r][b0 + 4 * q]);
+      float acc = (r == col) ? 1.f : 0.f;
 #pragma unroll
-      for (int r = m + 1; r < 16; ++r) x[r] -= sm.r1.A[b0 + r][b0 + m] * x[m];
+      for (int m = 0; m < r; ++m) acc -= ar[m >> 2][m & 3] * x[m];
+      x[r] = acc;
+      if (r >= col) M[b0 + col][b0 + r] = acc;
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sm.T[b0 + r][b0 + col] = x[r];
   }
   __syncthreads();
   // off-diagonal block (i, b), i = b + d:  T_ib = -T_ii * sum_{k=b}^{i-1} A_ik T_kb,
@@ -388,57 +392,61 @@ __global__ __launch_bounds__(kThreads, 3) void prep_kernel(PrefillArgs a) {
       f32x4 X = {0.f, 0.f, 0.f, 0.f};
       for (int kb = b; kb < i; ++kb) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          X = mfma_f32(sm.r1.A[16 * i + l16][16 * kb + 4 * ks + g4],
-                       sm.T[16 * kb + 4 * ks + g4][16 * b + l16], X);
+        for (int ks = 0; ks < 4; ++ks) {
+          // T[16 kb + 4 ks + g4][16 b + l16]; within the diagonal block only its lower part
+          const float t = M[16 * b + l16][16 * kb + 4 * ks + g4];
+          X = mfma_f32(M[16 * i + l16][16 * kb + 4 * ks + g4], (kb > b || 4 * ks + g4 >= l16) ? t : 0.f, X);
+        }
       }
       // X in the C layout feeds the next product as B with K order {4g + ks}
       f32x4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) Y = mfma_f32(-sm.T[16 * i + l16][16 * i + 4 * g4 + ks], X[ks], Y);
+      for (int ks = 0; ks < 4; ++ks) {
+        const float t = M[16 * i + 4 * g4 + ks][16 * i + l16];   // T[16 i + l16][16 i + 4 g4 + ks]
+        Y = mfma_f32(4 * g4 + ks <= l16 ? -t : 0.f, X[ks], Y);
+      }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.T[16 * i + 4 * g4 + r][16 * b + l16] = Y[r];
+      for (int r = 0; r < 4; ++r) M[16 * b + l16][16 * i + 4 * g4 + r] = Y[r];
     }
     __syncthreads();
   }
 
   // ---- operands from T: T diag(beta) as a hi + lo bf16 pair, straight to the workspace
   // in operand order, and -T diag(beta gam) into A's space (A is consumed) ------------------
+  // Lane = row r; wave w takes columns s0 = 8 (w + 4 it) .. + 7, so the reads of T's
+  // mirrored entries M[s][r] hit distinct banks.
   bf16* Thg = reinterpret_cast<bf16*>(wsh + kWsTh);
   bf16* Tlg = reinterpret_cast<bf16*>(wsh + kWsTl);
-  f32x4 Tv[2][2], bv[2][2], gmv[2][2];   // every LDS read first (see the epilogue above)
+  bf16x8 hv[2], lv[2], gv[2];
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
-    const int pc = tid + kThreads * it;         // 512 pieces of 8 elements
-    const int r = pc >> 3, s0 = (pc & 7) * 8;
+    const int r = lane, s0 = 8 * (w + 4 * it);
+    float tv[8];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      Tv[it][hh] = *reinterpret_cast<const f32x4*>(&sm.T[r][s0 + 4 * hh]);
-      bv[it][hh] = *reinterpret_cast<const f32x4*>(&sm.beta[s0 + 4 * hh]);
-      gmv[it][hh] = *reinterpret_cast<const f32x4*>(&sm.gam[s0 + 4 * hh]);
-    }
-  }
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int pc = tid + kThreads * it;
-    const int r = pc >> 3, s0 = (pc & 7) * 8;
-    bf16x8 hv, lv, gv;
+    for (int e = 0; e < 8; ++e) tv[e] = M[s0 + e][r];
+    const f32x4 bv[2] = {*reinterpret_cast<const f32x4*>(&sm.beta[s0]), *reinterpret_cast<const f32x4*>(&sm.beta[s0 + 4])};
+    const f32x4 gm[2] = {*reinterpret_cast<const f32x4*>(&sm.gam[s0]), *reinterpret_cast<const f32x4*>(&sm.gam[s0 + 4])};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      // T is lower triangular; its strict upper part is never written
-      const float tb = (s0 + e <= r) ? Tv[it][e >> 2][e & 3] * bv[it][e >> 2][e & 3] : 0.f;
+      // T is lower triangular; the mirror of its strict upper part holds A
+      const float tb = (s0 + e <= r) ? tv[e] * bv[e >> 2][e & 3] : 0.f;
       const bf16 hh = to_bf16(tb);
-      hv[e] = hh;
-      lv[e] = to_bf16(tb - (float)hh);
-      gv[e] = to_bf16(-tb * gmv[it][e >> 2][e & 3]);
+      hv[it][e] = hh;
+      lv[it][e] = to_bf16(tb - (float)hh);
+      gv[it][e] = to_bf16(-tb * gm[e >> 2][e & 3]);
     }
+  }
+  __syncthreads();   // T is read; its space takes -T diag(beta gam)
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int r = lane, s0 = 8 * (w + 4 * it);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int off = tb_frag_off(r, s0 + 4 * hh);
-      *reinterpret_cast<bf16x4*>(Thg + off) = bf16x4{hv[4 * hh], hv[4 * hh + 1], hv[4 * hh + 2], hv[4 * hh + 3]};
-      *reinterpret_cast<bf16x4*>(Tlg + off) = bf16x4{lv[4 * hh], lv[4 * hh + 1], lv[4 * hh + 2], lv[4 * hh + 3]};
+      *reinterpret_cast<bf16x4*>(Thg + off) = bf16x4{hv[it][4 * hh], hv[it][4 * hh + 1], hv[it][4 * hh + 2], hv[it][4 * hh + 3]};
+      *reinterpret_cast<bf16x4*>(Tlg + off) = bf16x4{lv[it][4 * hh], lv[it][4 * hh + 1], lv[it][4 * hh + 2], lv[it][4 * hh + 3]};
     }
-    *reinterpret_cast<bf16x8*>(&sm.r1.Tbg[r][s0]) = gv;
+    *reinterpret_cast<bf16x8*>(&sm.r1.Tbg[r][s0]) = gv[it];
   }
   __syncthreads();
 
@@ -657,8 +665,9 @@ __device__ __forceinline__ void dma_slot(int s, const DmaChunk& d, const DmaPlan
     if (p * dma_slots(NT) / P == s) dma_piece(p, d, dp, qk_stride, w, lane);
 }
 
-__device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& dst, int c, int t0, int t_seq1,
-                                              int h, int j, int col_base) {
+// Sources of chunk c's loads (destinations left unset).
+__device__ __forceinline__ DmaChunk dma_src(const PrefillArgs& a, int c, int t0, int t_seq1, int h, int j,
+                                           int col_base) {
   DmaChunk d;
   const uint8_t* head = a.ws + ((size_t)c * a.h_v + h) * kWsHead;
   const size_t qk_stride = (size_t)a.h_qk * kD;
@@ -670,12 +679,18 @@ __device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& ds
   d.th = reinterpret_cast<const bf16*>(head + kWsTh);
   d.tl = reinterpret_cast<const bf16*>(head + kWsTl);
   d.vb = a.v + ((size_t)t0 * a.h_v + h) * kD + col_base;
+  d.nv = min(kC, t_seq1 - t0);
+  return d;
+}
+
+__device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& dst, int c, int t0, int t_seq1,
+                                              int h, int j, int col_base) {
+  DmaChunk d = dma_src(a, c, t0, t_seq1, h, j, col_base);
   d.d_w = dst.W;
   d.d_pt = dst.Pt;
   d.d_q = dst.Q;
   d.d_k = dst.K;
   d.d_gl = dst.gl;
-  d.nv = min(kC, t_seq1 - t0);
   return d;
 }
 
@@ -868,8 +883,6 @@ __device__ __forceinline__ void dma_all(const DmaChunk& d, const DmaPlan& dp, in
 // The U~ inputs of one chunk, issued by one wave (the U~ wave of a DW workgroup): T diag(beta)
 // hi and lo and the workgroup's value tiles.
 template <int NTILE>
-__device__ __forceinline__ constexpr int dma_tv_pieces() { return 16 + 2 * NTILE; }
-template <int NTILE>
 __device__ __forceinline__ void dma_tv_all(const DmaChunk& d, TvBuf<NTILE>& tv, int v_stride, int lane) {
 #pragma unroll
   for (int f = 0; f < 16; ++f) dma_tb(f, d, tv, lane);
@@ -878,10 +891,6 @@ __device__ __forceinline__ void dma_tv_all(const DmaChunk& d, TvBuf<NTILE>& tv, 
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma_v(t, i, d, tv, v_stride, lane);
 }
-
-// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
-// (vmcnt split over bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
-__device__ __forceinline__ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // Workgroup barrier for the U~ wave: its LDS reads and writes complete first (lgkmcnt(0)),
 // but not its direct loads still in flight, which only it reads, after its own wait. The
@@ -912,17 +921,12 @@ __device__ __forceinline__ void utilde_all(const TvBuf<NW * NT>& tv, f32x4 (*dst
 // DW = true adds two helper waves. The loading wave (wave NW) issues the shared-operand
 // loads of the next chunk right after each chunk's barrier and waits for them, so the NW
 // compute waves never stall on issuing loads. The U~ wave (wave NW + 1) forms the next
-// chunk's U~ for all compute waves into a double buffer of tiles; with TVB = 2 buffers of
-// U~ inputs it loads them two chunks ahead, so their latency overlaps its products.
-template <int NW, int NT, bool DW, int TVB>
+// chunk's U~ for all compute waves into a double buffer of tiles.
+template <int NW, int NT, bool DW>
 __global__ __launch_bounds__((NW + 2 * DW) * kWave) void state_kernel(PrefillArgs a) {
-  static_assert(DW || TVB == 1, "without helper waves U~ inputs are single buffered");
   __shared__ StateBuf buf0;
   __shared__ StateBuf buf1;
-  // U~ inputs: one or two buffers, separate objects so reads of one never wait for loads
-  // into the other
   __shared__ TvBuf<NW * NT> tv;
-  __shared__ std::conditional_t<TVB == 2, TvBuf<NW * NT>, char> tv_b;
   __shared__ f32x4 utiles[DW ? 2 : 1][DW ? NW : 1][DW ? 4 * NT : 1][64];
   constexpr int kBlocks = 8 / (NW * NT);      // workgroups per (sequence, V head)
   constexpr int NI = 16 / NW;
@@ -970,58 +974,20 @@ __global__ __launch_bounds__((NW + 2 * DW) * kWave) void state_kernel(PrefillArg
       return;
     }
     if (w == NW + 1) {   // the U~ wave: chunk ci + 1's U~ during chunk ci
-      constexpr int kTv = dma_tv_pieces<NW * NT>();
-      auto issue = [&](int ci, TvBuf<NW * NT>& dst) {   // U~ inputs of chunk ci
-        dma_tv_all(dma_chunk(a, buf0, c_begin + ci, t_seq0 + ci * kC, t_seq1, h, j, col_base), dst, v_stride, lane);
+      auto issue = [&](int ci) {   // U~ inputs of chunk ci
+        dma_tv_all(dma_src(a, c_begin + ci, t_seq0 + ci * kC, t_seq1, h, j, col_base), tv, v_stride, lane);
       };
-      if constexpr (TVB == 2) {
-        // even chunks' inputs in tv, odd chunks' in tv_b: chunk ci + 2's are issued while
-        // chunk ci + 1's (issued a chunk earlier) are used
-        if (n_chunks > 0) {
-          issue(0, tv);
-          if (n_chunks > 1) {
-            issue(1, tv_b);
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTv));
-          } else {
-            __builtin_amdgcn_s_waitcnt(0);
-          }
-          utilde_all<NW, NT>(tv, utiles[0], lane);
-        }
-        for (int ci = 0; ci < n_chunks; ci += 2) {
-          barrier_lds_only();
-          if (ci + 1 < n_chunks) {
-            if (ci + 2 < n_chunks) {
-              issue(ci + 2, tv);
-              __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTv));
-            } else {
-              __builtin_amdgcn_s_waitcnt(0);
-            }
-            utilde_all<NW, NT>(tv_b, utiles[1], lane);
-            barrier_lds_only();
-            if (ci + 2 < n_chunks) {
-              if (ci + 3 < n_chunks) {
-                issue(ci + 3, tv_b);
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTv));
-              } else {
-                __builtin_amdgcn_s_waitcnt(0);
-              }
-              utilde_all<NW, NT>(tv, utiles[0], lane);
-            }
-          }
-        }
-      } else {
-        if (n_chunks > 0) {
-          issue(0, tv);
+      if (n_chunks > 0) {
+        issue(0);
+        __builtin_amdgcn_s_waitcnt(0);
+        utilde_all<NW, NT>(tv, utiles[0], lane);
+      }
+      for (int ci = 0; ci < n_chunks; ++ci) {
+        barrier_lds_only();
+        if (ci + 1 < n_chunks) {
+          issue(ci + 1);
           __builtin_amdgcn_s_waitcnt(0);
-          utilde_all<NW, NT>(tv, utiles[0], lane);
-        }
-        for (int ci = 0; ci < n_chunks; ++ci) {
-          barrier_lds_only();
-          if (ci + 1 < n_chunks) {
-            issue(ci + 1, tv);
-            __builtin_amdgcn_s_waitcnt(0);
-            utilde_all<NW, NT>(tv, utiles[(ci + 1) & 1], lane);
-          }
+          utilde_all<NW, NT>(tv, utiles[(ci + 1) & 1], lane);
         }
       }
       return;
@@ -1077,6 +1043,299 @@ __global__ __launch_bounds__((NW + 2 * DW) * kWave) void state_kernel(PrefillArg
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// state_ro_kernel: the fewest-heads state pass (one 16-row value tile per workgroup, eight
+// workgroups per head) with the read-out on a wave of its own. The chain wave (wave 0)
+// forms U = U~ - W S^T and the state update -- the chain from one chunk's state to the
+// next -- and hands S^T and U over as packed bf16 operands. The read-out wave (wave 3)
+// forms each chunk's (Q S^T)^T and O^T = scale gam (Q S^T)^T + U^T P^T during the next
+// chunk, from its own copies of Q, P^T and the decay factors. The loading wave (wave 1)
+// streams -W, K and the decay factors, the U~ wave (wave 2) forms U~ a chunk ahead. One
+// barrier per chunk and one at the end; the read-out is the same arithmetic as in
+// state_chunk, so results agree bit for bit with the other shapes.
+// ------------------------------------------------------------------------------------------
+
+// The chain wave's per-chunk operands, and the read-out wave's.
+struct ChainBuf {
+  bf16 W[kC * kD];       // -W, 256-byte rows
+  bf16 K[kC * kD];       // 256-byte rows
+  float gl[4 * kC];      // gam, then gam_C / gam (see dma_piece)
+};
+struct ReadBuf {
+  bf16 Q[kC * kD];       // 256-byte rows
+  bf16 Pt[kC * kC];      // P^T, 128-byte rows
+  float gl[4 * kC];
+};
+// What the chain wave hands the read-out wave for one chunk, in lane order: S^T for the
+// four K-steps of (Q S^T)^T and U for the two K-steps of U^T P^T.
+struct Exchange {
+  bf16x8 s[4][64];
+  bf16x8 u[2][64];
+};
+
+// Loads into a chain buffer (-W, K, decay factors) or a read-out buffer (Q, P^T, decay
+// factors), by one wave: the pieces of dma_piece with NI = 16 that each needs.
+__device__ __forceinline__ void dma_chain(const PrefillArgs& a, ChainBuf& dst, int c, int t0, int t_seq1, int h,
+                                          int j, int col_base, const DmaPlan& dp, int qk_stride, int lane) {
+  DmaChunk d = dma_src(a, c, t0, t_seq1, h, j, col_base);
+  d.d_w = dst.W;
+  d.d_k = dst.K;
+  d.d_gl = dst.gl;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    dma_piece(3 * i, d, dp, qk_stride, 0, lane);
+    dma_piece(3 * i + 2, d, dp, qk_stride, 0, lane);
+  }
+  dma_piece(3 * 16 + 8, d, dp, qk_stride, 0, lane);
+}
+__device__ __forceinline__ void dma_read(const PrefillArgs& a, ReadBuf& dst, int c, int t0, int t_seq1, int h,
+                                         int j, int col_base, const DmaPlan& dp, int qk_stride, int lane) {
+  DmaChunk d = dma_src(a, c, t0, t_seq1, h, j, col_base);
+  d.d_q = dst.Q;
+  d.d_pt = dst.Pt;
+  d.d_gl = dst.gl;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dma_piece(3 * i + 1, d, dp, qk_stride, 0, lane);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dma_piece(3 * 16 + i, d, dp, qk_stride, 0, lane);
+  dma_piece(3 * 16 + 8, d, dp, qk_stride, 0, lane);
+}
+
+// The chain wave's part of one chunk.
+__device__ __forceinline__ void chain_chunk(const ChainBuf& cur, const f32x4* my_u, Exchange& xo,
+                                            const LaneOffsets& lo, f32x4 (&St)[8], int lane) {
+  const int g4 = lane >> 4;
+  __syncthreads();                 // the chunk's operands and U~ are in
+  f32x4 U[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) U[rt] = my_u[rt * 64 + lane];
+  f32x4 lam4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) lam4[q] = *reinterpret_cast<const f32x4*>(&cur.gl[kC + 16 * q + 4 * g4]);
+  const float gC = cur.gl[kC - 1];
+  bf16x8 Sb[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    Sb[ks] = pack8(St[2 * ks], St[2 * ks + 1]);
+    xo.s[ks][lane] = Sb[ks];
+  }
+  // U -= W S^T, operands of K-step ks + 1 read while the products of K-step ks run
+  const bf16* Wl = cur.W;
+  bf16x8 aw[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) aw[0][rt] = lds8(Wl + lo.row[0] + 2048 * rt);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int cb = ks & 1;
+    if (ks + 1 < 4) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) aw[cb ^ 1][rt] = lds8(Wl + lo.row[ks + 1] + 2048 * rt);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) U[rt] = mfma16x16x32(aw[cb][rt], Sb[ks], U[rt]);
+  }
+  // U as bf16 for the read-out; the decayed U as a hi + lo pair for the state update
+  bf16x8 Bh[2], Bl[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    xo.u[ks][lane] = pack8(U[2 * ks], U[2 * ks + 1]);
+    f32x4 hi[2], lw[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float u = U[2 * ks + hh][i] * lam4[2 * ks + hh][i];
+        const float uh = (float)to_bf16(u);
+        hi[hh][i] = uh;
+        lw[hh][i] = u - uh;
+      }
+    Bh[ks] = pack8(hi[0], hi[1]);
+    Bl[ks] = pack8(lw[0], lw[1]);
+  }
+  // S^T <- gam_C S^T + K^T (diag(gam_C / gam) U), operands of tile mt + 1 read ahead
+  const bf16* K = cur.K;
+  bf16x8 ak[2][2];
+  ak[0][0] = join8(lds_tr4(K + lo.k[0]), lds_tr4(K + lo.k[0] + 2048));
+  ak[0][1] = join8(lds_tr4(K + lo.k[0] + 4096), lds_tr4(K + lo.k[0] + 6144));
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const int cb = mt & 1;
+    if (mt + 1 < 8) {
+      ak[cb ^ 1][0] = join8(lds_tr4(K + lo.k[mt + 1]), lds_tr4(K + lo.k[mt + 1] + 2048));
+      ak[cb ^ 1][1] = join8(lds_tr4(K + lo.k[mt + 1] + 4096), lds_tr4(K + lo.k[mt + 1] + 6144));
+    }
+    f32x4 s = St[mt] * gC;
+    s = mfma16x16x32(ak[cb][0], Bh[0], s);
+    s = mfma16x16x32(ak[cb][0], Bl[0], s);
+    s = mfma16x16x32(ak[cb][1], Bh[1], s);
+    St[mt] = mfma16x16x32(ak[cb][1], Bl[1], s);
+  }
+}
+
+// The read-out wave's part of one chunk (tokens t0 .. t0 + nv - 1).
+__device__ __forceinline__ void readout_chunk(const PrefillArgs& a, const ReadBuf& rb, const Exchange& xo,
+                                              const LaneOffsets& lo, int t0, int nv, int h, int col0, int lane) {
+  const int g4 = lane >> 4;
+  const int l16 = lane & 15;
+  f32x4 QSt[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) QSt[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const bf16x8 sb = xo.s[ks][lane];
+    bf16x8 aq[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) aq[rt] = lds8(rb.Q + lo.row[ks] + 2048 * rt);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) QSt[rt] = mfma16x16x32(sb, aq[rt], QSt[rt]);
+  }
+  float gs[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gs[q] = rb.gl[16 * q + l16];
+  const bf16x8 ub[2] = {xo.u[0][lane], xo.u[1][lane]};
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      a.o + ((size_t)t0 * a.h_v + h) * kD, (short)0, nv * a.h_v * kD * 2, 0x00020000);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    bf16x8 bp[2];
+#pragma unroll
+    for (int ks = 0; ks <= nt / 2; ++ks)
+      bp[ks] = join8(lds_tr4(rb.Pt + lo.t128[nt] + 2048 * ks), lds_tr4(rb.Pt + lo.t128[nt] + 2048 * ks + 1024));
+    const float gsn = a.scale * gs[nt];
+    const int tok = 16 * nt + l16;
+    f32x4 acc = QSt[nt] * gsn;
+#pragma unroll
+    for (int ks = 0; ks <= nt / 2; ++ks) acc = mfma16x16x32(ub[ks], bp[ks], acc);
+    bf16x4 ov;
+    ov[0] = to_bf16(acc[0]); ov[1] = to_bf16(acc[1]); ov[2] = to_bf16(acc[2]); ov[3] = to_bf16(acc[3]);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov), orsrc,
+                                          (tok * a.h_v * kD + col0 + 4 * g4) * 2, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(4 * kWave) void state_ro_kernel(PrefillArgs a) {
+  __shared__ ChainBuf cb0;
+  __shared__ ChainBuf cb1;
+  __shared__ TvBuf<1> tv;
+  __shared__ f32x4 utiles[2][1][4][64];
+  __shared__ Exchange xo0;
+  __shared__ Exchange xo1;
+  __shared__ ReadBuf rb0;
+  __shared__ ReadBuf rb1;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  const int lane = tid & 63;
+  const int g4 = lane >> 4;
+  const int l16 = lane & 15;
+
+  // eight workgroups per head; those of the V heads sharing one QK head sit on one XCD
+  const int per = 8 * a.group * 8;
+  const int bid = blockIdx.x;
+  const int grp = bid / per, rem = bid % per;
+  const int p = grp * 8 + rem % 8;            // (sequence, QK head) pair
+  if (p >= a.num_seqs * a.h_qk) return;
+  const int sub = rem / 8;
+  const int n = p / a.h_qk, j = p % a.h_qk;
+  const int h = j * a.group + sub / 8;
+  const int col0 = (sub % 8) * 16;            // the workgroup's value rows
+  const int t_seq0 = a.cu[n], t_seq1 = a.cu[n + 1];
+  const int n_chunks = (t_seq1 - t_seq0 + kC - 1) / kC;
+  const int c_begin = first_chunk(a.cu, n, lane);
+  const int qk_stride = a.h_qk * kD;
+  const int v_stride = a.h_v * kD;
+  DmaPlan dpl;
+  dma_plan(dpl, 16, 0, lane);
+  LaneOffsets lo;
+  lane_offsets(lo, g4, l16);
+
+  if (w == 1) {   // the loading wave: chunk ci + 1's chain operands during chunk ci
+    auto issue = [&](int ci, ChainBuf& dst) {
+      dma_chain(a, dst, c_begin + ci, t_seq0 + ci * kC, t_seq1, h, j, col0, dpl, qk_stride, lane);
+    };
+    if (n_chunks > 0) issue(0, cb0);
+    for (int ci = 0; ci < n_chunks; ci += 2) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (ci + 1 < n_chunks) {
+        issue(ci + 1, cb1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (ci + 2 < n_chunks) issue(ci + 2, cb0);
+      }
+    }
+    __syncthreads();
+    return;
+  }
+  if (w == 2) {   // the U~ wave: chunk ci + 1's U~ during chunk ci
+    auto issue = [&](int ci) {
+      dma_tv_all(dma_src(a, c_begin + ci, t_seq0 + ci * kC, t_seq1, h, j, col0), tv, v_stride, lane);
+    };
+    if (n_chunks > 0) {
+      issue(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      utilde_all<1, 1>(tv, utiles[0], lane);
+    }
+    for (int ci = 0; ci < n_chunks; ++ci) {
+      barrier_lds_only();
+      if (ci + 1 < n_chunks) {
+        issue(ci + 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        utilde_all<1, 1>(tv, utiles[(ci + 1) & 1], lane);
+      }
+    }
+    barrier_lds_only();
+    return;
+  }
+  if (w == 3) {   // the read-out wave: chunk ci's read-out after barrier ci + 1
+    auto issue = [&](int ci, ReadBuf& dst) {
+      dma_read(a, dst, c_begin + ci, t_seq0 + ci * kC, t_seq1, h, j, col0, dpl, qk_stride, lane);
+    };
+    auto readout = [&](int ci, const ReadBuf& rb, const Exchange& xo) {
+      const int t0 = t_seq0 + ci * kC;
+      __builtin_amdgcn_s_waitcnt(0);   // its Q, P^T and decay factors have landed
+      readout_chunk(a, rb, xo, lo, t0, min(kC, t_seq1 - t0), h, col0, lane);
+    };
+    if (n_chunks > 0) issue(0, rb0);
+    if (n_chunks > 1) issue(1, rb1);
+    for (int ci = 0; ci < n_chunks; ci += 2) {
+      barrier_lds_only();
+      if (ci >= 1) {
+        readout(ci - 1, rb1, xo1);
+        if (ci + 1 < n_chunks) issue(ci + 1, rb1);
+      }
+      if (ci + 1 < n_chunks) {
+        barrier_lds_only();
+        readout(ci, rb0, xo0);
+        if (ci + 2 < n_chunks) issue(ci + 2, rb0);
+      }
+    }
+    barrier_lds_only();
+    if (n_chunks > 0) {
+      if ((n_chunks - 1) & 1) readout(n_chunks - 1, rb1, xo1);
+      else readout(n_chunks - 1, rb0, xo0);
+    }
+    return;
+  }
+
+  // the chain wave. St[mt][i] = S[col0 + l16][32 (mt / 2) + 8 g4 + 4 (mt % 2) + i]
+  f32x4 St[8];
+  const size_t state_off = (((size_t)n * a.h_v + h) * kD + col0 + l16) * kD;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+    St[mt] = a.s0 ? *reinterpret_cast<const f32x4*>(a.s0 + state_off + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1))
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ci = 0; ci < n_chunks; ci += 2) {
+    chain_chunk(cb0, &utiles[0][0][0][0], xo0, lo, St, lane);
+    if (ci + 1 < n_chunks) chain_chunk(cb1, &utiles[1][0][0][0], xo1, lo, St, lane);
+  }
+  __syncthreads();   // the last chunk's hand-over is visible to the read-out wave
+  if (a.s_final) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      *reinterpret_cast<f32x4*>(a.s_final + state_off + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1)) = St[mt];
+  }
+}
+
 }  // namespace
 
 size_t chunk_prefill_workspace_bytes(int total_tokens, int num_seqs, int h_qk, int h_v) {
@@ -1121,13 +1380,13 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
   const size_t groups = (seq_pairs + 7) / 8 * 8 * (size_t)a.group;
   const size_t heads = (size_t)num_seqs * h_v;
   if (heads * 8 <= kStateCus) {
-    hipLaunchKernelGGL((state_kernel<1, 1, true, 2>), dim3((unsigned)(groups * 8)), dim3(3 * kWave), 0, stream, a);
+    hipLaunchKernelGGL(state_ro_kernel, dim3((unsigned)(groups * 8)), dim3(4 * kWave), 0, stream, a);
   } else if (heads * 4 <= kStateCus) {
-    hipLaunchKernelGGL((state_kernel<2, 1, true, 1>), dim3((unsigned)(groups * 4)), dim3(4 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<2, 1, true>), dim3((unsigned)(groups * 4)), dim3(4 * kWave), 0, stream, a);
   } else if (heads * 2 <= kStateCus) {
-    hipLaunchKernelGGL((state_kernel<4, 1, false, 1>), dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<4, 1, false>), dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((state_kernel<4, 2, false, 1>), dim3((unsigned)groups), dim3(4 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<4, 2, false>), dim3((unsigned)groups), dim3(4 * kWave), 0, stream, a);
   }
   return hipGetLastError();
 }
