@@ -320,7 +320,7 @@ def main():
                        "global_batch": 1, "seq_len": tokens, "parallelism": "none (1 GPU)"},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                         "kernel": "gdn_chunk_prefill call: prep_kernel + state_kernel<1, 1, true>",
+                         "kernel": "gdn_chunk_prefill call: prep_kernel + state_ro_kernel",
                          "call_ms": call_ms, "algorithmic_bytes": nbytes},
             "roofline_mfma": {"achieved": flops / (call_ms / 1e3) / 1e12,
                               "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

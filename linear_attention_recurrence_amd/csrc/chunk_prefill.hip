@@ -1113,27 +1113,31 @@ __device__ __forceinline__ void chain_chunk(const ChainBuf& cur, const f32x4* my
 #pragma unroll
   for (int q = 0; q < 4; ++q) lam4[q] = *reinterpret_cast<const f32x4*>(&cur.gl[kC + 16 * q + 4 * g4]);
   const float gC = cur.gl[kC - 1];
+  // every operand of the chunk is read up front (-W rows for U, then K^T for the update), so
+  // the LDS latency overlaps the products instead of stalling each step
+  const bf16* Wl = cur.W;
+  const bf16* K = cur.K;
+  bf16x8 aw[4][4], ak[8][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) aw[ks][rt] = lds8(Wl + lo.row[ks] + 2048 * rt);
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    ak[mt][0] = join8(lds_tr4(K + lo.k[mt]), lds_tr4(K + lo.k[mt] + 2048));
+    ak[mt][1] = join8(lds_tr4(K + lo.k[mt] + 4096), lds_tr4(K + lo.k[mt] + 6144));
+  }
   bf16x8 Sb[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     Sb[ks] = pack8(St[2 * ks], St[2 * ks + 1]);
     xo.s[ks][lane] = Sb[ks];
   }
-  // U -= W S^T, operands of K-step ks + 1 read while the products of K-step ks run
-  const bf16* Wl = cur.W;
-  bf16x8 aw[2][4];
+  // U -= W S^T
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) aw[0][rt] = lds8(Wl + lo.row[0] + 2048 * rt);
+  for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int cb = ks & 1;
-    if (ks + 1 < 4) {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) aw[cb ^ 1][rt] = lds8(Wl + lo.row[ks + 1] + 2048 * rt);
-    }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) U[rt] = mfma16x16x32(aw[cb][rt], Sb[ks], U[rt]);
-  }
+    for (int rt = 0; rt < 4; ++rt) U[rt] = mfma16x16x32(aw[ks][rt], Sb[ks], U[rt]);
   // U as bf16 for the read-out; the decayed U as a hi + lo pair for the state update
   bf16x8 Bh[2], Bl[2];
 #pragma unroll
@@ -1152,60 +1156,60 @@ __device__ __forceinline__ void chain_chunk(const ChainBuf& cur, const f32x4* my
     Bh[ks] = pack8(hi[0], hi[1]);
     Bl[ks] = pack8(lw[0], lw[1]);
   }
-  // S^T <- gam_C S^T + K^T (diag(gam_C / gam) U), operands of tile mt + 1 read ahead
-  const bf16* K = cur.K;
-  bf16x8 ak[2][2];
-  ak[0][0] = join8(lds_tr4(K + lo.k[0]), lds_tr4(K + lo.k[0] + 2048));
-  ak[0][1] = join8(lds_tr4(K + lo.k[0] + 4096), lds_tr4(K + lo.k[0] + 6144));
+  // S^T <- gam_C S^T + K^T (diag(gam_C / gam) U)
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
-    const int cb = mt & 1;
-    if (mt + 1 < 8) {
-      ak[cb ^ 1][0] = join8(lds_tr4(K + lo.k[mt + 1]), lds_tr4(K + lo.k[mt + 1] + 2048));
-      ak[cb ^ 1][1] = join8(lds_tr4(K + lo.k[mt + 1] + 4096), lds_tr4(K + lo.k[mt + 1] + 6144));
-    }
     f32x4 s = St[mt] * gC;
-    s = mfma16x16x32(ak[cb][0], Bh[0], s);
-    s = mfma16x16x32(ak[cb][0], Bl[0], s);
-    s = mfma16x16x32(ak[cb][1], Bh[1], s);
-    St[mt] = mfma16x16x32(ak[cb][1], Bl[1], s);
+    s = mfma16x16x32(ak[mt][0], Bh[0], s);
+    s = mfma16x16x32(ak[mt][0], Bl[0], s);
+    s = mfma16x16x32(ak[mt][1], Bh[1], s);
+    St[mt] = mfma16x16x32(ak[mt][1], Bl[1], s);
   }
 }
 
-// The read-out wave's part of one chunk (tokens t0 .. t0 + nv - 1).
+// The read-out wave's part of one chunk (tokens t0 .. t0 + nv - 1). Every operand is read
+// first; once those reads are done `reads_done()` runs (the caller refills `rb` there, so the
+// refill's latency overlaps the products).
+template <typename F>
 __device__ __forceinline__ void readout_chunk(const PrefillArgs& a, const ReadBuf& rb, const Exchange& xo,
-                                              const LaneOffsets& lo, int t0, int nv, int h, int col0, int lane) {
+                                              const LaneOffsets& lo, int t0, int nv, int h, int col0, int lane,
+                                              F reads_done) {
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
-  f32x4 QSt[4];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) QSt[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 sb[4], aq[4][4], bp[4][2];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const bf16x8 sb = xo.s[ks][lane];
-    bf16x8 aq[4];
+    sb[ks] = xo.s[ks][lane];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) aq[rt] = lds8(rb.Q + lo.row[ks] + 2048 * rt);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) QSt[rt] = mfma16x16x32(sb, aq[rt], QSt[rt]);
+    for (int rt = 0; rt < 4; ++rt) aq[ks][rt] = lds8(rb.Q + lo.row[ks] + 2048 * rt);
   }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int ks = 0; ks <= nt / 2; ++ks)
+      bp[nt][ks] = join8(lds_tr4(rb.Pt + lo.t128[nt] + 2048 * ks), lds_tr4(rb.Pt + lo.t128[nt] + 2048 * ks + 1024));
   float gs[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) gs[q] = rb.gl[16 * q + l16];
   const bf16x8 ub[2] = {xo.u[0][lane], xo.u[1][lane]};
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+  reads_done();
+  f32x4 QSt[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) QSt[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) QSt[rt] = mfma16x16x32(sb[ks], aq[ks][rt], QSt[rt]);
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
       a.o + ((size_t)t0 * a.h_v + h) * kD, (short)0, nv * a.h_v * kD * 2, 0x00020000);
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    bf16x8 bp[2];
-#pragma unroll
-    for (int ks = 0; ks <= nt / 2; ++ks)
-      bp[ks] = join8(lds_tr4(rb.Pt + lo.t128[nt] + 2048 * ks), lds_tr4(rb.Pt + lo.t128[nt] + 2048 * ks + 1024));
     const float gsn = a.scale * gs[nt];
     const int tok = 16 * nt + l16;
     f32x4 acc = QSt[nt] * gsn;
 #pragma unroll
-    for (int ks = 0; ks <= nt / 2; ++ks) acc = mfma16x16x32(ub[ks], bp[ks], acc);
+    for (int ks = 0; ks <= nt / 2; ++ks) acc = mfma16x16x32(ub[ks], bp[nt][ks], acc);
     bf16x4 ov;
     ov[0] = to_bf16(acc[0]); ov[1] = to_bf16(acc[1]); ov[2] = to_bf16(acc[2]); ov[3] = to_bf16(acc[3]);
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov), orsrc,
@@ -1290,23 +1294,22 @@ __global__ __launch_bounds__(4 * kWave) void state_ro_kernel(PrefillArgs a) {
     auto issue = [&](int ci, ReadBuf& dst) {
       dma_read(a, dst, c_begin + ci, t_seq0 + ci * kC, t_seq1, h, j, col0, dpl, qk_stride, lane);
     };
-    auto readout = [&](int ci, const ReadBuf& rb, const Exchange& xo) {
+    // chunk ci's read-out from buffer ci % 2, which then takes chunk ci + 2's operands
+    auto readout = [&](int ci, ReadBuf& rb, const Exchange& xo) {
       const int t0 = t_seq0 + ci * kC;
       __builtin_amdgcn_s_waitcnt(0);   // its Q, P^T and decay factors have landed
-      readout_chunk(a, rb, xo, lo, t0, min(kC, t_seq1 - t0), h, col0, lane);
+      readout_chunk(a, rb, xo, lo, t0, min(kC, t_seq1 - t0), h, col0, lane, [&] {
+        if (ci + 2 < n_chunks) issue(ci + 2, rb);
+      });
     };
     if (n_chunks > 0) issue(0, rb0);
     if (n_chunks > 1) issue(1, rb1);
     for (int ci = 0; ci < n_chunks; ci += 2) {
       barrier_lds_only();
-      if (ci >= 1) {
-        readout(ci - 1, rb1, xo1);
-        if (ci + 1 < n_chunks) issue(ci + 1, rb1);
-      }
+      if (ci >= 1) readout(ci - 1, rb1, xo1);
       if (ci + 1 < n_chunks) {
         barrier_lds_only();
         readout(ci, rb0, xo0);
-        if (ci + 2 < n_chunks) issue(ci + 2, rb0);
       }
     }
     barrier_lds_only();
