@@ -59,7 +59,7 @@ const char* gdn_status_string(gdn_status s);
 
 /*
  * Bytes of device workspace gdn_chunk_prefill needs (io_dtype GDN_BF16) for these sizes: for
- * every 64-token chunk, 41472 bytes per V head (-W, the masked and decayed Q K^T, decay
+ * every 64-token chunk, 37376 bytes per V head (-W, the masked and decayed Q K^T, decay
  * factors, and T diag(beta) = (I + A)^-1 diag(beta) as a hi + lo bf16 pair), sized for
  * ceil(total_tokens / 64) + num_seqs chunks so no host read of cu_seqlens is needed.
  * Returns 0 for invalid sizes. The contents are scratch: nothing persists between calls,

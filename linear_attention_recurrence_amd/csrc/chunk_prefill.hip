@@ -65,17 +65,22 @@ constexpr size_t kWsW = 0;                          // bf16 [64][128]: -W
 constexpr size_t kWsP = kWsW + kC * kD * 2;         // bf16 [64][64]: P^T
 constexpr size_t kWsGam = kWsP + kC * kC * 2;       // fp32 [64]: gam_r
 constexpr size_t kWsLam = kWsGam + kC * 4;          // fp32 [64]: gam_C / gam_r
+constexpr int kTbFrags = 6;                         // nonzero T diag(beta) operand fragments
 constexpr size_t kWsTh = kWsLam + kC * 4;          // bf16 T diag(beta), hi, operand order (below)
-constexpr size_t kWsTl = kWsTh + kC * kC * 2;       // bf16 T diag(beta), lo, operand order
-constexpr size_t kWsHead = kWsTl + kC * kC * 2;     // 41472 bytes
+constexpr size_t kWsTl = kWsTh + kTbFrags * 1024;  // bf16 T diag(beta), lo, operand order
+constexpr size_t kWsHead = kWsTl + kTbFrags * 1024; // 37376 bytes
 
 // T diag(beta) is stored in the order the state pass reads it as the A operand of
-// U~ = T diag(beta) V: fragment 2 rt + ks (row tile rt, K-step ks) holds, for lane
+// U~ = T diag(beta) V: the fragment of row tile rt and K-step ks holds, for lane
 // l = l16 + 16 g4, the eight entries T[16 rt + l16][32 ks + 16 h + 4 g4 + i] (h, i = 0, 1 /
-// 0..3, element 4 h + i), so one 16-byte read per lane fetches an operand. Element offset of
-// entry (r, s) for s a multiple of 4:
+// 0..3, element 4 h + i), so one 16-byte read per lane fetches an operand. T is lower
+// triangular, so the fragments with ks > rt / 2 are zero and are not stored: the six others
+// are numbered 0, 1 (rt = 0, 1), then 2 + 2 (rt - 2) + ks.
+__device__ __forceinline__ constexpr int tb_frag(int rt, int ks) { return rt < 2 ? rt : 2 * rt - 2 + ks; }
+// Element offset of entry (r, s) for s a multiple of 4 (r >= s rounded down to the fragment,
+// i.e. a stored fragment).
 __device__ __forceinline__ int tb_frag_off(int r, int s) {
-  return ((2 * (r >> 4) + (s >> 5)) * 64 + (r & 15) + 16 * ((s >> 2) & 3)) * 8 + 4 * ((s >> 4) & 1);
+  return (tb_frag(r >> 4, s >> 5) * 64 + (r & 15) + 16 * ((s >> 2) & 3)) * 8 + 4 * ((s >> 4) & 1);
 }
 
 __host__ __device__ inline size_t max_chunks(int total_tokens, int num_seqs) {
@@ -440,11 +445,13 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int r = lane, s0 = 8 * (w + 4 * it);
+    if ((s0 >> 5) <= (r >> 4) / 2) {   // a stored (not all-zero) fragment
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int off = tb_frag_off(r, s0 + 4 * hh);
-      *reinterpret_cast<bf16x4*>(Thg + off) = bf16x4{hv[it][4 * hh], hv[it][4 * hh + 1], hv[it][4 * hh + 2], hv[it][4 * hh + 3]};
-      *reinterpret_cast<bf16x4*>(Tlg + off) = bf16x4{lv[it][4 * hh], lv[it][4 * hh + 1], lv[it][4 * hh + 2], lv[it][4 * hh + 3]};
+      for (int hh = 0; hh < 2; ++hh) {
+        const int off = tb_frag_off(r, s0 + 4 * hh);
+        *reinterpret_cast<bf16x4*>(Thg + off) = bf16x4{hv[it][4 * hh], hv[it][4 * hh + 1], hv[it][4 * hh + 2], hv[it][4 * hh + 3]};
+        *reinterpret_cast<bf16x4*>(Tlg + off) = bf16x4{lv[it][4 * hh], lv[it][4 * hh + 1], lv[it][4 * hh + 2], lv[it][4 * hh + 3]};
+      }
     }
     *reinterpret_cast<bf16x8*>(&sm.r1.Tbg[r][s0]) = gv[it];
   }
@@ -498,8 +505,8 @@ struct StateBuf {
 // order, and the workgroup's NTILE value tiles, [tile][token][16] bf16 (32-byte rows).
 template <int NTILE>
 struct TvBuf {
-  bf16 th[kC * kC];
-  bf16 tl[kC * kC];
+  bf16 th[kTbFrags * 512];
+  bf16 tl[kTbFrags * 512];
   bf16 v[NTILE][kC * 16];
 };
 
@@ -533,12 +540,11 @@ __device__ __forceinline__ void lane_offsets(LaneOffsets& o, int g4, int l16) {
 __device__ __forceinline__ void utilde_tile(const bf16* th, const bf16* tl, const bf16* vt, f32x4 (&u)[4],
                                             int g4, int l16, int lane) {
   const int vo = (4 * g4 + (l16 >> 2)) * 16 + 4 * (l16 & 3);
-  bf16x8 bv[2], ah[8], al[8];   // every LDS read first, then the products
+  bf16x8 bv[2], ah[kTbFrags], al[kTbFrags];   // every LDS read first, then the products
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) bv[ks] = join8(lds_tr4(vt + vo + 512 * ks), lds_tr4(vt + vo + 512 * ks + 256));
 #pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    if ((f & 1) > (f >> 1) / 2) continue;   // fragments above the diagonal are zero
+  for (int f = 0; f < kTbFrags; ++f) {
     ah[f] = lds8(th + (f * 64 + lane) * 8);
     al[f] = lds8(tl + (f * 64 + lane) * 8);
   }
@@ -547,8 +553,8 @@ __device__ __forceinline__ void utilde_tile(const bf16* th, const bf16* tl, cons
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks <= rt / 2; ++ks) {
-      acc = mfma16x16x32(ah[2 * rt + ks], bv[ks], acc);
-      acc = mfma16x16x32(al[2 * rt + ks], bv[ks], acc);
+      acc = mfma16x16x32(ah[tb_frag(rt, ks)], bv[ks], acc);
+      acc = mfma16x16x32(al[tb_frag(rt, ks)], bv[ks], acc);
     }
     u[rt] = acc;
   }
@@ -632,11 +638,12 @@ __device__ __forceinline__ void dma_piece(int p, const DmaChunk& d, const DmaPla
   __builtin_amdgcn_global_load_lds(d.gl + (lane & 31) * 4, (lds_void_ptr)d.d_gl, 16, 0, 0);
 }
 
-// Direct load of T diag(beta) fragment f (0..7 hi, 8..15 lo): a straight 1 KB copy.
+// Direct load of stored T diag(beta) fragment f (0..5 hi, 6..11 lo): a straight 1 KB copy.
 template <int NTILE>
 __device__ __forceinline__ void dma_tb(int f, const DmaChunk& d, TvBuf<NTILE>& tv, int lane) {
-  const bf16* src = (f < 8 ? d.th : d.tl) + 512 * (f & 7) + 8 * lane;
-  bf16* dst = (f < 8 ? tv.th : tv.tl) + 512 * (f & 7);
+  const int g = f < kTbFrags ? f : f - kTbFrags;
+  const bf16* src = (f < kTbFrags ? d.th : d.tl) + 512 * g + 8 * lane;
+  bf16* dst = (f < kTbFrags ? tv.th : tv.tl) + 512 * g;
   __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
 }
 
@@ -700,7 +707,7 @@ template <int NW, int NT>
 __device__ __forceinline__ void dma_tv_share(const DmaChunk& d, TvBuf<NW * NT>& tv, int v_stride, int w,
                                              int lane) {
 #pragma unroll
-  for (int f = 0; f < 16 / NW; ++f) dma_tb(f + (16 / NW) * w, d, tv, lane);
+  for (int f = 0; f < 2 * kTbFrags / NW; ++f) dma_tb(f + (2 * kTbFrags / NW) * w, d, tv, lane);
 #pragma unroll
   for (int c = 0; c < NT; ++c)
 #pragma unroll
@@ -885,7 +892,7 @@ __device__ __forceinline__ void dma_all(const DmaChunk& d, const DmaPlan& dp, in
 template <int NTILE>
 __device__ __forceinline__ void dma_tv_all(const DmaChunk& d, TvBuf<NTILE>& tv, int v_stride, int lane) {
 #pragma unroll
-  for (int f = 0; f < 16; ++f) dma_tb(f, d, tv, lane);
+  for (int f = 0; f < 2 * kTbFrags; ++f) dma_tb(f, d, tv, lane);
 #pragma unroll
   for (int t = 0; t < NTILE; ++t)
 #pragma unroll
