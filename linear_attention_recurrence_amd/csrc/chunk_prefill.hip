@@ -65,10 +65,18 @@ constexpr size_t kWsW = 0;                          // bf16 [64][128]: -W
 constexpr size_t kWsP = kWsW + kC * kD * 2;         // bf16 [64][64]: P^T
 constexpr size_t kWsGam = kWsP + kC * kC * 2;       // fp32 [64]: gam_r
 constexpr size_t kWsLam = kWsGam + kC * 4;          // fp32 [64]: gam_C / gam_r
+constexpr size_t kWsG = kWsLam + kC * 4;            // fp32 [64]: G_r (the log-decay prefix sums)
 constexpr int kTbFrags = 6;                         // nonzero T diag(beta) operand fragments
-constexpr size_t kWsTh = kWsLam + kC * 4;          // bf16 T diag(beta), hi, operand order (below)
+constexpr size_t kWsTh = kWsGam + 1024;             // bf16 T diag(beta), hi, operand order (below)
 constexpr size_t kWsTl = kWsTh + kTbFrags * 1024;  // bf16 T diag(beta), lo, operand order
-constexpr size_t kWsHead = kWsTl + kTbFrags * 1024; // 37376 bytes
+constexpr size_t kWsTbg = kWsTl + kTbFrags * 1024; // bf16 -T diag(beta gam), operand order
+constexpr size_t kWsHead = kWsTbg + kTbFrags * 1024; // 44032 bytes
+
+// Which parts a block holds depends on how the state pass runs. With few heads (a loading
+// wave per workgroup) prep writes -W and P^T; with many heads the state pass forms both on
+// chip from Q, K and -T diag(beta gam) (bit for bit the same values), so prep writes
+// -T diag(beta gam) instead and reads no Q. The decay factors and T diag(beta) are always
+// written.
 
 // T diag(beta) is stored in the order the state pass reads it as the A operand of
 // U~ = T diag(beta) V: the fragment of row tile rt and K-step ks holds, for lane
@@ -290,6 +298,9 @@ __device__ __forceinline__ void gram_epilogue(PrepSmem& sm, const f32x4 (&acc)[5
   }
 }
 
+// FULL: write -W and P^T (few heads); otherwise -T diag(beta gam) for the state pass to
+// form them (see the workspace layout above).
+template <bool FULL>
 __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
   __shared__ PrepSmem sm;
   const int tid = threadIdx.x;
@@ -318,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     dma_rows256(a.k + (size_t)t0 * qk_stride + (size_t)j * kD, qk_stride, nv, sm.K, i, w, lane);
-    dma_rows256(a.q + (size_t)t0 * qk_stride + (size_t)j * kD, qk_stride, nv, sm.r1.Q, i, w, lane);
+    if (FULL) dma_rows256(a.q + (size_t)t0 * qk_stride + (size_t)j * kD, qk_stride, nv, sm.r1.Q, i, w, lane);
   }
   if (tid < kC) {
     float gg = 0.f, bb = 0.f;
@@ -346,6 +357,7 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
     sm.gam[lane] = gm;
     reinterpret_cast<float*>(wsh + kWsGam)[lane] = gm;
     reinterpret_cast<float*>(wsh + kWsLam)[lane] = __expf(GC - x);
+    reinterpret_cast<float*>(wsh + kWsG)[lane] = x;
   }
 
   // ---- K K^T and Q K^T: the 10 lower tiles of each; waves 0, 1 take K K^T, waves 2, 3
@@ -353,15 +365,15 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
   f32x4 acc[5];
   if (w == 0) gram_tiles<false, 0>(sm, acc, g4, l16);
   else if (w == 1) gram_tiles<false, 1>(sm, acc, g4, l16);
-  else if (w == 2) gram_tiles<true, 0>(sm, acc, g4, l16);
-  else gram_tiles<true, 1>(sm, acc, g4, l16);
+  else if (FULL && w == 2) gram_tiles<true, 0>(sm, acc, g4, l16);
+  else if (FULL) gram_tiles<true, 1>(sm, acc, g4, l16);
   __syncthreads();   // Q is consumed (its space becomes A) and G is ready
   bf16* Pt = reinterpret_cast<bf16*>(wsh + kWsP);
   if (w == 0) gram_epilogue<false, 0>(sm, acc, Pt, a.scale, g4, l16);
   else if (w == 1) gram_epilogue<false, 1>(sm, acc, Pt, a.scale, g4, l16);
-  else if (w == 2) gram_epilogue<true, 0>(sm, acc, Pt, a.scale, g4, l16);
-  else gram_epilogue<true, 1>(sm, acc, Pt, a.scale, g4, l16);
-  if (tid < 128) {   // the strictly upper tiles of P that the read-out's 32-token K-steps see
+  else if (FULL && w == 2) gram_epilogue<true, 0>(sm, acc, Pt, a.scale, g4, l16);
+  else if (FULL) gram_epilogue<true, 1>(sm, acc, Pt, a.scale, g4, l16);
+  if (FULL && tid < 128) {   // the strictly upper tiles of P that the read-out's 32-token K-steps see
     const int rt = (tid >> 6) * 2, ln = tid & 63;
     *reinterpret_cast<bf16x4*>(Pt + (16 * (rt + 1) + (ln & 15)) * kC + 16 * rt + 4 * (ln >> 4)) = bf16x4{};
   }
@@ -417,11 +429,13 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
   }
 
   // ---- operands from T: T diag(beta) as a hi + lo bf16 pair, straight to the workspace
-  // in operand order, and -T diag(beta gam) into A's space (A is consumed) ------------------
+  // in operand order, and -T diag(beta gam) into A's space (A is consumed) or, without
+  // FULL, to the workspace in operand order --------------------------------------------------
   // Lane = row r; wave w takes columns s0 = 8 (w + 4 it) .. + 7, so the reads of T's
   // mirrored entries M[s][r] hit distinct banks.
   bf16* Thg = reinterpret_cast<bf16*>(wsh + kWsTh);
   bf16* Tlg = reinterpret_cast<bf16*>(wsh + kWsTl);
+  bf16* Tbgg = reinterpret_cast<bf16*>(wsh + kWsTbg);
   bf16x8 hv[2], lv[2], gv[2];
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
@@ -451,10 +465,13 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
         const int off = tb_frag_off(r, s0 + 4 * hh);
         *reinterpret_cast<bf16x4*>(Thg + off) = bf16x4{hv[it][4 * hh], hv[it][4 * hh + 1], hv[it][4 * hh + 2], hv[it][4 * hh + 3]};
         *reinterpret_cast<bf16x4*>(Tlg + off) = bf16x4{lv[it][4 * hh], lv[it][4 * hh + 1], lv[it][4 * hh + 2], lv[it][4 * hh + 3]};
+        if (!FULL)
+          *reinterpret_cast<bf16x4*>(Tbgg + off) = bf16x4{gv[it][4 * hh], gv[it][4 * hh + 1], gv[it][4 * hh + 2], gv[it][4 * hh + 3]};
       }
     }
-    *reinterpret_cast<bf16x8*>(&sm.r1.Tbg[r][s0]) = gv[it];
+    if (FULL) *reinterpret_cast<bf16x8*>(&sm.r1.Tbg[r][s0]) = gv[it];
   }
+  if (!FULL) return;
   __syncthreads();
 
   // ---- -W = -T diag(beta gam) K; wave w: column tiles 2w, 2w+1. -W is formed transposed
@@ -498,7 +515,7 @@ struct StateBuf {
   bf16 Pt[kC * kC];      // P^T, 128-byte rows
   bf16 Q[kC * kD];       // 256-byte rows
   bf16 K[kC * kD];       // 256-byte rows
-  float gl[4 * kC];      // gam, then gam_C / gam, then a copy of both (see dma_piece)
+  float gl[4 * kC];      // gam, then gam_C / gam, then G (see dma_piece)
 };
 
 // The inputs of U~ = T diag(beta) V, single buffered: T diag(beta) hi and lo in operand
@@ -507,6 +524,7 @@ template <int NTILE>
 struct TvBuf {
   bf16 th[kTbFrags * 512];
   bf16 tl[kTbFrags * 512];
+  bf16 tbg[kTbFrags * 512];   // -T diag(beta gam), for the shapes that form -W on chip
   bf16 v[NTILE][kC * 16];
 };
 
@@ -592,8 +610,7 @@ struct DmaChunk {
   const bf16* qb;       // row 0 of the chunk, this QK head
   const bf16* kb;
   const float* gl;
-  const bf16* th;       // T diag(beta) hi, lo (operand order)
-  const bf16* tl;
+  const bf16* th;       // T diag(beta) hi, then lo and -T diag(beta gam) (operand order)
   const bf16* vb;       // row 0 of the chunk, this V head, the workgroup's first value row
   bf16* d_w;            // LDS destinations
   bf16* d_pt;
@@ -632,18 +649,19 @@ __device__ __forceinline__ void dma_piece(int p, const DmaChunk& d, const DmaPla
     __builtin_amdgcn_global_load_lds(d.pt + dp.pt[p], (lds_void_ptr)(d.d_pt + 8 * ((ni / 2) * w + p) * kC), 16, 0, 0);
     return;
   }
-  // gam then lam, 512 contiguous bytes. Every wave issues it (identical data, so the
-  // overlapping writes agree) and the upper 32 lanes repeat the lower ones: no branch,
-  // which would split the scheduling regions around it.
-  __builtin_amdgcn_global_load_lds(d.gl + (lane & 31) * 4, (lds_void_ptr)d.d_gl, 16, 0, 0);
+  // gam, lam and G: the 1 KB decay-factor area of the block. Every wave issues it
+  // (identical data, so the overlapping writes agree): no branch, which would split the
+  // scheduling regions around it.
+  __builtin_amdgcn_global_load_lds(d.gl + lane * 4, (lds_void_ptr)d.d_gl, 16, 0, 0);
 }
 
-// Direct load of stored T diag(beta) fragment f (0..5 hi, 6..11 lo): a straight 1 KB copy.
+// Direct load of stored fragment f: T diag(beta) hi (0..5), lo (6..11), -T diag(beta gam)
+// (12..17). A straight 1 KB copy; the three sets are contiguous in the block and in TvBuf.
 template <int NTILE>
 __device__ __forceinline__ void dma_tb(int f, const DmaChunk& d, TvBuf<NTILE>& tv, int lane) {
-  const int g = f < kTbFrags ? f : f - kTbFrags;
-  const bf16* src = (f < kTbFrags ? d.th : d.tl) + 512 * g + 8 * lane;
-  bf16* dst = (f < kTbFrags ? tv.th : tv.tl) + 512 * g;
+  static_assert(kWsTl == kWsTh + kTbFrags * 1024 && kWsTbg == kWsTl + kTbFrags * 1024, "fragment sets");
+  const bf16* src = d.th + 512 * f + 8 * lane;
+  bf16* dst = tv.th + 512 * f;
   __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
 }
 
@@ -662,14 +680,20 @@ __device__ __forceinline__ void dma_v(int t, int i, const DmaChunk& d, TvBuf<NTI
 // evenly: one per state tile of the update (off the chain that leads from U to the next
 // state) and, with two value tiles per wave (more compute to hide them behind), one per
 // K-step of U.
+// When -W and P^T are formed on chip (FORM) the shared operands loaded are Q, K and the decay
+// factors: pieces 3 i + 1 and 3 i + 2 of dma_piece, then the decay factors.
 __device__ __forceinline__ constexpr int dma_slots(int nt) { return nt == 2 ? 12 : 8; }
-template <int NI, int NT>
+__device__ __forceinline__ constexpr int dma_qk_pieces(int ni) { return 2 * ni + 1; }
+__device__ __forceinline__ constexpr int dma_qk_piece(int p, int ni) {
+  return p < 2 * ni ? 3 * (p / 2) + 1 + (p % 2) : 3 * ni + ni / 2;
+}
+template <int NI, int NT, bool FORM>
 __device__ __forceinline__ void dma_slot(int s, const DmaChunk& d, const DmaPlan& dp, int qk_stride,
                                          int w, int lane) {
-  constexpr int P = dma_pieces(NI);
+  constexpr int P = FORM ? dma_qk_pieces(NI) : dma_pieces(NI);
 #pragma unroll
   for (int p = 0; p < P; ++p)
-    if (p * dma_slots(NT) / P == s) dma_piece(p, d, dp, qk_stride, w, lane);
+    if (p * dma_slots(NT) / P == s) dma_piece(FORM ? dma_qk_piece(p, NI) : p, d, dp, qk_stride, w, lane);
 }
 
 // Sources of chunk c's loads (destinations left unset).
@@ -684,7 +708,7 @@ __device__ __forceinline__ DmaChunk dma_src(const PrefillArgs& a, int c, int t0,
   d.kb = a.k + (size_t)t0 * qk_stride + (size_t)j * kD;
   d.gl = reinterpret_cast<const float*>(head + kWsGam);
   d.th = reinterpret_cast<const bf16*>(head + kWsTh);
-  d.tl = reinterpret_cast<const bf16*>(head + kWsTl);
+
   d.vb = a.v + ((size_t)t0 * a.h_v + h) * kD + col_base;
   d.nv = min(kC, t_seq1 - t0);
   return d;
@@ -703,15 +727,73 @@ __device__ __forceinline__ DmaChunk dma_chunk(const PrefillArgs& a, StateBuf& ds
 
 // This wave's loads of the U~ inputs of chunk `d` without a loading wave: a share of the
 // T diag(beta) fragments and its own value tiles.
-template <int NW, int NT>
+template <int NW, int NT, bool FORM>
 __device__ __forceinline__ void dma_tv_share(const DmaChunk& d, TvBuf<NW * NT>& tv, int v_stride, int w,
                                              int lane) {
+  constexpr int NF = (FORM ? 3 : 2) * kTbFrags;   // hi, lo (and -T diag(beta gam))
 #pragma unroll
-  for (int f = 0; f < 2 * kTbFrags / NW; ++f) dma_tb(f + (2 * kTbFrags / NW) * w, d, tv, lane);
+  for (int jf = 0; jf < (NF + NW - 1) / NW; ++jf) {
+    const int f = w + NW * jf;
+    if (f < NF) dma_tb(f, d, tv, lane);
+  }
 #pragma unroll
   for (int c = 0; c < NT; ++c)
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma_v(NT * w + c, i, d, tv, v_stride, lane);
+}
+
+// The one-workgroup-per-head shape (two tiles per wave, no loading wave) forms -W and P^T
+// on chip; the others read them from the workspace.
+__host__ __device__ constexpr bool forms_w_p(int nt, bool dw) { return nt == 2 && !dw; }
+
+// The many-heads shape forms -W and P^T on chip, into the chunk's LDS buffer, from its Q, K,
+// decay factors and -T diag(beta gam), with the products, operand orders and roundings of
+// prep_kernel, so the values are bit for bit those prep writes for the other shapes. Wave w
+// takes column tiles w, w + NW, ... of -W and tiles w, w + NW, ... of the 10 lower tiles
+// of P (P^T is stored by key token, four query tokens per lane).
+template <int NW, int NTILE>
+__device__ __forceinline__ void form_w_p(StateBuf& cur, const TvBuf<NTILE>& tv, float scale, int w, int g4,
+                                         int l16, int lane) {
+#pragma unroll
+  for (int jc = 0; jc < 8 / NW; ++jc) {
+    const int ct = w + NW * jc;
+    bf16x8 bk[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) bk[ks] = perm_tr256(cur.K, 32 * ks, 16 * ct, g4, l16);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4 aw = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks <= rt / 2; ++ks)
+        aw = mfma16x16x32(bk[ks], lds8(tv.tbg + (tb_frag(rt, ks) * 64 + lane) * 8), aw);
+      bf16x4 wv;
+      wv[0] = to_bf16(aw[0]); wv[1] = to_bf16(aw[1]); wv[2] = to_bf16(aw[2]); wv[3] = to_bf16(aw[3]);
+      *reinterpret_cast<bf16x4*>(cur.W + sw256(16 * rt + l16, 16 * ct + 4 * g4)) = wv;
+    }
+  }
+  const float* G = cur.gl + 2 * kC;
+#pragma unroll
+  for (int jt = 0; jt < (10 + NW - 1) / NW; ++jt) {
+    const int t = w + NW * jt;
+    if (t >= 10) break;
+    const int rt = tile_row(t), ct = tile_col(t);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc = mfma16x16x32(lds8(cur.Q + sw256(16 * rt + l16, 32 * ks + 8 * g4)),
+                         lds8(cur.K + sw256(16 * ct + l16, 32 * ks + 8 * g4)), acc);
+    const f32x4 Gr = *reinterpret_cast<const f32x4*>(&G[16 * rt + 4 * g4]);
+    const float Gs = G[16 * ct + l16];
+    const int s = 16 * ct + l16;
+    bf16x4 pv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rt + 4 * g4 + i;
+      const float decay = __expf(fminf(Gr[i] - Gs, 0.f));
+      pv[i] = to_bf16(s <= r ? scale * decay * acc[i] : 0.f);
+    }
+    *reinterpret_cast<bf16x4*>(cur.Pt + sw128(s, 16 * rt + 4 * g4)) = pv;
+  }
 }
 
 // One chunk of the state pass for this wave's 16 NT value rows (tiles c at col0 + 16 c),
@@ -726,11 +808,12 @@ __device__ __forceinline__ void dma_tv_share(const DmaChunk& d, TvBuf<NW * NT>& 
 // one, from this wave's own products over `tv`, after which a second barrier frees `tv` for
 // the next chunk's T diag(beta) and values.
 template <int NW, int NT, bool DW>
-__device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf& cur, const f32x4* my_u,
+__device__ __forceinline__ void state_chunk(const PrefillArgs& a, StateBuf& cur, const f32x4* my_u,
                                             TvBuf<NW * NT>& tv, const LaneOffsets& lo, const DmaPlan& dp,
                                             f32x4 (&St)[NT][8], const DmaChunk& nx, int t0, int nv, int h,
                                             int col0, int w, int lane) {
   constexpr int NI = 16 / NW;
+  constexpr bool FORM = forms_w_p(NT, DW);
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
   const int qk_stride = a.h_qk * kD;
@@ -747,10 +830,11 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) U[c][rt] = my_u[(4 * c + rt) * 64 + lane];
   } else {
+    if (FORM) form_w_p<NW>(cur, tv, a.scale, w, g4, l16, lane);
 #pragma unroll
     for (int c = 0; c < NT; ++c) utilde_tile(tv.th, tv.tl, tv.v[NT * w + c], U[c], g4, l16, lane);
-    __syncthreads();               // every wave has read tv
-    dma_tv_share<NW, NT>(nx, tv, a.h_v * kD, w, lane);
+    __syncthreads();               // every wave has read tv (and with FORM, -W and P^T are in)
+    dma_tv_share<NW, NT, FORM>(nx, tv, a.h_v * kD, w, lane);
   }
 #pragma unroll
   for (int c = 0; c < NT; ++c)
@@ -789,7 +873,7 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) aw[cb ^ 1][rt] = lds8(Wl + lo.row[ks + 1] + 2048 * rt);
     }
-    if (!DW && NT == 2) dma_slot<NI, NT>(ks, nx, dp, qk_stride, w, lane);
+    if (!DW && NT == 2) dma_slot<NI, NT, FORM>(ks, nx, dp, qk_stride, w, lane);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -847,7 +931,7 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, const StateBuf
       ak[cb ^ 1][0] = join8(lds_tr4(K + lo.k[m1]), lds_tr4(K + lo.k[m1] + 2048));
       ak[cb ^ 1][1] = join8(lds_tr4(K + lo.k[m1] + 4096), lds_tr4(K + lo.k[m1] + 6144));
     }
-    if (!DW) dma_slot<NI, NT>((NT == 2 ? 4 : 0) + mt, nx, dp, qk_stride, w, lane);
+    if (!DW) dma_slot<NI, NT, FORM>((NT == 2 ? 4 : 0) + mt, nx, dp, qk_stride, w, lane);
     const int nt = mt >> 1;
     bf16x8 bp[2];
     if (mt & 1) {
@@ -1018,13 +1102,19 @@ __global__ __launch_bounds__((NW + 2 * DW) * kWave) void state_kernel(PrefillArg
                        : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  if (forms_w_p(NT, DW) && tid < 128) {   // the strictly upper tiles of P that the read-out's 32-token K-steps see
+    const int rt = (tid >> 6) * 2, ln = tid & 63;
+    const int sr = 16 * (rt + 1) + (ln & 15), col = 16 * rt + 4 * (ln >> 4);
+    *reinterpret_cast<bf16x4*>(buf0.Pt + sw128(sr, col)) = bf16x4{};
+    *reinterpret_cast<bf16x4*>(buf1.Pt + sw128(sr, col)) = bf16x4{};
+  }
   const f32x4* my_u0 = &utiles[0][DW ? w : 0][0][0];
   const f32x4* my_u1 = &utiles[DW ? 1 : 0][DW ? w : 0][0][0];
   if (!DW && n_chunks > 0) {
     const DmaChunk d0 = dma_chunk(a, buf0, c_begin, t_seq0, t_seq1, h, j, col_base);
-    dma_tv_share<NW, NT>(d0, tv, v_stride, w, lane);
+    dma_tv_share<NW, NT, forms_w_p(NT, DW)>(d0, tv, v_stride, w, lane);
 #pragma unroll
-    for (int s = 0; s < dma_slots(NT); ++s) dma_slot<NI, NT>(s, d0, dp, qk_stride, w, lane);
+    for (int s = 0; s < dma_slots(NT); ++s) dma_slot<NI, NT, forms_w_p(NT, DW)>(s, d0, dp, qk_stride, w, lane);
   }
   // chunks alternate between the two LDS buffers
   for (int ci = 0; ci < n_chunks; ci += 2) {
@@ -1377,10 +1467,15 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
   a.n_chunks_max = (int)nc;
   a.scale = scale;
 
+  // the shapes for up to 128 heads read -W and P^T from the workspace; the one-workgroup-
+  // per-head shape forms them on chip (forms_w_p)
+  const size_t heads = (size_t)num_seqs * h_v;
+  const bool full = heads * 2 <= kStateCus;
   if (total_tokens > 0) {
     const size_t pairs = nc * (size_t)h_qk;
     const size_t prep_blocks = (pairs + 7) / 8 * 8 * (size_t)a.group;
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(kThreads), 0, stream, a);
+    if (full) hipLaunchKernelGGL(prep_kernel<true>, dim3((unsigned)prep_blocks), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(prep_kernel<false>, dim3((unsigned)prep_blocks), dim3(kThreads), 0, stream, a);
   }
   // With few heads, eight or four workgroups per head of one or two compute waves (one
   // tile each) and a loading wave spread the heads over many CUs; once the heads fill the
@@ -1388,7 +1483,6 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
   // that every workgroup repeats.
   const size_t seq_pairs = (size_t)num_seqs * h_qk;
   const size_t groups = (seq_pairs + 7) / 8 * 8 * (size_t)a.group;
-  const size_t heads = (size_t)num_seqs * h_v;
   if (heads * 8 <= kStateCus) {
     hipLaunchKernelGGL(state_ro_kernel, dim3((unsigned)(groups * 8)), dim3(4 * kWave), 0, stream, a);
   } else if (heads * 4 <= kStateCus) {
