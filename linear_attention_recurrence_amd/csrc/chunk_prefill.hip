@@ -498,13 +498,14 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// state_kernel<NW, NT>: NW waves of NT 16-row value tiles each per workgroup, so
+// state_kernel<NW, NT, DW>: NW waves of NT 16-row value tiles each per workgroup, so
 // 8 / (NW NT) workgroups per (sequence, V head), placed on one XCD. Every wave reads the
-// chunk's shared operands (-W, Q, K, P^T) from LDS once for all of its tiles: NT = 2 halves
-// the LDS traffic per value row, NT = 1 halves the dependent work per wave. With few heads
-// the pass is bound by each wave's chain of dependent steps (NT = 1, small workgroups on
-// many CUs); once the heads fill the chip it is bound by LDS traffic (NT = 2, one
-// workgroup per head).
+// chunk's shared operands (-W, Q, K, P^T) from LDS once for all of its tiles: NT = 2 would
+// halve the LDS traffic per value row, NT = 1 halves the dependent work per wave. With few
+// heads the pass is bound by each wave's chain of dependent steps (small workgroups on many
+// CUs); once the heads fill the chip, one workgroup of eight one-tile waves per head keeps
+// two waves on each SIMD, which hides the LDS latency that bounds a single wave there.
+// (state_ro_kernel, further below, is the fewest-heads shape.)
 // ------------------------------------------------------------------------------------------
 
 // LDS of the state pass: the shared per-chunk operands, double buffered as two separate
@@ -742,9 +743,9 @@ __device__ __forceinline__ void dma_tv_share(const DmaChunk& d, TvBuf<NW * NT>& 
     for (int i = 0; i < 2; ++i) dma_v(NT * w + c, i, d, tv, v_stride, lane);
 }
 
-// The one-workgroup-per-head shape (two tiles per wave, no loading wave) forms -W and P^T
-// on chip; the others read them from the workspace.
-__host__ __device__ constexpr bool forms_w_p(int nt, bool dw) { return nt == 2 && !dw; }
+// The one-workgroup-per-head shape (no loading wave) forms -W and P^T on chip; the others
+// read them from the workspace.
+__host__ __device__ constexpr bool forms_w_p(int nw, int nt, bool dw) { return !dw && nw * nt == 8; }
 
 // The many-heads shape forms -W and P^T on chip, into the chunk's LDS buffer, from its Q, K,
 // decay factors and -T diag(beta gam), with the products, operand orders and roundings of
@@ -813,7 +814,7 @@ __device__ __forceinline__ void state_chunk(const PrefillArgs& a, StateBuf& cur,
                                             f32x4 (&St)[NT][8], const DmaChunk& nx, int t0, int nv, int h,
                                             int col0, int w, int lane) {
   constexpr int NI = 16 / NW;
-  constexpr bool FORM = forms_w_p(NT, DW);
+  constexpr bool FORM = forms_w_p(NW, NT, DW);
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
   const int qk_stride = a.h_qk * kD;
@@ -1102,7 +1103,7 @@ __global__ __launch_bounds__((NW + 2 * DW) * kWave) void state_kernel(PrefillArg
                        : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (forms_w_p(NT, DW) && tid < 128) {   // the strictly upper tiles of P that the read-out's 32-token K-steps see
+  if (forms_w_p(NW, NT, DW) && tid < 128) {   // the strictly upper tiles of P that the read-out's 32-token K-steps see
     const int rt = (tid >> 6) * 2, ln = tid & 63;
     const int sr = 16 * (rt + 1) + (ln & 15), col = 16 * rt + 4 * (ln >> 4);
     *reinterpret_cast<bf16x4*>(buf0.Pt + sw128(sr, col)) = bf16x4{};
@@ -1112,9 +1113,9 @@ __global__ __launch_bounds__((NW + 2 * DW) * kWave) void state_kernel(PrefillArg
   const f32x4* my_u1 = &utiles[DW ? 1 : 0][DW ? w : 0][0][0];
   if (!DW && n_chunks > 0) {
     const DmaChunk d0 = dma_chunk(a, buf0, c_begin, t_seq0, t_seq1, h, j, col_base);
-    dma_tv_share<NW, NT, forms_w_p(NT, DW)>(d0, tv, v_stride, w, lane);
+    dma_tv_share<NW, NT, forms_w_p(NW, NT, DW)>(d0, tv, v_stride, w, lane);
 #pragma unroll
-    for (int s = 0; s < dma_slots(NT); ++s) dma_slot<NI, NT, forms_w_p(NT, DW)>(s, d0, dp, qk_stride, w, lane);
+    for (int s = 0; s < dma_slots(NT); ++s) dma_slot<NI, NT, forms_w_p(NW, NT, DW)>(s, d0, dp, qk_stride, w, lane);
   }
   // chunks alternate between the two LDS buffers
   for (int ci = 0; ci < n_chunks; ci += 2) {
@@ -1478,9 +1479,9 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
     else hipLaunchKernelGGL(prep_kernel<false>, dim3((unsigned)prep_blocks), dim3(kThreads), 0, stream, a);
   }
   // With few heads, eight or four workgroups per head of one or two compute waves (one
-  // tile each) and a loading wave spread the heads over many CUs; once the heads fill the
-  // chip, one 4-wave workgroup of two tiles per wave per head avoids the operand traffic
-  // that every workgroup repeats.
+  // tile each) and helper waves spread the heads over many CUs; once the heads fill the
+  // chip, one 8-wave workgroup per head (two waves per SIMD to hide latency) avoids the
+  // operand traffic that every workgroup repeats, and forms -W and P^T itself.
   const size_t seq_pairs = (size_t)num_seqs * h_qk;
   const size_t groups = (seq_pairs + 7) / 8 * 8 * (size_t)a.group;
   if (heads * 8 <= kStateCus) {
@@ -1490,7 +1491,7 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
   } else if (heads * 2 <= kStateCus) {
     hipLaunchKernelGGL((state_kernel<4, 1, false>), dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((state_kernel<4, 2, false>), dim3((unsigned)groups), dim3(4 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<8, 1, false>), dim3((unsigned)groups), dim3(8 * kWave), 0, stream, a);
   }
   return hipGetLastError();
 }
