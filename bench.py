@@ -46,14 +46,14 @@ H_QK, H_V = 16, 32
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_amd", "csrc")
 
 # Hardware byte counters of one launch, from two rocprofv3 --pmc runs (FETCH_SIZE, then
-# WRITE_SIZE) of `python bench.py --workload prefill,decode,copy --steps 5 --warmup 1
+# WRITE_SIZE) of `python bench.py --workload prefill,decode,copy,frontend --steps 5 --warmup 1
 # --no-cpu-baseline`, in KiB per dispatch, scaled by what the same counters read for a
 # plain 1 GiB device copy. `sources` fingerprints the kernel sources the figures were taken
 # on: once they change, the figures no longer describe the kernel and traffic is reported
 # as null. Filled from the summaries kept under profiles/.
 COUNTER_TRAFFIC = {
-    "prefill": {"bytes": 294250582, "sources": "77e2ef7d00e930f1"},
-    "decode": {"bytes": 1083391389, "sources": "cdfecddd07ed50cc"},
+    "prefill": {"bytes": 295879653, "sources": "fd92581b92f22f17"},
+    "decode": {"bytes": 1083387096, "sources": "cdfecddd07ed50cc"},
 }
 
 
