@@ -245,13 +245,14 @@ struct PrepSmem {
 __device__ __forceinline__ constexpr int tile_row(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
 __device__ __forceinline__ constexpr int tile_col(int t) { return t - tile_row(t) * (tile_row(t) + 1) / 2; }
 
-// Tiles PAR, PAR + 2, ..., PAR + 8 of K K^T (ISQ = false) or Q K^T (ISQ = true).
-template <bool ISQ, int PAR>
+// Tiles FIRST, FIRST + STEP, ... (below 10) of K K^T (ISQ = false) or Q K^T (ISQ = true).
+template <bool ISQ, int FIRST, int STEP>
 __device__ __forceinline__ void gram_tiles(const PrepSmem& sm, f32x4 (&acc)[5], int g4, int l16) {
   const bf16* Am = ISQ ? sm.r1.Q : sm.K;
 #pragma unroll
   for (int jj = 0; jj < 5; ++jj) {
-    const int t = PAR + 2 * jj;
+    const int t = FIRST + STEP * jj;
+    if (t >= 10) break;
     const int rt = tile_row(t), ct = tile_col(t);
     acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -264,14 +265,15 @@ __device__ __forceinline__ void gram_tiles(const PrepSmem& sm, f32x4 (&acc)[5], 
 // Masked and decayed tiles: A = strictly-lower(beta_r Gam_rs (K K^T)_rs) into LDS, or
 // P = scale lower-incl(Gam_rs (Q K^T)_rs), stored transposed to the workspace (8 bytes per
 // lane: four adjacent query tokens of one key token).
-template <bool ISQ, int PAR>
+template <bool ISQ, int FIRST, int STEP>
 __device__ __forceinline__ void gram_epilogue(PrepSmem& sm, const f32x4 (&acc)[5], bf16* Pt, float scale,
                                               int g4, int l16) {
   f32x4 Gr[5], Br[5];
   float Gs[5];
 #pragma unroll
   for (int jj = 0; jj < 5; ++jj) {   // every LDS read first: the stores into A would order them
-    const int t = PAR + 2 * jj;
+    const int t = FIRST + STEP * jj;
+    if (t >= 10) break;
     const int rt = tile_row(t), ct = tile_col(t);
     Gr[jj] = *reinterpret_cast<const f32x4*>(&sm.G[16 * rt + 4 * g4]);
     if (!ISQ) Br[jj] = *reinterpret_cast<const f32x4*>(&sm.beta[16 * rt + 4 * g4]);
@@ -279,7 +281,8 @@ __device__ __forceinline__ void gram_epilogue(PrepSmem& sm, const f32x4 (&acc)[5
   }
 #pragma unroll
   for (int jj = 0; jj < 5; ++jj) {
-    const int t = PAR + 2 * jj;
+    const int t = FIRST + STEP * jj;
+    if (t >= 10) break;
     const int rt = tile_row(t), ct = tile_col(t);
     const int s = 16 * ct + l16;
     f32x4 val;
@@ -360,19 +363,34 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
     reinterpret_cast<float*>(wsh + kWsG)[lane] = x;
   }
 
-  // ---- K K^T and Q K^T: the 10 lower tiles of each; waves 0, 1 take K K^T, waves 2, 3
-  // Q K^T, alternate tiles each, held in registers ----
+  // ---- K K^T and Q K^T: the 10 lower tiles of each, held in registers. With FULL waves
+  // 0, 1 take K K^T and waves 2, 3 Q K^T, alternate tiles each; otherwise the four waves
+  // share K K^T (tiles w, w + 4, w + 8) ----
   f32x4 acc[5];
-  if (w == 0) gram_tiles<false, 0>(sm, acc, g4, l16);
-  else if (w == 1) gram_tiles<false, 1>(sm, acc, g4, l16);
-  else if (FULL && w == 2) gram_tiles<true, 0>(sm, acc, g4, l16);
-  else if (FULL) gram_tiles<true, 1>(sm, acc, g4, l16);
+  if (FULL) {
+    if (w == 0) gram_tiles<false, 0, 2>(sm, acc, g4, l16);
+    else if (w == 1) gram_tiles<false, 1, 2>(sm, acc, g4, l16);
+    else if (w == 2) gram_tiles<true, 0, 2>(sm, acc, g4, l16);
+    else gram_tiles<true, 1, 2>(sm, acc, g4, l16);
+  } else {
+    if (w == 0) gram_tiles<false, 0, 4>(sm, acc, g4, l16);
+    else if (w == 1) gram_tiles<false, 1, 4>(sm, acc, g4, l16);
+    else if (w == 2) gram_tiles<false, 2, 4>(sm, acc, g4, l16);
+    else gram_tiles<false, 3, 4>(sm, acc, g4, l16);
+  }
   __syncthreads();   // Q is consumed (its space becomes A) and G is ready
   bf16* Pt = reinterpret_cast<bf16*>(wsh + kWsP);
-  if (w == 0) gram_epilogue<false, 0>(sm, acc, Pt, a.scale, g4, l16);
-  else if (w == 1) gram_epilogue<false, 1>(sm, acc, Pt, a.scale, g4, l16);
-  else if (FULL && w == 2) gram_epilogue<true, 0>(sm, acc, Pt, a.scale, g4, l16);
-  else if (FULL) gram_epilogue<true, 1>(sm, acc, Pt, a.scale, g4, l16);
+  if (FULL) {
+    if (w == 0) gram_epilogue<false, 0, 2>(sm, acc, Pt, a.scale, g4, l16);
+    else if (w == 1) gram_epilogue<false, 1, 2>(sm, acc, Pt, a.scale, g4, l16);
+    else if (w == 2) gram_epilogue<true, 0, 2>(sm, acc, Pt, a.scale, g4, l16);
+    else gram_epilogue<true, 1, 2>(sm, acc, Pt, a.scale, g4, l16);
+  } else {
+    if (w == 0) gram_epilogue<false, 0, 4>(sm, acc, Pt, a.scale, g4, l16);
+    else if (w == 1) gram_epilogue<false, 1, 4>(sm, acc, Pt, a.scale, g4, l16);
+    else if (w == 2) gram_epilogue<false, 2, 4>(sm, acc, Pt, a.scale, g4, l16);
+    else gram_epilogue<false, 3, 4>(sm, acc, Pt, a.scale, g4, l16);
+  }
   if (FULL && tid < 128) {   // the strictly upper tiles of P that the read-out's 32-token K-steps see
     const int rt = (tid >> 6) * 2, ln = tid & 63;
     *reinterpret_cast<bf16x4*>(Pt + (16 * (rt + 1) + (ln & 15)) * kC + 16 * rt + 4 * (ln >> 4)) = bf16x4{};
