@@ -144,6 +144,24 @@ def _timed(fn, steps, warmup):
     return wall, float(np.mean(per))
 
 
+def _timed_batch(fn, steps, warmup):
+    """Like _timed, for kernels of a few microseconds: one HIP event pair around all `steps`
+    back-to-back calls (events around every call would add their own gaps). Returns the
+    mean device ms per call."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def _workspace(total_tokens, num_seqs):
     import torch
     import linear_attention_recurrence_amd as gdn
@@ -190,6 +208,46 @@ def bench_decode(steps, warmup):
         gdn.gdn_decode_step(q[r], k[r], v[r], g[r], b[r], pool, d.scale, o=o)
 
     return _timed(step, steps, warmup)
+
+
+def conv_decode_bytes(num_seqs: int, K=4, h_qk=H_QK, h_v=H_V) -> float:
+    """HBM bytes the decode-time front end must move: each sequence's input row read, its
+    K - 1 earlier inputs read, the new input kept (one row written) and q, k, v written
+    (bf16), plus the conv weights (fp32) once."""
+    ch = 2 * h_qk * D + h_v * D
+    return float(num_seqs * ch * 2 * (1 + (K - 1) + 1 + 1) + ch * K * 4)
+
+
+def bench_decode_front_end(steps, warmup):
+    """256 sequences x 1 token: gdn_conv_decode_step over a [256][3][8192] bf16 window pool,
+    then gdn_decode_step on its q, k and v over the 512 MiB state pool; a ring of 16 input
+    sets. Returns (conv ms per call, wall seconds and ms per step of both)."""
+    import torch
+    import linear_attention_recurrence_amd as gdn
+    import workloads
+    d = workloads.config3()
+    fe = workloads.make_frontend([16] * 256, with_initial_state=False, seed=1005)
+    C = fe.mixed.shape[1]
+    mixed = _dev(fe.mixed).view(256, 16, C).transpose(0, 1).contiguous()   # [ring][seq][C]
+    w = _dev(fe.conv_weight)
+    win = torch.zeros((256, 3, C), dtype=torch.bfloat16, device="cuda")
+    pool = _dev(d.pool)
+    g, b = _dev(d.g), _dev(d.beta)
+    q = torch.empty((256, H_QK, D), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty((256, H_V, D), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(v)
+
+    def conv(i):
+        gdn.gdn_conv_decode_step(mixed[i % 16], w, win, H_QK, H_V, D, D, fe.q_scale, q=q, k=k, v=v)
+
+    def both(i):
+        conv(i)
+        gdn.gdn_decode_step(q, k, v, g[i % 16], b[i % 16], pool, 1.0, o=o)
+
+    conv_ms = _timed_batch(conv, steps, warmup)
+    wall, both_ms = _timed(both, steps, warmup)
+    return conv_ms, wall, both_ms
 
 
 def bench_frontend(reps, warmup):
@@ -342,6 +400,19 @@ def main():
                          "traffic": counter_traffic("decode", DECODE_SOURCES),
                          "kernel": "decode_kernel<bf16>", "kernel_ms": dms,
                          "algorithmic_bytes": dbytes}}
+    if "decode" in work:
+        dsteps = args.decode_steps
+        cms, fwall, fms = bench_decode_front_end(dsteps, args.warmup)
+        cbytes = conv_decode_bytes(256)
+        out["decode_front_end"] = {
+            "workload": "decode step with the front end, 256 sequences x 1 token: conv k=4 over "
+                        "a bf16 window pool of the last 3 inputs, then the decode step; ring of "
+                        "16 input sets",
+            "steps": dsteps, "ms_per_step": fwall * 1e3 / dsteps,
+            "tokens_per_s": 256 * dsteps / fwall,
+            "conv_decode": {"kernel": "conv_decode_kernel", "kernel_ms_back_to_back": cms,
+                            "algorithmic_bytes": cbytes,
+                            "achieved_GBs": cbytes / (cms / 1e3) / 1e9}}
     if "frontend" in work:
         T4, N4, conv_ms, pre_ms = bench_frontend(10, 2)
         out["frontend_prefill"] = {

@@ -133,6 +133,44 @@ gdn_status gdn_conv_prep(const void* mixed_qkv, const float* conv_weight, int32_
                          int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, float q_scale,
                          void* q, void* k, void* v, void* stream);
 
+/*
+ * Front end at decode time: the short causal convolution of section "01 .
+ * GatedDeltaNet(config)" of the Evolving Transformer page (with gdn_conv_prep's SiLU and
+ * q/k normalisation) at one new token for each of num_seqs sequences, the inputs the
+ * convolution still needs from earlier tokens kept in a window pool. Every output equals
+ * what gdn_conv_prep gives for that token when run over the sequence so far (same
+ * arithmetic, bit for bit), so a prompt prefilled and then decoded token by token matches
+ * one prefill over the whole text.
+ *
+ *   mixed_qkv     [num_seqs][C] bf16, this step's projected inputs (C and channel order as
+ *                 for gdn_conv_prep)
+ *   conv_weight   [C][conv_kernel] fp32, as for gdn_conv_prep
+ *   conv_window   [pool_size][conv_kernel-1][C] bf16, read and written in place: row r of a
+ *                 slot holds the input conv_kernel-1-r tokens back (zeros for a new
+ *                 sequence). After the call it holds the window for the next token. May be
+ *                 NULL when conv_kernel is 1.
+ *   window_slots  [num_seqs] int32: sequence n uses slot window_slots[n]; NULL means slot n.
+ *                 Slots must be distinct.
+ *   q, k, v       [num_seqs][h_qk][d_k], [num_seqs][h_qk][d_k], [num_seqs][h_v][d_v] bf16,
+ *                 the inputs of gdn_decode_step
+ */
+gdn_status gdn_conv_decode_step(const void* mixed_qkv, const float* conv_weight, int32_t conv_kernel,
+                                void* conv_window, const int32_t* window_slots, int32_t num_seqs,
+                                int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, float q_scale,
+                                void* q, void* k, void* v, void* stream);
+
+/*
+ * The window a prefill leaves for gdn_conv_decode_step: for each sequence n of the packed
+ * batch (cu_seqlens as for gdn_conv_prep), its last conv_kernel-1 inputs from mixed_qkv,
+ * with zeros for positions before the sequence start, written to slot window_slots[n]
+ * (NULL: slot n) of conv_window. A no-op for conv_kernel 1.
+ */
+gdn_status gdn_conv_window_from_prefill(const void* mixed_qkv, int32_t conv_kernel,
+                                        const int32_t* cu_seqlens, int32_t num_seqs,
+                                        int32_t total_tokens, int32_t h_qk, int32_t h_v,
+                                        int32_t d_k, int32_t d_v, void* conv_window,
+                                        const int32_t* window_slots, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

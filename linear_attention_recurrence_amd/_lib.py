@@ -20,7 +20,8 @@ GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN
 GDN_BF16, GDN_F32 = 0, 1
 
 EXPORTED = ("gdn_status_string", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill",
-            "gdn_decode_step", "gdn_conv_prep")
+            "gdn_decode_step", "gdn_conv_prep", "gdn_conv_decode_step",
+            "gdn_conv_window_from_prefill")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -56,6 +57,11 @@ def load(path: Optional[str] = None):
     lib.gdn_conv_prep.restype = ctypes.c_int
     lib.gdn_conv_prep.argtypes = [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                                   _P, _P, _P, _P]
+    lib.gdn_conv_decode_step.restype = ctypes.c_int
+    lib.gdn_conv_decode_step.argtypes = [_P, _P, _I, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float,
+                                         _P, _P, _P, _P]
+    lib.gdn_conv_window_from_prefill.restype = ctypes.c_int
+    lib.gdn_conv_window_from_prefill.argtypes = [_P, _I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]
     if path is None:
         _lib = lib
     return lib
@@ -187,3 +193,58 @@ def gdn_conv_prep(mixed_qkv, conv_weight, cu_seqlens, h_qk, h_v, d_k, d_v, q_sca
                               _ptr(q), _ptr(k), _ptr(v), _stream(stream))
     _check(st, "gdn_conv_prep")
     return q, k, v
+
+
+def gdn_conv_decode_step(mixed_qkv, conv_weight, conv_window, h_qk, h_v, d_k, d_v, q_scale,
+                         window_slots=None, q=None, k=None, v=None, stream=None):
+    """Front end for one token per sequence; conv_window [P][K-1][C] bf16 is updated in
+    place. Returns (q, k, v) laid out as the decode-step inputs."""
+    N = mixed_qkv.shape[0]
+    K = int(conv_weight.shape[1])
+    dev = mixed_qkv.device
+    if q is None:
+        q = torch.empty((N, h_qk, d_k), dtype=torch.bfloat16, device=dev)
+    if k is None:
+        k = torch.empty((N, h_qk, d_k), dtype=torch.bfloat16, device=dev)
+    if v is None:
+        v = torch.empty((N, h_v, d_v), dtype=torch.bfloat16, device=dev)
+    C = 2 * h_qk * d_k + h_v * d_v
+    _expect(mixed_qkv, (N, C), torch.bfloat16, "mixed_qkv")
+    _expect(conv_weight, (C, K), torch.float32, "conv_weight")
+    if K > 1:
+        _expect(conv_window, (conv_window.shape[0], K - 1, C), torch.bfloat16, "conv_window")
+        if window_slots is None and conv_window.shape[0] < N:
+            raise ValueError("conv_window has fewer slots than sequences")
+    if window_slots is not None:
+        _expect(window_slots, (N,), torch.int32, "window_slots")
+    _expect(q, (N, h_qk, d_k), torch.bfloat16, "q")
+    _expect(k, (N, h_qk, d_k), torch.bfloat16, "k")
+    _expect(v, (N, h_v, d_v), torch.bfloat16, "v")
+    st = load().gdn_conv_decode_step(_ptr(mixed_qkv), _ptr(conv_weight), K,
+                                     _ptr(conv_window) if K > 1 else None, _ptr(window_slots), N,
+                                     h_qk, h_v, d_k, d_v, float(q_scale), _ptr(q), _ptr(k), _ptr(v),
+                                     _stream(stream))
+    _check(st, "gdn_conv_decode_step")
+    return q, k, v
+
+
+def gdn_conv_window_from_prefill(mixed_qkv, conv_kernel, cu_seqlens, conv_window, h_qk, h_v,
+                                 d_k, d_v, window_slots=None, stream=None):
+    """Writes each sequence's last conv_kernel-1 inputs (zeros before its start) into its
+    slot of conv_window [P][conv_kernel-1][C] bf16."""
+    T = mixed_qkv.shape[0]
+    N = cu_seqlens.numel() - 1
+    K = int(conv_kernel)
+    C = 2 * h_qk * d_k + h_v * d_v
+    _expect(mixed_qkv, (T, C), torch.bfloat16, "mixed_qkv")
+    _expect(cu_seqlens, (N + 1,), torch.int32, "cu_seqlens")
+    if K > 1:
+        _expect(conv_window, (conv_window.shape[0], K - 1, C), torch.bfloat16, "conv_window")
+        if window_slots is None and conv_window.shape[0] < N:
+            raise ValueError("conv_window has fewer slots than sequences")
+    if window_slots is not None:
+        _expect(window_slots, (N,), torch.int32, "window_slots")
+    st = load().gdn_conv_window_from_prefill(_ptr(mixed_qkv), K, _ptr(cu_seqlens), N, T, h_qk, h_v,
+                                             d_k, d_v, _ptr(conv_window) if K > 1 else None,
+                                             _ptr(window_slots), _stream(stream))
+    _check(st, "gdn_conv_window_from_prefill")

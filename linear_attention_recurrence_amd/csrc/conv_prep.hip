@@ -70,6 +70,57 @@ __device__ int find_sequence(const int32_t* cu, int num_seqs, int t) {
   return lo;
 }
 
+// The taps of this thread's 8 channels: wt[0][e] multiplies the current token, wt[d][e] the
+// token d positions earlier (zero past the kernel size K).
+__device__ __forceinline__ void load_taps(const float* w, int K, int c0, float (&wt)[4][8]) {
+  if (K == 4) {   // the model's kernel: each channel's taps are one 16-byte load
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(w + (size_t)(c0 + e) * 4);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) wt[d][e] = t[3 - d];
+    }
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) wt[d][e] = (d < K) ? w[(size_t)(c0 + e) * K + (K - 1 - d)] : 0.f;
+  }
+}
+
+// One token of this thread's 8 channels from its input x0 and the inputs h1, h2, h3 one,
+// two and three tokens earlier: the convolution, SiLU and, for q and k heads, the head's L2
+// normalisation over the 16 lanes that share the head (and the q scale). The prefill and
+// decode kernels both produce every output through this function.
+__device__ __forceinline__ bf16x8 conv_token(const float (&wt)[4][8], const float (&x0)[8], const float (&h1)[8],
+                                             const float (&h2)[8], const float (&h3)[8], bool is_q, bool is_k,
+                                             float q_scale) {
+  float z[8];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float y = wt[0][e] * x0[e] + wt[1][e] * h1[e] + wt[2][e] * h2[e] + wt[3][e] * h3[e];
+    z[e] = y * __builtin_amdgcn_rcpf(1.f + __expf(-y));   // hardware 1-ulp reciprocal
+    ss += z[e] * z[e];
+  }
+  bf16x8 out;
+  if (is_q || is_k) {
+    ss += __shfl_xor(ss, 8, 16);
+    ss += __shfl_xor(ss, 4, 16);
+    ss += __shfl_xor(ss, 2, 16);
+    ss += __shfl_xor(ss, 1, 16);
+    // 1 / max(||z||, 1e-12) = rsqrt(max(||z||^2, 1e-24)), hardware 1-ulp rsqrt
+    const float f = (is_q ? q_scale : 1.f) * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = to_bf16(z[e] * f);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = to_bf16(z[e]);
+  }
+  return out;
+}
+
 __global__ __launch_bounds__(kThreads) void conv_prep_kernel(ConvArgs a) {
   const int c0 = blockIdx.x * kChanPerBlock + threadIdx.x * kChanPerThread;
   const int t_begin = blockIdx.y * kTokensPerBlock;
@@ -82,14 +133,8 @@ __global__ __launch_bounds__(kThreads) void conv_prep_kernel(ConvArgs a) {
   const bool is_q = c0 < nq;
   const bool is_k = !is_q && c0 < 2 * nq;
 
-  // taps: wt[0] multiplies the current token, wt[d] the token d positions earlier
   float wt[4][8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      wt[d][e] = (d < a.K) ? a.w[(size_t)(c0 + e) * a.K + (a.K - 1 - d)] : 0.f;
-  }
+  load_taps(a.w, a.K, c0, wt);
 
   int n = find_sequence(a.cu, a.num_seqs, t_begin);
   int seq_start = a.cu[n], seq_end = a.cu[n + 1];
@@ -97,9 +142,9 @@ __global__ __launch_bounds__(kThreads) void conv_prep_kernel(ConvArgs a) {
   float h1[8], h2[8], h3[8];     // inputs at t-1, t-2, t-3 (zero before the sequence start)
 #pragma unroll
   for (int e = 0; e < 8; ++e) h1[e] = h2[e] = h3[e] = 0.f;
-  if (t_begin - 1 >= seq_start) load8(a.x + (size_t)(t_begin - 1) * a.C + c0, h1);
-  if (t_begin - 2 >= seq_start) load8(a.x + (size_t)(t_begin - 2) * a.C + c0, h2);
-  if (t_begin - 3 >= seq_start) load8(a.x + (size_t)(t_begin - 3) * a.C + c0, h3);
+  if (a.K > 1 && t_begin - 1 >= seq_start) load8(a.x + (size_t)(t_begin - 1) * a.C + c0, h1);
+  if (a.K > 2 && t_begin - 2 >= seq_start) load8(a.x + (size_t)(t_begin - 2) * a.C + c0, h2);
+  if (a.K > 3 && t_begin - 3 >= seq_start) load8(a.x + (size_t)(t_begin - 3) * a.C + c0, h3);
 
   const bf16* xc = a.x + c0;
   bf16x8 raw[2][kGroup];
@@ -122,35 +167,119 @@ __global__ __launch_bounds__(kThreads) void conv_prep_kernel(ConvArgs a) {
       float x0[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) x0[e] = (float)raw[gi & 1][u][e];
-      float z[8];
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float y = wt[0][e] * x0[e] + wt[1][e] * h1[e] + wt[2][e] * h2[e] + wt[3][e] * h3[e];
-        z[e] = y * __builtin_amdgcn_rcpf(1.f + __expf(-y));   // hardware 1-ulp reciprocal
-        ss += z[e] * z[e];
-      }
-      bf16x8 out;
-      if (is_q || is_k) {
-        ss += __shfl_xor(ss, 8, 16);
-        ss += __shfl_xor(ss, 4, 16);
-        ss += __shfl_xor(ss, 2, 16);
-        ss += __shfl_xor(ss, 1, 16);
-        // 1 / max(||z||, 1e-12) = rsqrt(max(||z||^2, 1e-24)), hardware 1-ulp rsqrt
-        const float f = (is_q ? a.q_scale : 1.f) * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] = to_bf16(z[e] * f);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] = to_bf16(z[e]);
-      }
+      const bf16x8 out = conv_token(wt, x0, h1, h2, h3, is_q, is_k, a.q_scale);
       bf16* dst = is_q ? a.q + (size_t)t * nq + c0
                 : is_k ? a.k + (size_t)t * nq + (c0 - nq)
                        : a.v + (size_t)t * nv + (c0 - 2 * nq);
       *reinterpret_cast<bf16x8*>(dst) = out;
+      // inputs more than K - 1 tokens back stay zero (as in the decode window), so every
+      // tap past the kernel multiplies zero by zero in both
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { h3[e] = h2[e]; h2[e] = h1[e]; h1[e] = x0[e]; }
+      for (int e = 0; e < 8; ++e) {
+        h3[e] = a.K > 3 ? h2[e] : 0.f;
+        h2[e] = a.K > 2 ? h1[e] : 0.f;
+        h1[e] = a.K > 1 ? x0[e] : 0.f;
+      }
     }
+  }
+}
+
+// ---- Decode side: one token per sequence, the last K - 1 inputs of each sequence in a
+// window pool [pool][K - 1][C] bf16 (row r holds the input K - 1 - r tokens back).
+
+struct ConvDecodeArgs {
+  const bf16* x;            // [num_seqs][C], this step's inputs
+  const float* w;
+  bf16* win;                // window pool, updated in place
+  const int32_t* slots;     // sequence n uses window slots[n] (n when null)
+  bf16* q;
+  bf16* k;
+  bf16* v;
+  int K, num_seqs, h_qk, h_v, C;
+  float q_scale;
+};
+
+// One block per (2048 channels, kSeqPerBlock sequences), 8 channels per thread: the taps are
+// loaded once for the block's sequences, and every sequence's loads are issued before any is
+// computed. The current input and the window give the same conv_token inputs as the prefill
+// kernel at that token; the window then moves one token on (row r takes row r + 1, the last
+// row the current input).
+constexpr int kSeqPerBlock = 4;
+
+__global__ __launch_bounds__(kThreads) void conv_decode_kernel(ConvDecodeArgs a) {
+  const int c0 = blockIdx.x * kChanPerBlock + threadIdx.x * kChanPerThread;
+  if (c0 >= a.C) return;          // whole 16-lane groups leave together (C % 128 == 0)
+  const int nq = a.h_qk * kHeadDim;
+  const int nv = a.h_v * kHeadDim;
+  const bool is_q = c0 < nq;
+  const bool is_k = !is_q && c0 < 2 * nq;
+  const int n0 = blockIdx.y * kSeqPerBlock;
+  const int ns = min(kSeqPerBlock, a.num_seqs - n0);
+  int slot[kSeqPerBlock];
+#pragma unroll
+  for (int s = 0; s < kSeqPerBlock; ++s)
+    slot[s] = s < ns ? (a.slots ? a.slots[n0 + s] : n0 + s) : 0;
+  bf16x8 xr[kSeqPerBlock], hr[kSeqPerBlock][3];   // hr[s][d - 1]: input d tokens back
+#pragma unroll
+  for (int s = 0; s < kSeqPerBlock; ++s) {
+    xr[s] = bf16x8{};
+    hr[s][0] = hr[s][1] = hr[s][2] = bf16x8{};
+    if (s < ns) {
+      xr[s] = *reinterpret_cast<const bf16x8*>(a.x + (size_t)(n0 + s) * a.C + c0);
+      const bf16* wrow = a.win + (size_t)slot[s] * (a.K - 1) * a.C + c0;
+#pragma unroll
+      for (int d = 1; d < 4; ++d)
+        if (d < a.K) hr[s][d - 1] = *reinterpret_cast<const bf16x8*>(wrow + (size_t)(a.K - 1 - d) * a.C);
+    }
+  }
+  float wt[4][8];
+  load_taps(a.w, a.K, c0, wt);
+#pragma unroll
+  for (int s = 0; s < kSeqPerBlock; ++s) {
+    if (s >= ns) break;
+    const int n = n0 + s;
+    float x0[8], h1[8], h2[8], h3[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x0[e] = (float)xr[s][e];
+      h1[e] = (float)hr[s][0][e];
+      h2[e] = (float)hr[s][1][e];
+      h3[e] = (float)hr[s][2][e];
+    }
+    const bf16x8 out = conv_token(wt, x0, h1, h2, h3, is_q, is_k, a.q_scale);
+    bf16* dst = is_q ? a.q + (size_t)n * nq + c0
+              : is_k ? a.k + (size_t)n * nq + (c0 - nq)
+                     : a.v + (size_t)n * nv + (c0 - 2 * nq);
+    *reinterpret_cast<bf16x8*>(dst) = out;
+    // row K - 1 - d now holds the input d - 1 tokens back (the current one for d = 1)
+    bf16* wrow = a.win + (size_t)slot[s] * (a.K - 1) * a.C + c0;
+#pragma unroll
+    for (int d = 1; d < 4; ++d)
+      if (d < a.K) *reinterpret_cast<bf16x8*>(wrow + (size_t)(a.K - 1 - d) * a.C) = d == 1 ? xr[s] : hr[s][d - 2];
+  }
+}
+
+struct ConvWindowArgs {
+  const bf16* x;            // [total_tokens][C] prefill inputs
+  const int32_t* cu;
+  bf16* win;
+  const int32_t* slots;
+  int K, C;
+};
+
+// The window each sequence of a prefill leaves for decode: its last K - 1 inputs, zero where
+// the sequence is shorter (the zero history the prefill started from).
+__global__ __launch_bounds__(kThreads) void conv_window_kernel(ConvWindowArgs a) {
+  const int c0 = blockIdx.x * kChanPerBlock + threadIdx.x * kChanPerThread;
+  const int n = blockIdx.y;
+  if (c0 >= a.C) return;
+  const int s0 = a.cu[n], s1 = a.cu[n + 1];
+  const int slot = a.slots ? a.slots[n] : n;
+  bf16* wrow = a.win + (size_t)slot * (a.K - 1) * a.C + c0;
+  for (int r = 0; r < a.K - 1; ++r) {
+    const int t = s1 - (a.K - 1) + r;
+    const bf16x8 val = t >= s0 ? *reinterpret_cast<const bf16x8*>(a.x + (size_t)t * a.C + c0) : bf16x8{};
+    *reinterpret_cast<bf16x8*>(wrow + (size_t)r * a.C) = val;
   }
 }
 
@@ -177,6 +306,48 @@ hipError_t launch_conv_prep(const void* mixed, const float* w, int K, const int3
   const dim3 grid((a.C + kChanPerBlock - 1) / kChanPerBlock,
                   (total_tokens + kTokensPerBlock - 1) / kTokensPerBlock);
   hipLaunchKernelGGL(conv_prep_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace gdn
+
+namespace gdn {
+
+hipError_t launch_conv_decode(const void* mixed, const float* w, int K, void* window,
+                              const int32_t* slots, int num_seqs, int h_qk, int h_v, float q_scale,
+                              void* q, void* k, void* v, hipStream_t stream) {
+  if (num_seqs == 0) return hipSuccess;
+  ConvDecodeArgs a;
+  a.x = static_cast<const bf16*>(mixed);
+  a.w = w;
+  a.win = static_cast<bf16*>(window);
+  a.slots = slots;
+  a.q = static_cast<bf16*>(q);
+  a.k = static_cast<bf16*>(k);
+  a.v = static_cast<bf16*>(v);
+  a.K = K;
+  a.num_seqs = num_seqs;
+  a.h_qk = h_qk;
+  a.h_v = h_v;
+  a.C = (2 * h_qk + h_v) * kHeadDim;
+  a.q_scale = q_scale;
+  const dim3 grid((a.C + kChanPerBlock - 1) / kChanPerBlock, (num_seqs + kSeqPerBlock - 1) / kSeqPerBlock);
+  hipLaunchKernelGGL(conv_decode_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_window(const void* mixed, int K, const int32_t* cu, int num_seqs, int h_qk,
+                              int h_v, void* window, const int32_t* slots, hipStream_t stream) {
+  if (num_seqs == 0 || K == 1) return hipSuccess;
+  ConvWindowArgs a;
+  a.x = static_cast<const bf16*>(mixed);
+  a.cu = cu;
+  a.win = static_cast<bf16*>(window);
+  a.slots = slots;
+  a.K = K;
+  a.C = (2 * h_qk + h_v) * kHeadDim;
+  const dim3 grid((a.C + kChanPerBlock - 1) / kChanPerBlock, num_seqs);
+  hipLaunchKernelGGL(conv_window_kernel, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -104,4 +104,39 @@ gdn_status gdn_conv_prep(const void* mixed_qkv, const float* conv_weight, int32_
                                         static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_conv_decode_step(const void* mixed_qkv, const float* conv_weight, int32_t conv_kernel,
+                                void* conv_window, const int32_t* window_slots, int32_t num_seqs,
+                                int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, float q_scale,
+                                void* q, void* k, void* v, void* stream) {
+  if (num_seqs < 0) return GDN_ERR_SHAPE;
+  const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  if (conv_kernel < 1) return GDN_ERR_SHAPE;
+  if (conv_kernel > 4) return GDN_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return GDN_OK;
+  if (!mixed_qkv || !conv_weight || !q || !k || !v) return GDN_ERR_NULL;
+  if (conv_kernel > 1 && !conv_window) return GDN_ERR_NULL;
+  return from_hip(gdn::launch_conv_decode(mixed_qkv, conv_weight, conv_kernel, conv_window,
+                                          window_slots, num_seqs, h_qk, h_v, q_scale, q, k, v,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_conv_window_from_prefill(const void* mixed_qkv, int32_t conv_kernel,
+                                        const int32_t* cu_seqlens, int32_t num_seqs,
+                                        int32_t total_tokens, int32_t h_qk, int32_t h_v,
+                                        int32_t d_k, int32_t d_v, void* conv_window,
+                                        const int32_t* window_slots, void* stream) {
+  if (num_seqs < 0 || total_tokens < 0) return GDN_ERR_SHAPE;
+  const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  if (conv_kernel < 1) return GDN_ERR_SHAPE;
+  if (conv_kernel > 4) return GDN_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
+  if (conv_kernel == 1) return GDN_OK;   // no window
+  if (!cu_seqlens || !conv_window || (total_tokens > 0 && !mixed_qkv)) return GDN_ERR_NULL;
+  return from_hip(gdn::launch_conv_window(mixed_qkv, conv_kernel, cu_seqlens, num_seqs, h_qk, h_v,
+                                          conv_window, window_slots,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -32,4 +32,14 @@ hipError_t launch_conv_prep(const void* mixed, const float* w, int K, const int3
                             int num_seqs, int total_tokens, int h_qk, int h_v, float q_scale,
                             void* q, void* k, void* v, hipStream_t stream);
 
+// Decode-side front end: one token per sequence against a window pool of the last K - 1
+// inputs, updated in place (conv_prep.hip).
+hipError_t launch_conv_decode(const void* mixed, const float* w, int K, void* window,
+                              const int32_t* slots, int num_seqs, int h_qk, int h_v, float q_scale,
+                              void* q, void* k, void* v, hipStream_t stream);
+
+// The window a prefill over packed sequences leaves for decode (conv_prep.hip).
+hipError_t launch_conv_window(const void* mixed, int K, const int32_t* cu, int num_seqs, int h_qk,
+                              int h_v, void* window, const int32_t* slots, hipStream_t stream);
+
 }  // namespace gdn

@@ -25,7 +25,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(["gdn_status_string", "gdn_chunk_prefill_workspace_bytes",
-                                            "gdn_chunk_prefill", "gdn_decode_step", "gdn_conv_prep"])
+                                            "gdn_chunk_prefill", "gdn_decode_step", "gdn_conv_prep",
+                                            "gdn_conv_decode_step", "gdn_conv_window_from_prefill"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -134,6 +135,55 @@ def test_conv_prep_validation():
     assert call(dv=64) == L.GDN_ERR_UNSUPPORTED
     assert call(T=-1) == L.GDN_ERR_SHAPE
     assert call(T=0) == L.GDN_OK
+
+
+def test_conv_decode_validation():
+    lib, L = _lib()
+    f = lib.gdn_conv_decode_step
+    P = _fake
+    ok = dict(x=P(1), w=P(2), K=4, win=P(3), slots=None, n=2, hqk=16, hv=32, dk=128, dv=128,
+              qs=0.1, q=P(4), k=P(5), v=P(6), st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["x"], a["w"], a["K"], a["win"], a["slots"], a["n"], a["hqk"], a["hv"], a["dk"],
+                 a["dv"], a["qs"], a["q"], a["k"], a["v"], a["st"])
+
+    assert call(x=None) == L.GDN_ERR_NULL
+    assert call(w=None) == L.GDN_ERR_NULL
+    assert call(win=None) == L.GDN_ERR_NULL
+    assert call(q=None) == L.GDN_ERR_NULL
+    assert call(K=0) == L.GDN_ERR_SHAPE
+    assert call(K=5) == L.GDN_ERR_UNSUPPORTED
+    assert call(n=-1) == L.GDN_ERR_SHAPE
+    assert call(hv=30) == L.GDN_ERR_SHAPE
+    assert call(dk=64) == L.GDN_ERR_UNSUPPORTED
+    assert call(n=0) == L.GDN_OK
+
+
+def test_conv_window_validation():
+    lib, L = _lib()
+    f = lib.gdn_conv_window_from_prefill
+    P = _fake
+    ok = dict(x=P(1), K=4, cu=P(2), n=2, T=10, hqk=16, hv=32, dk=128, dv=128, win=P(3),
+              slots=None, st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["x"], a["K"], a["cu"], a["n"], a["T"], a["hqk"], a["hv"], a["dk"], a["dv"],
+                 a["win"], a["slots"], a["st"])
+
+    assert call(x=None) == L.GDN_ERR_NULL
+    assert call(cu=None) == L.GDN_ERR_NULL
+    assert call(win=None) == L.GDN_ERR_NULL
+    assert call(K=0) == L.GDN_ERR_SHAPE
+    assert call(K=5) == L.GDN_ERR_UNSUPPORTED
+    assert call(T=-1) == L.GDN_ERR_SHAPE
+    assert call(n=0) == L.GDN_ERR_SHAPE
+    assert call(n=0, T=0) == L.GDN_OK
+    assert call(K=1, win=None) == L.GDN_OK
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

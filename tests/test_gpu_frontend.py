@@ -102,3 +102,76 @@ def test_config4_front_end_and_prefill():
         r_sel = np.stack([refp[(n, h)][0] for h in range(32)])
         check_outputs(o_sel, r_sel, "config4 seq %d" % n)
         check_state(fin_h[n], np.stack([refp[(n, h)][1] for h in range(32)]), "config4 seq %d" % n)
+
+
+def _prompt_then_decode(fe, prompt_lens, steps, slots_perm=None):
+    """Hand the window of each sequence's first prompt_lens[n] tokens (as a packed prefill
+    batch) to a slot pool, then run `steps` decode steps over the following tokens. Returns
+    the per-step (q, k, v) bf16 bit patterns and conv_prep over the whole sequences."""
+    import torch
+    import linear_attention_recurrence_amd as gdn
+    N = fe.num_seqs
+    K = fe.conv_weight.shape[1]
+    cu = fe.cu_seqlens
+    full_lens = np.diff(cu)
+    assert all(int(p) + steps <= int(L) for p, L in zip(prompt_lens, full_lens))
+    # the prompts as a packed batch of their own
+    rows = np.concatenate([np.arange(cu[n], cu[n] + prompt_lens[n]) for n in range(N)]).astype(np.int64)
+    pcu = np.zeros(N + 1, dtype=np.int32)
+    pcu[1:] = np.cumsum(prompt_lens)
+    mixed_p = (to_dev(fe.mixed[rows]) if len(rows)
+               else torch.empty((0, fe.mixed.shape[1]), dtype=torch.bfloat16, device="cuda"))
+    w = to_dev(fe.conv_weight)
+    pool = N + 3
+    slots = np.arange(N, dtype=np.int32) if slots_perm is None else slots_perm.astype(np.int32)
+    C = fe.mixed.shape[1]
+    win = torch.full((pool, max(K - 1, 1), C), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_conv_window_from_prefill(mixed_p, K, to_dev(pcu), win[:, :K - 1] if K > 1 else win,
+                                     fe.h_qk, fe.h_v, fe.d_k, fe.d_v, window_slots=to_dev(slots))
+    out = []
+    for s in range(steps):
+        tok = np.array([cu[n] + prompt_lens[n] + s for n in range(N)], dtype=np.int64)
+        q, k, v = gdn.gdn_conv_decode_step(to_dev(fe.mixed[tok]), w, win if K > 1 else None,
+                                           fe.h_qk, fe.h_v, fe.d_k, fe.d_v, fe.q_scale,
+                                           window_slots=to_dev(slots))
+        out.append((bf16_bits(q), bf16_bits(k), bf16_bits(v)))
+    qf, kf, vf = _conv_gpu(fe)
+    torch.cuda.synchronize()
+    return out, (bf16_bits(qf), bf16_bits(kf), bf16_bits(vf))
+
+
+@pytest.mark.parametrize("K", [4, 3, 2, 1])
+def test_conv_decode_equals_prefill_bitwise(K):
+    """Prompts of 0, 1, 2, 3, 5 and 40 tokens (some shorter than the window), windows handed
+    to a permuted slot pool, then 6 decode steps: every decode output equals, bit for bit,
+    the prefill front end run over the whole sequence at that token."""
+    prompts = [0, 1, 2, 3, 5, 40]
+    steps = 6
+    fe = workloads.make_frontend([p + steps + 2 for p in prompts], h_qk=2, h_v=4, conv_kernel=K,
+                                 seed=80 + K)
+    perm = np.array([4, 0, 7, 2, 8, 1], dtype=np.int32)
+    out, (qf, kf, vf) = _prompt_then_decode(fe, prompts, steps, perm)
+    cu = fe.cu_seqlens
+    for s, (q, k, v) in enumerate(out):
+        tok = np.array([cu[n] + prompts[n] + s for n in range(len(prompts))])
+        np.testing.assert_array_equal(q, qf[tok], err_msg="q step %d" % s)
+        np.testing.assert_array_equal(k, kf[tok], err_msg="k step %d" % s)
+        np.testing.assert_array_equal(v, vf[tok], err_msg="v step %d" % s)
+
+
+def test_conv_decode_against_oracle():
+    """Decode-time front end at the model's sizes (16 QK / 32 V heads, 8192 channels, k = 4)
+    for 8 sequences after prompts of 0..70 tokens, against the fp64 front end over the whole
+    sequences."""
+    prompts = [0, 1, 3, 7, 17, 33, 64, 70]
+    steps = 3
+    fe = workloads.make_frontend([p + steps for p in prompts], seed=91)
+    out, _ = _prompt_then_decode(fe, prompts, steps)
+    ref = _oracle_conv(fe)
+    for s, (q, k, v) in enumerate(out):
+        for n, p in enumerate(prompts):
+            qr, kr, vr = ref[n]
+            f = workloads.bf16_bits_to_f32
+            _check_one_rounding(f(q[n]).astype(np.float64), qr[p + s], "q seq %d step %d" % (n, s))
+            _check_one_rounding(f(k[n]).astype(np.float64), kr[p + s], "k seq %d step %d" % (n, s))
+            _check_one_rounding(f(v[n]).astype(np.float64), vr[p + s], "v seq %d step %d" % (n, s))
