@@ -250,6 +250,35 @@ def bench_decode_front_end(steps, warmup):
     return conv_ms, wall, both_ms
 
 
+def verify_bytes(num_seqs: int, n_tok: int, snapshots: bool, h_qk=H_QK, h_v=H_V) -> float:
+    """HBM bytes of one verify call: every state read and written once (fp32), the state
+    after every token when snapshots are kept, and q, k, v, o (bf16), g and beta (fp32) of
+    every token."""
+    state = num_seqs * h_v * D * D * 4 * (2 + (n_tok if snapshots else 0))
+    io = num_seqs * n_tok * (2 * h_qk * D * 2 + 2 * h_v * D * 2 + 2 * h_v * 4)
+    return float(state + io)
+
+
+def bench_verify(steps, warmup, n_tok=4):
+    """256 sequences x n_tok draft tokens over the 512 MiB pool, with and without per-token
+    snapshots (2 GiB at n_tok = 4). Returns {snapshots: (wall s, ms per call)}."""
+    import torch
+    import linear_attention_recurrence_amd as gdn
+    import workloads
+    d = workloads.make_decode(num_seqs=256, ring=n_tok, seed=1006)
+    sm = lambda a: _dev(np.ascontiguousarray(np.swapaxes(a, 0, 1)))
+    q, k, v, g, b = sm(d.q), sm(d.k), sm(d.v), sm(d.g), sm(d.beta)
+    pool = _dev(d.pool)
+    o = torch.empty((256, n_tok, H_V, D), dtype=torch.bfloat16, device="cuda")
+    snaps = torch.empty((256, n_tok, H_V, D, D), dtype=torch.float32, device="cuda")
+    out = {}
+    for keep in (True, False):
+        def call(i):
+            gdn.gdn_verify_step(q, k, v, g, b, pool, d.scale, snapshots=snaps if keep else None, o=o)
+        out[keep] = _timed(call, steps, warmup)
+    return out
+
+
 def bench_frontend(reps, warmup):
     """64 packed sequences (lengths uniform in [128, 8192]): gdn_conv_prep then
     gdn_chunk_prefill with per-sequence initial and final states."""
@@ -413,6 +442,21 @@ def main():
             "conv_decode": {"kernel": "conv_decode_kernel", "kernel_ms_back_to_back": cms,
                             "algorithmic_bytes": cbytes,
                             "achieved_GBs": cbytes / (cms / 1e3) / 1e9}}
+    if "decode" in work:
+        vsteps = max(20, args.decode_steps // 10)
+        res = bench_verify(vsteps, args.warmup)
+        out["verify"] = {
+            "workload": "verify step, 256 sequences x 4 draft tokens, 16 QK / 32 V heads, fp32 "
+                        "state pool 512 MiB updated in place",
+            "steps": vsteps}
+        for keep, (vwall, vms) in res.items():
+            vb = verify_bytes(256, 4, keep)
+            achieved = vb / (vms / 1e3) / 1e9
+            out["verify"]["with_snapshots" if keep else "without_snapshots"] = {
+                "ms_per_call": vms, "tokens_per_s": 256 * 4 * vsteps / vwall,
+                "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                             "kernel": "verify_kernel<bf16>", "algorithmic_bytes": vb}}
     if "frontend" in work:
         T4, N4, conv_ms, pre_ms = bench_frontend(10, 2)
         out["frontend_prefill"] = {

@@ -114,6 +114,32 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtyp
                            float scale, void* o, void* stream);
 
 /*
+ * Verify: num_tokens decode steps for each of num_seqs sequences in one call -- the draft
+ * tokens of a speculative step, which the main model checks together and keeps as far as it
+ * agrees (page "Qwen3-Next -- How a running memory and a searchable history cooperate",
+ * section "Speed depends on the serving software"). Token t of sequence n is the t-th step of
+ * gdn_decode_step for that sequence, with the same arithmetic, so the outputs and states are
+ * bit for bit those of num_tokens successive gdn_decode_step calls. The state is read once
+ * and written once; with snapshots set, the state after every token is kept as well, so a
+ * caller that accepts only the first m drafts can restore snapshot m-1.
+ *
+ *   q, k          [num_seqs][num_tokens][h_qk][d_k]   io_dtype
+ *   v             [num_seqs][num_tokens][h_v][d_v]    io_dtype
+ *   g, beta       [num_seqs][num_tokens][h_v]         fp32
+ *   state_pool    [pool_size][h_v][d_v][d_k] fp32, read and written in place: on return it
+ *                 holds each sequence's state after its last token
+ *   state_slots   [num_seqs] int32, as for gdn_decode_step (NULL: entry n); distinct
+ *   snapshots     [num_seqs][num_tokens][h_v][d_v][d_k] fp32: the state after each token,
+ *                 or NULL to keep none
+ *   o             [num_seqs][num_tokens][h_v][d_v]    io_dtype
+ */
+gdn_status gdn_verify_step(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
+                           const float* g, const float* beta,
+                           float* state_pool, const int32_t* state_slots, float* snapshots,
+                           int32_t num_seqs, int32_t num_tokens, int32_t h_qk, int32_t h_v,
+                           int32_t d_k, int32_t d_v, float scale, void* o, void* stream);
+
+/*
  * Front end: short causal depthwise convolution, SiLU, L2 normalisation of every q and k
  * head, and a scale on q (section "01 . GatedDeltaNet(config)" of the Evolving Transformer
  * page names the short convolution for local context and the key normalisation).

@@ -20,7 +20,7 @@ GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN
 GDN_BF16, GDN_F32 = 0, 1
 
 EXPORTED = ("gdn_status_string", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill",
-            "gdn_decode_step", "gdn_conv_prep", "gdn_conv_decode_step",
+            "gdn_decode_step", "gdn_verify_step", "gdn_conv_prep", "gdn_conv_decode_step",
             "gdn_conv_window_from_prefill")
 
 _lib = None
@@ -54,6 +54,9 @@ def load(path: Optional[str] = None):
     lib.gdn_decode_step.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [_P, _P, _P, ctypes.c_int, _P, _P, _P, _P, _I, _I, _I, _I,
                                     _I, ctypes.c_float, _P, _P]
+    lib.gdn_verify_step.restype = ctypes.c_int
+    lib.gdn_verify_step.argtypes = [_P, _P, _P, ctypes.c_int, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                    _I, _I, ctypes.c_float, _P, _P]
     lib.gdn_conv_prep.restype = ctypes.c_int
     lib.gdn_conv_prep.argtypes = [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                                   _P, _P, _P, _P]
@@ -166,6 +169,36 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, scale, state_slots=None, o=Non
                                 _ptr(state_pool), _ptr(state_slots), N, h_qk, h_v, d_k, d_v,
                                 float(scale), _ptr(o), _stream(stream))
     _check(st, "gdn_decode_step")
+    return o
+
+
+def gdn_verify_step(q, k, v, g, beta, state_pool, scale, state_slots=None, snapshots=None,
+                    o=None, stream=None):
+    """num_tokens decode steps per sequence in one call (q [N][n_tok][h_qk][d_k], ...);
+    state_pool is updated in place to the state after the last token, and snapshots
+    [N][n_tok][h_v][d_v][d_k] fp32, if given, receives the state after each token. Returns
+    o [N][n_tok][h_v][d_v]."""
+    N, n_tok, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[2], v.shape[3]
+    if o is None:
+        o = torch.empty((N, n_tok, h_v, d_v), dtype=v.dtype, device=v.device)
+    _expect(k, (N, n_tok, h_qk, d_k), q.dtype, "k")
+    _expect(v, (N, n_tok, h_v, d_v), q.dtype, "v")
+    _expect(g, (N, n_tok, h_v), torch.float32, "g")
+    _expect(beta, (N, n_tok, h_v), torch.float32, "beta")
+    _expect(state_pool, (state_pool.shape[0], h_v, d_v, d_k), torch.float32, "state_pool")
+    _expect(o, (N, n_tok, h_v, d_v), q.dtype, "o")
+    if snapshots is not None:
+        _expect(snapshots, (N, n_tok, h_v, d_v, d_k), torch.float32, "snapshots")
+    if state_slots is None:
+        if state_pool.shape[0] < N:
+            raise ValueError("state_pool has fewer entries than sequences")
+    else:
+        _expect(state_slots, (N,), torch.int32, "state_slots")
+    st = load().gdn_verify_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta),
+                                _ptr(state_pool), _ptr(state_slots), _ptr(snapshots), N, n_tok,
+                                h_qk, h_v, d_k, d_v, float(scale), _ptr(o), _stream(stream))
+    _check(st, "gdn_verify_step")
     return o
 
 

@@ -12,6 +12,13 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool io_bf
                          int num_seqs, int h_qk, int h_v, float scale, void* o,
                          hipStream_t stream);
 
+// Several decode steps per sequence, the state read and written once, per-token states
+// optionally written out (recurrent.hip).
+hipError_t launch_verify(const void* q, const void* k, const void* v, bool io_bf16, const float* g,
+                         const float* beta, float* pool, const int32_t* slots, float* snapshots,
+                         int num_seqs, int num_tokens, int h_qk, int h_v, float scale, void* o,
+                         hipStream_t stream);
+
 // Token-sequential prefill with the state on chip (recurrent.hip); used for fp32 I/O.
 hipError_t launch_recurrent_prefill(const void* q, const void* k, const void* v, bool io_bf16,
                                     const float* g, const float* beta, const int32_t* cu_seqlens,

@@ -19,6 +19,9 @@
 //    per head, 8 rows each: the layout that streams fastest on this chip.
 //  * recurrent_kernel: fp32 prefill, all tokens of a sequence with the state held on chip
 //    between tokens (256 threads, 16 rows each).
+// and verify_kernel, the decode step over several tokens per sequence (draft tokens to be
+// checked at once): decode_kernel's layout and per-token arithmetic (decode_token), the
+// state kept in registers between the tokens and, when asked, written out after each one.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -28,6 +31,8 @@ namespace {
 constexpr int kRowsPerThread = 16;   // 128 rows / (4 waves * 2 half-waves)
 
 struct RecArgs {
+  int n_tok;                   // verify: tokens per sequence
+  float* snap;                 // verify: per-token states, or NULL
   const void* q;
   const void* k;
   const void* v;
@@ -74,6 +79,35 @@ __device__ __forceinline__ float reduce_scatter16(float (&vals)[16], int lane32)
   return vals[0] + __shfl_xor(vals[0], 1, 32);
 }
 
+// One token of the decode layout (8 rows per thread, rows row_base + 16 i): u = S k and r = S q
+// on the rows, c = beta (v - alpha u) and the rank-one update of S in place. Returns
+// scale (alpha r + c (k . q)), this lane's output when (c4 & 3) == 2 (for row my_row).
+__device__ __forceinline__ float decode_token(f32x4 (&S)[8], f32x4 k4, f32x4 q4, float alpha, float beta,
+                                              float vrow, float scale, int c4) {
+  const bool my_is_r = (c4 & 2) != 0;
+  float vals[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    vals[2 * i] = S[i][0] * k4[0] + S[i][1] * k4[1] + S[i][2] * k4[2] + S[i][3] * k4[3];
+    vals[2 * i + 1] = S[i][0] * q4[0] + S[i][1] * q4[1] + S[i][2] * q4[2] + S[i][3] * q4[3];
+  }
+  const float mine = reduce_scatter16(vals, c4);
+  const float other = __shfl_xor(mine, 2, 32);
+  const float u = my_is_r ? other : mine;
+  const float r = my_is_r ? mine : other;
+  const float kq = half_wave_sum(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
+  const float c = beta * (vrow - alpha * u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float ci = __shfl(c, 4 * i, 32);
+    S[i][0] = alpha * S[i][0] + ci * k4[0];
+    S[i][1] = alpha * S[i][1] + ci * k4[1];
+    S[i][2] = alpha * S[i][2] + ci * k4[2];
+    S[i][3] = alpha * S[i][3] + ci * k4[3];
+  }
+  return scale * (alpha * r + c * kq);
+}
+
 // One decode step. Thread (wave w of 8, lane l) holds columns 4*(l%32) .. +3 of the 8 rows
 // i*16 + 2*w + l/32, i = 0..7: each load or store instruction of a wave covers two whole
 // rows (1 KB). Same arithmetic as recurrent_kernel for one token.
@@ -103,9 +137,7 @@ __global__ __launch_bounds__(512) void decode_kernel(RecArgs a) {
     S[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)i * 16 * kHeadDim));
 
   // lanes 4i, 4i+1 finish u of row slot i; lanes 4i+2, 4i+3 finish r
-  const int my_slot = c4 >> 2;
-  const int my_row = row_base + 16 * my_slot;
-  const bool my_is_r = (c4 & 2) != 0;
+  const int my_row = row_base + 16 * (c4 >> 2);
 
   const size_t qk_off = ((size_t)n * a.h_qk + j) * kHeadDim + 4 * c4;
   const f32x4 k4 = load4(k + qk_off);
@@ -114,29 +146,92 @@ __global__ __launch_bounds__(512) void decode_kernel(RecArgs a) {
   const float beta = a.beta[(size_t)n * a.h_v + h];
   const float vrow = load1(v + ((size_t)n * a.h_v + h) * kHeadDim + my_row);
 
-  float vals[16];
+  const float out = decode_token(S, k4, q4, alpha, beta, vrow, a.scale, c4);
+  if ((c4 & 3) == 2) store1(o + ((size_t)n * a.h_v + h) * kHeadDim + my_row, out);
 #pragma unroll
-  for (int i = 0; i < kRows; ++i) {
-    vals[2 * i] = S[i][0] * k4[0] + S[i][1] * k4[1] + S[i][2] * k4[2] + S[i][3] * k4[3];
-    vals[2 * i + 1] = S[i][0] * q4[0] + S[i][1] * q4[1] + S[i][2] * q4[2] + S[i][3] * q4[3];
-  }
-  const float mine = reduce_scatter16(vals, c4);
-  const float other = __shfl_xor(mine, 2, 32);
-  const float u = my_is_r ? other : mine;
-  const float r = my_is_r ? mine : other;
-  const float kq = half_wave_sum(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
-  const float c = beta * (vrow - alpha * u);
-  if ((c4 & 3) == 2) store1(o + ((size_t)n * a.h_v + h) * kHeadDim + my_row, a.scale * (alpha * r + c * kq));
-
-#pragma unroll
-  for (int i = 0; i < kRows; ++i) {
-    const float ci = __shfl(c, 4 * i, 32);
-    S[i][0] = alpha * S[i][0] + ci * k4[0];
-    S[i][1] = alpha * S[i][1] + ci * k4[1];
-    S[i][2] = alpha * S[i][2] + ci * k4[2];
-    S[i][3] = alpha * S[i][3] + ci * k4[3];
+  for (int i = 0; i < kRows; ++i)
     __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(sp + (size_t)i * 16 * kHeadDim));
+}
+
+// Several decode steps per sequence in one launch: tokens t = 0 .. n_tok - 1 of sequence n
+// are rows n * n_tok + t of q, k, v, g, beta and o. The state is read from the pool once,
+// kept in registers across the tokens (written to snap[n][t] after token t when snap is
+// set) and written back to the pool after the last token.
+template <typename IO>
+__global__ __launch_bounds__(512) void verify_kernel(RecArgs a) {
+  constexpr int kRows = 8;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int c4 = lane & 31;
+  const int n = blockIdx.x / a.h_v;
+  const int h = blockIdx.x % a.h_v;
+  const int j = h / (a.h_v / a.h_qk);
+  const IO* q = static_cast<const IO*>(a.q);
+  const IO* k = static_cast<const IO*>(a.k);
+  const IO* v = static_cast<const IO*>(a.v);
+  IO* o = static_cast<IO*>(a.o);
+  const int slot = a.slots ? a.slots[n] : n;
+  const size_t state = ((size_t)slot * a.h_v + h) * kHeadDim * kHeadDim;
+  const int row_base = w * 2 + half;        // rows row_base + 16*i
+  const size_t lane_off = (size_t)row_base * kHeadDim + 4 * c4;
+
+  float* sp = a.s_out + state + lane_off;
+  f32x4 S[kRows];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i)
+    S[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)i * 16 * kHeadDim));
+  const int my_row = row_base + 16 * (c4 >> 2);
+
+  // token t's inputs are requested during token t - 1 (before its stores, so waiting for
+  // them never waits for a store)
+  struct Tok {
+    f32x4 k4, q4;
+    float g, beta, vrow;
+  };
+  auto fetch = [&](int t) {
+    const size_t tok = (size_t)n * a.n_tok + t;
+    const size_t qk_off = (tok * a.h_qk + j) * kHeadDim + 4 * c4;
+    Tok x;
+    x.k4 = load4(k + qk_off);
+    x.q4 = load4(q + qk_off);
+    x.g = a.g[tok * a.h_v + h];
+    x.beta = a.beta[tok * a.h_v + h];
+    x.vrow = load1(v + (tok * a.h_v + h) * kHeadDim + my_row);
+    return x;
+  };
+  // one token: the read-out and update, the output, and the snapshot when asked
+  auto step = [&](Tok& x, int t) {
+    const size_t tok = (size_t)n * a.n_tok + t;
+    const float alpha = __expf(x.g);
+    const float out = decode_token(S, x.k4, x.q4, alpha, x.beta, x.vrow, a.scale, c4);
+    if ((c4 & 3) == 2) store1(o + (tok * a.h_v + h) * kHeadDim + my_row, out);
+    if (a.snap) {
+      float* dst = a.snap + (tok * a.h_v + h) * kHeadDim * kHeadDim + lane_off;
+#pragma unroll
+      for (int i = 0; i < kRows; ++i)
+        __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(dst + (size_t)i * 16 * kHeadDim));
+    }
+  };
+  // Two alternating input sets (no copy from one to the other, so a load never has to wait
+  // for the register it overwrites); past the last token the loads repeat it, unused.
+  Tok ta = fetch(0), tb;
+  for (int t = 0; t < a.n_tok; t += 2) {
+    tb = fetch(min(t + 1, a.n_tok - 1));
+    // the next token's loads are issued here: this token's k and q pass through the asm, so
+    // no product that uses them moves above it
+    asm volatile("" : "+v"(ta.k4), "+v"(ta.q4) :: "memory");
+    step(ta, t);
+    if (t + 1 < a.n_tok) {
+      ta = fetch(min(t + 2, a.n_tok - 1));
+      asm volatile("" : "+v"(tb.k4), "+v"(tb.q4) :: "memory");
+      step(tb, t + 1);
+    }
   }
+#pragma unroll
+  for (int i = 0; i < kRows; ++i)
+    __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(sp + (size_t)i * 16 * kHeadDim));
 }
 
 template <typename IO>
@@ -222,7 +317,7 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool io_bf
                          const float* g, const float* beta, float* pool, const int32_t* slots,
                          int num_seqs, int h_qk, int h_v, float scale, void* o,
                          hipStream_t stream) {
-  RecArgs a{q, k, v, g, beta, nullptr, slots, pool, pool, o, num_seqs, h_qk, h_v, scale};
+  RecArgs a{1, nullptr, q, k, v, g, beta, nullptr, slots, pool, pool, o, num_seqs, h_qk, h_v, scale};
   const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(512);
   if (io_bf16)
     hipLaunchKernelGGL((decode_kernel<bf16>), grid, block, 0, stream, a);
@@ -235,12 +330,25 @@ hipError_t launch_recurrent_prefill(const void* q, const void* k, const void* v,
                                     const float* g, const float* beta, const int32_t* cu_seqlens,
                                     int num_seqs, int h_qk, int h_v, float scale,
                                     const float* s0, float* s_final, void* o, hipStream_t stream) {
-  RecArgs a{q, k, v, g, beta, cu_seqlens, nullptr, s0, s_final, o, num_seqs, h_qk, h_v, scale};
+  RecArgs a{0, nullptr, q, k, v, g, beta, cu_seqlens, nullptr, s0, s_final, o, num_seqs, h_qk, h_v, scale};
   const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(256);
   if (io_bf16)
     hipLaunchKernelGGL((recurrent_kernel<bf16>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((recurrent_kernel<float>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const void* q, const void* k, const void* v, bool io_bf16, const float* g,
+                         const float* beta, float* pool, const int32_t* slots, float* snapshots,
+                         int num_seqs, int num_tokens, int h_qk, int h_v, float scale, void* o,
+                         hipStream_t stream) {
+  RecArgs a{num_tokens, snapshots, q, k, v, g, beta, nullptr, slots, pool, pool, o, num_seqs, h_qk, h_v, scale};
+  const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(512);
+  if (io_bf16)
+    hipLaunchKernelGGL((verify_kernel<bf16>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((verify_kernel<float>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -25,8 +25,9 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(["gdn_status_string", "gdn_chunk_prefill_workspace_bytes",
-                                            "gdn_chunk_prefill", "gdn_decode_step", "gdn_conv_prep",
-                                            "gdn_conv_decode_step", "gdn_conv_window_from_prefill"])
+                                            "gdn_chunk_prefill", "gdn_decode_step", "gdn_verify_step",
+                                            "gdn_conv_prep", "gdn_conv_decode_step",
+                                            "gdn_conv_window_from_prefill"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -135,6 +136,33 @@ def test_conv_prep_validation():
     assert call(dv=64) == L.GDN_ERR_UNSUPPORTED
     assert call(T=-1) == L.GDN_ERR_SHAPE
     assert call(T=0) == L.GDN_OK
+
+
+def test_verify_validation():
+    lib, L = _lib()
+    f = lib.gdn_verify_step
+    P = _fake
+    ok = dict(q=P(1), k=P(2), v=P(3), dt=0, g=P(4), b=P(5), pool=P(6), slots=None, snap=None,
+              n=2, nt=3, hqk=16, hv=32, dk=128, dv=128, sc=0.1, o=P(7), st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["dt"], a["g"], a["b"], a["pool"], a["slots"],
+                 a["snap"], a["n"], a["nt"], a["hqk"], a["hv"], a["dk"], a["dv"], a["sc"], a["o"],
+                 a["st"])
+
+    assert call(q=None) == L.GDN_ERR_NULL
+    assert call(b=None) == L.GDN_ERR_NULL
+    assert call(pool=None) == L.GDN_ERR_NULL
+    assert call(o=None) == L.GDN_ERR_NULL
+    assert call(n=-1) == L.GDN_ERR_SHAPE
+    assert call(nt=-1) == L.GDN_ERR_SHAPE
+    assert call(hv=24) == L.GDN_ERR_SHAPE
+    assert call(dk=64) == L.GDN_ERR_UNSUPPORTED
+    assert call(dt=7) == L.GDN_ERR_UNSUPPORTED
+    assert call(nt=0) == L.GDN_OK
+    assert call(n=0) == L.GDN_OK
 
 
 def test_conv_decode_validation():
