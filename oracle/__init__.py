@@ -48,6 +48,8 @@ def load_library(path: Optional[str] = None):
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_double, _D, _D, _D, _D,
                                        ctypes.c_int]
+    lib.gdn_ref_recurrence_channel.restype = ctypes.c_int
+    lib.gdn_ref_recurrence_channel.argtypes = lib.gdn_ref_recurrence.argtypes
     lib.gdn_ref_conv_prep.restype = ctypes.c_int
     lib.gdn_ref_conv_prep.argtypes = [_D, _D, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -107,6 +109,36 @@ def recurrence(q, k, v, g, beta, cu_seqlens, scale, initial_state=None,
                                     h_qk, h_v, d_k, d_v, float(scale), _dp(s0), _dp(fin),
                                     _dp(o), _dp(traj),
                                     int(n_threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return o, fin, traj
+
+
+def recurrence_channel(q, k, v, g, beta, cu_seqlens, scale, initial_state=None,
+                       want_final=True, want_traj=False, n_threads=None, lib=None):
+    """The per-channel form, fp64: one log-decay per value channel, g [T][h_v][d_v], and the
+    correction taken from the state before the decay (code panel of section
+    "01 . GatedDeltaNet(config)" of "Qwen3-Next 80B-A3B -- The Evolving Transformer").
+    Other arguments and the returned tuple as for recurrence()."""
+    f = lambda a: np.ascontiguousarray(a, dtype=np.float64)
+    q, k, v, g, beta = f(q), f(k), f(v), f(g), f(beta)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    T, h_qk, d_k = q.shape
+    _, h_v, d_v = v.shape
+    N = len(cu) - 1
+    assert k.shape == q.shape and v.shape[0] == T and g.shape == (T, h_v, d_v)
+    assert beta.shape == (T, h_v)
+    assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    s0 = None if initial_state is None else f(initial_state)
+    if s0 is not None:
+        assert s0.shape == (N, h_v, d_v, d_k)
+    o = np.zeros((T, h_v, d_v), dtype=np.float64)
+    fin = np.zeros((N, h_v, d_v, d_k), dtype=np.float64) if want_final else None
+    traj = np.zeros((h_v, T, d_v, d_k), dtype=np.float64) if want_traj else None
+    rc = (lib or _load()).gdn_ref_recurrence_channel(
+        _dp(q), _dp(k), _dp(v), _dp(g), _dp(beta), cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        N, h_qk, h_v, d_k, d_v, float(scale), _dp(s0), _dp(fin), _dp(o), _dp(traj),
+        int(n_threads or default_threads()))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return o, fin, traj

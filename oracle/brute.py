@@ -88,3 +88,40 @@ def rank1_chain(S0: Mat, qs, ks, vs, alphas, betas, scale=Fraction(1)):
         outs.append([scale * sum((S[i][j] * q[j] for j in range(len(q))), Fraction(0))
                      for i in range(len(S))])
     return states, outs
+
+
+def unrolled_chain_channel(S0: Mat, qs, ks, vs, alpha_rows, betas, scale=Fraction(1)):
+    """The per-channel form (code panel of section "01 . GatedDeltaNet(config)" of the
+    Evolving Transformer page) by its unrolled product, row by row. Row i of the state
+    evolves on its own: S_i -> S_i (alpha_i I - beta k k^T) + beta v_i k^T, so
+
+        S_{i,T} = S_{i,0} N_1 ... N_T + sum_t beta_t v_{t,i} k_t^T N_{t+1} ... N_T,
+        N_t = alpha_{t,i} I - beta_t k_t k_t^T.
+
+    alpha_rows[t][i] is the decay of value channel i at token t. Each S_t is evaluated from
+    scratch, the brute force; returns (states, outputs) as unrolled_chain does."""
+    T = len(ks)
+    d_v, d_k = len(S0), len(S0[0])
+    I = _eye(d_k)
+
+    def N(t, i):
+        return [[alpha_rows[t][i] * I[a][b] - betas[t] * ks[t][a] * ks[t][b] for b in range(d_k)]
+                for a in range(d_k)]
+
+    states, outs = [], []
+    for t_end in range(1, T + 1):
+        S = []
+        for i in range(d_v):
+            row = [list(S0[i])]
+            for t in range(t_end):
+                row = _matmul(row, N(t, i))
+            for t in range(t_end):
+                term = [[betas[t] * vs[t][i] * kj for kj in ks[t]]]
+                for s in range(t + 1, t_end):
+                    term = _matmul(term, N(s, i))
+                row = _add(row, term)
+            S.append(row[0])
+        states.append(S)
+        qt = qs[t_end - 1]
+        outs.append([scale * sum((S[i][j] * qt[j] for j in range(d_k)), Fraction(0)) for i in range(d_v)])
+    return states, outs

@@ -21,6 +21,11 @@
  *    Overview"); V head h reads QK head h / (h_v / h_qk), the repeat-interleave convention
  *    of the GQA code in section "02 . GatedAttention(config)" of the Evolving Transformer
  *    page.
+ *  - The per-channel form of the code panel in section "01 . GatedDeltaNet(config)" of the
+ *    Evolving Transformer page: one decay per value channel, and the correction measured
+ *    against the state before the decay:
+ *        S_t = diag(alpha_t) S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T
+ *    (alpha_t a vector of d_v decays; o_t = scale * S_t q_t as above).
  *  - The front end: a short causal depthwise convolution over the projected q|k|v
  *    channels, SiLU, L2 normalisation of each q and k head and a scale on q (the
  *    GatedDeltaNet section names a short 1-D convolution for local context and normalises
@@ -94,6 +99,55 @@ void gdn_ref_chain(int T, int d_k, int d_v,
     }
 }
 
+/*
+ * The per-channel form for T tokens of one chain: as gdn_ref_chain, with g holding d_v
+ * log-decays per token (token t at g + t*g_stride, one per value channel i) and the
+ * correction taken from the state before the decay.
+ */
+void gdn_ref_chain_channel(int T, int d_k, int d_v,
+                           const double* q, ptrdiff_t qk_stride_q,
+                           const double* k, ptrdiff_t qk_stride_k,
+                           const double* v, ptrdiff_t v_stride,
+                           const double* g, ptrdiff_t g_stride,
+                           const double* beta, ptrdiff_t b_stride,
+                           double scale, double* S, double* o, ptrdiff_t o_stride,
+                           double* traj, double* u)
+{
+    for (int t = 0; t < T; ++t) {
+        const double* qt = q + (ptrdiff_t)t * qk_stride_q;
+        const double* kt = k + (ptrdiff_t)t * qk_stride_k;
+        const double* vt = v + (ptrdiff_t)t * v_stride;
+        const double* gt = g + (ptrdiff_t)t * g_stride;
+        const double b = beta[(ptrdiff_t)t * b_stride];
+
+        /* u = S k, from the state before this token's decay */
+        for (int i = 0; i < d_v; ++i) {
+            const double* Si = S + (ptrdiff_t)i * d_k;
+            double acc = 0.0;
+            for (int j = 0; j < d_k; ++j) acc += Si[j] * kt[j];
+            u[i] = acc;
+        }
+        /* row i: S_i <- alpha_i S_i + b (v_i - u_i) k^T */
+        for (int i = 0; i < d_v; ++i) {
+            double* Si = S + (ptrdiff_t)i * d_k;
+            const double ai = exp(gt[i]);
+            const double ci = b * (vt[i] - u[i]);
+            for (int j = 0; j < d_k; ++j) Si[j] = ai * Si[j] + ci * kt[j];
+        }
+        /* read-out after the update */
+        if (o) {
+            double* ot = o + (ptrdiff_t)t * o_stride;
+            for (int i = 0; i < d_v; ++i) {
+                const double* Si = S + (ptrdiff_t)i * d_k;
+                double acc = 0.0;
+                for (int j = 0; j < d_k; ++j) acc += Si[j] * qt[j];
+                ot[i] = scale * acc;
+            }
+        }
+        if (traj) memcpy(traj + (ptrdiff_t)t * d_v * d_k, S, sizeof(double) * (size_t)d_v * d_k);
+    }
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* Packed variable-length batch.                                                         */
 /* ------------------------------------------------------------------------------------ */
@@ -107,6 +161,7 @@ typedef struct {
     double* s_final;
     double* o;
     double* traj;
+    int channel;            /* 1: per-channel form, g is [T][h_v][d_v] */
     int next;               /* next chain index, taken under the lock */
     pthread_mutex_t lock;
 } batch_job;
@@ -123,14 +178,25 @@ static void run_chain(batch_job* J, int chain, double* S, double* u)
     const ptrdiff_t v_stride = (ptrdiff_t)J->h_v * J->d_v;
     /* trajectory layout [h_v][T_total][d_v][d_k]: the chain's states are consecutive */
     double* traj = J->traj ? J->traj + ((size_t)h * J->cu[J->num_seqs] + (size_t)t0) * sz : NULL;
-    gdn_ref_chain((int)T, J->d_k, J->d_v,
-                  J->q + t0 * qk_stride + (ptrdiff_t)j * J->d_k, qk_stride,
-                  J->k + t0 * qk_stride + (ptrdiff_t)j * J->d_k, qk_stride,
-                  J->v + t0 * v_stride + (ptrdiff_t)h * J->d_v, v_stride,
-                  J->g + t0 * J->h_v + h, J->beta + t0 * J->h_v + h, J->h_v,
-                  J->scale, S,
-                  J->o ? J->o + t0 * v_stride + (ptrdiff_t)h * J->d_v : NULL, v_stride,
-                  traj, u);
+    if (J->channel)
+        gdn_ref_chain_channel((int)T, J->d_k, J->d_v,
+                              J->q + t0 * qk_stride + (ptrdiff_t)j * J->d_k, qk_stride,
+                              J->k + t0 * qk_stride + (ptrdiff_t)j * J->d_k, qk_stride,
+                              J->v + t0 * v_stride + (ptrdiff_t)h * J->d_v, v_stride,
+                              J->g + t0 * v_stride + (ptrdiff_t)h * J->d_v, v_stride,
+                              J->beta + t0 * J->h_v + h, J->h_v,
+                              J->scale, S,
+                              J->o ? J->o + t0 * v_stride + (ptrdiff_t)h * J->d_v : NULL, v_stride,
+                              traj, u);
+    else
+        gdn_ref_chain((int)T, J->d_k, J->d_v,
+                      J->q + t0 * qk_stride + (ptrdiff_t)j * J->d_k, qk_stride,
+                      J->k + t0 * qk_stride + (ptrdiff_t)j * J->d_k, qk_stride,
+                      J->v + t0 * v_stride + (ptrdiff_t)h * J->d_v, v_stride,
+                      J->g + t0 * J->h_v + h, J->beta + t0 * J->h_v + h, J->h_v,
+                      J->scale, S,
+                      J->o ? J->o + t0 * v_stride + (ptrdiff_t)h * J->d_v : NULL, v_stride,
+                      traj, u);
     if (J->s_final) memcpy(J->s_final + ((size_t)n * J->h_v + h) * sz, S, sizeof(double) * sz);
 }
 
@@ -154,19 +220,19 @@ static void* batch_worker(void* arg)
 }
 
 /*
- * Gated delta rule over a packed batch.
+ * Gated delta rule over a packed batch (gdn_ref_recurrence below; the shared driver).
  *   q, k  [T][h_qk][d_k];  v [T][h_v][d_v];  g, beta [T][h_v];  cu_seqlens [N+1]
  *   initial_state [N][h_v][d_v][d_k] or NULL (zeros); final_state same shape or NULL
  *   o [T][h_v][d_v] or NULL
  *   traj: NULL, or [h_v][T][d_v][d_k] receiving the state after every token (small cases)
  * Returns 0, or -1 on a bad argument.
  */
-int gdn_ref_recurrence(const double* q, const double* k, const double* v,
-                       const double* g, const double* beta,
-                       const int64_t* cu_seqlens, int num_seqs,
-                       int h_qk, int h_v, int d_k, int d_v, double scale,
-                       const double* initial_state, double* final_state,
-                       double* o, double* traj, int n_threads)
+static int run_batch(const double* q, const double* k, const double* v,
+                     const double* g, const double* beta,
+                     const int64_t* cu_seqlens, int num_seqs,
+                     int h_qk, int h_v, int d_k, int d_v, double scale,
+                     const double* initial_state, double* final_state,
+                     double* o, double* traj, int n_threads, int channel)
 {
     if (num_seqs < 0 || h_qk <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0) return -1;
     if (h_v % h_qk != 0) return -1;
@@ -175,6 +241,7 @@ int gdn_ref_recurrence(const double* q, const double* k, const double* v,
     J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.cu = cu_seqlens;
     J.num_seqs = num_seqs; J.h_qk = h_qk; J.h_v = h_v; J.d_k = d_k; J.d_v = d_v;
     J.scale = scale; J.s0 = initial_state; J.s_final = final_state; J.o = o; J.traj = traj;
+    J.channel = channel;
     J.next = 0;
     pthread_mutex_init(&J.lock, NULL);
     if (n_threads < 1) n_threads = 1;
@@ -189,6 +256,32 @@ int gdn_ref_recurrence(const double* q, const double* k, const double* v,
     }
     pthread_mutex_destroy(&J.lock);
     return 0;
+}
+
+int gdn_ref_recurrence(const double* q, const double* k, const double* v,
+                       const double* g, const double* beta,
+                       const int64_t* cu_seqlens, int num_seqs,
+                       int h_qk, int h_v, int d_k, int d_v, double scale,
+                       const double* initial_state, double* final_state,
+                       double* o, double* traj, int n_threads)
+{
+    return run_batch(q, k, v, g, beta, cu_seqlens, num_seqs, h_qk, h_v, d_k, d_v, scale,
+                     initial_state, final_state, o, traj, n_threads, 0);
+}
+
+/*
+ * The per-channel form over a packed batch: as gdn_ref_recurrence, with g [T][h_v][d_v]
+ * (one log-decay per value channel) and beta [T][h_v].
+ */
+int gdn_ref_recurrence_channel(const double* q, const double* k, const double* v,
+                               const double* g, const double* beta,
+                               const int64_t* cu_seqlens, int num_seqs,
+                               int h_qk, int h_v, int d_k, int d_v, double scale,
+                               const double* initial_state, double* final_state,
+                               double* o, double* traj, int n_threads)
+{
+    return run_batch(q, k, v, g, beta, cu_seqlens, num_seqs, h_qk, h_v, d_k, d_v, scale,
+                     initial_state, final_state, o, traj, n_threads, 1);
 }
 
 /* ------------------------------------------------------------------------------------ */

@@ -368,6 +368,133 @@ def test_front_end_closed_forms():
 
 
 # ---------------------------------------------------------------------------------------
+# per-channel form (one decay per value channel, correction from the state before the
+# decay: the code panel of section "01 . GatedDeltaNet(config)" of the Evolving Transformer)
+# ---------------------------------------------------------------------------------------
+
+def _channel_rational_case(seed, seq_lens, h_qk, h_v, d_k=3, d_v=2):
+    c = _rational_case(seed, seq_lens, h_qk, h_v, d_k, d_v)
+    rng = np.random.default_rng(seed + 1000)
+    T = sum(seq_lens)
+    c["alpha_rows"] = [[[Fraction(int(rng.integers(1, 9)), 8) for _ in range(d_v)] for _ in range(h_v)]
+                       for _ in range(T)]
+    return c
+
+
+def _channel_brute_pass(seed, seq_lens, h_qk, h_v, lib=None):
+    c = _channel_rational_case(seed, seq_lens, h_qk, h_v)
+    scale = Fraction(1, 2)
+    cu = np.concatenate([[0], np.cumsum(seq_lens)]).astype(np.int64)
+    f = lambda x: np.array(x, dtype=object).astype(np.float64)
+    o, fin, _ = oracle.recurrence_channel(
+        f(c["q"]), f(c["k"]), f(c["v"]), np.log(f(c["alpha_rows"])), f(c["beta"]), cu,
+        float(scale), initial_state=f(c["S0"]), lib=lib)
+    group = h_v // h_qk
+    for n in range(len(seq_lens)):
+        sl = range(int(cu[n]), int(cu[n + 1]))
+        for h in range(h_v):
+            j = h // group
+            states, outs = brute.unrolled_chain_channel(
+                c["S0"][n][h], [c["q"][t][j] for t in sl], [c["k"][t][j] for t in sl],
+                [c["v"][t][h] for t in sl], [c["alpha_rows"][t][h] for t in sl],
+                [c["beta"][t][h] for t in sl], scale)
+            final = states[-1] if states else c["S0"][n][h]
+            if not np.allclose(fin[n, h], f(final), rtol=1e-13, atol=1e-14):
+                return False
+            if len(sl) and not np.allclose(o[list(sl), h], f(outs), rtol=1e-13, atol=1e-14):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("seed,seq_lens,h_qk,h_v", [(21, [6], 1, 1), (22, [0, 3, 5], 1, 2),
+                                                    (23, [4, 2], 2, 4)])
+def test_channel_form_brute_force_exact(seed, seq_lens, h_qk, h_v):
+    """Against the row-by-row unrolled product (exact rationals; d_k = 3, d_v = 2)."""
+    assert _channel_brute_pass(seed, seq_lens, h_qk, h_v)
+
+
+def test_channel_form_alpha_one_is_the_main_form():
+    """With every decay 1 the two forms are one rule (decay first or not makes no difference)."""
+    x = workloads.make_prefill([30, 7], h_qk=2, h_v=4, d_k=8, d_v=6, io_dtype="f32",
+                               with_initial_state=True, seed=31)
+    q, k, v, b = x.as_f64("q"), x.as_f64("k"), x.as_f64("v"), x.as_f64("beta")
+    S0 = x.as_f64("initial_state")
+    o1, f1, _ = oracle.recurrence(q, k, v, np.zeros_like(b), b, x.cu_seqlens, x.scale, initial_state=S0)
+    o2, f2, _ = oracle.recurrence_channel(q, k, v, np.zeros(b.shape + (6,)), b, x.cu_seqlens,
+                                          x.scale, initial_state=S0)
+    np.testing.assert_allclose(o2, o1, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(f2, f1, rtol=1e-13, atol=1e-15)
+
+
+def test_channel_form_equal_decays_map_onto_the_main_form():
+    """With one decay a for every channel, a S + b (v - S k) k^T is the main form's
+    a S + b' (v' - a S k) k^T at b' = b / a and v' = a v: the correction is taken from the
+    state before the decay in one form and after it in the other."""
+    x = workloads.make_prefill([25], h_qk=1, h_v=2, d_k=8, d_v=6, io_dtype="f32",
+                               with_initial_state=True, seed=32)
+    q, k, v, b, g = x.as_f64("q"), x.as_f64("k"), x.as_f64("v"), x.as_f64("beta"), x.as_f64("g")
+    S0 = x.as_f64("initial_state")
+    a = np.exp(g)                                   # [T][h_v]
+    o1, f1, _ = oracle.recurrence_channel(q, k, v, np.repeat(g[:, :, None], 6, axis=2), b,
+                                          x.cu_seqlens, x.scale, initial_state=S0)
+    o2, f2, _ = oracle.recurrence(q, k, v * a[:, :, None], g, b / a, x.cu_seqlens, x.scale,
+                                  initial_state=S0)
+    np.testing.assert_allclose(o1, o2, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(f1, f2, rtol=1e-11, atol=1e-14)
+
+
+def test_channel_form_beta_zero_is_row_decay():
+    """beta = 0: row i of the state is scaled by the running product of its own decays (a
+    decay applied to columns instead, or with the wrong channel index, fails this)."""
+    x = workloads.make_prefill([20], h_qk=1, h_v=2, d_k=7, d_v=5, io_dtype="f32",
+                               with_initial_state=True, seed=33)
+    rng = np.random.default_rng(33)
+    g = -np.abs(rng.standard_normal((20, 2, 5))) * 0.1
+    S0 = x.as_f64("initial_state")
+    q = x.as_f64("q")
+    o, fin, _ = oracle.recurrence_channel(q, x.as_f64("k"), x.as_f64("v"), g,
+                                          np.zeros((20, 2)), x.cu_seqlens, x.scale, initial_state=S0)
+    cum = np.exp(np.cumsum(g, axis=0))              # [T][h_v][d_v]
+    np.testing.assert_allclose(fin[0], cum[-1][:, :, None] * S0[0], rtol=1e-13)
+    for h in range(2):
+        expect = x.scale * cum[:, h, :] * (q[:, 0] @ S0[0, h].T)
+        np.testing.assert_allclose(o[:, h], expect, rtol=1e-12, atol=1e-15)
+
+
+_CH_MUTATIONS = {
+    "channel: correction from the decayed state": ("const double ci = b * (vt[i] - u[i]);",
+                                                   "const double ci = b * (vt[i] - ai * u[i]);"),
+    "channel: decay by key channel": ("for (int j = 0; j < d_k; ++j) Si[j] = ai * Si[j] + ci * kt[j];",
+                                      "for (int j = 0; j < d_k; ++j) Si[j] = exp(gt[j % d_v]) * Si[j] + ci * kt[j];"),
+    "channel: no decay": ("const double ai = exp(gt[i]);", "const double ai = 1.0;"),
+    "channel: read-out before the update": ("/* read-out after the update */\n        if (o) {",
+                                            "/* mutated */\n        if (0) {"),
+}
+
+
+@pytest.fixture(scope="module")
+def channel_mutant_libs():
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "gdn_oracle.c")).read()
+    libs = {}
+    with tempfile.TemporaryDirectory() as td:
+        for name, (a, b) in _CH_MUTATIONS.items():
+            assert src.count(a) == 1, name
+            path = os.path.join(td, "c%d.c" % len(libs))
+            with open(path, "w") as f:
+                f.write(src.replace(a, b))
+            so = path[:-2] + ".so"
+            subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                                   path, "-o", so, "-lm"])
+            libs[name] = oracle.load_library(so)
+        yield libs
+
+
+@pytest.mark.parametrize("name", sorted(_CH_MUTATIONS))
+def test_channel_pins_catch_planted_mistake(channel_mutant_libs, name):
+    assert not _channel_brute_pass(22, [0, 3, 5], 1, 2, lib=channel_mutant_libs[name]), name
+
+
+# ---------------------------------------------------------------------------------------
 # planted mistakes: each plausible slip in the oracle fails at least one pin above
 # ---------------------------------------------------------------------------------------
 
