@@ -279,6 +279,37 @@ def bench_verify(steps, warmup, n_tok=4):
     return out
 
 
+def bench_channel_decay(steps, warmup, prefill_reps=5):
+    """The per-channel form: one decode step at 256 sequences over the 512 MiB pool (a ring of
+    16 input sets, per-channel log-decays [256][32][128]), and the token-sequential prefill
+    at B = 1, T = 4096. Returns (decode wall s, decode ms, prefill ms)."""
+    import torch
+    import linear_attention_recurrence_amd as gdn
+    import workloads
+    d = workloads.config3()
+    pool = _dev(d.pool)
+    q, k, v, b = _dev(d.q), _dev(d.k), _dev(d.v), _dev(d.beta)
+    g = _dev(workloads.channel_log_alpha(16 * 256, seed=1008).reshape(16, 256, H_V, D))
+    o = torch.empty((256, H_V, D), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        r = i % 16
+        gdn.gdn_channel_decay_decode_step(q[r], k[r], v[r], g[r], b[r], pool, d.scale, o=o)
+
+    dwall, dms = _timed(step, steps, warmup)
+    x = workloads.config1()
+    xq, xk, xv, xb, cu = _dev(x.q), _dev(x.k), _dev(x.v), _dev(x.beta), _dev(x.cu_seqlens)
+    xg = _dev(workloads.channel_log_alpha(4096, seed=1009))
+    xo = torch.empty((4096, H_V, D), dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty((1, H_V, D, D), dtype=torch.float32, device="cuda")
+
+    def prefill(i):
+        gdn.gdn_channel_decay_prefill(xq, xk, xv, xg, xb, cu, x.scale, final_state=fin, o=xo)
+
+    _, pms = _timed(prefill, prefill_reps, 1)
+    return dwall, dms, pms
+
+
 def bench_frontend(reps, warmup):
     """64 packed sequences (lengths uniform in [128, 8192]): gdn_conv_prep then
     gdn_chunk_prefill with per-sequence initial and final states."""
@@ -457,6 +488,23 @@ def main():
                 "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                              "kernel": "verify_kernel<bf16>", "algorithmic_bytes": vb}}
+    if "decode" in work:
+        csteps = max(20, args.decode_steps // 10)
+        cwall, cms, cpms = bench_channel_decay(csteps, args.warmup)
+        cb = decode_bytes(256) + 256 * H_V * D * 4 - 256 * H_V * 4   # g per channel
+        achieved = cb / (cms / 1e3) / 1e9
+        out["channel_decay"] = {
+            "workload": "per-channel decay form (one decay per value channel, correction from the "
+                        "state before the decay): decode step at 256 sequences x 1 token over the "
+                        "512 MiB pool; token-sequential prefill at B=1, T=4096, 32 V heads",
+            "decode": {"steps": csteps, "ms_per_step": cwall * 1e3 / csteps,
+                       "tokens_per_s": 256 * csteps / cwall,
+                       "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                                    "kernel": "seq_kernel<bf16, true>", "kernel_ms": cms,
+                                    "algorithmic_bytes": cb}},
+            "prefill_b1_t4096": {"ms_per_call": cpms, "tokens_per_s": 4096 / (cpms / 1e3),
+                                 "bound": "latency: one chain of 4096 dependent tokens per V head"}}
     if "frontend" in work:
         T4, N4, conv_ms, pre_ms = bench_frontend(10, 2)
         out["frontend_prefill"] = {

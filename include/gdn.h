@@ -140,6 +140,38 @@ gdn_status gdn_verify_step(const void* q, const void* k, const void* v, gdn_dtyp
                            int32_t d_k, int32_t d_v, float scale, void* o, void* stream);
 
 /*
+ * The per-channel form of the rule, as the code panel of section "01 . GatedDeltaNet(config)"
+ * of page "Qwen3-Next 80B-A3B -- The Evolving Transformer" writes it: one decay per value
+ * channel (row i of S), and the correction measured against the state before the decay:
+ *
+ *     S_t = diag(alpha_t) S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T,   o_t = scale * S_t q_t
+ *
+ * Each value row then has its own transition, so these run token by token (no chunked
+ * form); arithmetic in fp32, states in fp32.
+ *
+ * Prefill over a packed batch, arguments as for gdn_chunk_prefill except
+ *   g             [total_tokens][h_v][d_v] fp32: log alpha per token, V head and value channel
+ * and no workspace (none is used).
+ */
+gdn_status gdn_channel_decay_prefill(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
+                                     const float* g, const float* beta,
+                                     const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                                     int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, float scale,
+                                     const float* initial_state, float* final_state, void* o,
+                                     void* stream);
+
+/*
+ * The per-channel form at one token per sequence over a state pool, in place; arguments as
+ * for gdn_decode_step except
+ *   g             [num_seqs][h_v][d_v] fp32: log alpha per V head and value channel
+ */
+gdn_status gdn_channel_decay_decode_step(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
+                                         const float* g, const float* beta,
+                                         float* state_pool, const int32_t* state_slots,
+                                         int32_t num_seqs, int32_t h_qk, int32_t h_v, int32_t d_k,
+                                         int32_t d_v, float scale, void* o, void* stream);
+
+/*
  * Front end: short causal depthwise convolution, SiLU, L2 normalisation of every q and k
  * head, and a scale on q (section "01 . GatedDeltaNet(config)" of the Evolving Transformer
  * page names the short convolution for local context and the key normalisation).

@@ -20,7 +20,8 @@ GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN
 GDN_BF16, GDN_F32 = 0, 1
 
 EXPORTED = ("gdn_status_string", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill",
-            "gdn_decode_step", "gdn_verify_step", "gdn_conv_prep", "gdn_conv_decode_step",
+            "gdn_decode_step", "gdn_verify_step", "gdn_channel_decay_prefill",
+            "gdn_channel_decay_decode_step", "gdn_conv_prep", "gdn_conv_decode_step",
             "gdn_conv_window_from_prefill")
 
 _lib = None
@@ -57,6 +58,11 @@ def load(path: Optional[str] = None):
     lib.gdn_verify_step.restype = ctypes.c_int
     lib.gdn_verify_step.argtypes = [_P, _P, _P, ctypes.c_int, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                     _I, _I, ctypes.c_float, _P, _P]
+    lib.gdn_channel_decay_prefill.restype = ctypes.c_int
+    lib.gdn_channel_decay_prefill.argtypes = [_P, _P, _P, ctypes.c_int, _P, _P, _P, _I, _I, _I, _I,
+                                              _I, _I, ctypes.c_float, _P, _P, _P, _P]
+    lib.gdn_channel_decay_decode_step.restype = ctypes.c_int
+    lib.gdn_channel_decay_decode_step.argtypes = lib.gdn_decode_step.argtypes
     lib.gdn_conv_prep.restype = ctypes.c_int
     lib.gdn_conv_prep.argtypes = [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                                   _P, _P, _P, _P]
@@ -199,6 +205,58 @@ def gdn_verify_step(q, k, v, g, beta, state_pool, scale, state_slots=None, snaps
                                 _ptr(state_pool), _ptr(state_slots), _ptr(snapshots), N, n_tok,
                                 h_qk, h_v, d_k, d_v, float(scale), _ptr(o), _stream(stream))
     _check(st, "gdn_verify_step")
+    return o
+
+
+def gdn_channel_decay_prefill(q, k, v, g, beta, cu_seqlens, scale, initial_state=None,
+                              final_state=None, o=None, stream=None):
+    """The per-channel form over a packed batch; g [T][h_v][d_v]. Returns o."""
+    T, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    N = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((T, h_v, d_v), dtype=v.dtype, device=v.device)
+    _expect(k, (T, h_qk, d_k), q.dtype, "k")
+    _expect(v, (T, h_v, d_v), q.dtype, "v")
+    _expect(g, (T, h_v, d_v), torch.float32, "g")
+    _expect(beta, (T, h_v), torch.float32, "beta")
+    _expect(cu_seqlens, (N + 1,), torch.int32, "cu_seqlens")
+    _expect(o, (T, h_v, d_v), q.dtype, "o")
+    for name, st in (("initial_state", initial_state), ("final_state", final_state)):
+        if st is not None:
+            _expect(st, (N, h_v, d_v, d_k), torch.float32, name)
+    st = load().gdn_channel_decay_prefill(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g),
+                                          _ptr(beta), _ptr(cu_seqlens), N, T, h_qk, h_v, d_k, d_v,
+                                          float(scale), _ptr(initial_state), _ptr(final_state),
+                                          _ptr(o), _stream(stream))
+    _check(st, "gdn_channel_decay_prefill")
+    return o
+
+
+def gdn_channel_decay_decode_step(q, k, v, g, beta, state_pool, scale, state_slots=None, o=None,
+                                  stream=None):
+    """The per-channel form at one token per sequence; g [N][h_v][d_v]; state_pool is
+    updated in place. Returns o."""
+    N, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    if o is None:
+        o = torch.empty((N, h_v, d_v), dtype=v.dtype, device=v.device)
+    _expect(k, (N, h_qk, d_k), q.dtype, "k")
+    _expect(v, (N, h_v, d_v), q.dtype, "v")
+    _expect(g, (N, h_v, d_v), torch.float32, "g")
+    _expect(beta, (N, h_v), torch.float32, "beta")
+    _expect(state_pool, (state_pool.shape[0], h_v, d_v, d_k), torch.float32, "state_pool")
+    _expect(o, (N, h_v, d_v), q.dtype, "o")
+    if state_slots is None:
+        if state_pool.shape[0] < N:
+            raise ValueError("state_pool has fewer entries than sequences")
+    else:
+        _expect(state_slots, (N,), torch.int32, "state_slots")
+    st = load().gdn_channel_decay_decode_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g),
+                                              _ptr(beta), _ptr(state_pool), _ptr(state_slots), N,
+                                              h_qk, h_v, d_k, d_v, float(scale), _ptr(o),
+                                              _stream(stream))
+    _check(st, "gdn_channel_decay_decode_step")
     return o
 
 

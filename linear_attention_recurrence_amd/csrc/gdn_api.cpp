@@ -103,6 +103,41 @@ gdn_status gdn_verify_step(const void* q, const void* k, const void* v, gdn_dtyp
                                      scale, o, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_channel_decay_prefill(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
+                                     const float* g, const float* beta,
+                                     const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                                     int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, float scale,
+                                     const float* initial_state, float* final_state, void* o,
+                                     void* stream) {
+  if (num_seqs < 0 || total_tokens < 0) return GDN_ERR_SHAPE;
+  const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
+  if (!cu_seqlens) return GDN_ERR_NULL;
+  if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+  if (!final_state && total_tokens == 0) return GDN_OK;   // nothing observable to do
+  return from_hip(gdn::launch_channel_prefill(q, k, v, io_dtype == GDN_BF16, g, beta, cu_seqlens,
+                                              num_seqs, h_qk, h_v, scale, initial_state,
+                                              final_state, o, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_channel_decay_decode_step(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
+                                         const float* g, const float* beta,
+                                         float* state_pool, const int32_t* state_slots,
+                                         int32_t num_seqs, int32_t h_qk, int32_t h_v, int32_t d_k,
+                                         int32_t d_v, float scale, void* o, void* stream) {
+  if (num_seqs < 0) return GDN_ERR_SHAPE;
+  const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return GDN_OK;
+  if (!q || !k || !v || !g || !beta || !state_pool || !o) return GDN_ERR_NULL;
+  return from_hip(gdn::launch_channel_decode(q, k, v, io_dtype == GDN_BF16, g, beta, state_pool,
+                                             state_slots, num_seqs, h_qk, h_v, scale, o,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 gdn_status gdn_conv_prep(const void* mixed_qkv, const float* conv_weight, int32_t conv_kernel,
                          const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
                          int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, float q_scale,

@@ -19,6 +19,18 @@ hipError_t launch_verify(const void* q, const void* k, const void* v, bool io_bf
                          int num_seqs, int num_tokens, int h_qk, int h_v, float scale, void* o,
                          hipStream_t stream);
 
+// The per-channel form (one decay per value row, the correction from the state before the
+// decay): token-sequential prefill over a packed batch, and one decode step over a pool
+// (recurrent.hip).
+hipError_t launch_channel_prefill(const void* q, const void* k, const void* v, bool io_bf16,
+                                  const float* g, const float* beta, const int32_t* cu_seqlens,
+                                  int num_seqs, int h_qk, int h_v, float scale, const float* s0,
+                                  float* s_final, void* o, hipStream_t stream);
+hipError_t launch_channel_decode(const void* q, const void* k, const void* v, bool io_bf16,
+                                 const float* g, const float* beta, float* pool, const int32_t* slots,
+                                 int num_seqs, int h_qk, int h_v, float scale, void* o,
+                                 hipStream_t stream);
+
 // Token-sequential prefill with the state on chip (recurrent.hip); used for fp32 I/O.
 hipError_t launch_recurrent_prefill(const void* q, const void* k, const void* v, bool io_bf16,
                                     const float* g, const float* beta, const int32_t* cu_seqlens,

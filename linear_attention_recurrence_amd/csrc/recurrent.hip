@@ -19,9 +19,12 @@
 //    per head, 8 rows each: the layout that streams fastest on this chip.
 //  * recurrent_kernel: fp32 prefill, all tokens of a sequence with the state held on chip
 //    between tokens (256 threads, 16 rows each).
-// and verify_kernel, the decode step over several tokens per sequence (draft tokens to be
-// checked at once): decode_kernel's layout and per-token arithmetic (decode_token), the
-// state kept in registers between the tokens and, when asked, written out after each one.
+// and seq_kernel, decode_kernel's layout over several tokens per (sequence, V head) with the
+// state kept in registers between them: the verify step (draft tokens checked at once, with
+// decode_token's arithmetic, the state optionally written out after each token), and the
+// per-channel form of the code panel of section "01 . GatedDeltaNet(config)" on the
+// Evolving Transformer page (one decay per value row, the correction from the state before
+// the decay) for prefill and decode.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -153,12 +156,47 @@ __global__ __launch_bounds__(512) void decode_kernel(RecArgs a) {
     __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(sp + (size_t)i * 16 * kHeadDim));
 }
 
-// Several decode steps per sequence in one launch: tokens t = 0 .. n_tok - 1 of sequence n
-// are rows n * n_tok + t of q, k, v, g, beta and o. The state is read from the pool once,
-// kept in registers across the tokens (written to snap[n][t] after token t when snap is
-// set) and written back to the pool after the last token.
-template <typename IO>
-__global__ __launch_bounds__(512) void verify_kernel(RecArgs a) {
+// The per-channel form at one token, decode layout: each value row i has its own decay
+// alpha_i and the correction comes from the state before the decay,
+// c_i = beta (v_i - u_i), S_i <- alpha_i S_i + c_i k^T. arow[i] is the decay of row
+// row_base + 16 i, a_mine that of this lane's output row. Returns
+// scale (a_mine r + c (k . q)), the output on lanes with (c4 & 3) == 2.
+__device__ __forceinline__ float decode_token_channel(f32x4 (&S)[8], f32x4 k4, f32x4 q4, const float (&arow)[8],
+                                                      float a_mine, float beta, float vrow, float scale, int c4) {
+  const bool my_is_r = (c4 & 2) != 0;
+  float vals[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    vals[2 * i] = S[i][0] * k4[0] + S[i][1] * k4[1] + S[i][2] * k4[2] + S[i][3] * k4[3];
+    vals[2 * i + 1] = S[i][0] * q4[0] + S[i][1] * q4[1] + S[i][2] * q4[2] + S[i][3] * q4[3];
+  }
+  const float mine = reduce_scatter16(vals, c4);
+  const float other = __shfl_xor(mine, 2, 32);
+  const float u = my_is_r ? other : mine;
+  const float r = my_is_r ? mine : other;
+  const float kq = half_wave_sum(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
+  const float c = beta * (vrow - u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float ci = __shfl(c, 4 * i, 32);
+    S[i][0] = arow[i] * S[i][0] + ci * k4[0];
+    S[i][1] = arow[i] * S[i][1] + ci * k4[1];
+    S[i][2] = arow[i] * S[i][2] + ci * k4[2];
+    S[i][3] = arow[i] * S[i][3] + ci * k4[3];
+  }
+  return scale * (a_mine * r + c * kq);
+}
+
+// Several tokens per (sequence, V head) with the state in registers, decode layout.
+//  * verify (cu_seqlens NULL): tokens t = 0 .. n_tok - 1 of sequence n are rows
+//    n * n_tok + t of the inputs; the state comes from the pool and goes back to it, and
+//    the state after each token goes to snap[n][t] when snap is set.
+//  * prefill (cu_seqlens set): the tokens of sequence n are rows cu[n] .. cu[n+1] - 1; the
+//    state comes from s_in[n] (zero when NULL) and goes to s_out[n] (when set).
+// CH selects the per-channel form (g holds one log-decay per value row: [row][h_v][128]);
+// otherwise decode_token, the main form with one decay per V head.
+template <typename IO, bool CH>
+__global__ __launch_bounds__(512) void seq_kernel(RecArgs a) {
   constexpr int kRows = 8;
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -172,16 +210,24 @@ __global__ __launch_bounds__(512) void verify_kernel(RecArgs a) {
   const IO* k = static_cast<const IO*>(a.k);
   const IO* v = static_cast<const IO*>(a.v);
   IO* o = static_cast<IO*>(a.o);
-  const int slot = a.slots ? a.slots[n] : n;
+  const bool pooled = a.cu_seqlens == nullptr;
+  const int row0 = pooled ? n * a.n_tok : a.cu_seqlens[n];
+  const int n_tok = pooled ? a.n_tok : a.cu_seqlens[n + 1] - row0;
+  const int slot = pooled ? (a.slots ? a.slots[n] : n) : n;
   const size_t state = ((size_t)slot * a.h_v + h) * kHeadDim * kHeadDim;
   const int row_base = w * 2 + half;        // rows row_base + 16*i
   const size_t lane_off = (size_t)row_base * kHeadDim + 4 * c4;
 
-  float* sp = a.s_out + state + lane_off;
   f32x4 S[kRows];
+  if (a.s_in) {
+    const float* src = a.s_in + state + lane_off;
 #pragma unroll
-  for (int i = 0; i < kRows; ++i)
-    S[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)i * 16 * kHeadDim));
+    for (int i = 0; i < kRows; ++i)
+      S[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (size_t)i * 16 * kHeadDim));
+  } else {
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const int my_row = row_base + 16 * (c4 >> 2);
 
   // token t's inputs are requested during token t - 1 (before its stores, so waiting for
@@ -189,23 +235,38 @@ __global__ __launch_bounds__(512) void verify_kernel(RecArgs a) {
   struct Tok {
     f32x4 k4, q4;
     float g, beta, vrow;
+    float grow[CH ? kRows : 1];   // per-channel form: the log-decays of this thread's rows
   };
   auto fetch = [&](int t) {
-    const size_t tok = (size_t)n * a.n_tok + t;
+    const size_t tok = (size_t)row0 + t;
     const size_t qk_off = (tok * a.h_qk + j) * kHeadDim + 4 * c4;
     Tok x;
     x.k4 = load4(k + qk_off);
     x.q4 = load4(q + qk_off);
-    x.g = a.g[tok * a.h_v + h];
     x.beta = a.beta[tok * a.h_v + h];
     x.vrow = load1(v + (tok * a.h_v + h) * kHeadDim + my_row);
+    if constexpr (CH) {
+      const float* gh = a.g + (tok * a.h_v + h) * kHeadDim;
+      x.g = gh[my_row];
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) x.grow[i] = gh[row_base + 16 * i];
+    } else {
+      x.g = a.g[tok * a.h_v + h];
+    }
     return x;
   };
   // one token: the read-out and update, the output, and the snapshot when asked
   auto step = [&](Tok& x, int t) {
-    const size_t tok = (size_t)n * a.n_tok + t;
-    const float alpha = __expf(x.g);
-    const float out = decode_token(S, x.k4, x.q4, alpha, x.beta, x.vrow, a.scale, c4);
+    const size_t tok = (size_t)row0 + t;
+    float out;
+    if constexpr (CH) {
+      float arow[kRows];
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) arow[i] = __expf(x.grow[i]);
+      out = decode_token_channel(S, x.k4, x.q4, arow, __expf(x.g), x.beta, x.vrow, a.scale, c4);
+    } else {
+      out = decode_token(S, x.k4, x.q4, __expf(x.g), x.beta, x.vrow, a.scale, c4);
+    }
     if ((c4 & 3) == 2) store1(o + (tok * a.h_v + h) * kHeadDim + my_row, out);
     if (a.snap) {
       float* dst = a.snap + (tok * a.h_v + h) * kHeadDim * kHeadDim + lane_off;
@@ -216,22 +277,27 @@ __global__ __launch_bounds__(512) void verify_kernel(RecArgs a) {
   };
   // Two alternating input sets (no copy from one to the other, so a load never has to wait
   // for the register it overwrites); past the last token the loads repeat it, unused.
-  Tok ta = fetch(0), tb;
-  for (int t = 0; t < a.n_tok; t += 2) {
-    tb = fetch(min(t + 1, a.n_tok - 1));
-    // the next token's loads are issued here: this token's k and q pass through the asm, so
-    // no product that uses them moves above it
-    asm volatile("" : "+v"(ta.k4), "+v"(ta.q4) :: "memory");
-    step(ta, t);
-    if (t + 1 < a.n_tok) {
-      ta = fetch(min(t + 2, a.n_tok - 1));
-      asm volatile("" : "+v"(tb.k4), "+v"(tb.q4) :: "memory");
-      step(tb, t + 1);
+  if (n_tok > 0) {
+    Tok ta = fetch(0), tb;
+    for (int t = 0; t < n_tok; t += 2) {
+      tb = fetch(min(t + 1, n_tok - 1));
+      // the next token's loads are issued here: this token's k and q pass through the asm,
+      // so no product that uses them moves above it
+      asm volatile("" : "+v"(ta.k4), "+v"(ta.q4) :: "memory");
+      step(ta, t);
+      if (t + 1 < n_tok) {
+        ta = fetch(min(t + 2, n_tok - 1));
+        asm volatile("" : "+v"(tb.k4), "+v"(tb.q4) :: "memory");
+        step(tb, t + 1);
+      }
     }
   }
+  if (a.s_out) {
+    float* dst = a.s_out + state + lane_off;
 #pragma unroll
-  for (int i = 0; i < kRows; ++i)
-    __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(sp + (size_t)i * 16 * kHeadDim));
+    for (int i = 0; i < kRows; ++i)
+      __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(dst + (size_t)i * 16 * kHeadDim));
+  }
 }
 
 template <typename IO>
@@ -346,9 +412,35 @@ hipError_t launch_verify(const void* q, const void* k, const void* v, bool io_bf
   RecArgs a{num_tokens, snapshots, q, k, v, g, beta, nullptr, slots, pool, pool, o, num_seqs, h_qk, h_v, scale};
   const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(512);
   if (io_bf16)
-    hipLaunchKernelGGL((verify_kernel<bf16>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((seq_kernel<bf16, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((verify_kernel<float>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((seq_kernel<float, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_channel_prefill(const void* q, const void* k, const void* v, bool io_bf16,
+                                  const float* g, const float* beta, const int32_t* cu_seqlens,
+                                  int num_seqs, int h_qk, int h_v, float scale, const float* s0,
+                                  float* s_final, void* o, hipStream_t stream) {
+  RecArgs a{0, nullptr, q, k, v, g, beta, cu_seqlens, nullptr, s0, s_final, o, num_seqs, h_qk, h_v, scale};
+  const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(512);
+  if (io_bf16)
+    hipLaunchKernelGGL((seq_kernel<bf16, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((seq_kernel<float, true>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_channel_decode(const void* q, const void* k, const void* v, bool io_bf16,
+                                 const float* g, const float* beta, float* pool, const int32_t* slots,
+                                 int num_seqs, int h_qk, int h_v, float scale, void* o,
+                                 hipStream_t stream) {
+  RecArgs a{1, nullptr, q, k, v, g, beta, nullptr, slots, pool, pool, o, num_seqs, h_qk, h_v, scale};
+  const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(512);
+  if (io_bf16)
+    hipLaunchKernelGGL((seq_kernel<bf16, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((seq_kernel<float, true>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -26,6 +26,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(["gdn_status_string", "gdn_chunk_prefill_workspace_bytes",
                                             "gdn_chunk_prefill", "gdn_decode_step", "gdn_verify_step",
+                                            "gdn_channel_decay_prefill",
+                                            "gdn_channel_decay_decode_step",
                                             "gdn_conv_prep", "gdn_conv_decode_step",
                                             "gdn_conv_window_from_prefill"])
 
@@ -163,6 +165,33 @@ def test_verify_validation():
     assert call(dt=7) == L.GDN_ERR_UNSUPPORTED
     assert call(nt=0) == L.GDN_OK
     assert call(n=0) == L.GDN_OK
+
+
+def test_channel_decay_validation():
+    lib, L = _lib()
+    P = _fake
+    f = lib.gdn_channel_decay_prefill
+    ok = dict(q=P(1), k=P(2), v=P(3), dt=0, g=P(4), b=P(5), cu=P(6), n=2, T=10, hqk=16, hv=32,
+              dk=128, dv=128, sc=0.1, s0=None, sf=None, o=P(7), st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["dt"], a["g"], a["b"], a["cu"], a["n"], a["T"],
+                 a["hqk"], a["hv"], a["dk"], a["dv"], a["sc"], a["s0"], a["sf"], a["o"], a["st"])
+
+    assert call(g=None) == L.GDN_ERR_NULL
+    assert call(cu=None) == L.GDN_ERR_NULL
+    assert call(T=-1) == L.GDN_ERR_SHAPE
+    assert call(n=0) == L.GDN_ERR_SHAPE
+    assert call(dt=3) == L.GDN_ERR_UNSUPPORTED
+    assert call(dv=64) == L.GDN_ERR_UNSUPPORTED
+    assert call(T=0) == L.GDN_OK
+    d = lib.gdn_channel_decay_decode_step
+    assert d(P(1), P(2), P(3), 0, None, P(5), P(6), None, 2, 16, 32, 128, 128, 0.1, P(7), None) == L.GDN_ERR_NULL
+    assert d(P(1), P(2), P(3), 0, P(4), P(5), None, None, 2, 16, 32, 128, 128, 0.1, P(7), None) == L.GDN_ERR_NULL
+    assert d(P(1), P(2), P(3), 0, P(4), P(5), P(6), None, -1, 16, 32, 128, 128, 0.1, P(7), None) == L.GDN_ERR_SHAPE
+    assert d(P(1), P(2), P(3), 0, P(4), P(5), P(6), None, 0, 16, 32, 128, 128, 0.1, P(7), None) == L.GDN_OK
 
 
 def test_conv_decode_validation():

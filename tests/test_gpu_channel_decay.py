@@ -1,0 +1,88 @@
+"""The per-channel form (one decay per value channel, correction from the state before the
+decay): gdn_channel_decay_prefill and gdn_channel_decay_decode_step against the fp64 oracle,
+and decode steps against prefill (GPU)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests._util import check_outputs, check_state, prefill_to_dev, to_dev, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(x, g, heads=None):
+    ref_o, ref_s, _ = oracle.recurrence_channel(x.as_f64("q"), x.as_f64("k"), x.as_f64("v"),
+                                                g.astype(np.float64), x.as_f64("beta"),
+                                                x.cu_seqlens, x.scale,
+                                                initial_state=x.as_f64("initial_state")
+                                                if x.initial_state is not None else None)
+    return ref_o, ref_s
+
+
+def _run_prefill(x, g):
+    import torch
+    import linear_attention_recurrence_amd as gdn
+    d = prefill_to_dev(x)
+    N = x.num_seqs
+    fin = torch.full((N, x.h_v, 128, 128), float("nan"), dtype=torch.float32, device="cuda")
+    o = gdn.gdn_channel_decay_prefill(d["q"], d["k"], d["v"], to_dev(g), d["beta"], d["cu"], x.scale,
+                                      initial_state=d["s0"], final_state=fin)
+    torch.cuda.synchronize()
+    return to_host_f64(o), to_host_f64(fin)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_channel_prefill_varlen(io):
+    """Lengths 0, 1, 17, 64 and 150 (a zero-length sequence keeps its initial state)."""
+    x = workloads.make_prefill([0, 1, 17, 64, 150], h_qk=2, h_v=4, io_dtype=io,
+                               with_initial_state=True, seed=150)
+    g = workloads.channel_log_alpha(x.total_tokens, 4, 128, seed=151)
+    o, fin = _run_prefill(x, g)
+    ref_o, ref_s = _oracle(x, g)
+    res_o = check_outputs(o, ref_o, "channel prefill %s" % io)
+    res_s = check_state(fin, ref_s, "channel prefill %s" % io)
+    if io == "f32":
+        assert res_o[1] < 1e-5 and res_s < 1e-5
+    np.testing.assert_array_equal(fin[0], x.initial_state[0].astype(np.float64))
+
+
+def test_channel_prefill_model_size():
+    """B = 1, T = 1024, 16 QK / 32 V heads, bf16, S0 ~ N(0, 0.02): every head against the oracle."""
+    x = workloads.make_prefill([1024], with_initial_state=True, seed=152)
+    g = workloads.channel_log_alpha(1024, seed=153)
+    o, fin = _run_prefill(x, g)
+    ref_o, ref_s = _oracle(x, g)
+    check_outputs(o, ref_o, "channel prefill T=1024")
+    check_state(fin, ref_s, "channel prefill T=1024")
+
+
+def test_channel_decode_equals_prefill():
+    """Token-by-token decode over a permuted pool equals, bit for bit, the prefill of the same
+    tokens (both run the same per-token arithmetic), and both match the oracle."""
+    import torch
+    import linear_attention_recurrence_amd as gdn
+    T, N = 12, 3
+    x = workloads.make_prefill([T] * N, h_qk=1, h_v=2, with_initial_state=True, seed=154)
+    g = workloads.channel_log_alpha(T * N, 2, 128, seed=155)
+    o_p, fin_p = _run_prefill(x, g)
+    d = prefill_to_dev(x)
+    slots = torch.tensor([4, 0, 2], dtype=torch.int32, device="cuda")
+    pool = torch.zeros((5, 2, 128, 128), dtype=torch.float32, device="cuda")
+    pool[slots.long()] = d["s0"]
+    gd = to_dev(g)
+    rows = lambda t: torch.arange(N, device="cuda") * T + t
+    outs = []
+    for t in range(T):
+        r = rows(t)
+        outs.append(gdn.gdn_channel_decay_decode_step(
+            d["q"][r].contiguous(), d["k"][r].contiguous(), d["v"][r].contiguous(), gd[r].contiguous(),
+            d["beta"][r].contiguous(), pool, x.scale, state_slots=slots))
+    torch.cuda.synchronize()
+    o_d = np.stack([to_host_f64(o_) for o_ in outs], axis=1).reshape(N * T, 2, 128)
+    np.testing.assert_array_equal(o_d, o_p)
+    np.testing.assert_array_equal(to_host_f64(pool[slots.long()]), fin_p)
+    ref_o, ref_s = _oracle(x, g)
+    check_outputs(o_d, ref_o, "channel decode")
+    check_state(fin_p, ref_s, "channel decode")

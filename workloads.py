@@ -174,6 +174,13 @@ def make_prefill(seq_lens, h_qk=H_QK, h_v=H_V, d_k=D_HEAD, d_v=D_HEAD, io_dtype=
                          scale=float(SCALE if scale is None else scale), io_dtype=io_dtype)
 
 
+def channel_log_alpha(rows: int, h_v=H_V, d_v=D_HEAD, seed=1007) -> np.ndarray:
+    """Per-channel log-decays [rows][h_v][d_v] (float32) for the per-channel form, with the
+    distribution of the per-head ones."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _log_alpha(rng, (rows, h_v, d_v))
+
+
 def config0(seed=1000) -> PrefillInputs:
     """B=1, T=256, one QK head and one V head, d=128, fp32 everywhere, S0 = 0."""
     return make_prefill([256], h_qk=1, h_v=1, io_dtype="f32", seed=seed)
