@@ -487,7 +487,7 @@ def main():
                 "ms_per_call": vms, "tokens_per_s": 256 * 4 * vsteps / vwall,
                 "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                             "kernel": "verify_kernel<bf16>", "algorithmic_bytes": vb}}
+                             "kernel": "seq_kernel<bf16, false>", "algorithmic_bytes": vb}}
     if "decode" in work:
         csteps = max(20, args.decode_steps // 10)
         cwall, cms, cpms = bench_channel_decay(csteps, args.warmup)
@@ -501,7 +501,7 @@ def main():
                        "tokens_per_s": 256 * csteps / cwall,
                        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                                    "kernel": "seq_kernel<bf16, true>", "kernel_ms": cms,
+                                    "kernel": "decode_kernel<bf16, true>", "kernel_ms": cms,
                                     "algorithmic_bytes": cb}},
             "prefill_b1_t4096": {"ms_per_call": cpms, "tokens_per_s": 4096 / (cpms / 1e3),
                                  "bound": "latency: one chain of 4096 dependent tokens per V head"}}

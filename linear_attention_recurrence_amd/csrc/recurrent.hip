@@ -50,36 +50,77 @@ struct RecArgs {
   float scale;
 };
 
+// Lane exchanges within a half-wave without the LDS crossbar where the pattern stays inside
+// a 16-lane row: the value of lane l ^ m, by DPP for m = 1 and 2 (quad permutes), 4 (half-row
+// mirror, then quad reversal: l ^ 7 ^ 3), 8 (row rotation by 8), and by ds_swizzle (xor mask
+// within 32 lanes) for m = 16. Pure data movement: sums built from it are unchanged.
+__device__ __forceinline__ float xor_lane(float x, int m) {
+  const int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (m) {
+    case 1: r = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false),
+                                            0x1B, 0xF, 0xF, false); break;
+    case 8: r = __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_ds_swizzle(v, 0x401F); break;   // m = 16
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+// Value of lane `src` (a constant below 32) of this lane's half-wave: two lane reads into
+// scalars and a select, instead of a crossbar permute.
+__device__ __forceinline__ float half_lane(float x, int src, bool upper) {
+  const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
+  const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src + 32));
+  return upper ? hi : lo;
+}
+
+// Sum over the 32 lanes of each half-wave; every lane receives its half's total.
+__device__ __forceinline__ float half_sum(float x) {
+  x += xor_lane(x, 16);
+  x += xor_lane(x, 8);
+  x += xor_lane(x, 4);
+  x += xor_lane(x, 2);
+  x += xor_lane(x, 1);
+  return x;
+}
+
+// One level of a half-wave reduce-scatter over n partial sums: lanes with bit m set keep
+// the upper half of the indices and send the lower half to their partner l ^ m, the others
+// the reverse, so each half of the lanes ends with n/2 partial sums of twice as many lanes.
+// Sizes are template constants so every index is static (a runtime index would turn the
+// array into select chains).
+template <int M, int N, int L>
+__device__ __forceinline__ void rs_level(float (&vals)[L], int lane32) {
+  const bool upper = (lane32 & M) != 0;
+#pragma unroll
+  for (int idx = 0; idx < N / 2; ++idx) {
+    const float send = upper ? vals[idx] : vals[idx + N / 2];
+    const float keep = upper ? vals[idx + N / 2] : vals[idx];
+    vals[idx] = keep + xor_lane(send, M);
+  }
+}
+
 // Reduce-scatter of 32 partial sums over the 32 lanes of a half-wave: afterwards
 // vals[0] of lane c holds the half-wave total of index c. 31 exchanges instead of 160.
 __device__ __forceinline__ float reduce_scatter32(float (&vals)[32], int lane32) {
-#pragma unroll
-  for (int m = 16, n = 32; m >= 1; m >>= 1, n >>= 1) {
-    const bool upper = (lane32 & m) != 0;
-#pragma unroll
-    for (int idx = 0; idx < n / 2; ++idx) {
-      const float send = upper ? vals[idx] : vals[idx + n / 2];
-      const float keep = upper ? vals[idx + n / 2] : vals[idx];
-      vals[idx] = keep + __shfl_xor(send, m, 32);
-    }
-  }
+  rs_level<16, 32>(vals, lane32);
+  rs_level<8, 16>(vals, lane32);
+  rs_level<4, 8>(vals, lane32);
+  rs_level<2, 4>(vals, lane32);
+  rs_level<1, 2>(vals, lane32);
   return vals[0];
 }
 
 // Reduce-scatter of 16 partial sums over the 32 lanes of a half-wave: afterwards lanes
 // 2c and 2c + 1 both hold the half-wave total of index c.
 __device__ __forceinline__ float reduce_scatter16(float (&vals)[16], int lane32) {
-#pragma unroll
-  for (int m = 16, n = 16; m >= 2; m >>= 1, n >>= 1) {
-    const bool upper = (lane32 & m) != 0;
-#pragma unroll
-    for (int idx = 0; idx < n / 2; ++idx) {
-      const float send = upper ? vals[idx] : vals[idx + n / 2];
-      const float keep = upper ? vals[idx + n / 2] : vals[idx];
-      vals[idx] = keep + __shfl_xor(send, m, 32);
-    }
-  }
-  return vals[0] + __shfl_xor(vals[0], 1, 32);
+  rs_level<16, 16>(vals, lane32);
+  rs_level<8, 8>(vals, lane32);
+  rs_level<4, 4>(vals, lane32);
+  rs_level<2, 2>(vals, lane32);
+  return vals[0] + xor_lane(vals[0], 1);
 }
 
 // One token of the decode layout (8 rows per thread, rows row_base + 16 i): u = S k and r = S q
@@ -88,6 +129,7 @@ __device__ __forceinline__ float reduce_scatter16(float (&vals)[16], int lane32)
 __device__ __forceinline__ float decode_token(f32x4 (&S)[8], f32x4 k4, f32x4 q4, float alpha, float beta,
                                               float vrow, float scale, int c4) {
   const bool my_is_r = (c4 & 2) != 0;
+  const bool upper = (__lane_id() & 32) != 0;   // which half-wave (rows of this lane)
   float vals[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -95,14 +137,14 @@ __device__ __forceinline__ float decode_token(f32x4 (&S)[8], f32x4 k4, f32x4 q4,
     vals[2 * i + 1] = S[i][0] * q4[0] + S[i][1] * q4[1] + S[i][2] * q4[2] + S[i][3] * q4[3];
   }
   const float mine = reduce_scatter16(vals, c4);
-  const float other = __shfl_xor(mine, 2, 32);
+  const float other = xor_lane(mine, 2);
   const float u = my_is_r ? other : mine;
   const float r = my_is_r ? mine : other;
-  const float kq = half_wave_sum(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
+  const float kq = half_sum(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
   const float c = beta * (vrow - alpha * u);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float ci = __shfl(c, 4 * i, 32);
+    const float ci = half_lane(c, 4 * i, upper);
     S[i][0] = alpha * S[i][0] + ci * k4[0];
     S[i][1] = alpha * S[i][1] + ci * k4[1];
     S[i][2] = alpha * S[i][2] + ci * k4[2];
@@ -111,10 +153,43 @@ __device__ __forceinline__ float decode_token(f32x4 (&S)[8], f32x4 k4, f32x4 q4,
   return scale * (alpha * r + c * kq);
 }
 
+// The per-channel form at one token, decode layout: each value row i has its own decay
+// alpha_i and the correction comes from the state before the decay,
+// c_i = beta (v_i - u_i), S_i <- alpha_i S_i + c_i k^T. arow[i] is the decay of row
+// row_base + 16 i, a_mine that of this lane's output row. Returns
+// scale (a_mine r + c (k . q)), the output on lanes with (c4 & 3) == 2.
+__device__ __forceinline__ float decode_token_channel(f32x4 (&S)[8], f32x4 k4, f32x4 q4, const float (&arow)[8],
+                                                      float a_mine, float beta, float vrow, float scale, int c4) {
+  const bool my_is_r = (c4 & 2) != 0;
+  const bool upper = (__lane_id() & 32) != 0;   // which half-wave (rows of this lane)
+  float vals[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    vals[2 * i] = S[i][0] * k4[0] + S[i][1] * k4[1] + S[i][2] * k4[2] + S[i][3] * k4[3];
+    vals[2 * i + 1] = S[i][0] * q4[0] + S[i][1] * q4[1] + S[i][2] * q4[2] + S[i][3] * q4[3];
+  }
+  const float mine = reduce_scatter16(vals, c4);
+  const float other = xor_lane(mine, 2);
+  const float u = my_is_r ? other : mine;
+  const float r = my_is_r ? mine : other;
+  const float kq = half_sum(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
+  const float c = beta * (vrow - u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float ci = half_lane(c, 4 * i, upper);
+    S[i][0] = arow[i] * S[i][0] + ci * k4[0];
+    S[i][1] = arow[i] * S[i][1] + ci * k4[1];
+    S[i][2] = arow[i] * S[i][2] + ci * k4[2];
+    S[i][3] = arow[i] * S[i][3] + ci * k4[3];
+  }
+  return scale * (a_mine * r + c * kq);
+}
+
 // One decode step. Thread (wave w of 8, lane l) holds columns 4*(l%32) .. +3 of the 8 rows
 // i*16 + 2*w + l/32, i = 0..7: each load or store instruction of a wave covers two whole
-// rows (1 KB). Same arithmetic as recurrent_kernel for one token.
-template <typename IO>
+// rows (1 KB). Same arithmetic as recurrent_kernel for one token. CH selects the
+// per-channel form (g [seq][h_v][128], one log-decay per value row, decode_token_channel).
+template <typename IO, bool CH>
 __global__ __launch_bounds__(512) void decode_kernel(RecArgs a) {
   constexpr int kRows = 8;
   const int tid = threadIdx.x;
@@ -145,46 +220,23 @@ __global__ __launch_bounds__(512) void decode_kernel(RecArgs a) {
   const size_t qk_off = ((size_t)n * a.h_qk + j) * kHeadDim + 4 * c4;
   const f32x4 k4 = load4(k + qk_off);
   const f32x4 q4 = load4(q + qk_off);
-  const float alpha = __expf(a.g[(size_t)n * a.h_v + h]);
   const float beta = a.beta[(size_t)n * a.h_v + h];
   const float vrow = load1(v + ((size_t)n * a.h_v + h) * kHeadDim + my_row);
 
-  const float out = decode_token(S, k4, q4, alpha, beta, vrow, a.scale, c4);
+  float out;
+  if constexpr (CH) {
+    const float* gh = a.g + ((size_t)n * a.h_v + h) * kHeadDim;
+    float arow[kRows];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) arow[i] = __expf(gh[row_base + 16 * i]);
+    out = decode_token_channel(S, k4, q4, arow, __expf(gh[my_row]), beta, vrow, a.scale, c4);
+  } else {
+    out = decode_token(S, k4, q4, __expf(a.g[(size_t)n * a.h_v + h]), beta, vrow, a.scale, c4);
+  }
   if ((c4 & 3) == 2) store1(o + ((size_t)n * a.h_v + h) * kHeadDim + my_row, out);
 #pragma unroll
   for (int i = 0; i < kRows; ++i)
     __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(sp + (size_t)i * 16 * kHeadDim));
-}
-
-// The per-channel form at one token, decode layout: each value row i has its own decay
-// alpha_i and the correction comes from the state before the decay,
-// c_i = beta (v_i - u_i), S_i <- alpha_i S_i + c_i k^T. arow[i] is the decay of row
-// row_base + 16 i, a_mine that of this lane's output row. Returns
-// scale (a_mine r + c (k . q)), the output on lanes with (c4 & 3) == 2.
-__device__ __forceinline__ float decode_token_channel(f32x4 (&S)[8], f32x4 k4, f32x4 q4, const float (&arow)[8],
-                                                      float a_mine, float beta, float vrow, float scale, int c4) {
-  const bool my_is_r = (c4 & 2) != 0;
-  float vals[16];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    vals[2 * i] = S[i][0] * k4[0] + S[i][1] * k4[1] + S[i][2] * k4[2] + S[i][3] * k4[3];
-    vals[2 * i + 1] = S[i][0] * q4[0] + S[i][1] * q4[1] + S[i][2] * q4[2] + S[i][3] * q4[3];
-  }
-  const float mine = reduce_scatter16(vals, c4);
-  const float other = __shfl_xor(mine, 2, 32);
-  const float u = my_is_r ? other : mine;
-  const float r = my_is_r ? mine : other;
-  const float kq = half_wave_sum(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
-  const float c = beta * (vrow - u);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float ci = __shfl(c, 4 * i, 32);
-    S[i][0] = arow[i] * S[i][0] + ci * k4[0];
-    S[i][1] = arow[i] * S[i][1] + ci * k4[1];
-    S[i][2] = arow[i] * S[i][2] + ci * k4[2];
-    S[i][3] = arow[i] * S[i][3] + ci * k4[3];
-  }
-  return scale * (a_mine * r + c * kq);
 }
 
 // Several tokens per (sequence, V head) with the state in registers, decode layout.
@@ -306,6 +358,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecArgs a) {
   const int w = tid >> 6;
   const int lane = tid & 63;
   const int half = lane >> 5;
+  const bool upper = half != 0;
   const int c4 = lane & 31;                 // this thread's 4 columns: 4*c4 .. 4*c4+3
   const int n = blockIdx.x / a.h_v;
   const int h = blockIdx.x % a.h_v;
@@ -352,16 +405,16 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecArgs a) {
       vals[2 * i + 1] = S[i][0] * q4[0] + S[i][1] * q4[1] + S[i][2] * q4[2] + S[i][3] * q4[3];
     }
     const float mine = reduce_scatter32(vals, c4);
-    const float other = __shfl_xor(mine, 1, 32);
+    const float other = xor_lane(mine, 1);
     const float u = my_is_r ? other : mine;
     const float r = my_is_r ? mine : other;
-    const float kq = half_wave_sum(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
+    const float kq = half_sum(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
     const float c = beta * (vrow - alpha * u);
     if (my_is_r) store1(o + ((size_t)t * a.h_v + h) * kHeadDim + my_row, a.scale * (alpha * r + c * kq));
 
 #pragma unroll
     for (int i = 0; i < kRowsPerThread; ++i) {
-      const float ci = __shfl(c, 2 * i, 32);
+      const float ci = half_lane(c, 2 * i, upper);
       S[i][0] = alpha * S[i][0] + ci * k4[0];
       S[i][1] = alpha * S[i][1] + ci * k4[1];
       S[i][2] = alpha * S[i][2] + ci * k4[2];
@@ -386,9 +439,9 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool io_bf
   RecArgs a{1, nullptr, q, k, v, g, beta, nullptr, slots, pool, pool, o, num_seqs, h_qk, h_v, scale};
   const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(512);
   if (io_bf16)
-    hipLaunchKernelGGL((decode_kernel<bf16>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<bf16, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<float>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<float, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -438,9 +491,9 @@ hipError_t launch_channel_decode(const void* q, const void* k, const void* v, bo
   RecArgs a{1, nullptr, q, k, v, g, beta, nullptr, slots, pool, pool, o, num_seqs, h_qk, h_v, scale};
   const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(512);
   if (io_bf16)
-    hipLaunchKernelGGL((seq_kernel<bf16, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<bf16, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((seq_kernel<float, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<float, true>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
