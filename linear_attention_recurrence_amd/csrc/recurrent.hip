@@ -13,25 +13,24 @@
 //   S <- alpha * S + c k^T
 //   o = scale * S q = scale * (alpha * r + c * (k . q))
 //
-// Two kernels:
+// Three kernels:
 //  * decode_kernel: one token per sequence, the state streamed from and back to an fp32
 //    pool in HBM (64 KB read + 64 KB written per head; bound by HBM bandwidth). 512 threads
 //    per head, 8 rows each: the layout that streams fastest on this chip.
-//  * recurrent_kernel: fp32 prefill, all tokens of a sequence with the state held on chip
-//    between tokens (256 threads, 16 rows each).
-// and seq_kernel, decode_kernel's layout over several tokens per (sequence, V head) with the
-// state kept in registers between them: the verify step (draft tokens checked at once, with
-// decode_token's arithmetic, the state optionally written out after each token), and the
-// per-channel form of the code panel of section "01 . GatedDeltaNet(config)" on the
-// Evolving Transformer page (one decay per value row, the correction from the state before
-// the decay) for prefill and decode.
+//  * seq_kernel: decode_kernel's layout and arithmetic (decode_token) over several tokens per
+//    sequence with the state in registers between them: the verify step (draft tokens
+//    checked at once, the state optionally written out after each token).
+//  * rows_kernel: token-sequential prefill, 16 value rows per one-wave workgroup: the fp32
+//    I/O prefill and the per-channel form.
+// The per-channel form is the code panel of section "01 . GatedDeltaNet(config)" on the
+// Evolving Transformer page: one decay per value row, the correction taken from the state
+// before the decay (decode_kernel and rows_kernel with CH = true).
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 namespace {
 
-constexpr int kRowsPerThread = 16;   // 128 rows / (4 waves * 2 half-waves)
 
 struct RecArgs {
   int n_tok;                   // verify: tokens per sequence
@@ -100,17 +99,6 @@ __device__ __forceinline__ void rs_level(float (&vals)[L], int lane32) {
     const float keep = upper ? vals[idx + N / 2] : vals[idx];
     vals[idx] = keep + xor_lane(send, M);
   }
-}
-
-// Reduce-scatter of 32 partial sums over the 32 lanes of a half-wave: afterwards
-// vals[0] of lane c holds the half-wave total of index c. 31 exchanges instead of 160.
-__device__ __forceinline__ float reduce_scatter32(float (&vals)[32], int lane32) {
-  rs_level<16, 32>(vals, lane32);
-  rs_level<8, 16>(vals, lane32);
-  rs_level<4, 8>(vals, lane32);
-  rs_level<2, 4>(vals, lane32);
-  rs_level<1, 2>(vals, lane32);
-  return vals[0];
 }
 
 // Reduce-scatter of 16 partial sums over the 32 lanes of a half-wave: afterwards lanes
@@ -187,7 +175,7 @@ __device__ __forceinline__ float decode_token_channel(f32x4 (&S)[8], f32x4 k4, f
 
 // One decode step. Thread (wave w of 8, lane l) holds columns 4*(l%32) .. +3 of the 8 rows
 // i*16 + 2*w + l/32, i = 0..7: each load or store instruction of a wave covers two whole
-// rows (1 KB). Same arithmetic as recurrent_kernel for one token. CH selects the
+// rows (1 KB). CH selects the
 // per-channel form (g [seq][h_v][128], one log-decay per value row, decode_token_channel).
 template <typename IO, bool CH>
 __global__ __launch_bounds__(512) void decode_kernel(RecArgs a) {
@@ -239,15 +227,11 @@ __global__ __launch_bounds__(512) void decode_kernel(RecArgs a) {
     __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(sp + (size_t)i * 16 * kHeadDim));
 }
 
-// Several tokens per (sequence, V head) with the state in registers, decode layout.
-//  * verify (cu_seqlens NULL): tokens t = 0 .. n_tok - 1 of sequence n are rows
-//    n * n_tok + t of the inputs; the state comes from the pool and goes back to it, and
-//    the state after each token goes to snap[n][t] when snap is set.
-//  * prefill (cu_seqlens set): the tokens of sequence n are rows cu[n] .. cu[n+1] - 1; the
-//    state comes from s_in[n] (zero when NULL) and goes to s_out[n] (when set).
-// CH selects the per-channel form (g holds one log-decay per value row: [row][h_v][128]);
-// otherwise decode_token, the main form with one decay per V head.
-template <typename IO, bool CH>
+// The verify step: tokens t = 0 .. n_tok - 1 of sequence n are rows n * n_tok + t of the
+// inputs; the state comes from the pool, stays in registers across the tokens (decode
+// layout, decode_token's arithmetic, so the bits of n_tok decode steps) and goes back to the
+// pool, and the state after each token goes to snap[n][t] when snap is set.
+template <typename IO>
 __global__ __launch_bounds__(512) void seq_kernel(RecArgs a) {
   constexpr int kRows = 8;
   const int tid = threadIdx.x;
@@ -262,10 +246,9 @@ __global__ __launch_bounds__(512) void seq_kernel(RecArgs a) {
   const IO* k = static_cast<const IO*>(a.k);
   const IO* v = static_cast<const IO*>(a.v);
   IO* o = static_cast<IO*>(a.o);
-  const bool pooled = a.cu_seqlens == nullptr;
-  const int row0 = pooled ? n * a.n_tok : a.cu_seqlens[n];
-  const int n_tok = pooled ? a.n_tok : a.cu_seqlens[n + 1] - row0;
-  const int slot = pooled ? (a.slots ? a.slots[n] : n) : n;
+  const int row0 = n * a.n_tok;
+  const int n_tok = a.n_tok;
+  const int slot = a.slots ? a.slots[n] : n;
   const size_t state = ((size_t)slot * a.h_v + h) * kHeadDim * kHeadDim;
   const int row_base = w * 2 + half;        // rows row_base + 16*i
   const size_t lane_off = (size_t)row_base * kHeadDim + 4 * c4;
@@ -287,7 +270,6 @@ __global__ __launch_bounds__(512) void seq_kernel(RecArgs a) {
   struct Tok {
     f32x4 k4, q4;
     float g, beta, vrow;
-    float grow[CH ? kRows : 1];   // per-channel form: the log-decays of this thread's rows
   };
   auto fetch = [&](int t) {
     const size_t tok = (size_t)row0 + t;
@@ -297,28 +279,13 @@ __global__ __launch_bounds__(512) void seq_kernel(RecArgs a) {
     x.q4 = load4(q + qk_off);
     x.beta = a.beta[tok * a.h_v + h];
     x.vrow = load1(v + (tok * a.h_v + h) * kHeadDim + my_row);
-    if constexpr (CH) {
-      const float* gh = a.g + (tok * a.h_v + h) * kHeadDim;
-      x.g = gh[my_row];
-#pragma unroll
-      for (int i = 0; i < kRows; ++i) x.grow[i] = gh[row_base + 16 * i];
-    } else {
-      x.g = a.g[tok * a.h_v + h];
-    }
+    x.g = a.g[tok * a.h_v + h];
     return x;
   };
   // one token: the read-out and update, the output, and the snapshot when asked
   auto step = [&](Tok& x, int t) {
     const size_t tok = (size_t)row0 + t;
-    float out;
-    if constexpr (CH) {
-      float arow[kRows];
-#pragma unroll
-      for (int i = 0; i < kRows; ++i) arow[i] = __expf(x.grow[i]);
-      out = decode_token_channel(S, x.k4, x.q4, arow, __expf(x.g), x.beta, x.vrow, a.scale, c4);
-    } else {
-      out = decode_token(S, x.k4, x.q4, __expf(x.g), x.beta, x.vrow, a.scale, c4);
-    }
+    const float out = decode_token(S, x.k4, x.q4, __expf(x.g), x.beta, x.vrow, a.scale, c4);
     if ((c4 & 3) == 2) store1(o + (tok * a.h_v + h) * kHeadDim + my_row, out);
     if (a.snap) {
       float* dst = a.snap + (tok * a.h_v + h) * kHeadDim * kHeadDim + lane_off;
@@ -352,81 +319,101 @@ __global__ __launch_bounds__(512) void seq_kernel(RecArgs a) {
   }
 }
 
-template <typename IO>
-__global__ __launch_bounds__(256) void recurrent_kernel(RecArgs a) {
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
-  const int half = lane >> 5;
-  const bool upper = half != 0;
-  const int c4 = lane & 31;                 // this thread's 4 columns: 4*c4 .. 4*c4+3
-  const int n = blockIdx.x / a.h_v;
-  const int h = blockIdx.x % a.h_v;
-  const int j = h / (a.h_v / a.h_qk);       // QK head read by V head h
+// Token-sequential prefill with value rows split over workgroups: rows evolve independently
+// in both forms, so each workgroup of one wave takes 16 rows of one (sequence, V head) and
+// walks the sequence's tokens with its rows in registers. Lane (r = lane / 4, quarter
+// p = lane % 4) holds columns 32 p .. 32 p + 31 of row 16 rb + r, so every per-row sum (S k,
+// S q) and k . q is a partial over 32 columns and two quad exchanges (DPP), and one token
+// costs a short chain instead of a 128-column cross-lane reduction. Each token's inputs are
+// requested while the previous token computes. CH selects the per-channel form (g
+// [row][h_v][128]: one log-decay per value row, the correction from the state before the
+// decay); otherwise the main form (one decay per V head).
+template <typename IO, bool CH>
+__global__ __launch_bounds__(64) void rows_kernel(RecArgs a) {
+  const int lane = threadIdx.x;
+  const int rb = blockIdx.x & 7;            // row block of 16
+  const int nh = blockIdx.x >> 3;
+  const int n = nh / a.h_v;
+  const int h = nh % a.h_v;
+  const int j = h / (a.h_v / a.h_qk);
+  const int row = 16 * rb + (lane >> 2);
+  const int c0 = 32 * (lane & 3);
   const IO* q = static_cast<const IO*>(a.q);
   const IO* k = static_cast<const IO*>(a.k);
   const IO* v = static_cast<const IO*>(a.v);
   IO* o = static_cast<IO*>(a.o);
-
   const int t0 = a.cu_seqlens[n];
-  const int t1 = a.cu_seqlens[n + 1];
-  const size_t state_in = ((size_t)n * a.h_v + h) * kHeadDim * kHeadDim;
-  const size_t state_out = state_in;
-  const int row_base = w * 2 + half;        // rows row_base + 8*i
+  const int n_tok = a.cu_seqlens[n + 1] - t0;
+  const size_t state = (((size_t)n * a.h_v + h) * kHeadDim + row) * kHeadDim + c0;
 
-  f32x4 S[kRowsPerThread];
+  f32x4 S[8];
   if (a.s_in) {
-    const float* src = a.s_in + state_in + (size_t)row_base * kHeadDim + 4 * c4;
 #pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i)
-      S[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (size_t)i * 8 * kHeadDim));
+    for (int i = 0; i < 8; ++i) S[i] = *reinterpret_cast<const f32x4*>(a.s_in + state + 4 * i);
   } else {
 #pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 8; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  // Lane c4 of each half-wave finishes row slot c4/2 (even lane: u, odd lane: r).
-  const int my_slot = c4 >> 1;
-  const int my_row = row_base + 8 * my_slot;
-  const bool my_is_r = (c4 & 1) != 0;
-
-  for (int t = t0; t < t1; ++t) {
-    const size_t qk_off = ((size_t)t * a.h_qk + j) * kHeadDim + 4 * c4;
-    const f32x4 k4 = load4(k + qk_off);
-    const f32x4 q4 = load4(q + qk_off);
-    const float alpha = __expf(a.g[(size_t)t * a.h_v + h]);
-    const float beta = a.beta[(size_t)t * a.h_v + h];
-    const float vrow = load1(v + ((size_t)t * a.h_v + h) * kHeadDim + my_row);
-
-    float vals[32];
+  struct Tok {
+    f32x4 k4[8], q4[8];
+    float g, beta, vrow;
+  };
+  auto fetch = [&](int t) {
+    const size_t tok = (size_t)t0 + t;
+    const size_t qk_off = (tok * a.h_qk + j) * kHeadDim + c0;
+    Tok x;
 #pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-      vals[2 * i] = S[i][0] * k4[0] + S[i][1] * k4[1] + S[i][2] * k4[2] + S[i][3] * k4[3];
-      vals[2 * i + 1] = S[i][0] * q4[0] + S[i][1] * q4[1] + S[i][2] * q4[2] + S[i][3] * q4[3];
+    for (int i = 0; i < 8; ++i) {
+      x.k4[i] = load4(k + qk_off + 4 * i);
+      x.q4[i] = load4(q + qk_off + 4 * i);
     }
-    const float mine = reduce_scatter32(vals, c4);
-    const float other = xor_lane(mine, 1);
-    const float u = my_is_r ? other : mine;
-    const float r = my_is_r ? mine : other;
-    const float kq = half_sum(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
-    const float c = beta * (vrow - alpha * u);
-    if (my_is_r) store1(o + ((size_t)t * a.h_v + h) * kHeadDim + my_row, a.scale * (alpha * r + c * kq));
-
+    x.g = CH ? a.g[(tok * a.h_v + h) * kHeadDim + row] : a.g[tok * a.h_v + h];
+    x.beta = a.beta[tok * a.h_v + h];
+    x.vrow = load1(v + (tok * a.h_v + h) * kHeadDim + row);
+    return x;
+  };
+  auto step = [&](Tok& x, int t) {
+    float u = 0.f, r = 0.f, kq = 0.f;
 #pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-      const float ci = half_lane(c, 2 * i, upper);
-      S[i][0] = alpha * S[i][0] + ci * k4[0];
-      S[i][1] = alpha * S[i][1] + ci * k4[1];
-      S[i][2] = alpha * S[i][2] + ci * k4[2];
-      S[i][3] = alpha * S[i][3] + ci * k4[3];
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u += S[i][e] * x.k4[i][e];
+        r += S[i][e] * x.q4[i][e];
+        kq += x.k4[i][e] * x.q4[i][e];
+      }
+    u += xor_lane(u, 1);
+    r += xor_lane(r, 1);
+    kq += xor_lane(kq, 1);
+    u += xor_lane(u, 2);
+    r += xor_lane(r, 2);
+    kq += xor_lane(kq, 2);
+    const float alpha = __expf(x.g);
+    // main form: the correction of the decayed memory; per-channel form: of the memory before
+    // this row's decay
+    const float c = CH ? x.beta * (x.vrow - u) : x.beta * (x.vrow - alpha * u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) S[i] = alpha * S[i] + c * x.k4[i];
+    if ((lane & 3) == 0) store1(o + (((size_t)t0 + t) * a.h_v + h) * kHeadDim + row, a.scale * (alpha * r + c * kq));
+  };
+  if (n_tok > 0) {
+    Tok ta = fetch(0), tb;
+    for (int t = 0; t < n_tok; t += 2) {
+      tb = fetch(min(t + 1, n_tok - 1));
+      // the next token's loads are issued here: this token's k passes through the asm, so no
+      // product that uses it moves above it
+      asm volatile("" : "+v"(ta.k4[0]), "+v"(ta.q4[0]) :: "memory");
+      step(ta, t);
+      if (t + 1 < n_tok) {
+        ta = fetch(min(t + 2, n_tok - 1));
+        asm volatile("" : "+v"(tb.k4[0]), "+v"(tb.q4[0]) :: "memory");
+        step(tb, t + 1);
+      }
     }
   }
-
   if (a.s_out) {
-    float* dst = a.s_out + state_out + (size_t)row_base * kHeadDim + 4 * c4;
 #pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i)
-      __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(dst + (size_t)i * 8 * kHeadDim));
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4*>(a.s_out + state + 4 * i) = S[i];
   }
 }
 
@@ -450,11 +437,11 @@ hipError_t launch_recurrent_prefill(const void* q, const void* k, const void* v,
                                     int num_seqs, int h_qk, int h_v, float scale,
                                     const float* s0, float* s_final, void* o, hipStream_t stream) {
   RecArgs a{0, nullptr, q, k, v, g, beta, cu_seqlens, nullptr, s0, s_final, o, num_seqs, h_qk, h_v, scale};
-  const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(256);
+  const dim3 grid((unsigned)num_seqs * (unsigned)h_v * 8), block(64);
   if (io_bf16)
-    hipLaunchKernelGGL((recurrent_kernel<bf16>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((rows_kernel<bf16, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((recurrent_kernel<float>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((rows_kernel<float, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -465,9 +452,9 @@ hipError_t launch_verify(const void* q, const void* k, const void* v, bool io_bf
   RecArgs a{num_tokens, snapshots, q, k, v, g, beta, nullptr, slots, pool, pool, o, num_seqs, h_qk, h_v, scale};
   const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(512);
   if (io_bf16)
-    hipLaunchKernelGGL((seq_kernel<bf16, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((seq_kernel<bf16>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((seq_kernel<float, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((seq_kernel<float>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -476,11 +463,11 @@ hipError_t launch_channel_prefill(const void* q, const void* k, const void* v, b
                                   int num_seqs, int h_qk, int h_v, float scale, const float* s0,
                                   float* s_final, void* o, hipStream_t stream) {
   RecArgs a{0, nullptr, q, k, v, g, beta, cu_seqlens, nullptr, s0, s_final, o, num_seqs, h_qk, h_v, scale};
-  const dim3 grid((unsigned)num_seqs * (unsigned)h_v), block(512);
+  const dim3 grid((unsigned)num_seqs * (unsigned)h_v * 8), block(64);
   if (io_bf16)
-    hipLaunchKernelGGL((seq_kernel<bf16, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((rows_kernel<bf16, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((seq_kernel<float, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((rows_kernel<float, true>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -59,8 +59,9 @@ def test_channel_prefill_model_size():
 
 
 def test_channel_decode_equals_prefill():
-    """Token-by-token decode over a permuted pool equals, bit for bit, the prefill of the same
-    tokens (both run the same per-token arithmetic), and both match the oracle."""
+    """Token-by-token decode over a permuted pool agrees with the prefill of the same tokens
+    (the two kernels sum the per-row products in different orders, so to rounding), and both
+    match the oracle."""
     import torch
     import linear_attention_recurrence_amd as gdn
     T, N = 12, 3
@@ -81,8 +82,11 @@ def test_channel_decode_equals_prefill():
             d["beta"][r].contiguous(), pool, x.scale, state_slots=slots))
     torch.cuda.synchronize()
     o_d = np.stack([to_host_f64(o_) for o_ in outs], axis=1).reshape(N * T, 2, 128)
-    np.testing.assert_array_equal(o_d, o_p)
-    np.testing.assert_array_equal(to_host_f64(pool[slots.long()]), fin_p)
+    fin_d = to_host_f64(pool[slots.long()])
+    check_outputs(o_d, o_p, "channel decode vs prefill")
+    check_state(fin_d, fin_p, "channel decode vs prefill")
     ref_o, ref_s = _oracle(x, g)
     check_outputs(o_d, ref_o, "channel decode")
-    check_state(fin_p, ref_s, "channel decode")
+    check_state(fin_d, ref_s, "channel decode")
+    check_outputs(o_p, ref_o, "channel prefill")
+    check_state(fin_p, ref_s, "channel prefill")
