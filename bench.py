@@ -37,6 +37,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "GDN prefill tokens/s/GPU (H_v=32,d=128) + decode state GB/s vs HBM peak"
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, published (packed issue), TFLOP/s
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
 
@@ -282,7 +283,8 @@ def bench_verify(steps, warmup, n_tok=4):
 def bench_channel_decay(steps, warmup, prefill_reps=5):
     """The per-channel form: one decode step at 256 sequences over the 512 MiB pool (a ring of
     16 input sets, per-channel log-decays [256][32][128]), and the token-sequential prefill
-    at B = 1, T = 4096. Returns (decode wall s, decode ms, prefill ms)."""
+    at B = 1, T = 4096 and at B = 16, T = 1024. Returns (decode wall s, decode ms, B = 1
+    prefill ms, B = 16 prefill ms)."""
     import torch
     import linear_attention_recurrence_amd as gdn
     import workloads
@@ -307,7 +309,17 @@ def bench_channel_decay(steps, warmup, prefill_reps=5):
         gdn.gdn_channel_decay_prefill(xq, xk, xv, xg, xb, cu, x.scale, final_state=fin, o=xo)
 
     _, pms = _timed(prefill, prefill_reps, 1)
-    return dwall, dms, pms
+    y = workloads.make_prefill([1024] * 16, seed=1010)
+    yq, yk, yv, yb, ycu = _dev(y.q), _dev(y.k), _dev(y.v), _dev(y.beta), _dev(y.cu_seqlens)
+    yg = _dev(workloads.channel_log_alpha(16 * 1024, seed=1011))
+    yo = torch.empty((16 * 1024, H_V, D), dtype=torch.bfloat16, device="cuda")
+    yfin = torch.empty((16, H_V, D, D), dtype=torch.float32, device="cuda")
+
+    def prefill16(i):
+        gdn.gdn_channel_decay_prefill(yq, yk, yv, yg, yb, ycu, y.scale, final_state=yfin, o=yo)
+
+    _, pms16 = _timed(prefill16, prefill_reps, 1)
+    return dwall, dms, pms, pms16
 
 
 def bench_frontend(reps, warmup):
@@ -490,13 +502,18 @@ def main():
                              "kernel": "seq_kernel<bf16, false>", "algorithmic_bytes": vb}}
     if "decode" in work:
         csteps = max(20, args.decode_steps // 10)
-        cwall, cms, cpms = bench_channel_decay(csteps, args.warmup)
+        cwall, cms, cpms, cpms16 = bench_channel_decay(csteps, args.warmup)
+        # 7 d^2 flops per (token, V head): S k and S q (2 d^2 each), the decay and the rank-1
+        # update (3 d^2)
+        cflops = 16 * 1024 * H_V * 7 * D * D
+        ctf = cflops / (cpms16 / 1e3) / 1e12
         cb = decode_bytes(256) + 256 * H_V * D * 4 - 256 * H_V * 4   # g per channel
         achieved = cb / (cms / 1e3) / 1e9
         out["channel_decay"] = {
             "workload": "per-channel decay form (one decay per value channel, correction from the "
                         "state before the decay): decode step at 256 sequences x 1 token over the "
-                        "512 MiB pool; token-sequential prefill at B=1, T=4096, 32 V heads",
+                        "512 MiB pool; token-sequential prefill at B=1, T=4096 and at "
+                        "B=16, T=1024, 32 V heads",
             "decode": {"steps": csteps, "ms_per_step": cwall * 1e3 / csteps,
                        "tokens_per_s": 256 * csteps / cwall,
                        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -504,7 +521,13 @@ def main():
                                     "kernel": "decode_kernel<bf16, true>", "kernel_ms": cms,
                                     "algorithmic_bytes": cb}},
             "prefill_b1_t4096": {"ms_per_call": cpms, "tokens_per_s": 4096 / (cpms / 1e3),
-                                 "bound": "latency: one chain of 4096 dependent tokens per V head"}}
+                                 "bound": "latency: one chain of 4096 dependent tokens per V head"},
+            "prefill_b16_t1024": {"ms_per_call": cpms16, "tokens_per_s": 16 * 1024 / (cpms16 / 1e3),
+                                  "roofline": {"bound": "alu", "achieved": ctf,
+                                               "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                               "frac": ctf / FP32_PEAK_TFLOPS,
+                                               "kernel": "rows_kernel<bf16, true, 8, 4>",
+                                               "algorithmic_flops": cflops}}}
     if "frontend" in work:
         T4, N4, conv_ms, pre_ms = bench_frontend(10, 2)
         out["frontend_prefill"] = {

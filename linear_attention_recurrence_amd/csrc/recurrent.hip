@@ -52,16 +52,18 @@ struct RecArgs {
 // Lane exchanges within a half-wave without the LDS crossbar where the pattern stays inside
 // a 16-lane row: the value of lane l ^ m, by DPP for m = 1 and 2 (quad permutes), 4 (half-row
 // mirror, then quad reversal: l ^ 7 ^ 3), 8 (row rotation by 8), and by ds_swizzle (xor mask
-// within 32 lanes) for m = 16. Pure data movement: sums built from it are unchanged.
+// within 32 lanes) for m = 16. Pure data movement: sums built from it are unchanged. Every
+// DPP pattern here reads a lane of the same row and all rows and banks are written, so the
+// move needs no old value (none is materialised) and the bound control never applies.
 __device__ __forceinline__ float xor_lane(float x, int m) {
   const int v = __builtin_bit_cast(int, x);
   int r;
   switch (m) {
-    case 1: r = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); break;
-    case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); break;
-    case 4: r = __builtin_amdgcn_update_dpp(0, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false),
-                                            0x1B, 0xF, 0xF, false); break;
-    case 8: r = __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false); break;
+    case 1: r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true); break;
+    case 4: r = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true),
+                                         0x1B, 0xF, 0xF, true); break;
+    case 8: r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true); break;
     default: r = __builtin_amdgcn_ds_swizzle(v, 0x401F); break;   // m = 16
   }
   return __builtin_bit_cast(float, r);
@@ -319,25 +321,70 @@ __global__ __launch_bounds__(512) void seq_kernel(RecArgs a) {
   }
 }
 
+// CPL consecutive inputs (k or q columns) of one token as the 32-bit words a load returns,
+// converted to fp32 only where they are used: a ring of tokens in flight then carries loaded
+// registers across the loop, and the compiler waits for each set by its own count instead
+// of draining every load to convert it before the loop's back edge.
+template <typename IO, int CPL>
+struct RawCols {
+  static constexpr int NW = CPL * (int)sizeof(IO) / 4;
+  uint32_t w[NW];
+};
+
+template <typename IO, int CPL>
+__device__ __forceinline__ RawCols<IO, CPL> load_cols(const IO* p) {
+  RawCols<IO, CPL> r;
+  constexpr int NW = RawCols<IO, CPL>::NW;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(p);
+  if constexpr (NW % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src + 4 * i);
+      r.w[4 * i] = x[0]; r.w[4 * i + 1] = x[1]; r.w[4 * i + 2] = x[2]; r.w[4 * i + 3] = x[3];
+    }
+  } else {
+    static_assert(NW == 2, "column group of 8 bytes or a multiple of 16");
+    const u32x2 x = *reinterpret_cast<const u32x2*>(src);
+    r.w[0] = x[0]; r.w[1] = x[1];
+  }
+  return r;
+}
+
+// Column e as fp32: a bf16 is the upper half of the fp32 with the same bits (element 2i sits
+// in the low half of word i).
+template <typename IO, int CPL>
+__device__ __forceinline__ float col(const RawCols<IO, CPL>& r, int e) {
+  if constexpr (sizeof(IO) == 2)
+    return __builtin_bit_cast(float, (e & 1) ? (r.w[e / 2] & 0xffff0000u) : (r.w[e / 2] << 16));
+  else
+    return __builtin_bit_cast(float, r.w[e]);
+}
+
 // Token-sequential prefill with value rows split over workgroups: rows evolve independently
-// in both forms, so each workgroup of one wave takes 16 rows of one (sequence, V head) and
-// walks the sequence's tokens with its rows in registers. Lane (r = lane / 4, quarter
-// p = lane % 4) holds columns 32 p .. 32 p + 31 of row 16 rb + r, so every per-row sum (S k,
-// S q) and k . q is a partial over 32 columns and two quad exchanges (DPP), and one token
-// costs a short chain instead of a 128-column cross-lane reduction. Each token's inputs are
-// requested while the previous token computes. CH selects the per-channel form (g
-// [row][h_v][128]: one log-decay per value row, the correction from the state before the
-// decay); otherwise the main form (one decay per V head).
-template <typename IO, bool CH>
+// in both forms, so each workgroup of one wave takes R rows of one (sequence, V head) and
+// walks the sequence's tokens with its rows in registers. Lane (r = lane / L, p = lane % L,
+// L = 64 / R lanes per row) holds columns 2R p .. 2R p + 2R - 1 of row R rb + r, so every
+// per-row sum (S k, S q) and k . q is a partial over 2R columns and log2(L) lane exchanges
+// inside a 16-lane DPP row (plus one swizzle when L = 32). Fewer rows per wave mean fewer
+// columns, so less arithmetic per token on the chain, and more waves to spread over the
+// chip's SIMDs; more rows per wave cost less in total when the grid is full anyway. The
+// inputs of the next D tokens are in flight while a token computes. CH selects the
+// per-channel form (g [row][h_v][128]: one log-decay per value row, the correction from the
+// state before the decay); otherwise the main form (one decay per V head).
+template <typename IO, bool CH, int R, int D>
 __global__ __launch_bounds__(64) void rows_kernel(RecArgs a) {
+  constexpr int L = 64 / R;          // lanes per row
+  constexpr int CPL = 128 / L;       // columns per lane
+  constexpr int NV = CPL / 4;        // f32x4 per lane
+  constexpr int NB = 128 / R;        // workgroups per (sequence, V head)
   const int lane = threadIdx.x;
-  const int rb = blockIdx.x & 7;            // row block of 16
-  const int nh = blockIdx.x >> 3;
+  const int rb = blockIdx.x % NB;
+  const int nh = blockIdx.x / NB;
   const int n = nh / a.h_v;
   const int h = nh % a.h_v;
   const int j = h / (a.h_v / a.h_qk);
-  const int row = 16 * rb + (lane >> 2);
-  const int c0 = 32 * (lane & 3);
+  const int row = R * rb + lane / L;
+  const int c0 = CPL * (lane % L);
   const IO* q = static_cast<const IO*>(a.q);
   const IO* k = static_cast<const IO*>(a.k);
   const IO* v = static_cast<const IO*>(a.v);
@@ -346,75 +393,133 @@ __global__ __launch_bounds__(64) void rows_kernel(RecArgs a) {
   const int n_tok = a.cu_seqlens[n + 1] - t0;
   const size_t state = (((size_t)n * a.h_v + h) * kHeadDim + row) * kHeadDim + c0;
 
-  f32x4 S[8];
+  f32x4 S[NV];
   if (a.s_in) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) S[i] = *reinterpret_cast<const f32x4*>(a.s_in + state + 4 * i);
+    for (int i = 0; i < NV; ++i) S[i] = *reinterpret_cast<const f32x4*>(a.s_in + state + 4 * i);
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NV; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   struct Tok {
-    f32x4 k4[8], q4[8];
-    float g, beta, vrow;
+    RawCols<IO, CPL> k, q;
+    float g, beta;
+    IO vrow;
   };
-  auto fetch = [&](int t) {
-    const size_t tok = (size_t)t0 + t;
-    const size_t qk_off = (tok * a.h_qk + j) * kHeadDim + c0;
+  // Inputs are addressed from uniform per-token bases (scalar registers, advanced by one
+  // token at a time) plus this lane's zero-extended offset, so each load is one instruction
+  // with no per-lane address arithmetic. f is the next token to fetch, held at the last one
+  // once the sequence is exhausted (the ring then refills with copies it never uses).
+  const unsigned urow = (unsigned)row, uc0 = (unsigned)c0;
+  const size_t s_qk = (size_t)a.h_qk * kHeadDim;
+  int f = 0;
+  size_t f_qk = ((size_t)t0 * a.h_qk + j) * kHeadDim;
+  size_t f_vh = (size_t)t0 * a.h_v + h;
+  auto fetch = [&]() {
     Tok x;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x.k4[i] = load4(k + qk_off + 4 * i);
-      x.q4[i] = load4(q + qk_off + 4 * i);
+    x.k = load_cols<IO, CPL>(k + f_qk + uc0);
+    x.q = load_cols<IO, CPL>(q + f_qk + uc0);
+    x.g = CH ? a.g[f_vh * kHeadDim + urow] : a.g[f_vh];
+    x.beta = a.beta[f_vh];
+    x.vrow = v[f_vh * kHeadDim + urow];
+    if (f < n_tok - 1) {
+      ++f;
+      f_qk += s_qk;
+      f_vh += a.h_v;
     }
-    x.g = CH ? a.g[(tok * a.h_v + h) * kHeadDim + row] : a.g[tok * a.h_v + h];
-    x.beta = a.beta[tok * a.h_v + h];
-    x.vrow = load1(v + (tok * a.h_v + h) * kHeadDim + row);
     return x;
   };
-  auto step = [&](Tok& x, int t) {
-    float u = 0.f, r = 0.f, kq = 0.f;
+  size_t o_vh = (size_t)t0 * a.h_v + h;
+  // The read-out is taken from the updated state (o = S_t q): its sum is off the chain that
+  // carries the state to the next token, and k . q is not needed. Every lane of a row holds
+  // the row's sums after the exchanges, so all of them store the same value (no branch, so
+  // one token's read-out can overlap the next token's chain).
+  auto step = [&](const Tok& x) {
+    float kc[CPL];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int e = 0; e < CPL; ++e) kc[e] = col(x.k, e);
+    float u = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        u += S[i][e] * x.k4[i][e];
-        r += S[i][e] * x.q4[i][e];
-        kq += x.k4[i][e] * x.q4[i][e];
-      }
-    u += xor_lane(u, 1);
-    r += xor_lane(r, 1);
-    kq += xor_lane(kq, 1);
-    u += xor_lane(u, 2);
-    r += xor_lane(r, 2);
-    kq += xor_lane(kq, 2);
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u += S[i][e] * kc[4 * i + e];
+#pragma unroll
+    for (int m = 1; m < L; m *= 2) u += xor_lane(u, m);
     const float alpha = __expf(x.g);
+    const float vrow = (float)x.vrow;
     // main form: the correction of the decayed memory; per-channel form: of the memory before
     // this row's decay
-    const float c = CH ? x.beta * (x.vrow - u) : x.beta * (x.vrow - alpha * u);
+    const float c = CH ? x.beta * (vrow - u) : x.beta * (vrow - alpha * u);
+    float r = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) S[i] = alpha * S[i] + c * x.k4[i];
-    if ((lane & 3) == 0) store1(o + (((size_t)t0 + t) * a.h_v + h) * kHeadDim + row, a.scale * (alpha * r + c * kq));
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        S[i][e] = alpha * S[i][e] + c * kc[4 * i + e];
+        r += S[i][e] * col(x.q, 4 * i + e);
+      }
+#pragma unroll
+    for (int m = 1; m < L; m *= 2) r += xor_lane(r, m);
+    store1(o + o_vh * kHeadDim + urow, a.scale * r);
+    o_vh += a.h_v;
+  };
+  // A token's inputs pass through an empty asm just before its step: what is computed from
+  // them (the bf16 widening, exp of the decay) cannot be hoisted above it, so no earlier
+  // token waits for a later token's loads.
+  auto pin = [&](Tok& x) {
+#pragma unroll
+    for (int i = 0; i < RawCols<IO, CPL>::NW; ++i) asm volatile("" : "+v"(x.k.w[i]), "+v"(x.q.w[i]));
+    if constexpr (sizeof(IO) == 2) {
+      unsigned short vb = __builtin_bit_cast(unsigned short, x.vrow);
+      asm volatile("" : "+v"(x.g), "+v"(x.beta), "+v"(vb));
+      x.vrow = __builtin_bit_cast(IO, vb);
+    } else {
+      asm volatile("" : "+v"(x.g), "+v"(x.beta), "+v"(x.vrow));
+    }
   };
   if (n_tok > 0) {
-    Tok ta = fetch(0), tb;
-    for (int t = 0; t < n_tok; t += 2) {
-      tb = fetch(min(t + 1, n_tok - 1));
-      // the next token's loads are issued here: this token's k passes through the asm, so no
-      // product that uses it moves above it
-      asm volatile("" : "+v"(ta.k4[0]), "+v"(ta.q4[0]) :: "memory");
-      step(ta, t);
-      if (t + 1 < n_tok) {
-        ta = fetch(min(t + 2, n_tok - 1));
-        asm volatile("" : "+v"(tb.k4[0]), "+v"(tb.q4[0]) :: "memory");
-        step(tb, t + 1);
+    // ring of D token input sets; the loads are unconditional (see fetch), so the compiler
+    // waits for each set by its own count
+    Tok buf[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) buf[d] = fetch();
+    int t = 0;
+    for (; t + D <= n_tok; t += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        // the refill goes into the registers this token has just used, so nothing is copied
+        // around the loop (a copy of a load in flight would have to wait for it)
+        pin(buf[d]);
+        step(buf[d]);
+        buf[d] = fetch();
+        // keeps the refill's loads here: left free, the scheduler sinks them towards their
+        // use a whole ring later, and the wait for them lands on the next token
+        asm volatile("" ::: "memory");
       }
     }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (t + d < n_tok) step(buf[d]);
   }
   if (a.s_out) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4*>(a.s_out + state + 4 * i) = S[i];
+    for (int i = 0; i < NV; ++i) *reinterpret_cast<f32x4*>(a.s_out + state + 4 * i) = S[i];
   }
+}
+
+// Shape of the token-sequential prefill by the number of (sequence, V head) pairs: up to 64
+// pairs (two sequences of 32 V heads) the chain of one wave is the limit and 4 rows per wave
+// (32 waves per pair, 8 tokens in flight) spread it over the most SIMDs; beyond that the
+// chip is full and arithmetic per row is the limit, which 8 rows per wave (4 in flight)
+// keeps lower.
+template <typename IO, bool CH>
+hipError_t launch_rows(const RecArgs& a, hipStream_t stream) {
+  const unsigned pairs = (unsigned)a.num_seqs * (unsigned)a.h_v;
+  if (pairs <= 64)
+    hipLaunchKernelGGL((rows_kernel<IO, CH, 4, 8>), dim3(pairs * 32), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((rows_kernel<IO, CH, 8, 4>), dim3(pairs * 16), dim3(64), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -437,12 +542,7 @@ hipError_t launch_recurrent_prefill(const void* q, const void* k, const void* v,
                                     int num_seqs, int h_qk, int h_v, float scale,
                                     const float* s0, float* s_final, void* o, hipStream_t stream) {
   RecArgs a{0, nullptr, q, k, v, g, beta, cu_seqlens, nullptr, s0, s_final, o, num_seqs, h_qk, h_v, scale};
-  const dim3 grid((unsigned)num_seqs * (unsigned)h_v * 8), block(64);
-  if (io_bf16)
-    hipLaunchKernelGGL((rows_kernel<bf16, false>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((rows_kernel<float, false>), grid, block, 0, stream, a);
-  return hipGetLastError();
+  return io_bf16 ? launch_rows<bf16, false>(a, stream) : launch_rows<float, false>(a, stream);
 }
 
 hipError_t launch_verify(const void* q, const void* k, const void* v, bool io_bf16, const float* g,
@@ -463,12 +563,7 @@ hipError_t launch_channel_prefill(const void* q, const void* k, const void* v, b
                                   int num_seqs, int h_qk, int h_v, float scale, const float* s0,
                                   float* s_final, void* o, hipStream_t stream) {
   RecArgs a{0, nullptr, q, k, v, g, beta, cu_seqlens, nullptr, s0, s_final, o, num_seqs, h_qk, h_v, scale};
-  const dim3 grid((unsigned)num_seqs * (unsigned)h_v * 8), block(64);
-  if (io_bf16)
-    hipLaunchKernelGGL((rows_kernel<bf16, true>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((rows_kernel<float, true>), grid, block, 0, stream, a);
-  return hipGetLastError();
+  return io_bf16 ? launch_rows<bf16, true>(a, stream) : launch_rows<float, true>(a, stream);
 }
 
 hipError_t launch_channel_decode(const void* q, const void* k, const void* v, bool io_bf16,

@@ -48,6 +48,22 @@ def test_channel_prefill_varlen(io):
     np.testing.assert_array_equal(fin[0], x.initial_state[0].astype(np.float64))
 
 
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_channel_prefill_many_pairs(io):
+    """More than 64 (sequence, V head) pairs: the prefill takes its other shape (8 rows per
+    wave, 4 tokens in flight). Lengths below, at and past multiples of the ring depth."""
+    x = workloads.make_prefill([0, 3, 40, 130, 7], h_qk=16, h_v=32, io_dtype=io,
+                               with_initial_state=True, seed=156)
+    g = workloads.channel_log_alpha(x.total_tokens, 32, 128, seed=157)
+    o, fin = _run_prefill(x, g)
+    ref_o, ref_s = _oracle(x, g)
+    res_o = check_outputs(o, ref_o, "channel prefill 160 pairs %s" % io)
+    res_s = check_state(fin, ref_s, "channel prefill 160 pairs %s" % io)
+    if io == "f32":
+        assert res_o[1] < 1e-5 and res_s < 1e-5
+    np.testing.assert_array_equal(fin[0], x.initial_state[0].astype(np.float64))
+
+
 def test_channel_prefill_model_size():
     """B = 1, T = 1024, 16 QK / 32 V heads, bf16, S0 ~ N(0, 0.02): every head against the oracle."""
     x = workloads.make_prefill([1024], with_initial_state=True, seed=152)

@@ -178,6 +178,16 @@ def test_prefill_fp32_varlen():
     assert res[1] < 1e-5 and res[2] < 1e-5
 
 
+def test_prefill_fp32_many_pairs():
+    """fp32 I/O with more than 64 (sequence, V head) pairs: the token-sequential kernel's
+    other shape (8 rows per wave)."""
+    x = workloads.make_prefill([0, 5, 77, 200], h_qk=8, h_v=32, io_dtype="f32",
+                               with_initial_state=True, seed=14)
+    o, fin = _run(x)
+    res = _compare(x, o, fin, label="f32 128 pairs")
+    assert res[1] < 1e-5 and res[2] < 1e-5
+
+
 def test_config1_full():
     """B=1, T=4096, 16 QK / 32 V heads, bf16, S0 = 0: every head against the oracle."""
     x = workloads.config1()
