@@ -55,6 +55,9 @@ def load_library(path: Optional[str] = None):
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                       _D, _D, _D, ctypes.c_int]
+    lib.gdn_ref_gated_rmsnorm.restype = ctypes.c_int
+    lib.gdn_ref_gated_rmsnorm.argtypes = [_D, _D, _D, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_double, ctypes.c_int, _D]
     return lib
 
 
@@ -165,3 +168,29 @@ def conv_prep(mixed, conv_weight, cu_seqlens, h_qk, h_v, d_k, d_v, q_scale, eps=
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return q, k, v
+
+
+GATE_SIGMOID = 0
+GATE_SILU = 1
+
+
+def gated_rmsnorm(o, z, weight, eps=1e-6, gate=GATE_SIGMOID, lib=None):
+    """Output epilogue (gdn_oracle.c, gdn_ref_gated_rmsnorm): per V head, RMS norm over the
+    d_v read-out channels with the zero-centred scale (1 + weight) (architecture
+    knowledge-base page "Qwen3-Next 80B-A3B", table "Architecture", row "Norm type"), then
+    the output gate of the GatedDeltaNet section of the Evolving Transformer page,
+    sigmoid(z) or SiLU(z), elementwise.
+
+    o, z: [rows][h_v][d_v] float64; weight: [d_v] float64. Returns out, same shape as o."""
+    o = np.ascontiguousarray(o, dtype=np.float64)
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    weight = np.ascontiguousarray(weight, dtype=np.float64)
+    rows, h_v, d_v = o.shape
+    assert z.shape == o.shape and weight.shape == (d_v,)
+    out = np.empty_like(o)
+    L = lib or _load()
+    st = L.gdn_ref_gated_rmsnorm(_dp(o), _dp(z), _dp(weight), rows, h_v, d_v, float(eps),
+                                 int(gate), _dp(out))
+    if st != 0:
+        raise ValueError("gated_rmsnorm: unknown gate %r" % (gate,))
+    return out

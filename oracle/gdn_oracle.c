@@ -31,6 +31,14 @@
  *    GatedDeltaNet section names a short 1-D convolution for local context and normalises
  *    the keys; kernel size, channels and the q normalisation follow the layer shape of
  *    the workload).
+ *  - The epilogue after the mixer: an RMS norm over each V head's d_v read-out channels
+ *    with the zero-centred scale (1 + w_i) (page "Qwen3-Next 80B-A3B", the architecture
+ *    knowledge-base page, table "Architecture", row "Norm type": zero-centred RMSNorm),
+ *    then an elementwise output gate from a second projection z (the GatedDeltaNet section
+ *    of the Evolving Transformer page: a gate decides how much of the recurrent read-out
+ *    reaches the output). The pages give no formula: the norm is taken over one head at a
+ *    time, the gate is applied after the norm, and the gate function is sigmoid (a
+ *    fraction between 0 and 1) or, on request, SiLU.
  *
  * Plain loops, fp64, no blocking or reordering beyond the definitions above. Threads only
  * split independent (sequence, V head) chains or tokens.
@@ -361,5 +369,41 @@ int gdn_ref_conv_prep(const double* mixed, const double* conv_weight, int conv_k
     }
     free(th);
     free(jobs);
+    return 0;
+}
+
+
+/* ------------------------------------------------------------------------------------ */
+/* Output epilogue: per-head RMS norm with zero-centred scale, then the output gate.     */
+/* ------------------------------------------------------------------------------------ */
+
+/*
+ * For each of rows * h_v vectors x = o[r][h][0 .. d_v-1] (and the gate input z at the same
+ * place):
+ *     ms    = (1/d_v) * sum_i x_i^2
+ *     y_i   = x_i / sqrt(ms + eps) * (1 + weight[i])
+ *     out_i = y_i * sigmoid(z_i)          (gate == 0)
+ *     out_i = y_i * z_i * sigmoid(z_i)    (gate == 1, SiLU)
+ * weight has d_v entries, shared by all heads. Returns 0, or -1 for an unknown gate.
+ */
+int gdn_ref_gated_rmsnorm(const double* o, const double* z, const double* weight,
+                          int64_t rows, int h_v, int d_v, double eps, int gate, double* out)
+{
+    if (gate != 0 && gate != 1) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int h = 0; h < h_v; ++h) {
+            const size_t base = ((size_t)r * h_v + h) * d_v;
+            double ms = 0.0;
+            for (int i = 0; i < d_v; ++i) ms += o[base + i] * o[base + i];
+            ms /= d_v;
+            const double inv_rms = 1.0 / sqrt(ms + eps);
+            for (int i = 0; i < d_v; ++i) {
+                const double y = o[base + i] * inv_rms * (1.0 + weight[i]);
+                const double zi = z[base + i];
+                const double sig = 1.0 / (1.0 + exp(-zi));
+                out[base + i] = y * (gate == 0 ? sig : zi * sig);
+            }
+        }
+    }
     return 0;
 }

@@ -561,3 +561,115 @@ def test_pins_pass_on_the_oracle():
 @pytest.mark.parametrize("name", sorted(_MUTATIONS))
 def test_pins_catch_planted_mistake(mutant_libs, name):
     assert not _pins_pass(mutant_libs[name]), name
+
+
+# ---------------------------------------------------------------------------------------
+# output epilogue: per-head RMS norm with the zero-centred scale (1 + w), then the gate
+# ---------------------------------------------------------------------------------------
+
+def _norm_pins(lib=None):
+    """Every pin of gated_rmsnorm; returns the names of those that fail."""
+    fails = []
+    gr = lambda o, z, w, eps, gate: oracle.gated_rmsnorm(np.array(o, dtype=np.float64),
+                                                        np.array(z, dtype=np.float64),
+                                                        np.array(w, dtype=np.float64),
+                                                        eps=eps, gate=gate, lib=lib)
+    # worked by hand: x = (3, 4) has mean square 12.5, so x / rms = (3, 4) / sqrt(12.5)
+    ref = np.array([3.0, 4.0]) / np.sqrt(12.5)
+    out = gr([[[3.0, 4.0]]], [[[60.0, 60.0]]], [0.0, 0.0], 0.0, oracle.GATE_SIGMOID)[0, 0]
+    if not np.allclose(out, ref, rtol=1e-14, atol=0):
+        fails.append("hand example, gate open")
+    # sigmoid(0) = 1/2; SiLU(0) = 0
+    out = gr([[[3.0, 4.0]]], [[[0.0, 0.0]]], [0.0, 0.0], 0.0, oracle.GATE_SIGMOID)[0, 0]
+    if not np.allclose(out, ref / 2, rtol=1e-14, atol=0):
+        fails.append("sigmoid(0) = 1/2")
+    out = gr([[[3.0, 4.0]]], [[[0.0, 0.0]]], [0.0, 0.0], 0.0, oracle.GATE_SILU)[0, 0]
+    if not np.all(out == 0.0):
+        fails.append("silu(0) = 0")
+    # sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4 exactly; SiLU multiplies by z. A constant
+    # vector has rms equal to its value, so y = 1 and out is the gate itself.
+    z = [np.log(3.0), -np.log(3.0)]
+    out = gr([[[2.0, 2.0]]], [[z]], [0.0, 0.0], 0.0, oracle.GATE_SIGMOID)[0, 0]
+    if not np.allclose(out, [0.75, 0.25], rtol=1e-14, atol=0):
+        fails.append("sigmoid(+-ln 3)")
+    out = gr([[[2.0, 2.0]]], [[z]], [0.0, 0.0], 0.0, oracle.GATE_SILU)[0, 0]
+    if not np.allclose(out, [0.75 * np.log(3.0), -0.25 * np.log(3.0)], rtol=1e-14, atol=0):
+        fails.append("silu(+-ln 3)")
+    # zero-centred scale: weight w multiplies by (1 + w), so w = 0 is the identity scale
+    out = gr([[[3.0, 4.0]]], [[[60.0, 60.0]]], [1.0, -0.5], 0.0, oracle.GATE_SIGMOID)[0, 0]
+    if not np.allclose(out, ref * np.array([2.0, 0.5]), rtol=1e-14, atol=0):
+        fails.append("scale 1 + w")
+    # one head at a time: heads with proportional values give equal outputs (eps = 0), and
+    # a change in one head leaves the other alone
+    out = gr([[[3.0, 4.0], [30.0, 40.0]]], np.full((1, 2, 2), 60.0), [0.0, 0.0], 0.0,
+             oracle.GATE_SIGMOID)[0]
+    if not (np.allclose(out[0], ref, rtol=1e-14, atol=0) and np.allclose(out[1], ref, rtol=1e-14, atol=0)):
+        fails.append("per-head norm")
+    # closed form with eps: mean(out^2) = ms / (ms + eps) for an open gate and w = 0
+    rng = np.random.Generator(np.random.PCG64(160))
+    o = rng.standard_normal((5, 3, 128)) * 0.05
+    eps = 1e-3
+    out = gr(o, np.full(o.shape, 60.0), np.zeros(128), eps, oracle.GATE_SIGMOID)
+    ms = np.mean(o * o, axis=-1)
+    if not np.allclose(np.mean(out * out, axis=-1), ms / (ms + eps), rtol=1e-12, atol=0):
+        fails.append("mean square with eps")
+    # scale invariance without eps
+    w = rng.standard_normal(128) * 0.1
+    zz = rng.standard_normal(o.shape)
+    b = gr(o * 37.0, zz, w, 0.0, oracle.GATE_SILU)
+    c = gr(o, zz, w, 0.0, oracle.GATE_SILU)
+    if not np.allclose(b, c, rtol=1e-12, atol=1e-15):
+        fails.append("scale invariance")
+    # all-zero read-out with eps > 0: zero out, no NaN
+    out = gr(np.zeros((1, 1, 128)), np.ones((1, 1, 128)), np.zeros(128), 1e-6, oracle.GATE_SIGMOID)
+    if not np.all(out == 0.0):
+        fails.append("zero read-out")
+    return fails
+
+
+def test_gated_rmsnorm_pins():
+    assert _norm_pins() == []
+
+
+def test_gated_rmsnorm_rejects_unknown_gate():
+    with pytest.raises(ValueError):
+        oracle.gated_rmsnorm(np.ones((1, 1, 4)), np.ones((1, 1, 4)), np.zeros(4), gate=2)
+
+
+_NORM_MUTATIONS = {
+    "norm: sum instead of mean": ("    ms /= d_v;\n", "    ms /= 1;\n"),
+    "norm: weight without the zero-centred 1": ("* (1.0 + weight[i]);", "* (weight[i]);"),
+    "norm: no square root": ("const double inv_rms = 1.0 / sqrt(ms + eps);",
+                             "const double inv_rms = 1.0 / (ms + eps);"),
+    "norm: over all heads of a row": ("const size_t base = ((size_t)r * h_v + h) * d_v;",
+                                      "const size_t base = ((size_t)r * h_v + 0) * d_v + (size_t)h * 0;"),
+    "gate: sign of the sigmoid": ("const double sig = 1.0 / (1.0 + exp(-zi));",
+                                  "const double sig = 1.0 / (1.0 + exp(zi));"),
+    "gate: sigmoid and SiLU swapped": ("out[base + i] = y * (gate == 0 ? sig : zi * sig);",
+                                       "out[base + i] = y * (gate == 1 ? sig : zi * sig);"),
+    "norm of the gated read-out": ("for (int i = 0; i < d_v; ++i) ms += o[base + i] * o[base + i];",
+                                   "for (int i = 0; i < d_v; ++i) { const double gz = 1.0 / (1.0 + exp(-z[base + i])); "
+                                   "ms += o[base + i] * gz * o[base + i] * gz; }"),
+}
+
+
+@pytest.fixture(scope="module")
+def norm_mutant_libs():
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "gdn_oracle.c")).read()
+    libs = {}
+    with tempfile.TemporaryDirectory() as td:
+        for name, (a, b) in _NORM_MUTATIONS.items():
+            assert src.count(a) == 1, name
+            path = os.path.join(td, "n%d.c" % len(libs))
+            with open(path, "w") as f:
+                f.write(src.replace(a, b))
+            so = path[:-2] + ".so"
+            subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                                   path, "-o", so, "-lm"])
+            libs[name] = oracle.load_library(so)
+        yield libs
+
+
+@pytest.mark.parametrize("name", sorted(_NORM_MUTATIONS))
+def test_norm_pins_catch_planted_mistake(norm_mutant_libs, name):
+    assert _norm_pins(lib=norm_mutant_libs[name]) != [], name
