@@ -322,6 +322,23 @@ def bench_channel_decay(steps, warmup, prefill_reps=5):
     return dwall, dms, pms, pms16
 
 
+def bench_epilogue(reps, warmup):
+    """The output epilogue on the prefill's read-out shape (B = 1, T = 4096, 32 V heads,
+    bf16, sigmoid gate): gdn_gated_rmsnorm back to back. Returns (vectors, device ms per
+    call)."""
+    import torch
+    import linear_attention_recurrence_amd as gdn
+    import workloads
+    o, z, w = workloads.epilogue_inputs(4096, H_V)
+    od, zd, wd = _dev(o), _dev(z), _dev(w)
+    out = torch.empty_like(od)
+
+    def call(i):
+        gdn.gdn_gated_rmsnorm(od, zd, wd, out=out)
+
+    return 4096 * H_V, _timed_batch(call, reps, warmup)
+
+
 def bench_frontend(reps, warmup):
     """64 packed sequences (lengths uniform in [128, 8192]): gdn_conv_prep then
     gdn_chunk_prefill with per-sequence initial and final states."""
@@ -407,8 +424,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--workload", default="prefill,decode,frontend",
-                    help="comma list of prefill, decode, frontend, copy")
+    ap.add_argument("--workload", default="prefill,decode,frontend,epilogue",
+                    help="comma list of prefill, decode, frontend, epilogue, copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", metavar="DIR")
     args = ap.parse_args()
@@ -539,6 +556,17 @@ def main():
             "conv_prep_GBs": conv_prep_bytes(T4) / (conv_ms / 1e3) / 1e9,
             "prefill_GBs": prefill_bytes(T4, N4, True) / (pre_ms / 1e3) / 1e9,
             "prefill_TFLOPs": prefill_flops(T4) / (pre_ms / 1e3) / 1e12}
+    if "epilogue" in work:
+        nvec, ems = bench_epilogue(200, 10)
+        eb = nvec * D * 2 * 3          # o and z read, out written, bf16
+        achieved = eb / (ems / 1e3) / 1e9
+        out["epilogue"] = {
+            "workload": "output epilogue (per-head RMS norm with the zero-centred scale, then "
+                        "the sigmoid output gate) on the read-out of B=1, T=4096, 32 V heads, bf16",
+            "ms_per_call": ems, "tokens_per_s": 4096 / (ems / 1e3),
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "kernel": "gated_rmsnorm_kernel<bf16, false>",
+                         "algorithmic_bytes": eb}}
     if "copy" in work:
         nb, cms = bench_copy(max(5, args.steps), args.warmup)
         out["copy"] = {"bytes_each_way": nb, "ms": cms, "GBs_read_plus_write": 2 * nb / (cms / 1e3) / 1e9}

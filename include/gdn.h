@@ -229,6 +229,38 @@ gdn_status gdn_conv_window_from_prefill(const void* mixed_qkv, int32_t conv_kern
                                         int32_t d_k, int32_t d_v, void* conv_window,
                                         const int32_t* window_slots, void* stream);
 
+/* Output gate function of gdn_gated_rmsnorm. */
+typedef enum {
+    GDN_GATE_SIGMOID = 0,     /* sigmoid(z) */
+    GDN_GATE_SILU = 1         /* z * sigmoid(z) */
+} gdn_gate;
+
+/*
+ * Output epilogue after the mixer. The architecture knowledge-base page "Qwen3-Next
+ * 80B-A3B" names the model's norm in its "Architecture" table (row "Norm type") as a
+ * zero-centred RMSNorm, and section "01 . GatedDeltaNet(config)" of page "Qwen3-Next
+ * 80B-A3B -- The Evolving Transformer" says a gate decides how much of the recurrent
+ * read-out reaches the output. Neither gives a formula; this computes, for every token row
+ * r and V head h, with x = o[r][h][:] and the gate input z[r][h][:],
+ *
+ *     out = x / sqrt(mean(x^2) + eps) * (1 + weight) * gate(z)     (elementwise)
+ *
+ * i.e. the norm over one head's d_v channels with the zero-centred scale, then the gate.
+ *
+ *   o, z, out   [rows][h_v][d_v] in io_dtype (GDN_BF16 or GDN_F32); out may be o or z
+ *               itself (in place); other overlaps are not allowed
+ *   weight      [d_v] fp32, shared by the heads (0 means a scale of 1)
+ *   eps         finite and >= 0
+ *   gate        GDN_GATE_SIGMOID or GDN_GATE_SILU
+ * d_v must be 128; arithmetic in fp32, bf16 outputs rounded to nearest even.
+ * GDN_ERR_SHAPE for negative rows, h_v < 1 or a bad eps; GDN_ERR_UNSUPPORTED for another
+ * d_v, dtype or gate, or more than 2^34 vectors; GDN_ERR_NULL for a missing pointer when
+ * rows > 0. rows = 0 does nothing.
+ */
+gdn_status gdn_gated_rmsnorm(const void* o, const void* z, gdn_dtype io_dtype, const float* weight,
+                             int32_t rows, int32_t h_v, int32_t d_v, float eps, gdn_gate gate,
+                             void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,7 @@ GDN_BF16, GDN_F32 = 0, 1
 EXPORTED = ("gdn_status_string", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill",
             "gdn_decode_step", "gdn_verify_step", "gdn_channel_decay_prefill",
             "gdn_channel_decay_decode_step", "gdn_conv_prep", "gdn_conv_decode_step",
-            "gdn_conv_window_from_prefill")
+            "gdn_conv_window_from_prefill", "gdn_gated_rmsnorm")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -71,6 +71,9 @@ def load(path: Optional[str] = None):
                                          _P, _P, _P, _P]
     lib.gdn_conv_window_from_prefill.restype = ctypes.c_int
     lib.gdn_conv_window_from_prefill.argtypes = [_P, _I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]
+    lib.gdn_gated_rmsnorm.restype = ctypes.c_int
+    lib.gdn_gated_rmsnorm.argtypes = [_P, _P, ctypes.c_int, _P, _I, _I, _I, ctypes.c_float,
+                                      ctypes.c_int, _P, _P]
     if path is None:
         _lib = lib
     return lib
@@ -339,3 +342,24 @@ def gdn_conv_window_from_prefill(mixed_qkv, conv_kernel, cu_seqlens, conv_window
                                              d_k, d_v, _ptr(conv_window) if K > 1 else None,
                                              _ptr(window_slots), _stream(stream))
     _check(st, "gdn_conv_window_from_prefill")
+
+
+GATES = {"sigmoid": 0, "silu": 1}
+
+
+def gdn_gated_rmsnorm(o, z, weight, eps=1e-6, gate="sigmoid", out=None, stream=None):
+    """Output epilogue: per V head, o / rms(o) * (1 + weight) * gate(z). o, z [T][h_v][d_v]
+    (bf16 or fp32, same dtype); weight [d_v] fp32; gate "sigmoid" or "silu". out may be o
+    or z (in place). Returns out."""
+    T, h_v, d_v = o.shape
+    if out is None:
+        out = torch.empty_like(o)
+    _expect(z, (T, h_v, d_v), o.dtype, "z")
+    _expect(weight, (d_v,), torch.float32, "weight")
+    _expect(out, (T, h_v, d_v), o.dtype, "out")
+    if gate not in GATES:
+        raise ValueError("gate must be one of %s" % sorted(GATES))
+    st = load().gdn_gated_rmsnorm(_ptr(o), _ptr(z), _dtype_code(o), _ptr(weight), T, h_v, d_v,
+                                  float(eps), GATES[gate], _ptr(out), _stream(stream))
+    _check(st, "gdn_gated_rmsnorm")
+    return out

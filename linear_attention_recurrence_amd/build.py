@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 ARCH = "gfx950"
-SOURCES = ["recurrent.hip", "conv_prep.hip", "chunk_prefill.hip", "gdn_api.cpp"]
+SOURCES = ["recurrent.hip", "conv_prep.hip", "chunk_prefill.hip", "epilogue.hip", "gdn_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]

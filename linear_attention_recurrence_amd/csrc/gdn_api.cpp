@@ -2,6 +2,7 @@
 //
 // Every entry point validates its arguments before touching the HIP runtime, so a rejected
 // call launches nothing and writes nothing. Launch errors are reported as GDN_ERR_HIP.
+#include <cmath>
 #include "gdn.h"
 
 #include <hip/hip_runtime.h>
@@ -188,6 +189,23 @@ gdn_status gdn_conv_window_from_prefill(const void* mixed_qkv, int32_t conv_kern
   return from_hip(gdn::launch_conv_window(mixed_qkv, conv_kernel, cu_seqlens, num_seqs, h_qk, h_v,
                                           conv_window, window_slots,
                                           static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_gated_rmsnorm(const void* o, const void* z, gdn_dtype io_dtype, const float* weight,
+                             int32_t rows, int32_t h_v, int32_t d_v, float eps, gdn_gate gate,
+                             void* out, void* stream) {
+  if (rows < 0 || h_v < 1 || d_v < 1) return GDN_ERR_SHAPE;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return GDN_ERR_SHAPE;
+  if (d_v != 128) return GDN_ERR_UNSUPPORTED;
+  if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (gate != GDN_GATE_SIGMOID && gate != GDN_GATE_SILU) return GDN_ERR_UNSUPPORTED;
+  const long long n_vec = (long long)rows * h_v;
+  if (n_vec > (1LL << 34)) return GDN_ERR_UNSUPPORTED;
+  if (rows == 0) return GDN_OK;
+  if (!o || !z || !weight || !out) return GDN_ERR_NULL;
+  return from_hip(gdn::launch_gated_rmsnorm(o, z, io_dtype == GDN_BF16, weight, n_vec, eps,
+                                            gate == GDN_GATE_SILU,
+                                            out, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -55,6 +55,26 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Lane exchanges within a half-wave without the LDS crossbar where the pattern stays inside
+// a 16-lane row: the value of lane l ^ m, by DPP for m = 1 and 2 (quad permutes), 4 (half-row
+// mirror, then quad reversal: l ^ 7 ^ 3), 8 (row rotation by 8), and by ds_swizzle (xor mask
+// within 32 lanes) for m = 16. Pure data movement: sums built from it are unchanged. Every
+// DPP pattern here reads a lane of the same row and all rows and banks are written, so the
+// move needs no old value (none is materialised) and the bound control never applies.
+__device__ __forceinline__ float xor_lane(float x, int m) {
+  const int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (m) {
+    case 1: r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true); break;
+    case 4: r = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true),
+                                         0x1B, 0xF, 0xF, true); break;
+    case 8: r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true); break;
+    default: r = __builtin_amdgcn_ds_swizzle(v, 0x401F); break;   // m = 16
+  }
+  return __builtin_bit_cast(float, r);
+}
+
 // Sum over the 32 lanes of each half-wave; every lane receives its half's total.
 __device__ __forceinline__ float half_wave_sum(float x) {
   x += __shfl_xor(x, 16, 32);

@@ -31,6 +31,12 @@ hipError_t launch_channel_decode(const void* q, const void* k, const void* v, bo
                                  int num_seqs, int h_qk, int h_v, float scale, void* o,
                                  hipStream_t stream);
 
+// Output epilogue: per-head RMS norm with the zero-centred scale, then the output gate, over
+// n_vec vectors of 128 channels (epilogue.hip).
+hipError_t launch_gated_rmsnorm(const void* o, const void* z, bool io_bf16, const float* weight,
+                                long long n_vec, float eps, bool silu, void* out,
+                                hipStream_t stream);
+
 // Token-sequential prefill with the state on chip (recurrent.hip); used for fp32 I/O.
 hipError_t launch_recurrent_prefill(const void* q, const void* k, const void* v, bool io_bf16,
                                     const float* g, const float* beta, const int32_t* cu_seqlens,

@@ -49,26 +49,6 @@ struct RecArgs {
   float scale;
 };
 
-// Lane exchanges within a half-wave without the LDS crossbar where the pattern stays inside
-// a 16-lane row: the value of lane l ^ m, by DPP for m = 1 and 2 (quad permutes), 4 (half-row
-// mirror, then quad reversal: l ^ 7 ^ 3), 8 (row rotation by 8), and by ds_swizzle (xor mask
-// within 32 lanes) for m = 16. Pure data movement: sums built from it are unchanged. Every
-// DPP pattern here reads a lane of the same row and all rows and banks are written, so the
-// move needs no old value (none is materialised) and the bound control never applies.
-__device__ __forceinline__ float xor_lane(float x, int m) {
-  const int v = __builtin_bit_cast(int, x);
-  int r;
-  switch (m) {
-    case 1: r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true); break;
-    case 2: r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true); break;
-    case 4: r = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true),
-                                         0x1B, 0xF, 0xF, true); break;
-    case 8: r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true); break;
-    default: r = __builtin_amdgcn_ds_swizzle(v, 0x401F); break;   // m = 16
-  }
-  return __builtin_bit_cast(float, r);
-}
-
 // Value of lane `src` (a constant below 32) of this lane's half-wave: two lane reads into
 // scalars and a select, instead of a crossbar permute.
 __device__ __forceinline__ float half_lane(float x, int src, bool upper) {

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
                                             "gdn_channel_decay_prefill",
                                             "gdn_channel_decay_decode_step",
                                             "gdn_conv_prep", "gdn_conv_decode_step",
-                                            "gdn_conv_window_from_prefill"])
+                                            "gdn_conv_window_from_prefill", "gdn_gated_rmsnorm"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -241,6 +241,36 @@ def test_conv_window_validation():
     assert call(n=0) == L.GDN_ERR_SHAPE
     assert call(n=0, T=0) == L.GDN_OK
     assert call(K=1, win=None) == L.GDN_OK
+
+
+def test_gated_rmsnorm_validation():
+    lib, L = _lib()
+    f = lib.gdn_gated_rmsnorm
+    P = _fake
+    ok = dict(o=P(1), z=P(2), dt=L.GDN_BF16, w=P(3), rows=10, hv=32, dv=128, eps=1e-6, gate=0,
+              out=P(4), st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["o"], a["z"], a["dt"], a["w"], a["rows"], a["hv"], a["dv"], a["eps"],
+                 a["gate"], a["out"], a["st"])
+
+    assert call(o=None) == L.GDN_ERR_NULL
+    assert call(z=None) == L.GDN_ERR_NULL
+    assert call(w=None) == L.GDN_ERR_NULL
+    assert call(out=None) == L.GDN_ERR_NULL
+    assert call(rows=-1) == L.GDN_ERR_SHAPE
+    assert call(hv=0) == L.GDN_ERR_SHAPE
+    assert call(eps=-1.0) == L.GDN_ERR_SHAPE
+    assert call(eps=float("nan")) == L.GDN_ERR_SHAPE
+    assert call(eps=float("inf")) == L.GDN_ERR_SHAPE
+    assert call(dv=64) == L.GDN_ERR_UNSUPPORTED
+    assert call(dt=7) == L.GDN_ERR_UNSUPPORTED
+    assert call(gate=2) == L.GDN_ERR_UNSUPPORTED
+    assert call(rows=2 ** 31 - 1, hv=2 ** 20) == L.GDN_ERR_UNSUPPORTED
+    assert call(rows=0) == L.GDN_OK
+    assert call(rows=0, o=None, z=None, w=None, out=None) == L.GDN_OK
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

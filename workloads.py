@@ -292,3 +292,18 @@ def config4_lengths(seed=1004, num_seqs=64, lo=128, hi=8192):
 def config4(seed=1004) -> FrontEndInputs:
     """64 sequences, lengths uniform in [128, 8192], mixed bf16 [sum T][8192], conv k=4."""
     return make_frontend(config4_lengths(seed), seed=seed + 100)
+
+
+def epilogue_inputs(rows: int, h_v: int = H_V, d_v: int = D_HEAD, io_dtype: str = "bf16",
+                    seed: int = 1012):
+    """Inputs of the output epilogue: a read-out o whose (token, head) vectors span eight
+    e-folds of size (as a mixer's read-out does across heads and positions), a gate input z
+    ~ N(0, 3^2) and a small zero-centred scale w ~ N(0, 0.1^2) [d_v] fp32. o and z are bf16
+    bit patterns for io_dtype "bf16", else fp32. Returns (o, z, w)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    o = rng.standard_normal((rows, h_v, d_v)) * np.exp(rng.uniform(-6, 2, (rows, h_v, 1)))
+    z = rng.standard_normal((rows, h_v, d_v)) * 3.0
+    w = (rng.standard_normal(d_v) * 0.1).astype(np.float32)
+    if io_dtype == "bf16":
+        return f32_to_bf16_bits(o.astype(np.float32)), f32_to_bf16_bits(z.astype(np.float32)), w
+    return o.astype(np.float32), z.astype(np.float32), w
