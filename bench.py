@@ -324,17 +324,27 @@ def bench_channel_decay(steps, warmup, prefill_reps=5):
 
 def bench_epilogue(reps, warmup):
     """The output epilogue on the prefill's read-out shape (B = 1, T = 4096, 32 V heads,
-    bf16, sigmoid gate): gdn_gated_rmsnorm back to back. Returns (vectors, device ms per
-    call)."""
+    bf16, sigmoid gate): gdn_gated_rmsnorm back to back over four input sets in turn (400
+    MB, more than the last-level cache holds). Returns (vectors, device ms per call)."""
     import torch
     import linear_attention_recurrence_amd as gdn
     import workloads
-    o, z, w = workloads.epilogue_inputs(4096, H_V)
-    od, zd, wd = _dev(o), _dev(z), _dev(w)
-    out = torch.empty_like(od)
+    sets = []
+    for s in range(4):
+        o, z, w = workloads.epilogue_inputs(4096, H_V, seed=1012 + s)
+        od = _dev(o)
+        sets.append((od, _dev(z), _dev(w), torch.empty_like(od)))
+
+    gdn.gdn_gated_rmsnorm(*sets[0][:3], out=sets[0][3])     # argument checks once
+    # The timed loop calls the C entry point with its arguments prepared: a 20 us kernel is
+    # shorter than the binding's per-call checks, which would otherwise set the pace.
+    lib = gdn.load()
+    args = [(od.data_ptr(), zd.data_ptr(), 0, wd.data_ptr(), 4096, H_V, D, 1e-6, 0, out.data_ptr(),
+             torch.cuda.current_stream().cuda_stream) for od, zd, wd, out in sets]
+    fn = lib.gdn_gated_rmsnorm
 
     def call(i):
-        gdn.gdn_gated_rmsnorm(od, zd, wd, out=out)
+        fn(*args[i % 4])
 
     return 4096 * H_V, _timed_batch(call, reps, warmup)
 
@@ -562,7 +572,8 @@ def main():
         achieved = eb / (ems / 1e3) / 1e9
         out["epilogue"] = {
             "workload": "output epilogue (per-head RMS norm with the zero-centred scale, then "
-                        "the sigmoid output gate) on the read-out of B=1, T=4096, 32 V heads, bf16",
+                        "the sigmoid output gate) on the read-out of B=1, T=4096, 32 V heads, bf16; "
+                        "four input sets in turn",
             "ms_per_call": ems, "tokens_per_s": 4096 / (ems / 1e3),
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "kernel": "gated_rmsnorm_kernel<bf16, false>",
