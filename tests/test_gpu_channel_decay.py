@@ -64,6 +64,28 @@ def test_channel_prefill_many_pairs(io):
     np.testing.assert_array_equal(fin[0], x.initial_state[0].astype(np.float64))
 
 
+def test_channel_prefill_shape_boundary():
+    """64 (sequence, V head) pairs take the 4-row shape and 65 the 8-row one: the same two
+    sequences run alone (2 x 32 pairs) and beside a third (3 x 32 pairs) agree to rounding,
+    and both match the oracle."""
+    lens = [150, 77]
+    x3 = workloads.make_prefill(lens + [33], h_qk=16, h_v=32, with_initial_state=True, seed=158)
+    g3 = workloads.channel_log_alpha(x3.total_tokens, 32, 128, seed=159)
+    T2 = sum(lens)
+    x2 = workloads.PrefillInputs(q=x3.q[:T2], k=x3.k[:T2], v=x3.v[:T2], g=x3.g[:T2],
+                                 beta=x3.beta[:T2], cu_seqlens=x3.cu_seqlens[:3].copy(),
+                                 initial_state=x3.initial_state[:2], scale=x3.scale,
+                                 io_dtype="bf16")
+    o3, f3 = _run_prefill(x3, g3)
+    o2, f2 = _run_prefill(x2, g3[:T2])
+    check_outputs(o2, o3[:T2], "2 vs 3 sequences")
+    check_state(f2, f3[:2], "2 vs 3 sequences")
+    ref_o, ref_s = _oracle(x2, g3[:T2])
+    check_outputs(o2, ref_o, "64 pairs")
+    check_state(f2, ref_s, "64 pairs")
+    assert np.isfinite(o3).all()
+
+
 def test_channel_prefill_model_size():
     """B = 1, T = 1024, 16 QK / 32 V heads, bf16, S0 ~ N(0, 0.02): every head against the oracle."""
     x = workloads.make_prefill([1024], with_initial_state=True, seed=152)
