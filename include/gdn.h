@@ -27,8 +27,14 @@
  *    launched; on a nonzero status nothing has been written. A failed launch returns
  *    GDN_ERR_HIP. Nothing is thrown across the ABI.
  *  - Device-side contracts that the host cannot check without a synchronisation:
- *    cu_seqlens is nondecreasing from 0 to total_tokens, and state_slots holds distinct
- *    indices below the pool size. Breaking them is undefined behaviour.
+ *    cu_seqlens is nondecreasing from 0 to total_tokens, and state_slots (and
+ *    window_slots) hold distinct indices below the pool size. Breaking them is undefined
+ *    behaviour. For debugging a caller, the environment variable GDN_CHECK_CONTRACTS=1
+ *    makes every call copy these arrays to the host on its stream and wait for them (the
+ *    one case where the library synchronises), and return GDN_ERR_SHAPE, with nothing
+ *    launched, for a cu_seqlens that does not start at 0, decreases or does not end at
+ *    total_tokens, or for negative or repeated slots (the pool size is not passed, so its
+ *    bound stays the caller's). A failed copy returns GDN_ERR_HIP.
  */
 #ifndef GDN_H
 #define GDN_H

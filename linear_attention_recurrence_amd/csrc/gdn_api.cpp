@@ -2,7 +2,10 @@
 //
 // Every entry point validates its arguments before touching the HIP runtime, so a rejected
 // call launches nothing and writes nothing. Launch errors are reported as GDN_ERR_HIP.
+#include <algorithm>
 #include <cmath>
+#include <cstdlib>
+#include <vector>
 #include "gdn.h"
 
 #include <hip/hip_runtime.h>
@@ -23,6 +26,55 @@ gdn_status check_common(int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v) {
 }
 
 gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+// Opt-in checks of the device-side contracts, for debugging a caller: with the environment
+// variable GDN_CHECK_CONTRACTS set to 1, the index arrays are copied to the host on the
+// call's stream and waited for (so such a call synchronises its stream), and a violation
+// returns GDN_ERR_SHAPE before anything is launched. Off, nothing is read.
+bool contract_checks() {
+  const char* e = std::getenv("GDN_CHECK_CONTRACTS");
+  return e && e[0] == '1' && e[1] == '\0';
+}
+
+gdn_status fetch_ints(const int32_t* src, int32_t n, void* stream, std::vector<int32_t>& out) {
+  out.resize((size_t)n);
+  if (n == 0) return GDN_OK;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(out.data(), src, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, st) != hipSuccess)
+    return GDN_ERR_HIP;
+  return hipStreamSynchronize(st) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+// cu_seqlens[0] = 0, nondecreasing, cu_seqlens[num_seqs] = total_tokens.
+gdn_status check_seqlens(const int32_t* cu, int32_t num_seqs, int32_t total_tokens, void* stream) {
+  if (!contract_checks()) return GDN_OK;
+  std::vector<int32_t> h;
+  const gdn_status st = fetch_ints(cu, num_seqs + 1, stream, h);
+  if (st != GDN_OK) return st;
+  if (h[0] != 0 || h[(size_t)num_seqs] != total_tokens) return GDN_ERR_SHAPE;
+  for (int32_t i = 0; i < num_seqs; ++i)
+    if (h[(size_t)i + 1] < h[(size_t)i]) return GDN_ERR_SHAPE;
+  return GDN_OK;
+}
+
+// Slot indices non-negative and distinct (the pool size is not passed, so the upper bound
+// stays the caller's).
+gdn_status check_slots(const int32_t* slots, int32_t num_seqs, void* stream) {
+  if (!slots || !contract_checks()) return GDN_OK;
+  std::vector<int32_t> h;
+  const gdn_status st = fetch_ints(slots, num_seqs, stream, h);
+  if (st != GDN_OK) return st;
+  std::sort(h.begin(), h.end());
+  for (size_t i = 0; i < h.size(); ++i)
+    if (h[i] < 0 || (i > 0 && h[i] == h[i - 1])) return GDN_ERR_SHAPE;
+  return GDN_OK;
+}
+
+#define GDN_TRY(expr)                      \
+  do {                                     \
+    const gdn_status gdn_st_ = (expr);     \
+    if (gdn_st_ != GDN_OK) return gdn_st_; \
+  } while (0)
 
 }  // namespace
 
@@ -60,6 +112,7 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dt
   if (!cu_seqlens) return GDN_ERR_NULL;
   if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
   if (!final_state && total_tokens == 0) return GDN_OK;   // nothing observable to do
+  GDN_TRY(check_seqlens(cu_seqlens, num_seqs, total_tokens, stream));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (io_dtype == GDN_F32)
     return from_hip(gdn::launch_recurrent_prefill(q, k, v, false, g, beta, cu_seqlens, num_seqs,
@@ -83,6 +136,7 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtyp
   if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
   if (num_seqs == 0) return GDN_OK;
   if (!q || !k || !v || !g || !beta || !state_pool || !o) return GDN_ERR_NULL;
+  GDN_TRY(check_slots(state_slots, num_seqs, stream));
   return from_hip(gdn::launch_decode(q, k, v, io_dtype == GDN_BF16, g, beta, state_pool,
                                      state_slots, num_seqs, h_qk, h_v, scale, o,
                                      static_cast<hipStream_t>(stream)));
@@ -99,6 +153,7 @@ gdn_status gdn_verify_step(const void* q, const void* k, const void* v, gdn_dtyp
   if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0) return GDN_OK;
   if (!q || !k || !v || !g || !beta || !state_pool || !o) return GDN_ERR_NULL;
+  GDN_TRY(check_slots(state_slots, num_seqs, stream));
   return from_hip(gdn::launch_verify(q, k, v, io_dtype == GDN_BF16, g, beta, state_pool,
                                      state_slots, snapshots, num_seqs, num_tokens, h_qk, h_v,
                                      scale, o, static_cast<hipStream_t>(stream)));
@@ -118,6 +173,7 @@ gdn_status gdn_channel_decay_prefill(const void* q, const void* k, const void* v
   if (!cu_seqlens) return GDN_ERR_NULL;
   if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
   if (!final_state && total_tokens == 0) return GDN_OK;   // nothing observable to do
+  GDN_TRY(check_seqlens(cu_seqlens, num_seqs, total_tokens, stream));
   return from_hip(gdn::launch_channel_prefill(q, k, v, io_dtype == GDN_BF16, g, beta, cu_seqlens,
                                               num_seqs, h_qk, h_v, scale, initial_state,
                                               final_state, o, static_cast<hipStream_t>(stream)));
@@ -134,6 +190,7 @@ gdn_status gdn_channel_decay_decode_step(const void* q, const void* k, const voi
   if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
   if (num_seqs == 0) return GDN_OK;
   if (!q || !k || !v || !g || !beta || !state_pool || !o) return GDN_ERR_NULL;
+  GDN_TRY(check_slots(state_slots, num_seqs, stream));
   return from_hip(gdn::launch_channel_decode(q, k, v, io_dtype == GDN_BF16, g, beta, state_pool,
                                              state_slots, num_seqs, h_qk, h_v, scale, o,
                                              static_cast<hipStream_t>(stream)));
@@ -151,6 +208,7 @@ gdn_status gdn_conv_prep(const void* mixed_qkv, const float* conv_weight, int32_
   if (num_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
   if (total_tokens == 0) return GDN_OK;
   if (!mixed_qkv || !conv_weight || !cu_seqlens || !q || !k || !v) return GDN_ERR_NULL;
+  GDN_TRY(check_seqlens(cu_seqlens, num_seqs, total_tokens, stream));
   return from_hip(gdn::launch_conv_prep(mixed_qkv, conv_weight, conv_kernel, cu_seqlens, num_seqs,
                                         total_tokens, h_qk, h_v, q_scale, q, k, v,
                                         static_cast<hipStream_t>(stream)));
@@ -168,6 +226,7 @@ gdn_status gdn_conv_decode_step(const void* mixed_qkv, const float* conv_weight,
   if (num_seqs == 0) return GDN_OK;
   if (!mixed_qkv || !conv_weight || !q || !k || !v) return GDN_ERR_NULL;
   if (conv_kernel > 1 && !conv_window) return GDN_ERR_NULL;
+  GDN_TRY(check_slots(window_slots, num_seqs, stream));
   return from_hip(gdn::launch_conv_decode(mixed_qkv, conv_weight, conv_kernel, conv_window,
                                           window_slots, num_seqs, h_qk, h_v, q_scale, q, k, v,
                                           static_cast<hipStream_t>(stream)));
@@ -186,6 +245,8 @@ gdn_status gdn_conv_window_from_prefill(const void* mixed_qkv, int32_t conv_kern
   if (num_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
   if (conv_kernel == 1) return GDN_OK;   // no window
   if (!cu_seqlens || !conv_window || (total_tokens > 0 && !mixed_qkv)) return GDN_ERR_NULL;
+  GDN_TRY(check_seqlens(cu_seqlens, num_seqs, total_tokens, stream));
+  GDN_TRY(check_slots(window_slots, num_seqs, stream));
   return from_hip(gdn::launch_conv_window(mixed_qkv, conv_kernel, cu_seqlens, num_seqs, h_qk, h_v,
                                           conv_window, window_slots,
                                           static_cast<hipStream_t>(stream)));
