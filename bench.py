@@ -222,7 +222,8 @@ def conv_decode_bytes(num_seqs: int, K=4, h_qk=H_QK, h_v=H_V) -> float:
 def bench_decode_front_end(steps, warmup):
     """256 sequences x 1 token: gdn_conv_decode_step over a [256][3][8192] bf16 window pool,
     then gdn_decode_step on its q, k and v over the 512 MiB state pool; a ring of 16 input
-    sets. Returns (conv ms per call, wall seconds and ms per step of both)."""
+    sets; and gdn_decode_step_with_conv, the two in one launch. Returns (conv ms per call,
+    wall seconds and ms per step of the two calls, the same for the one-launch form)."""
     import torch
     import linear_attention_recurrence_amd as gdn
     import workloads
@@ -246,9 +247,14 @@ def bench_decode_front_end(steps, warmup):
         conv(i)
         gdn.gdn_decode_step(q, k, v, g[i % 16], b[i % 16], pool, 1.0, o=o)
 
+    def fused(i):
+        gdn.gdn_decode_step_with_conv(mixed[i % 16], w, win, g[i % 16], b[i % 16], pool, H_QK, H_V,
+                                      D, D, fe.q_scale, 1.0, o=o)
+
     conv_ms = _timed_batch(conv, steps, warmup)
     wall, both_ms = _timed(both, steps, warmup)
-    return conv_ms, wall, both_ms
+    fwall, fused_ms = _timed(fused, steps, warmup)
+    return conv_ms, wall, both_ms, fwall, fused_ms
 
 
 def verify_bytes(num_seqs: int, n_tok: int, snapshots: bool, h_qk=H_QK, h_v=H_V) -> float:
@@ -501,7 +507,8 @@ def main():
                          "algorithmic_bytes": dbytes}}
     if "decode" in work:
         dsteps = args.decode_steps
-        cms, fwall, fms = bench_decode_front_end(dsteps, args.warmup)
+        cms, fwall, fms, uwall, ums = bench_decode_front_end(dsteps, args.warmup)
+        ubytes = decode_bytes(256) + conv_decode_bytes(256) - 256 * (2 * H_QK + H_V) * D * 2 * 2
         cbytes = conv_decode_bytes(256)
         out["decode_front_end"] = {
             "workload": "decode step with the front end, 256 sequences x 1 token: conv k=4 over "
@@ -511,7 +518,14 @@ def main():
             "tokens_per_s": 256 * dsteps / fwall,
             "conv_decode": {"kernel": "conv_decode_kernel", "kernel_ms_back_to_back": cms,
                             "algorithmic_bytes": cbytes,
-                            "achieved_GBs": cbytes / (cms / 1e3) / 1e9}}
+                            "achieved_GBs": cbytes / (cms / 1e3) / 1e9},
+            "one_launch": {"entry_point": "gdn_decode_step_with_conv", "ms_per_step": uwall * 1e3 / dsteps,
+                           "tokens_per_s": 256 * dsteps / uwall, "kernel": "decode_conv_kernel<2>",
+                           "kernel_ms": ums,
+                           "roofline": {"bound": "hbm", "achieved": ubytes / (ums / 1e3) / 1e9,
+                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                        "frac": ubytes / (ums / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                        "algorithmic_bytes": ubytes}}}
     if "decode" in work:
         vsteps = max(20, args.decode_steps // 10)
         res = bench_verify(vsteps, args.warmup)

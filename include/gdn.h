@@ -224,6 +224,29 @@ gdn_status gdn_conv_decode_step(const void* mixed_qkv, const float* conv_weight,
                                 void* q, void* k, void* v, void* stream);
 
 /*
+ * gdn_conv_decode_step followed by gdn_decode_step, in one launch: the front end of section
+ * "01 . GatedDeltaNet(config)" of the Evolving Transformer page at one new token per
+ * sequence, then one step of the rule of section "Correcting a memory instead of adding to
+ * it" of page "Qwen3-Next -- How a running memory and a searchable history cooperate", with
+ * the front end's q, k and v kept on chip. Outputs, the state pool and the window pool are
+ * bit for bit those of the two calls; q, k and v are not written out.
+ *
+ *   mixed_qkv, conv_weight, conv_kernel, conv_window, window_slots, q_scale
+ *                 as for gdn_conv_decode_step
+ *   g, beta, state_pool, state_slots, scale, o
+ *                 as for gdn_decode_step (bf16 output)
+ * h_v / h_qk must be 1 or 2 (one workgroup covers the V heads of a QK head, so the shared q
+ * and k channels of the window are read and shifted once); GDN_ERR_UNSUPPORTED otherwise.
+ */
+gdn_status gdn_decode_step_with_conv(const void* mixed_qkv, const float* conv_weight,
+                                     int32_t conv_kernel, void* conv_window,
+                                     const int32_t* window_slots, float q_scale, const float* g,
+                                     const float* beta, float* state_pool,
+                                     const int32_t* state_slots, int32_t num_seqs, int32_t h_qk,
+                                     int32_t h_v, int32_t d_k, int32_t d_v, float scale, void* o,
+                                     void* stream);
+
+/*
  * The window a prefill leaves for gdn_conv_decode_step: for each sequence n of the packed
  * batch (cu_seqlens as for gdn_conv_prep), its last conv_kernel-1 inputs from mixed_qkv,
  * with zeros for positions before the sequence start, written to slot window_slots[n]

@@ -22,7 +22,7 @@ GDN_BF16, GDN_F32 = 0, 1
 EXPORTED = ("gdn_status_string", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill",
             "gdn_decode_step", "gdn_verify_step", "gdn_channel_decay_prefill",
             "gdn_channel_decay_decode_step", "gdn_conv_prep", "gdn_conv_decode_step",
-            "gdn_conv_window_from_prefill", "gdn_gated_rmsnorm")
+            "gdn_conv_window_from_prefill", "gdn_gated_rmsnorm", "gdn_decode_step_with_conv")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -71,6 +71,9 @@ def load(path: Optional[str] = None):
                                          _P, _P, _P, _P]
     lib.gdn_conv_window_from_prefill.restype = ctypes.c_int
     lib.gdn_conv_window_from_prefill.argtypes = [_P, _I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]
+    lib.gdn_decode_step_with_conv.restype = ctypes.c_int
+    lib.gdn_decode_step_with_conv.argtypes = [_P, _P, _I, _P, _P, ctypes.c_float, _P, _P, _P, _P,
+                                              _I, _I, _I, _I, _I, ctypes.c_float, _P, _P]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [_P, _P, ctypes.c_int, _P, _I, _I, _I, ctypes.c_float,
                                       ctypes.c_int, _P, _P]
@@ -363,3 +366,33 @@ def gdn_gated_rmsnorm(o, z, weight, eps=1e-6, gate="sigmoid", out=None, stream=N
                                   float(eps), GATES[gate], _ptr(out), _stream(stream))
     _check(st, "gdn_gated_rmsnorm")
     return out
+
+
+def gdn_decode_step_with_conv(mixed_qkv, conv_weight, conv_window, g, beta, state_pool, h_qk, h_v,
+                              d_k, d_v, q_scale, scale, window_slots=None, state_slots=None,
+                              o=None, stream=None):
+    """gdn_conv_decode_step then gdn_decode_step in one launch (bit for bit the same results);
+    mixed_qkv [N][C] bf16, conv_weight [C][K] fp32, conv_window [P][K-1][C] bf16 (or None for
+    K = 1), g, beta [N][h_v] fp32, state_pool [P'][h_v][d_v][d_k] fp32. Returns o
+    [N][h_v][d_v] bf16."""
+    N, C = mixed_qkv.shape
+    K = conv_weight.shape[1]
+    if o is None:
+        o = torch.empty((N, h_v, d_v), dtype=torch.bfloat16, device=mixed_qkv.device)
+    _expect(mixed_qkv, (N, 2 * h_qk * d_k + h_v * d_v), torch.bfloat16, "mixed_qkv")
+    _expect(conv_weight, (C, K), torch.float32, "conv_weight")
+    if conv_window is not None:
+        _expect(conv_window, (conv_window.shape[0], K - 1, C), torch.bfloat16, "conv_window")
+    _expect(g, (N, h_v), torch.float32, "g")
+    _expect(beta, (N, h_v), torch.float32, "beta")
+    _expect(state_pool, (state_pool.shape[0], h_v, d_v, d_k), torch.float32, "state_pool")
+    _expect(o, (N, h_v, d_v), torch.bfloat16, "o")
+    for name, sl in (("window_slots", window_slots), ("state_slots", state_slots)):
+        if sl is not None:
+            _expect(sl, (N,), torch.int32, name)
+    st = load().gdn_decode_step_with_conv(_ptr(mixed_qkv), _ptr(conv_weight), K, _ptr(conv_window),
+                                          _ptr(window_slots), float(q_scale), _ptr(g), _ptr(beta),
+                                          _ptr(state_pool), _ptr(state_slots), N, h_qk, h_v, d_k,
+                                          d_v, float(scale), _ptr(o), _stream(stream))
+    _check(st, "gdn_decode_step_with_conv")
+    return o

@@ -17,6 +17,7 @@
 // cover one 128-channel head, so the head norm is a 16-lane reduction. A block covers 2048
 // channels x R tokens. (R = 32 with cached loads ran at 4.0 TB/s; R = 128 with
 // non-temporal loads at 4.7 TB/s, on 64 packed sequences of 128..8192 tokens.)
+#include "conv_device.h"
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -68,57 +69,6 @@ __device__ int find_sequence(const int32_t* cu, int num_seqs, int t) {
   // zero-length sequences share their start with the next one; cu[lo] <= t holds and the
   // search picked the last such n, whose end lies beyond t
   return lo;
-}
-
-// The taps of this thread's 8 channels: wt[0][e] multiplies the current token, wt[d][e] the
-// token d positions earlier (zero past the kernel size K).
-__device__ __forceinline__ void load_taps(const float* w, int K, int c0, float (&wt)[4][8]) {
-  if (K == 4) {   // the model's kernel: each channel's taps are one 16-byte load
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const f32x4 t = *reinterpret_cast<const f32x4*>(w + (size_t)(c0 + e) * 4);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) wt[d][e] = t[3 - d];
-    }
-    return;
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) wt[d][e] = (d < K) ? w[(size_t)(c0 + e) * K + (K - 1 - d)] : 0.f;
-  }
-}
-
-// One token of this thread's 8 channels from its input x0 and the inputs h1, h2, h3 one,
-// two and three tokens earlier: the convolution, SiLU and, for q and k heads, the head's L2
-// normalisation over the 16 lanes that share the head (and the q scale). The prefill and
-// decode kernels both produce every output through this function.
-__device__ __forceinline__ bf16x8 conv_token(const float (&wt)[4][8], const float (&x0)[8], const float (&h1)[8],
-                                             const float (&h2)[8], const float (&h3)[8], bool is_q, bool is_k,
-                                             float q_scale) {
-  float z[8];
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float y = wt[0][e] * x0[e] + wt[1][e] * h1[e] + wt[2][e] * h2[e] + wt[3][e] * h3[e];
-    z[e] = y * __builtin_amdgcn_rcpf(1.f + __expf(-y));   // hardware 1-ulp reciprocal
-    ss += z[e] * z[e];
-  }
-  bf16x8 out;
-  if (is_q || is_k) {
-    ss += __shfl_xor(ss, 8, 16);
-    ss += __shfl_xor(ss, 4, 16);
-    ss += __shfl_xor(ss, 2, 16);
-    ss += __shfl_xor(ss, 1, 16);
-    // 1 / max(||z||, 1e-12) = rsqrt(max(||z||^2, 1e-24)), hardware 1-ulp rsqrt
-    const float f = (is_q ? q_scale : 1.f) * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = to_bf16(z[e] * f);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = to_bf16(z[e]);
-  }
-  return out;
 }
 
 __global__ __launch_bounds__(kThreads) void conv_prep_kernel(ConvArgs a) {

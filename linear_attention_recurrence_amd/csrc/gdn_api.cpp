@@ -232,6 +232,30 @@ gdn_status gdn_conv_decode_step(const void* mixed_qkv, const float* conv_weight,
                                           static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_decode_step_with_conv(const void* mixed_qkv, const float* conv_weight,
+                                     int32_t conv_kernel, void* conv_window,
+                                     const int32_t* window_slots, float q_scale, const float* g,
+                                     const float* beta, float* state_pool,
+                                     const int32_t* state_slots, int32_t num_seqs, int32_t h_qk,
+                                     int32_t h_v, int32_t d_k, int32_t d_v, float scale, void* o,
+                                     void* stream) {
+  if (num_seqs < 0) return GDN_ERR_SHAPE;
+  const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  if (conv_kernel < 1) return GDN_ERR_SHAPE;
+  if (conv_kernel > 4) return GDN_ERR_UNSUPPORTED;
+  if (h_v != h_qk && h_v != 2 * h_qk) return GDN_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return GDN_OK;
+  if (!mixed_qkv || !conv_weight || !g || !beta || !state_pool || !o) return GDN_ERR_NULL;
+  if (conv_kernel > 1 && !conv_window) return GDN_ERR_NULL;
+  GDN_TRY(check_slots(window_slots, num_seqs, stream));
+  GDN_TRY(check_slots(state_slots, num_seqs, stream));
+  return from_hip(gdn::launch_decode_with_conv(mixed_qkv, conv_weight, conv_kernel, conv_window,
+                                               window_slots, q_scale, g, beta, state_pool,
+                                               state_slots, num_seqs, h_qk, h_v, scale, o,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 gdn_status gdn_conv_window_from_prefill(const void* mixed_qkv, int32_t conv_kernel,
                                         const int32_t* cu_seqlens, int32_t num_seqs,
                                         int32_t total_tokens, int32_t h_qk, int32_t h_v,

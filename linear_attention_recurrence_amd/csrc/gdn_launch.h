@@ -12,6 +12,14 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool io_bf
                          int num_seqs, int h_qk, int h_v, float scale, void* o,
                          hipStream_t stream);
 
+// The decode-time front end and the decode step in one launch (recurrent.hip): one
+// workgroup per (sequence, QK head); h_v / h_qk must be 1 or 2.
+hipError_t launch_decode_with_conv(const void* mixed_qkv, const float* conv_weight, int conv_kernel,
+                                  void* conv_window, const int32_t* window_slots, float q_scale,
+                                  const float* g, const float* beta, float* pool,
+                                  const int32_t* slots, int num_seqs, int h_qk, int h_v,
+                                  float scale, void* o, hipStream_t stream);
+
 // Several decode steps per sequence, the state read and written once, per-token states
 // optionally written out (recurrent.hip).
 hipError_t launch_verify(const void* q, const void* k, const void* v, bool io_bf16, const float* g,

@@ -25,6 +25,7 @@
 // The per-channel form is the code panel of section "01 . GatedDeltaNet(config)" on the
 // Evolving Transformer page: one decay per value row, the correction taken from the state
 // before the decay (decode_kernel and rows_kernel with CH = true).
+#include "conv_device.h"
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -98,29 +99,34 @@ __device__ __forceinline__ float reduce_scatter16(float (&vals)[16], int lane32)
 // scale (alpha r + c (k . q)), this lane's output when (c4 & 3) == 2 (for row my_row).
 __device__ __forceinline__ float decode_token(f32x4 (&S)[8], f32x4 k4, f32x4 q4, float alpha, float beta,
                                               float vrow, float scale, int c4) {
+  // Every operation is spelled out (explicit fused multiply-adds, no contraction left to the
+  // compiler): the decode, verify and fused decode kernels all run this and must agree bit
+  // for bit, and the compiler's own contraction choices can differ between them.
+#pragma clang fp contract(off)
   const bool my_is_r = (c4 & 2) != 0;
   const bool upper = (__lane_id() & 32) != 0;   // which half-wave (rows of this lane)
   float vals[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    vals[2 * i] = S[i][0] * k4[0] + S[i][1] * k4[1] + S[i][2] * k4[2] + S[i][3] * k4[3];
-    vals[2 * i + 1] = S[i][0] * q4[0] + S[i][1] * q4[1] + S[i][2] * q4[2] + S[i][3] * q4[3];
+    vals[2 * i] = __builtin_fmaf(S[i][3], k4[3], __builtin_fmaf(S[i][2], k4[2],
+                  __builtin_fmaf(S[i][1], k4[1], S[i][0] * k4[0])));
+    vals[2 * i + 1] = __builtin_fmaf(S[i][3], q4[3], __builtin_fmaf(S[i][2], q4[2],
+                      __builtin_fmaf(S[i][1], q4[1], S[i][0] * q4[0])));
   }
   const float mine = reduce_scatter16(vals, c4);
   const float other = xor_lane(mine, 2);
   const float u = my_is_r ? other : mine;
   const float r = my_is_r ? mine : other;
-  const float kq = half_sum(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
-  const float c = beta * (vrow - alpha * u);
+  const float kq = half_sum(__builtin_fmaf(k4[3], q4[3], __builtin_fmaf(k4[2], q4[2],
+                            __builtin_fmaf(k4[1], q4[1], k4[0] * q4[0]))));
+  const float c = beta * __builtin_fmaf(-alpha, u, vrow);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float ci = half_lane(c, 4 * i, upper);
-    S[i][0] = alpha * S[i][0] + ci * k4[0];
-    S[i][1] = alpha * S[i][1] + ci * k4[1];
-    S[i][2] = alpha * S[i][2] + ci * k4[2];
-    S[i][3] = alpha * S[i][3] + ci * k4[3];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[i][e] = __builtin_fmaf(ci, k4[e], alpha * S[i][e]);
   }
-  return scale * (alpha * r + c * kq);
+  return scale * __builtin_fmaf(c, kq, alpha * r);
 }
 
 // The per-channel form at one token, decode layout: each value row i has its own decay
@@ -204,6 +210,98 @@ __global__ __launch_bounds__(512) void decode_kernel(RecArgs a) {
     out = decode_token(S, k4, q4, __expf(a.g[(size_t)n * a.h_v + h]), beta, vrow, a.scale, c4);
   }
   if ((c4 & 3) == 2) store1(o + ((size_t)n * a.h_v + h) * kHeadDim + my_row, out);
+#pragma unroll
+  for (int i = 0; i < kRows; ++i)
+    __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(sp + (size_t)i * 16 * kHeadDim));
+}
+
+// The decode step with the decode-time front end in front of it, one launch: one workgroup
+// per (sequence, QK head) covers the G = h_v / h_qk V heads that share the QK head (512
+// threads each, decode_kernel's layout), so the q and k channels of the window are read and
+// shifted by a single workgroup. Every wave first requests its share of the states; wave 0
+// then runs the front end for the workgroup's 256 + 128 G channels (8 per lane, one 16-lane
+// group per head: lanes 0-15 q, 16-31 k, then the V heads) with the same conv_token as the
+// front-end kernels, shifts the window and leaves the bf16 q, k and v in LDS; after a
+// barrier every half runs decode_token on its V head. Outputs, states and window are bit for
+// bit those of the front-end call followed by the decode step.
+struct DecConvArgs {
+  const bf16* x;          // [num_seqs][C] this step's projected inputs
+  const float* w;         // [C][K] taps
+  bf16* win;              // [pool][K - 1][C], in place
+  const int32_t* wslots;  // window slot per sequence (NULL = identity)
+  const float* g;
+  const float* beta;
+  const int32_t* slots;   // state slot per sequence (NULL = identity)
+  float* pool;
+  bf16* o;
+  int num_seqs, h_qk, h_v, K, C;
+  float q_scale, scale;
+};
+
+template <int G>
+__global__ __launch_bounds__(512 * G) void decode_conv_kernel(DecConvArgs a) {
+  constexpr int kRows = 8;
+  __shared__ float qkv[(2 + G) * kHeadDim];   // q | k | v of the G heads, bf16 values
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int c4 = lane & 31;
+  const int n = blockIdx.x / a.h_qk;
+  const int j = blockIdx.x % a.h_qk;
+  const int hl = w >> 3;                      // V head within the group
+  const int h = j * G + hl;
+  const int slot = a.slots ? a.slots[n] : n;
+  const size_t state = ((size_t)slot * a.h_v + h) * kHeadDim * kHeadDim;
+  const int row_base = (w & 7) * 2 + half;
+  float* sp = a.pool + state + (size_t)row_base * kHeadDim + 4 * c4;
+  f32x4 S[kRows];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i)
+    S[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)i * 16 * kHeadDim));
+
+  if (w == 0) {
+    const int grp = lane >> 4;                // 0: q, 1: k, 2..: V head grp - 2
+    const int nq = a.h_qk * kHeadDim;
+    const int c0 = grp == 0 ? j * kHeadDim + 8 * (lane & 15)
+                 : grp == 1 ? nq + j * kHeadDim + 8 * (lane & 15)
+                            : 2 * nq + (j * G + grp - 2) * kHeadDim + 8 * (lane & 15);
+    const bool live = grp < 2 + G;            // G = 1 leaves the last 16 lanes idle
+    if (live) {
+      const bf16x8 xr = *reinterpret_cast<const bf16x8*>(a.x + (size_t)n * a.C + c0);
+      const int wslot = a.wslots ? a.wslots[n] : n;
+      bf16* wrow = a.win + (size_t)wslot * (a.K - 1) * a.C + c0;
+      bf16x8 hr[3] = {bf16x8{}, bf16x8{}, bf16x8{}};
+#pragma unroll
+      for (int d = 1; d < 4; ++d)
+        if (d < a.K) hr[d - 1] = *reinterpret_cast<const bf16x8*>(wrow + (size_t)(a.K - 1 - d) * a.C);
+      float wt[4][8];
+      load_taps(a.w, a.K, c0, wt);
+      float x0[8], h1[8], h2[8], h3[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x0[e] = (float)xr[e];
+        h1[e] = (float)hr[0][e];
+        h2[e] = (float)hr[1][e];
+        h3[e] = (float)hr[2][e];
+      }
+      const bf16x8 out = conv_token(wt, x0, h1, h2, h3, grp == 0, grp == 1, a.q_scale);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qkv[grp * kHeadDim + 8 * (lane & 15) + e] = (float)out[e];
+#pragma unroll
+      for (int d = 1; d < 4; ++d)
+        if (d < a.K) *reinterpret_cast<bf16x8*>(wrow + (size_t)(a.K - 1 - d) * a.C) = d == 1 ? xr : hr[d - 2];
+    }
+  }
+  __syncthreads();
+
+  const int my_row = row_base + 16 * (c4 >> 2);
+  const f32x4 k4 = *reinterpret_cast<const f32x4*>(&qkv[kHeadDim + 4 * c4]);
+  const f32x4 q4 = *reinterpret_cast<const f32x4*>(&qkv[4 * c4]);
+  const float vrow = qkv[(2 + hl) * kHeadDim + my_row];
+  const float beta = a.beta[(size_t)n * a.h_v + h];
+  const float out = decode_token(S, k4, q4, __expf(a.g[(size_t)n * a.h_v + h]), beta, vrow, a.scale, c4);
+  if ((c4 & 3) == 2) a.o[((size_t)n * a.h_v + h) * kHeadDim + my_row] = to_bf16(out);
 #pragma unroll
   for (int i = 0; i < kRows; ++i)
     __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(sp + (size_t)i * 16 * kHeadDim));
@@ -514,6 +612,22 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool io_bf
     hipLaunchKernelGGL((decode_kernel<bf16, false>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((decode_kernel<float, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_with_conv(const void* mixed_qkv, const float* conv_weight, int conv_kernel,
+                                  void* conv_window, const int32_t* window_slots, float q_scale,
+                                  const float* g, const float* beta, float* pool,
+                                  const int32_t* slots, int num_seqs, int h_qk, int h_v,
+                                  float scale, void* o, hipStream_t stream) {
+  DecConvArgs a{static_cast<const bf16*>(mixed_qkv), conv_weight, static_cast<bf16*>(conv_window),
+                window_slots, g, beta, slots, pool, static_cast<bf16*>(o), num_seqs, h_qk, h_v,
+                conv_kernel, (2 * h_qk + h_v) * kHeadDim, q_scale, scale};
+  const dim3 grid((unsigned)num_seqs * (unsigned)h_qk);
+  if (h_v == h_qk)
+    hipLaunchKernelGGL((decode_conv_kernel<1>), grid, dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_conv_kernel<2>), grid, dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
                                             "gdn_channel_decay_prefill",
                                             "gdn_channel_decay_decode_step",
                                             "gdn_conv_prep", "gdn_conv_decode_step",
-                                            "gdn_conv_window_from_prefill", "gdn_gated_rmsnorm"])
+                                            "gdn_conv_window_from_prefill", "gdn_gated_rmsnorm",
+                                            "gdn_decode_step_with_conv"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -271,6 +272,31 @@ def test_gated_rmsnorm_validation():
     assert call(rows=2 ** 31 - 1, hv=2 ** 20) == L.GDN_ERR_UNSUPPORTED
     assert call(rows=0) == L.GDN_OK
     assert call(rows=0, o=None, z=None, w=None, out=None) == L.GDN_OK
+
+
+def test_decode_with_conv_validation():
+    lib, L = _lib()
+    f = lib.gdn_decode_step_with_conv
+    P = _fake
+    ok = dict(x=P(1), w=P(2), K=4, win=P(3), ws=None, qs=1.0, g=P(4), b=P(5), pool=P(6), ss=None,
+              n=2, hqk=16, hv=32, dk=128, dv=128, sc=1.0, o=P(7), st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["x"], a["w"], a["K"], a["win"], a["ws"], a["qs"], a["g"], a["b"], a["pool"],
+                 a["ss"], a["n"], a["hqk"], a["hv"], a["dk"], a["dv"], a["sc"], a["o"], a["st"])
+
+    for name in ("x", "w", "win", "g", "b", "pool", "o"):
+        assert call(**{name: None}) == L.GDN_ERR_NULL, name
+    assert call(K=1, win=None, n=0) == L.GDN_OK
+    assert call(K=0) == L.GDN_ERR_SHAPE
+    assert call(K=5) == L.GDN_ERR_UNSUPPORTED
+    assert call(hqk=8, hv=32) == L.GDN_ERR_UNSUPPORTED   # four V heads per QK head
+    assert call(hv=30) == L.GDN_ERR_SHAPE
+    assert call(dk=64) == L.GDN_ERR_UNSUPPORTED
+    assert call(n=-1) == L.GDN_ERR_SHAPE
+    assert call(n=0) == L.GDN_OK
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

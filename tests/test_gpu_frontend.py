@@ -175,3 +175,43 @@ def test_conv_decode_against_oracle():
             _check_one_rounding(f(q[n]).astype(np.float64), qr[p + s], "q seq %d step %d" % (n, s))
             _check_one_rounding(f(k[n]).astype(np.float64), kr[p + s], "k seq %d step %d" % (n, s))
             _check_one_rounding(f(v[n]).astype(np.float64), vr[p + s], "v seq %d step %d" % (n, s))
+
+
+@pytest.mark.parametrize("K,h_qk,h_v", [(4, 2, 4), (3, 2, 4), (1, 2, 4), (4, 3, 3)])
+def test_decode_with_conv_equals_two_calls(K, h_qk, h_v):
+    """gdn_decode_step_with_conv against gdn_conv_decode_step followed by gdn_decode_step,
+    over 5 steps on permuted window and state slots: outputs, state pool and window pool
+    equal bit for bit (both paths run the same front-end and token code). h_v / h_qk of 2
+    and of 1."""
+    import torch
+    import linear_attention_recurrence_amd as gdn
+    N, steps = 5, 5
+    fe = workloads.make_frontend([steps] * N, h_qk=h_qk, h_v=h_v, conv_kernel=K, seed=90 + K + h_v)
+    C = fe.mixed.shape[1]
+    rng = np.random.Generator(np.random.PCG64(91 + K))
+    wslots = torch.tensor([3, 0, 6, 1, 4], dtype=torch.int32, device="cuda")
+    sslots = torch.tensor([2, 5, 0, 6, 3], dtype=torch.int32, device="cuda")
+    win0 = torch.from_numpy(rng.standard_normal((7, max(K - 1, 1), C)).astype(np.float32)).to(torch.bfloat16).cuda()
+    pool0 = torch.from_numpy(rng.standard_normal((7, h_v, 128, 128)).astype(np.float32) * 0.02).cuda()
+    g = torch.from_numpy(-np.abs(rng.standard_normal((steps, N, h_v))).astype(np.float32) * 0.1).cuda()
+    b = torch.from_numpy(rng.uniform(0.1, 0.9, (steps, N, h_v)).astype(np.float32)).cuda()
+    w = to_dev(fe.conv_weight)
+    cu = fe.cu_seqlens
+    win_a, pool_a = win0.clone(), pool0.clone()
+    win_b, pool_b = win0.clone(), pool0.clone()
+    scale = 128 ** -0.5
+    for s in range(steps):
+        x = to_dev(fe.mixed[np.array([cu[n] + s for n in range(N)])])
+        q, k, v = gdn.gdn_conv_decode_step(x, w, win_a if K > 1 else None, h_qk, h_v, 128, 128,
+                                           fe.q_scale, window_slots=wslots)
+        o_a = gdn.gdn_decode_step(q, k, v, g[s].contiguous(), b[s].contiguous(), pool_a, scale,
+                                  state_slots=sslots)
+        o_b = gdn.gdn_decode_step_with_conv(x, w, win_b if K > 1 else None, g[s].contiguous(),
+                                            b[s].contiguous(), pool_b, h_qk, h_v, 128, 128,
+                                            fe.q_scale, scale, window_slots=wslots,
+                                            state_slots=sslots)
+        torch.cuda.synchronize()
+        assert torch.equal(o_a, o_b), "o at step %d" % s
+    assert torch.equal(pool_a, pool_b)
+    if K > 1:
+        assert torch.equal(win_a, win_b)
