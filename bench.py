@@ -4,13 +4,15 @@ Headline: chunked prefill throughput (tokens/s) on the Qwen3-Next layer shape, B
 16 QK heads shared by 32 V heads, head dim 128, bf16 q/k/v/o, S0 = 0, fp32 final states. A
 step is one gdn_chunk_prefill call over the whole batch: its two launches (the
 chunk-parallel prep and the sequential state pass) run every step of the chunked method.
-Alongside: the decode step on a 256-sequence fp32 state pool (HBM-bound, no matrix cores)
-and the packed variable-length front end + prefill. The fp64 oracle is timed on the host
-cores on the headline workload as a CPU baseline.
+Alongside: the decode step on a 256-sequence fp32 state pool (HBM-bound, no matrix cores),
+with the decode-time front end (two calls and one launch), the multi-token verify step, the
+per-channel decay form (decode and token-sequential prefill), the packed variable-length
+front end + prefill, and the output epilogue. The fp64 oracle is timed on the host cores on
+the headline workload as a CPU baseline.
 
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps K2]
-                  [--workload prefill,decode,frontend] [--no-cpu-baseline]
+                  [--workload prefill,decode,frontend,epilogue] [--no-cpu-baseline]
       prints one JSON line
   python bench.py --workload copy
       a plain 1 GiB device copy, the calibration run for hardware byte counters
