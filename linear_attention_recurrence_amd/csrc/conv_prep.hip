@@ -47,15 +47,16 @@ __device__ __forceinline__ void load8(const bf16* p, float (&x)[8]) {
   for (int e = 0; e < 8; ++e) x[e] = (float)r[e];
 }
 
-// Rows t0 .. t0 + kGroup - 1 of this thread's channels (rows at or past t_end read as 0).
+// Rows t0 .. t0 + kGroup - 1 of this thread's channels; rows at or past t_end repeat row
+// t_end - 1 (those tokens are never processed). The loads are unconditional: loads under a
+// branch made the compiler wait for every load in flight, the next group's included, before
+// each token.
 __device__ __forceinline__ void load_group(const bf16* x, size_t C, int t0, int t_end,
                                            bf16x8 (&raw)[kGroup]) {
 #pragma unroll
   for (int u = 0; u < kGroup; ++u)
-    raw[u] = (t0 + u < t_end)
-                 ? __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
-                                                  reinterpret_cast<const u32x4*>(x + (size_t)(t0 + u) * C)))
-                 : bf16x8{};
+    raw[u] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+                 reinterpret_cast<const u32x4*>(x + (size_t)min(t0 + u, t_end - 1) * C)));
 }
 
 // Largest n with cu[n] <= t < cu[n+1] (t < total_tokens, so such n exists).
@@ -86,37 +87,51 @@ __global__ __launch_bounds__(kThreads) void conv_prep_kernel(ConvArgs a) {
   float wt[4][8];
   load_taps(a.w, a.K, c0, wt);
 
-  int n = find_sequence(a.cu, a.num_seqs, t_begin);
-  int seq_start = a.cu[n], seq_end = a.cu[n + 1];
+  const int n = find_sequence(a.cu, a.num_seqs, t_begin);
+  const int seq_start = a.cu[n];
+  // the tokens of this block that start a sequence (offsets from t_begin, never 0: the first
+  // token's history comes from the rows before it), one bit each; found once here so the
+  // token loop reads nothing but its rows
+  uint64_t starts_lo = 0, starts_hi = 0;
+  for (int m = n + 1; m <= a.num_seqs && a.cu[m] < t_end; ++m) {
+    const int off = a.cu[m] - t_begin;
+    if (off < 64) starts_lo |= 1ull << off;
+    else starts_hi |= 1ull << (off - 64);
+  }
 
   float h1[8], h2[8], h3[8];     // inputs at t-1, t-2, t-3 (zero before the sequence start)
+  {
+    float r1[8], r2[8], r3[8];
+    load8(a.x + (size_t)max(t_begin - 1, 0) * a.C + c0, r1);
+    load8(a.x + (size_t)max(t_begin - 2, 0) * a.C + c0, r2);
+    load8(a.x + (size_t)max(t_begin - 3, 0) * a.C + c0, r3);
+    const bool k1 = a.K > 1 && t_begin - 1 >= seq_start;
+    const bool k2 = a.K > 2 && t_begin - 2 >= seq_start;
+    const bool k3 = a.K > 3 && t_begin - 3 >= seq_start;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) h1[e] = h2[e] = h3[e] = 0.f;
-  if (a.K > 1 && t_begin - 1 >= seq_start) load8(a.x + (size_t)(t_begin - 1) * a.C + c0, h1);
-  if (a.K > 2 && t_begin - 2 >= seq_start) load8(a.x + (size_t)(t_begin - 2) * a.C + c0, h2);
-  if (a.K > 3 && t_begin - 3 >= seq_start) load8(a.x + (size_t)(t_begin - 3) * a.C + c0, h3);
+    for (int e = 0; e < 8; ++e) {
+      h1[e] = k1 ? r1[e] : 0.f;
+      h2[e] = k2 ? r2[e] : 0.f;
+      h3[e] = k3 ? r3[e] : 0.f;
+    }
+  }
 
   const bf16* xc = a.x + c0;
-  bf16x8 raw[2][kGroup];
-  load_group(xc, a.C, t_begin, t_end, raw[0]);
-#pragma unroll
-  for (int gi = 0; gi < kTokensPerBlock / kGroup; ++gi) {
-    const int tg = t_begin + gi * kGroup;
-    if (gi + 1 < kTokensPerBlock / kGroup) load_group(xc, a.C, tg + kGroup, t_end, raw[(gi + 1) & 1]);
+  // One group of kGroup tokens from its loaded rows. Returns false once the block's tokens
+  // are done.
+  auto process = [&](const bf16x8 (&raw)[kGroup], int gi) {
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) {
-      const int t = tg + u;
-      if (t >= t_end) break;
-      if (t >= seq_end) {           // entering the next non-empty sequence: no history
-        while (a.cu[n + 1] <= t) ++n;
-        seq_start = a.cu[n];
-        seq_end = a.cu[n + 1];
+      const int t = t_begin + gi * kGroup + u;
+      if (t >= t_end) return false;
+      const int off = gi * kGroup + u;
+      if (((off < 64 ? starts_lo >> off : starts_hi >> (off - 64)) & 1) != 0) {   // a new sequence: no history
 #pragma unroll
         for (int e = 0; e < 8; ++e) h1[e] = h2[e] = h3[e] = 0.f;
       }
       float x0[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x0[e] = (float)raw[gi & 1][u][e];
+      for (int e = 0; e < 8; ++e) x0[e] = (float)raw[u][e];
       const bf16x8 out = conv_token(wt, x0, h1, h2, h3, is_q, is_k, a.q_scale);
       bf16* dst = is_q ? a.q + (size_t)t * nq + c0
                 : is_k ? a.k + (size_t)t * nq + (c0 - nq)
@@ -131,6 +146,20 @@ __global__ __launch_bounds__(kThreads) void conv_prep_kernel(ConvArgs a) {
         h1[e] = a.K > 1 ? x0[e] : 0.f;
       }
     }
+    return true;
+  };
+  // two buffers named apart (every index static, so neither lands in scratch memory), the
+  // next group's rows in flight while a group computes
+  bf16x8 ra[kGroup], rb[kGroup];
+  load_group(xc, a.C, t_begin, t_end, ra);
+#pragma unroll
+  for (int gi = 0; gi < kTokensPerBlock / kGroup; gi += 2) {
+    load_group(xc, a.C, t_begin + (gi + 1) * kGroup, t_end, rb);
+    asm volatile("" ::: "memory");   // the refill stays here
+    if (!process(ra, gi)) break;
+    if (gi + 2 < kTokensPerBlock / kGroup) load_group(xc, a.C, t_begin + (gi + 2) * kGroup, t_end, ra);
+    asm volatile("" ::: "memory");
+    if (!process(rb, gi + 1)) break;
   }
 }
 
