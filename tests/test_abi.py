@@ -299,6 +299,19 @@ def test_decode_with_conv_validation():
     assert call(n=0) == L.GDN_OK
 
 
+def test_header_is_plain_c(tmp_path):
+    """include/gdn.h compiles as strict C99 (ctypes callers and C code include it)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "use.c"
+    src.write_text('#include "gdn.h"\nint main(void) { return (int)GDN_GATE_SILU + (int)GDN_OK; }\n')
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     from linear_attention_recurrence_amd import _lib as L
     with pytest.raises(RuntimeError, match="not built"):
