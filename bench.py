@@ -1,14 +1,16 @@
 """Benchmark of the Gated DeltaNet mixer on one MI355X.
 
-Headline: chunked prefill throughput (tokens/s) on the Qwen3-Next layer shape, B=1, T=4096,
-16 QK heads shared by 32 V heads, head dim 128, bf16 q/k/v/o, S0 = 0, fp32 final states. A
-step is one gdn_chunk_prefill call over the whole batch: its two launches (the
-chunk-parallel prep and the sequential state pass) run every step of the chunked method.
-Alongside: the decode step on a 256-sequence fp32 state pool (HBM-bound, no matrix cores),
-with the decode-time front end (two calls and one launch), the multi-token verify step, the
-per-channel decay form (decode and token-sequential prefill), the packed variable-length
-front end + prefill, and the output epilogue. The fp64 oracle is timed on the host cores on
-the headline workload as a CPU baseline.
+Headline: chunked prefill throughput (tokens/s) on the Qwen3-Next layer shape at long
+context, B=1, T=32768, 16 QK heads shared by 32 V heads, head dim 128, bf16 q/k/v/o, fp32
+initial state S0 ~ N(0, 0.02) in and fp32 final state out. A step is one gdn_chunk_prefill
+call over the whole batch: its launches (the chunk-parallel prep and the sequential state
+pass) run every step of the chunked method. Alongside: the same prefill at T=4096 with S0 =
+0; the packed variable-length batch (64 sequences, lengths uniform in [128, 8192]) through
+the front end and the prefill; the decode step on a 256-sequence fp32 state pool (HBM-bound,
+no matrix cores), with the decode-time front end (two calls and one launch); the
+multi-token verify step; the per-channel decay form (decode and token-sequential prefill);
+and the output epilogue. The fp64 oracle is timed on the host cores on the headline
+workload as a CPU baseline.
 
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps K2]
@@ -48,15 +50,22 @@ C = 64
 H_QK, H_V = 16, 32
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_amd", "csrc")
 
-# Hardware byte counters of one launch, from two rocprofv3 --pmc runs (FETCH_SIZE, then
-# WRITE_SIZE) of `python bench.py --workload prefill,decode,copy,frontend --steps 5 --warmup 1
-# --no-cpu-baseline`, in KiB per dispatch, scaled by what the same counters read for a
-# plain 1 GiB device copy. `sources` fingerprints the kernel sources the figures were taken
-# on: once they change, the figures no longer describe the kernel and traffic is reported
-# as null. Filled from the summaries kept under profiles/.
-COUNTER_TRAFFIC = {
-    "prefill": {"bytes": 295862094, "sources": "78b0f61ea316fb24"},
-    "decode": {"bytes": 1083357477, "sources": "47d685d5456327c3"},
+# Hardware counters of one call, from rocprofv3 --pmc runs of `python bench.py --workload
+# prefill,frontend,decode,copy --steps 5 --warmup 1 --decode-steps 20 --no-cpu-baseline`
+# (the commands and raw per-kernel figures are kept under profiles/):
+#  * "bytes": HBM bytes per call, FETCH_SIZE plus WRITE_SIZE (KiB per dispatch, summed over
+#    the call's kernels) in two passes, each scaled by what the same counter reads for a
+#    plain 1 GiB device copy;
+#  * "mfma_busy": the fraction of the matrix cores' cycles spent busy over the call,
+#    sum(SQ_VALU_MFMA_BUSY_CYCLES) / (GRBM_GUI_ACTIVE x 1024 SIMDs) per kernel, weighted by
+#    each kernel's share of the call's time.
+# `sources` fingerprints the kernel sources the figures were taken on: once they change,
+# the figures no longer describe the kernels and are reported as null.
+COUNTERS = {
+    "prefill_t32768": {"bytes": None, "mfma_busy": None, "sources": None},
+    "prefill_t4096": {"bytes": None, "mfma_busy": None, "sources": None},
+    "prefill_packed64": {"bytes": None, "mfma_busy": None, "sources": None},
+    "decode": {"bytes": None, "sources": None},
 }
 
 
@@ -72,13 +81,13 @@ PREFILL_SOURCES = ("chunk_prefill.hip", "gdn_device.h")
 DECODE_SOURCES = ("recurrent.hip", "gdn_device.h")
 
 
-def counter_traffic(name, sources):
-    """Counter-measured HBM bytes per call for `name`, or None when not measured on these
-    kernel sources."""
-    rec = COUNTER_TRAFFIC.get(name)
-    if rec is None or rec["sources"] != _sources_sha(sources):
+def counter(name, field, sources):
+    """A counter figure recorded for `name`, or None when not measured on these kernel
+    sources."""
+    rec = COUNTERS.get(name)
+    if rec is None or rec.get(field) is None or rec["sources"] != _sources_sha(sources):
         return None
-    return rec["bytes"]
+    return rec[field]
 
 
 # ---------------------------------------------------------------------------------------
@@ -172,28 +181,65 @@ def _workspace(total_tokens, num_seqs):
     return torch.empty(need, dtype=torch.uint8, device="cuda")
 
 
-def bench_prefill(steps, warmup, copies=4):
-    """B=1, T=4096 prefill; `copies` input sets rotate so the 256 MB last-level cache cannot
-    hold the working set across steps."""
+PREFILL_KERNELS = "gdn_chunk_prefill call: prep_kernel + state pass"
+
+PREFILL_WORKLOADS = {
+    # name: (input generator, seed, input sets rotated, with initial state, description)
+    "t32768": ("config2", 1002, 2, True,
+               "gated delta rule chunked prefill, B=1, T=32768, 16 QK / 32 V heads, d=128, "
+               "chunk 64, bf16 q/k/v/o, fp32 state, S0 ~ N(0, 0.02) in, final state out"),
+    "t4096": ("config1", 1001, 4, False,
+              "gated delta rule chunked prefill, B=1, T=4096, 16 QK / 32 V heads, d=128, "
+              "chunk 64, bf16 q/k/v/o, fp32 state, S0=0, final state out"),
+}
+
+
+def bench_prefill(name, steps, warmup):
+    """One B=1 prefill workload of PREFILL_WORKLOADS; its input sets rotate so the 256 MB
+    last-level cache cannot hold the working set across steps (one T=32768 set alone is
+    about 0.8 GB). Returns (tokens, wall seconds, mean device ms per call)."""
     import torch
     import linear_attention_recurrence_amd as gdn
     import workloads
+    gen, seed, copies, with_s0, _ = PREFILL_WORKLOADS[name]
     sets = []
+    T = None
     for c in range(copies):
-        x = workloads.config1(seed=1001 + 97 * c)
+        x = getattr(workloads, gen)(seed=seed + 97 * c)
+        T = x.total_tokens
         sets.append(dict(q=_dev(x.q), k=_dev(x.k), v=_dev(x.v), g=_dev(x.g), b=_dev(x.beta),
-                         cu=_dev(x.cu_seqlens),
-                         o=torch.empty((4096, H_V, D), dtype=torch.bfloat16, device="cuda"),
+                         cu=_dev(x.cu_seqlens), s0=_dev(x.initial_state),
+                         o=torch.empty((T, H_V, D), dtype=torch.bfloat16, device="cuda"),
                          fin=torch.empty((1, H_V, D, D), dtype=torch.float32, device="cuda")))
-    ws = _workspace(4096, 1)
+        del x
+    ws = _workspace(T, 1)
     scale = D ** -0.5
 
     def step(i):
         s = sets[i % copies]
         gdn.gdn_chunk_prefill(s["q"], s["k"], s["v"], s["g"], s["b"], s["cu"], scale,
-                              final_state=s["fin"], o=s["o"], workspace=ws)
+                              initial_state=s["s0"], final_state=s["fin"], o=s["o"], workspace=ws)
 
-    return _timed(step, steps, warmup)
+    wall, ms = _timed(step, steps, warmup)
+    return T, wall, ms
+
+
+def prefill_rooflines(tokens, num_seqs, with_s0, call_ms, counter_name, kernel):
+    """HBM and matrix-core roofline objects of one prefill call: algorithmic bytes and FLOPs
+    over the call's mean device time, with the counter figures when they describe the
+    current kernels."""
+    flops = prefill_flops(tokens)
+    nbytes = prefill_bytes(tokens, num_seqs, with_s0)
+    achieved = nbytes / (call_ms / 1e3) / 1e9
+    tf = flops / (call_ms / 1e3) / 1e12
+    hbm = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": achieved / HBM_PEAK_GBS,
+           "traffic": counter(counter_name, "bytes", PREFILL_SOURCES),
+           "kernel": kernel, "call_ms": call_ms, "algorithmic_bytes": nbytes}
+    mfma = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": tf / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": flops,
+            "mfma_busy_counter": counter(counter_name, "mfma_busy", PREFILL_SOURCES)}
+    return hbm, mfma
 
 
 def bench_decode(steps, warmup):
@@ -397,24 +443,26 @@ def bench_copy(steps, warmup, nbytes=1 << 30):
 
 
 def cpu_baseline(min_core_seconds=10.0):
-    """The fp64 oracle, as it stands, on the headline workload (B=1, T=4096, all 32 heads),
-    run whole and repeated until about `min_core_seconds` of CPU work has been done."""
+    """The fp64 oracle, as it stands, on the headline workload (B=1, T=32768, all 32 heads,
+    S0 ~ N(0, 0.02)), run whole and repeated until about `min_core_seconds` of CPU work has
+    been done."""
     import oracle
     import workloads
-    x = workloads.config1()
+    x = workloads.config2()
     args = [x.as_f64(n) for n in ("q", "k", "v", "g", "beta")]
+    s0 = x.as_f64("initial_state")
     threads = oracle.default_threads()
     reps, t = 0, time.perf_counter()
     while True:
-        oracle.recurrence(*args, x.cu_seqlens, x.scale, n_threads=threads)
+        oracle.recurrence(*args, x.cu_seqlens, x.scale, initial_state=s0, n_threads=threads)
         reps += 1
         dt = time.perf_counter() - t
         if dt * threads >= min_core_seconds:
             break
     return {"value": reps * x.total_tokens / dt, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": "the whole headline workload (B=1, T=4096, 32 V heads, fp64 token loop) "
-                      "run %d times, %.2f s wall on %d threads" % (reps, dt, threads)}
+            "sample": "the whole headline workload (B=1, T=32768, 32 V heads, S0 given, fp64 "
+                      "token loop) run %d times, %.2f s wall on %d threads" % (reps, dt, threads)}
 
 
 def pmc_summary(root):
@@ -439,7 +487,7 @@ def pmc_summary(root):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--workload", default="prefill,decode,frontend,epilogue",
@@ -460,15 +508,11 @@ def main():
     out = {}
 
     if "prefill" in work:
-        wall, call_ms = bench_prefill(args.steps, args.warmup)
-        tokens = 4096
-        flops = prefill_flops(tokens)
-        nbytes = prefill_bytes(tokens, 1, with_s0=False)
-        achieved = nbytes / (call_ms / 1e3) / 1e9
-        traffic = counter_traffic("prefill", PREFILL_SOURCES)
+        T, wall, call_ms = bench_prefill("t32768", args.steps, args.warmup)
+        hbm, mfma = prefill_rooflines(T, 1, True, call_ms, "prefill_t32768", PREFILL_KERNELS)
         out.update({
             "metric": METRIC,
-            "value": tokens * args.steps / wall,
+            "value": T * args.steps / wall,
             "unit": "tokens/s",
             "n_gpus": 1,
             "steps": args.steps,
@@ -479,19 +523,18 @@ def main():
             "vs_baseline": None,
             "dtype": "bf16",
             "data": "synthetic",
-            "config": {"workload": "gated delta rule chunked prefill, B=1, T=4096, 16 QK / 32 V "
-                                   "heads, d=128, chunk 64, bf16 q/k/v/o, fp32 state, S0=0, "
-                                   "final state out",
-                       "global_batch": 1, "seq_len": tokens, "parallelism": "none (1 GPU)"},
-            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                         "kernel": "gdn_chunk_prefill call: prep_kernel + state_ro_kernel",
-                         "call_ms": call_ms, "algorithmic_bytes": nbytes},
-            "roofline_mfma": {"achieved": flops / (call_ms / 1e3) / 1e12,
-                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                              "frac": flops / (call_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                              "algorithmic_flops": flops},
+            "config": {"workload": PREFILL_WORKLOADS["t32768"][4],
+                       "global_batch": 1, "seq_len": T, "parallelism": "none (1 GPU)"},
+            "roofline": hbm,
+            "roofline_mfma": mfma,
         })
+        psteps = max(20, args.steps)
+        T1, wall1, ms1 = bench_prefill("t4096", psteps, args.warmup)
+        hbm1, mfma1 = prefill_rooflines(T1, 1, False, ms1, "prefill_t4096", PREFILL_KERNELS)
+        out["prefill_b1_t4096"] = {"workload": PREFILL_WORKLOADS["t4096"][4], "steps": psteps,
+                                   "ms_per_step": wall1 * 1e3 / psteps,
+                                   "tokens_per_s": T1 * psteps / wall1,
+                                   "roofline": hbm1, "roofline_mfma": mfma1}
     if "decode" in work:
         dsteps = args.decode_steps
         wall, dms = bench_decode(dsteps, args.warmup)
@@ -504,7 +547,7 @@ def main():
             "tokens_per_s": 256 * dsteps / wall,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS,
-                         "traffic": counter_traffic("decode", DECODE_SOURCES),
+                         "traffic": counter("decode", "bytes", DECODE_SOURCES),
                          "kernel": "decode_kernel<bf16>", "kernel_ms": dms,
                          "algorithmic_bytes": dbytes}}
     if "decode" in work:
@@ -573,15 +616,20 @@ def main():
                                                "algorithmic_flops": cflops}}}
     if "frontend" in work:
         T4, N4, conv_ms, pre_ms = bench_frontend(10, 2)
+        hbm4, mfma4 = prefill_rooflines(T4, N4, True, pre_ms, "prefill_packed64", PREFILL_KERNELS)
+        cb = conv_prep_bytes(T4)
         out["frontend_prefill"] = {
             "workload": "64 packed sequences, lengths uniform in [128, 8192], conv k=4 front end "
                         "then prefill with S0 and final states",
             "total_tokens": T4, "conv_prep_ms": conv_ms, "prefill_ms": pre_ms,
             "tokens_per_s_with_front_end": T4 / ((conv_ms + pre_ms) / 1e3),
             "tokens_per_s_prefill_only": T4 / (pre_ms / 1e3),
-            "conv_prep_GBs": conv_prep_bytes(T4) / (conv_ms / 1e3) / 1e9,
-            "prefill_GBs": prefill_bytes(T4, N4, True) / (pre_ms / 1e3) / 1e9,
-            "prefill_TFLOPs": prefill_flops(T4) / (pre_ms / 1e3) / 1e12}
+            "conv_prep_roofline": {"bound": "hbm", "achieved": cb / (conv_ms / 1e3) / 1e9,
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": cb / (conv_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                   "kernel": "conv_prep_kernel", "kernel_ms": conv_ms,
+                                   "algorithmic_bytes": cb},
+            "prefill_roofline": hbm4, "prefill_roofline_mfma": mfma4}
     if "epilogue" in work:
         nvec, ems = bench_epilogue(200, 10)
         eb = nvec * D * 2 * 3          # o and z read, out written, bf16

@@ -27,14 +27,19 @@
  *    launched; on a nonzero status nothing has been written. A failed launch returns
  *    GDN_ERR_HIP. Nothing is thrown across the ABI.
  *  - Device-side contracts that the host cannot check without a synchronisation:
- *    cu_seqlens is nondecreasing from 0 to total_tokens, and state_slots (and
- *    window_slots) hold distinct indices below the pool size. Breaking them is undefined
- *    behaviour. For debugging a caller, the environment variable GDN_CHECK_CONTRACTS=1
- *    makes every call copy these arrays to the host on its stream and wait for them (the
- *    one case where the library synchronises), and return GDN_ERR_SHAPE, with nothing
- *    launched, for a cu_seqlens that does not start at 0, decreases or does not end at
- *    total_tokens, or for negative or repeated slots (the pool size is not passed, so its
- *    bound stays the caller's). A failed copy returns GDN_ERR_HIP.
+ *    cu_seqlens is nondecreasing from 0 to total_tokens; state_slots (and window_slots)
+ *    hold distinct indices below the pool size; every log-decay g is finite and <= 0, i.e.
+ *    alpha = exp(g) lies in (0, 1] (a decay shrinks the state, as the first page's section
+ *    "Correcting a memory instead of adding to it" describes it). Breaking them is
+ *    undefined behaviour: for g > 0 the chunked prefill bounds every in-chunk decay ratio
+ *    by 1 while the token-sequential kernels do not, so the two would disagree. For
+ *    debugging a caller, the environment variable GDN_CHECK_CONTRACTS=1 makes every call
+ *    copy these arrays to the host on its stream and wait for them (the one case where the
+ *    library synchronises), and return GDN_ERR_SHAPE, with nothing launched, for a
+ *    cu_seqlens that does not start at 0, decreases or does not end at total_tokens, for
+ *    negative or repeated slots (the pool size is not passed, so its bound stays the
+ *    caller's), or for a g that is positive, infinite or NaN. A failed copy returns
+ *    GDN_ERR_HIP.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -80,7 +85,7 @@ size_t gdn_chunk_prefill_workspace_bytes(int32_t total_tokens, int32_t num_seqs,
  *
  *   q, k          [total_tokens][h_qk][d_k]      io_dtype
  *   v             [total_tokens][h_v][d_v]       io_dtype
- *   g, beta       [total_tokens][h_v]            fp32; alpha = exp(g), g <= 0 expected
+ *   g, beta       [total_tokens][h_v]            fp32; alpha = exp(g), g finite and <= 0
  *   cu_seqlens    [num_seqs + 1]                 int32; sequence n spans tokens
  *                                                cu_seqlens[n] .. cu_seqlens[n+1]-1
  *   scale         multiplies the read-out (o = scale * S q)

@@ -7,6 +7,7 @@ fallback: if the library is missing or a call fails, an exception is raised.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -100,6 +101,14 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(int(stream.cuda_stream))
 
 
+def _on(stream):
+    """Allocation context for a call launched on `stream`: tensors the binding allocates
+    (outputs, the prefill workspace) then belong to that stream in torch's caching
+    allocator, so their memory is not handed to work queued on another stream while the
+    call's kernels may still use it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return GDN_BF16
@@ -137,8 +146,12 @@ def gdn_chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, initial_state=None,
     T, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
     N = cu_seqlens.numel() - 1
-    if o is None:
-        o = torch.empty((T, h_v, d_v), dtype=v.dtype, device=v.device)
+    with _on(stream):
+        if o is None:
+            o = torch.empty((T, h_v, d_v), dtype=v.dtype, device=v.device)
+        need = gdn_chunk_prefill_workspace_bytes(T, N, h_qk, h_v, d_k, d_v)
+        if need and workspace is None and q.dtype == torch.bfloat16:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _expect(k, (T, h_qk, d_k), q.dtype, "k")
     _expect(v, (T, h_v, d_v), q.dtype, "v")
     _expect(g, (T, h_v), torch.float32, "g")
@@ -147,9 +160,6 @@ def gdn_chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, initial_state=None,
     _expect(initial_state, (N, h_v, d_v, d_k), torch.float32, "initial_state")
     _expect(final_state, (N, h_v, d_v, d_k), torch.float32, "final_state")
     _expect(o, (T, h_v, d_v), q.dtype, "o")
-    need = gdn_chunk_prefill_workspace_bytes(T, N, h_qk, h_v, d_k, d_v)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().gdn_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta),
                                   _ptr(cu_seqlens), N, T, h_qk, h_v, d_k, d_v, float(scale),
@@ -165,7 +175,8 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, scale, state_slots=None, o=Non
     N, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
     if o is None:
-        o = torch.empty((N, h_v, d_v), dtype=v.dtype, device=v.device)
+        with _on(stream):
+            o = torch.empty((N, h_v, d_v), dtype=v.dtype, device=v.device)
     _expect(k, (N, h_qk, d_k), q.dtype, "k")
     _expect(v, (N, h_v, d_v), q.dtype, "v")
     _expect(g, (N, h_v), torch.float32, "g")
@@ -193,7 +204,8 @@ def gdn_verify_step(q, k, v, g, beta, state_pool, scale, state_slots=None, snaps
     N, n_tok, h_qk, d_k = q.shape
     h_v, d_v = v.shape[2], v.shape[3]
     if o is None:
-        o = torch.empty((N, n_tok, h_v, d_v), dtype=v.dtype, device=v.device)
+        with _on(stream):
+            o = torch.empty((N, n_tok, h_v, d_v), dtype=v.dtype, device=v.device)
     _expect(k, (N, n_tok, h_qk, d_k), q.dtype, "k")
     _expect(v, (N, n_tok, h_v, d_v), q.dtype, "v")
     _expect(g, (N, n_tok, h_v), torch.float32, "g")
@@ -221,7 +233,8 @@ def gdn_channel_decay_prefill(q, k, v, g, beta, cu_seqlens, scale, initial_state
     h_v, d_v = v.shape[1], v.shape[2]
     N = cu_seqlens.numel() - 1
     if o is None:
-        o = torch.empty((T, h_v, d_v), dtype=v.dtype, device=v.device)
+        with _on(stream):
+            o = torch.empty((T, h_v, d_v), dtype=v.dtype, device=v.device)
     _expect(k, (T, h_qk, d_k), q.dtype, "k")
     _expect(v, (T, h_v, d_v), q.dtype, "v")
     _expect(g, (T, h_v, d_v), torch.float32, "g")
@@ -246,7 +259,8 @@ def gdn_channel_decay_decode_step(q, k, v, g, beta, state_pool, scale, state_slo
     N, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
     if o is None:
-        o = torch.empty((N, h_v, d_v), dtype=v.dtype, device=v.device)
+        with _on(stream):
+            o = torch.empty((N, h_v, d_v), dtype=v.dtype, device=v.device)
     _expect(k, (N, h_qk, d_k), q.dtype, "k")
     _expect(v, (N, h_v, d_v), q.dtype, "v")
     _expect(g, (N, h_v, d_v), torch.float32, "g")
@@ -272,12 +286,13 @@ def gdn_conv_prep(mixed_qkv, conv_weight, cu_seqlens, h_qk, h_v, d_k, d_v, q_sca
     T = mixed_qkv.shape[0]
     N = cu_seqlens.numel() - 1
     dev = mixed_qkv.device
-    if q is None:
-        q = torch.empty((T, h_qk, d_k), dtype=torch.bfloat16, device=dev)
-    if k is None:
-        k = torch.empty((T, h_qk, d_k), dtype=torch.bfloat16, device=dev)
-    if v is None:
-        v = torch.empty((T, h_v, d_v), dtype=torch.bfloat16, device=dev)
+    with _on(stream):
+        if q is None:
+            q = torch.empty((T, h_qk, d_k), dtype=torch.bfloat16, device=dev)
+        if k is None:
+            k = torch.empty((T, h_qk, d_k), dtype=torch.bfloat16, device=dev)
+        if v is None:
+            v = torch.empty((T, h_v, d_v), dtype=torch.bfloat16, device=dev)
     C = 2 * h_qk * d_k + h_v * d_v
     _expect(mixed_qkv, (T, C), torch.bfloat16, "mixed_qkv")
     _expect(conv_weight, (C, conv_weight.shape[1]), torch.float32, "conv_weight")
@@ -299,12 +314,13 @@ def gdn_conv_decode_step(mixed_qkv, conv_weight, conv_window, h_qk, h_v, d_k, d_
     N = mixed_qkv.shape[0]
     K = int(conv_weight.shape[1])
     dev = mixed_qkv.device
-    if q is None:
-        q = torch.empty((N, h_qk, d_k), dtype=torch.bfloat16, device=dev)
-    if k is None:
-        k = torch.empty((N, h_qk, d_k), dtype=torch.bfloat16, device=dev)
-    if v is None:
-        v = torch.empty((N, h_v, d_v), dtype=torch.bfloat16, device=dev)
+    with _on(stream):
+        if q is None:
+            q = torch.empty((N, h_qk, d_k), dtype=torch.bfloat16, device=dev)
+        if k is None:
+            k = torch.empty((N, h_qk, d_k), dtype=torch.bfloat16, device=dev)
+        if v is None:
+            v = torch.empty((N, h_v, d_v), dtype=torch.bfloat16, device=dev)
     C = 2 * h_qk * d_k + h_v * d_v
     _expect(mixed_qkv, (N, C), torch.bfloat16, "mixed_qkv")
     _expect(conv_weight, (C, K), torch.float32, "conv_weight")
@@ -356,7 +372,8 @@ def gdn_gated_rmsnorm(o, z, weight, eps=1e-6, gate="sigmoid", out=None, stream=N
     or z (in place). Returns out."""
     T, h_v, d_v = o.shape
     if out is None:
-        out = torch.empty_like(o)
+        with _on(stream):
+            out = torch.empty_like(o)
     _expect(z, (T, h_v, d_v), o.dtype, "z")
     _expect(weight, (d_v,), torch.float32, "weight")
     _expect(out, (T, h_v, d_v), o.dtype, "out")
@@ -378,7 +395,8 @@ def gdn_decode_step_with_conv(mixed_qkv, conv_weight, conv_window, g, beta, stat
     N, C = mixed_qkv.shape
     K = conv_weight.shape[1]
     if o is None:
-        o = torch.empty((N, h_v, d_v), dtype=torch.bfloat16, device=mixed_qkv.device)
+        with _on(stream):
+            o = torch.empty((N, h_v, d_v), dtype=torch.bfloat16, device=mixed_qkv.device)
     _expect(mixed_qkv, (N, 2 * h_qk * d_k + h_v * d_v), torch.bfloat16, "mixed_qkv")
     _expect(conv_weight, (C, K), torch.float32, "conv_weight")
     if conv_window is not None:

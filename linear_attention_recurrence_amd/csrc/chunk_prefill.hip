@@ -289,6 +289,9 @@ __device__ __forceinline__ void gram_epilogue(PrepSmem& sm, const f32x4 (&acc)[5
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rt + 4 * g4 + i;
+      // G is nonincreasing (every g <= 0 by contract), but the prefix sums above are added
+      // in a different order for each token, so G_r - G_s (s <= r) may round to a tiny
+      // positive value; the bound keeps every in-chunk ratio at most 1, as it is exactly.
       const float decay = __expf(fminf(Gr[jj][i] - Gs[jj], 0.f));
       if (ISQ) val[i] = s <= r ? scale * decay * acc[jj][i] : 0.f;
       else sm.r1.A[r][s] = s < r ? Br[jj][i] * decay * acc[jj][i] : 0.f;
@@ -808,7 +811,7 @@ __device__ __forceinline__ void form_w_p(StateBuf& cur, const TvBuf<NTILE>& tv, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rt + 4 * g4 + i;
-      const float decay = __expf(fminf(Gr[i] - Gs, 0.f));
+      const float decay = __expf(fminf(Gr[i] - Gs, 0.f));   // bounded as in gram_epilogue
       pv[i] = to_bf16(s <= r ? scale * decay * acc[i] : 0.f);
     }
     *reinterpret_cast<bf16x4*>(cur.Pt + sw128(s, 16 * rt + 4 * g4)) = pv;

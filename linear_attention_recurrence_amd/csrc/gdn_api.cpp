@@ -70,6 +70,19 @@ gdn_status check_slots(const int32_t* slots, int32_t num_seqs, void* stream) {
   return GDN_OK;
 }
 
+// Every log-decay finite and <= 0 (alpha = exp(g) in (0, 1]).
+gdn_status check_log_decay(const float* g, size_t count, void* stream) {
+  if (!g || count == 0 || !contract_checks()) return GDN_OK;
+  std::vector<float> h(count);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(h.data(), g, sizeof(float) * count, hipMemcpyDeviceToHost, st) != hipSuccess)
+    return GDN_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return GDN_ERR_HIP;
+  for (const float x : h)
+    if (!(x <= 0.f) || !std::isfinite(x)) return GDN_ERR_SHAPE;
+  return GDN_OK;
+}
+
 #define GDN_TRY(expr)                      \
   do {                                     \
     const gdn_status gdn_st_ = (expr);     \
@@ -113,6 +126,7 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dt
   if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
   if (!final_state && total_tokens == 0) return GDN_OK;   // nothing observable to do
   GDN_TRY(check_seqlens(cu_seqlens, num_seqs, total_tokens, stream));
+  GDN_TRY(check_log_decay(g, (size_t)total_tokens * h_v, stream));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (io_dtype == GDN_F32)
     return from_hip(gdn::launch_recurrent_prefill(q, k, v, false, g, beta, cu_seqlens, num_seqs,
@@ -137,6 +151,7 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtyp
   if (num_seqs == 0) return GDN_OK;
   if (!q || !k || !v || !g || !beta || !state_pool || !o) return GDN_ERR_NULL;
   GDN_TRY(check_slots(state_slots, num_seqs, stream));
+  GDN_TRY(check_log_decay(g, (size_t)num_seqs * h_v, stream));
   return from_hip(gdn::launch_decode(q, k, v, io_dtype == GDN_BF16, g, beta, state_pool,
                                      state_slots, num_seqs, h_qk, h_v, scale, o,
                                      static_cast<hipStream_t>(stream)));
@@ -154,6 +169,7 @@ gdn_status gdn_verify_step(const void* q, const void* k, const void* v, gdn_dtyp
   if (num_seqs == 0 || num_tokens == 0) return GDN_OK;
   if (!q || !k || !v || !g || !beta || !state_pool || !o) return GDN_ERR_NULL;
   GDN_TRY(check_slots(state_slots, num_seqs, stream));
+  GDN_TRY(check_log_decay(g, (size_t)num_seqs * num_tokens * h_v, stream));
   return from_hip(gdn::launch_verify(q, k, v, io_dtype == GDN_BF16, g, beta, state_pool,
                                      state_slots, snapshots, num_seqs, num_tokens, h_qk, h_v,
                                      scale, o, static_cast<hipStream_t>(stream)));
@@ -174,6 +190,7 @@ gdn_status gdn_channel_decay_prefill(const void* q, const void* k, const void* v
   if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
   if (!final_state && total_tokens == 0) return GDN_OK;   // nothing observable to do
   GDN_TRY(check_seqlens(cu_seqlens, num_seqs, total_tokens, stream));
+  GDN_TRY(check_log_decay(g, (size_t)total_tokens * h_v * d_v, stream));
   return from_hip(gdn::launch_channel_prefill(q, k, v, io_dtype == GDN_BF16, g, beta, cu_seqlens,
                                               num_seqs, h_qk, h_v, scale, initial_state,
                                               final_state, o, static_cast<hipStream_t>(stream)));
@@ -191,6 +208,7 @@ gdn_status gdn_channel_decay_decode_step(const void* q, const void* k, const voi
   if (num_seqs == 0) return GDN_OK;
   if (!q || !k || !v || !g || !beta || !state_pool || !o) return GDN_ERR_NULL;
   GDN_TRY(check_slots(state_slots, num_seqs, stream));
+  GDN_TRY(check_log_decay(g, (size_t)num_seqs * h_v * d_v, stream));
   return from_hip(gdn::launch_channel_decode(q, k, v, io_dtype == GDN_BF16, g, beta, state_pool,
                                              state_slots, num_seqs, h_qk, h_v, scale, o,
                                              static_cast<hipStream_t>(stream)));
@@ -250,6 +268,7 @@ gdn_status gdn_decode_step_with_conv(const void* mixed_qkv, const float* conv_we
   if (conv_kernel > 1 && !conv_window) return GDN_ERR_NULL;
   GDN_TRY(check_slots(window_slots, num_seqs, stream));
   GDN_TRY(check_slots(state_slots, num_seqs, stream));
+  GDN_TRY(check_log_decay(g, (size_t)num_seqs * h_v, stream));
   return from_hip(gdn::launch_decode_with_conv(mixed_qkv, conv_weight, conv_kernel, conv_window,
                                                window_slots, q_scale, g, beta, state_pool,
                                                state_slots, num_seqs, h_qk, h_v, scale, o,

@@ -86,3 +86,33 @@ def test_decode_slot_contracts(monkeypatch):
                             b.reshape(N, 1, 2).contiguous(), pool0.clone(), 1.0,
                             state_slots=torch.tensor([0, 0, 1], dtype=torch.int32, device="cuda"))
     assert e.value.status == GDN_ERR_SHAPE
+
+
+def test_log_decay_contract(monkeypatch):
+    """A log-decay that is positive, infinite or NaN breaks the contract alpha = exp(g) in
+    (0, 1]; with the checks on, prefill and decode reject it with nothing written."""
+    import torch
+    import linear_attention_recurrence_amd as gdn
+    x = workloads.make_prefill([70, 33], h_qk=1, h_v=2, with_initial_state=True, seed=182)
+    monkeypatch.setenv("GDN_CHECK_CONTRACTS", "1")
+    d = prefill_to_dev(x)
+    for bad in (0.25, float("inf"), float("-inf"), float("nan")):
+        g = d["g"].clone()
+        g[40, 1] = bad
+        fin = torch.full((2, 2, 128, 128), 7.0, dtype=torch.float32, device="cuda")
+        with pytest.raises(gdn.GdnError) as e:
+            gdn.gdn_chunk_prefill(d["q"], d["k"], d["v"], g, d["beta"], d["cu"], x.scale,
+                                  initial_state=d["s0"], final_state=fin)
+        assert e.value.status == GDN_ERR_SHAPE, bad
+        torch.cuda.synchronize()
+        assert bool((fin == 7.0).all())
+        pool = d["s0"].clone()
+        with pytest.raises(gdn.GdnError) as e:
+            gdn.gdn_decode_step(d["q"][:2], d["k"][:2], d["v"][:2], g[40:42], d["beta"][:2],
+                                pool, x.scale)
+        assert e.value.status == GDN_ERR_SHAPE, bad
+    g = d["g"].clone()
+    g[5, 0] = 0.0                      # alpha = 1 is inside the contract
+    gdn.gdn_chunk_prefill(d["q"], d["k"], d["v"], g, d["beta"], d["cu"], x.scale,
+                          initial_state=d["s0"])
+    torch.cuda.synchronize()

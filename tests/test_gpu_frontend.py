@@ -67,9 +67,10 @@ def test_conv_prep_short_kernels(K):
 
 def test_config4_front_end_and_prefill():
     """64 sequences, lengths uniform in [128, 8192], mixed bf16 [sum T][8192], conv k = 4,
-    S0 ~ N(0, 0.02), final states. Stage 1: the front end on three whole sequences against
-    the fp64 front end. Stage 2: the recurrence on the GPU's own bf16 q, k, v for those
-    sequences (all heads) against the oracle fed the same bits."""
+    S0 ~ N(0, 0.02), final states. Stage 1: the front end on three whole sequences (the
+    shortest, the first and the longest) against the fp64 front end. Stage 2: the
+    recurrence on the GPU's own bf16 q, k, v, every sequence and head, against the oracle
+    fed the same bits."""
     import torch
     import linear_attention_recurrence_amd as gdn
     fe = workloads.config4()
@@ -89,19 +90,35 @@ def test_config4_front_end_and_prefill():
         _check_one_rounding(to_host_f64(q[t0:t1]), qr, "q seq %d" % n)
         _check_one_rounding(to_host_f64(k[t0:t1]), kr, "k seq %d" % n)
         _check_one_rounding(to_host_f64(v[t0:t1]), vr, "v seq %d" % n)
-    # stage 2: the recurrence on the GPU's own front-end output (scale 1: q is pre-scaled)
+    # stage 2: the recurrence on the GPU's own front-end output (scale 1: q is pre-scaled),
+    # every sequence and head against the oracle fed the same bits, eight sequences at a time
+    # (the fp64 read-out of the whole batch would take 9 GB)
     qb, kb, vb = bf16_bits(q), bf16_bits(k), bf16_bits(v)
     x = workloads.PrefillInputs(q=qb, k=kb, v=vb, g=fe.g, beta=fe.beta, cu_seqlens=cu,
                                 initial_state=fe.initial_state, scale=1.0, io_dtype="bf16")
-    o_h = to_host_f64(o)
+    o_h = o.float()
     fin_h = to_host_f64(fin)
-    refp = oracle_prefill(x, seqs=seqs)
-    for n in seqs:
-        t0, t1 = int(cu[n]), int(cu[n + 1])
-        o_sel = np.stack([o_h[t0:t1, h] for h in range(32)])
-        r_sel = np.stack([refp[(n, h)][0] for h in range(32)])
-        check_outputs(o_sel, r_sel, "config4 seq %d" % n)
-        check_state(fin_h[n], np.stack([refp[(n, h)][1] for h in range(32)]), "config4 seq %d" % n)
+    dsq = osq = 0.0
+    max_abs = 0.0
+    s_rel = []
+    for b0 in range(0, fe.num_seqs, 8):
+        seqs_b = list(range(b0, min(fe.num_seqs, b0 + 8)))
+        refp = oracle_prefill(x, seqs=seqs_b)
+        for n in seqs_b:
+            t0, t1 = int(cu[n]), int(cu[n + 1])
+            o_n = o_h[t0:t1].double().cpu().numpy()
+            r_n = np.stack([refp[(n, h)][0] for h in range(32)], axis=1)
+            d = o_n - r_n
+            dsq += float(np.sum(d * d))
+            osq += float(np.sum(r_n * r_n))
+            max_abs = max(max_abs, float(np.abs(d).max()))
+            s_rel.append(check_state(fin_h[n], np.stack([refp[(n, h)][1] for h in range(32)]),
+                                     "config4 seq %d" % n))
+        del refp
+    rel_o = (dsq / osq) ** 0.5
+    print("config4 all sequences: max|do| %.2e relF(o) %.2e worst relF(S) %.2e"
+          % (max_abs, rel_o, max(s_rel)))
+    assert max_abs <= 2e-2 and rel_o <= 5e-3
 
 
 def _prompt_then_decode(fe, prompt_lens, steps, slots_perm=None):

@@ -263,28 +263,37 @@ def test_beta_zero_is_pure_decay():
         np.testing.assert_allclose(o[:, h], expect, rtol=1e-12, atol=1e-15)
 
 
-def _printed_loop_alpha_one(Q, K, V, beta):
-    """The token loop printed in section "01 . GatedDeltaNet(config)" of page
-    "Qwen3-Next 80B-A3B -- The Evolving Transformer", restated with torch on the CPU for
-    one head and alpha = 1 (its per-channel gate fixed to one): the correction is taken
-    against the state, the state is updated, then read out with the query."""
-    W = torch.zeros(V.shape[1], K.shape[1], dtype=torch.float64)
-    outs = []
-    for t in range(Q.shape[0]):
-        err = V[t] - W @ K[t]
-        W = W + beta[t] * torch.outer(err, K[t])
-        outs.append(W @ Q[t])
-    return torch.stack(outs), W
+def _product_form(Q, K, V, beta, S0):
+    """States and read-outs of one chain at alpha = 1 from the transition-matrix product
+    (not from the per-token rank-1 update): with M_t = I - beta_t k_t k_t^T,
+        S_t = S_0 M_1 ... M_t + sum_{s <= t} beta_s v_s k_s^T M_{s+1} ... M_t,
+    every S_t formed from scratch by numpy matrix products, and o_t = S_t q_t."""
+    T, d_k = K.shape
+    Ms = [np.eye(d_k) - beta[t] * np.outer(K[t], K[t]) for t in range(T)]
+    outs, S = [], None
+    for t in range(T):
+        P = np.eye(d_k)
+        S = np.zeros_like(S0)
+        for s in range(t, -1, -1):          # P = M_{s+1} ... M_t, built from the right
+            S = S + beta[s] * np.outer(V[s], K[s]) @ P
+            P = Ms[s] @ P
+        S = S + S0 @ P
+        outs.append(S @ Q[t])
+    return np.stack(outs), S
 
 
-def test_alpha_one_matches_printed_loop():
-    x = workloads.make_prefill([50], h_qk=1, h_v=1, d_k=12, d_v=10, io_dtype="f32", seed=12)
+def test_alpha_one_matches_product_form():
+    """At alpha = 1 (no decay) the oracle equals the transition-matrix product form of the
+    update, at a float size (T = 50, d_k = 12, d_v = 10) beyond the exact brute force."""
+    x = workloads.make_prefill([50], h_qk=1, h_v=1, d_k=12, d_v=10, io_dtype="f32",
+                               with_initial_state=True, seed=12)
     q, k, v, b = x.as_f64("q"), x.as_f64("k"), x.as_f64("v"), x.as_f64("beta")
-    o, fin, _ = oracle.recurrence(q, k, v, np.zeros_like(b), b, x.cu_seqlens, 1.0)
-    o_ref, W = _printed_loop_alpha_one(torch.from_numpy(q[:, 0]), torch.from_numpy(k[:, 0]),
-                                       torch.from_numpy(v[:, 0]), torch.from_numpy(b[:, 0]))
-    np.testing.assert_allclose(o[:, 0], o_ref.numpy(), rtol=1e-12, atol=1e-14)
-    np.testing.assert_allclose(fin[0, 0], W.numpy(), rtol=1e-12, atol=1e-14)
+    s0 = x.as_f64("initial_state")
+    o, fin, _ = oracle.recurrence(q, k, v, np.zeros_like(b), b, x.cu_seqlens, 1.0,
+                                  initial_state=s0)
+    o_ref, S = _product_form(q[:, 0], k[:, 0], v[:, 0], b[:, 0], s0[0, 0])
+    np.testing.assert_allclose(o[:, 0], o_ref, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(fin[0, 0], S, rtol=1e-11, atol=1e-13)
 
 
 def test_chaining_and_varlen_and_zero_length():

@@ -15,6 +15,9 @@ section "Model Overview": 32 V heads, 16 QK heads, head dim 128):
   N(0, 1) (tails cut at about 4.3 sigma) that is several times faster to draw than
   numpy's ziggurat, which matters for the 2.3-billion-element packed batch.
 * v ~ N(0, 1).
+* fp32 tensors (q, k, v of an fp32-I/O batch, and every fp32 state) are drawn at full fp32
+  precision with numpy's own normal generator, so no fp32 input is exactly representable
+  in bf16 by construction (a kernel that rounded one to bf16 would show it).
 * beta = sigmoid(N(0, 1)), so beta lies in (0, 1).
 * g = log(alpha) = -softplus(N(0, 1)) * 0.1, so alpha lies in (0, 1).
 * initial states ~ N(0, 0.02) (0.02 is a standard deviation).
@@ -91,9 +94,15 @@ def normal_f32(rng: np.random.Generator, shape) -> np.ndarray:
     return bf16_bits_to_f32(normal_bf16_bits(rng, shape))
 
 
-def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
-    """N(0,1) vectors along the last axis, divided by their L2 norm (fp32)."""
-    x = normal_f32(rng, shape)
+def normal_full_f32(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0, 1) draws at full fp32 precision (numpy's normal generator)."""
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def _unit_rows(rng: np.random.Generator, shape, full: bool = False) -> np.ndarray:
+    """N(0,1) vectors along the last axis, divided by their L2 norm (fp32). `full` draws the
+    vectors at full fp32 precision instead of from the bf16-precision table."""
+    x = normal_full_f32(rng, shape) if full else normal_f32(rng, shape)
     n = np.sqrt(np.einsum("...i,...i->...", x, x, dtype=np.float32))[..., None]
     return (x / np.maximum(n, np.float32(1e-12))).astype(np.float32)
 
@@ -158,20 +167,82 @@ def make_prefill(seq_lens, h_qk=H_QK, h_v=H_V, d_k=D_HEAD, d_v=D_HEAD, io_dtype=
     T = int(sum(seq_lens))
     cu = np.zeros(len(seq_lens) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(seq_lens)
-    q = _unit_rows(rng, (T, h_qk, d_k))
-    k = _unit_rows(rng, (T, h_qk, d_k))
-    v = normal_f32(rng, (T, h_v, d_v))
+    if io_dtype not in ("bf16", "f32"):
+        raise ValueError(io_dtype)
+    full = io_dtype == "f32"
+    q = _unit_rows(rng, (T, h_qk, d_k), full)
+    k = _unit_rows(rng, (T, h_qk, d_k), full)
+    v = normal_full_f32(rng, (T, h_v, d_v)) if full else normal_f32(rng, (T, h_v, d_v))
     beta = _beta(rng, (T, h_v))
     g = _log_alpha(rng, (T, h_v))
     s0 = None
     if with_initial_state:
-        s0 = normal_f32(rng, (len(seq_lens), h_v, d_v, d_k)) * np.float32(state_std)
+        s0 = normal_full_f32(rng, (len(seq_lens), h_v, d_v, d_k)) * np.float32(state_std)
     if io_dtype == "bf16":
         q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
-    elif io_dtype != "f32":
-        raise ValueError(io_dtype)
     return PrefillInputs(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu, initial_state=s0,
                          scale=float(SCALE if scale is None else scale), io_dtype=io_dtype)
+
+
+EDGE_CASES = ("no_decay", "strong_decay", "repeated_key", "near_parallel_keys", "zero_rows")
+
+
+def make_prefill_edge(case: str, seq_lens, h_qk=H_QK, h_v=H_V, io_dtype="bf16",
+                      with_initial_state=False, seed=0) -> PrefillInputs:
+    """A packed batch drawn as make_prefill, then changed into one of the regimes where the
+    update's decay and write strength sit at their limits (page "Qwen3-Next -- How a running
+    memory and a searchable history cooperate", section "Correcting a memory instead of
+    adding to it": alpha sets how much is kept, beta how hard the key's slot is rewritten):
+
+    * "no_decay": alpha = 1 (g = 0) everywhere;
+    * "strong_decay": g = -5 per token, so exp of the running sum underflows fp32 inside a
+      64-token block;
+    * "repeated_key": beta = 0.999 and, in every 64-token block of each sequence (counted
+      from its first token), every token of a QK head carries that block's first key;
+    * "near_parallel_keys": beta = 0.999 and keys alternating between two unit vectors whose
+      inner product is about 0.999;
+    * "zero_rows": tokens 10..20 and 40 of every 64-token block have all-zero k and q rows.
+
+    Only inputs change; nothing of the method is computed here."""
+    if case not in EDGE_CASES:
+        raise ValueError(case)
+    x = make_prefill(seq_lens, h_qk=h_qk, h_v=h_v, io_dtype=io_dtype,
+                     with_initial_state=with_initial_state, seed=seed)
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    T = x.total_tokens
+    cu = x.cu_seqlens
+    pos = np.zeros(T, dtype=np.int64)          # position of each token in its sequence
+    for n in range(x.num_seqs):
+        pos[cu[n]:cu[n + 1]] = np.arange(cu[n + 1] - cu[n])
+    as_f32 = (lambda a: bf16_bits_to_f32(a)) if io_dtype == "bf16" else (lambda a: a)
+    store = f32_to_bf16_bits if io_dtype == "bf16" else (lambda a: a.astype(np.float32))
+    if case == "no_decay":
+        x.g = np.zeros_like(x.g)
+    elif case == "strong_decay":
+        x.g = np.full_like(x.g, -5.0)
+    elif case == "repeated_key":
+        x.beta = np.full_like(x.beta, 0.999)
+        k = as_f32(x.k).copy()
+        first = np.arange(T) - (pos % 64)      # token index of each token's block start
+        k = k[first]
+        x.k = store(k)
+    elif case == "near_parallel_keys":
+        x.beta = np.full_like(x.beta, 0.999)
+        d_k = x.k.shape[2]
+        a = _unit_rows(rng, (h_qk, d_k))
+        e = _unit_rows(rng, (h_qk, d_k))
+        b = a + np.float32(0.045) * (e - np.sum(a * e, axis=-1, keepdims=True) * a)
+        b = (b / np.linalg.norm(b, axis=-1, keepdims=True)).astype(np.float32)
+        k = np.where((pos % 2 == 0)[:, None, None], a[None], b[None]).astype(np.float32)
+        x.k = store(k)
+    elif case == "zero_rows":
+        z = ((pos % 64 >= 10) & (pos % 64 <= 20)) | (pos % 64 == 40)
+        k = as_f32(x.k).copy()
+        q = as_f32(x.q).copy()
+        k[z] = 0.0
+        q[z] = 0.0
+        x.k, x.q = store(k), store(q)
+    return x
 
 
 def channel_log_alpha(rows: int, h_v=H_V, d_v=D_HEAD, seed=1007) -> np.ndarray:
@@ -217,7 +288,7 @@ def make_decode(num_seqs=256, h_qk=H_QK, h_v=H_V, d=D_HEAD, ring=16, pool_size=N
     """A state pool and a ring of per-step single-token inputs."""
     rng = np.random.Generator(np.random.PCG64(seed))
     P = num_seqs if pool_size is None else int(pool_size)
-    pool = normal_f32(rng, (P, h_v, d, d)) * np.float32(state_std)
+    pool = normal_full_f32(rng, (P, h_v, d, d)) * np.float32(state_std)
     q = f32_to_bf16_bits(_unit_rows(rng, (ring, num_seqs, h_qk, d)))
     k = f32_to_bf16_bits(_unit_rows(rng, (ring, num_seqs, h_qk, d)))
     v = normal_bf16_bits(rng, (ring, num_seqs, h_v, d))
@@ -278,7 +349,7 @@ def make_frontend(seq_lens, h_qk=H_QK, h_v=H_V, d_k=D_HEAD, d_v=D_HEAD, conv_ker
     g = _log_alpha(rng, (T, h_v))
     s0 = None
     if with_initial_state:
-        s0 = normal_f32(rng, (len(seq_lens), h_v, d_v, d_k)) * np.float32(0.02)
+        s0 = normal_full_f32(rng, (len(seq_lens), h_v, d_v, d_k)) * np.float32(0.02)
     return FrontEndInputs(mixed=mixed, conv_weight=w, cu_seqlens=cu, g=g, beta=beta,
                           initial_state=s0, h_qk=h_qk, h_v=h_v, d_k=d_k, d_v=d_v,
                           q_scale=float(d_k ** -0.5))
