@@ -70,10 +70,10 @@ const char* gdn_status_string(gdn_status s);
 
 /*
  * Bytes of device workspace gdn_chunk_prefill needs (io_dtype GDN_BF16) for these sizes: for
- * every 64-token chunk, 44032 bytes per V head (decay factors, T diag(beta) =
- * (I + A)^-1 diag(beta) as a hi + lo bf16 pair, and either -W with the masked and decayed
- * Q K^T or -T diag(beta gam), depending on how many heads the call has), sized for
- * ceil(total_tokens / 64) + num_seqs chunks so no host read of cu_seqlens is needed.
+ * every 64-token chunk, 25600 bytes per V head (decay factors, and T diag(beta) =
+ * (I + A)^-1 diag(beta) and the masked and decayed Q K^T each as a hi + lo bf16 pair),
+ * sized for ceil(total_tokens / 64) + num_seqs chunks so no host read of cu_seqlens is
+ * needed.
  * Returns 0 for invalid sizes. The contents are scratch: nothing persists between calls,
  * and calls sharing a workspace must not overlap.
  */

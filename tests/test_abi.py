@@ -48,11 +48,11 @@ def test_status_strings():
 
 
 def test_workspace_query():
-    """The documented size: per chunk 44032 B per V head, for ceil(T / 64) + N chunks."""
+    """The documented size: per chunk 25600 B per V head, for ceil(T / 64) + N chunks."""
     lib, _ = _lib()
     for T, N in ((4096, 1), (32768, 1), (276989, 64), (0, 3), (65, 2)):
         chunks = -(-T // 64) + N
-        expect = chunks * 32 * 44032
+        expect = chunks * 32 * 25600
         assert lib.gdn_chunk_prefill_workspace_bytes(T, N, 16, 32, 128, 128) == expect
     assert lib.gdn_chunk_prefill_workspace_bytes(-1, 1, 16, 32, 128, 128) == 0
     assert lib.gdn_chunk_prefill_workspace_bytes(10, 1, 16, 30, 128, 128) == 0
