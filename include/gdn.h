@@ -107,6 +107,37 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dt
                              const float* initial_state, float* final_state,
                              void* o, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the library's own device scratch behind gdn_chunk_prefill_noalloc (per GPU). */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * gdn_chunk_prefill for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same operation,
+ * arguments and results as gdn_chunk_prefill (bit for bit: the same kernels), without the
+ * workspace arguments: the workspace is a static device array of GDN_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per GPU, held from the first such call on that GPU until the
+ * process ends. The call allocates nothing (no hipMalloc, no hipFree, no allocating library
+ * routine); the caller still owns q, k, v, g, beta, cu_seqlens, the states and o.
+ *
+ * Limit: sizes for which gdn_chunk_prefill_workspace_bytes(...) exceeds
+ * GDN_NOALLOC_SCRATCH_BYTES return GDN_ERR_WORKSPACE with nothing launched (with 32 V heads:
+ * ceil(total_tokens / 64) + num_seqs <= 81, e.g. one sequence of up to 5,120 tokens);
+ * GDN_F32 needs no workspace and has no limit.
+ *
+ * Sharing: every call on one GPU uses that GPU's one array, which keeps whatever the last
+ * call left in it; nothing in it needs to start at zero (each call writes every byte of it
+ * that it later reads). Calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race on the array and give undefined results; calls
+ * ordered on one stream, or on different GPUs, are safe. The first call on a GPU looks up
+ * that GPU's copy of the array (hipGetSymbolAddress); a failure there returns GDN_ERR_HIP.
+ */
+gdn_status gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
+                                     const float* g, const float* beta,
+                                     const int32_t* cu_seqlens, int32_t num_seqs,
+                                     int32_t total_tokens, int32_t h_qk, int32_t h_v, int32_t d_k,
+                                     int32_t d_v, float scale, const float* initial_state,
+                                     float* final_state, void* o, void* stream);
+
 /*
  * Decode: one token for each of num_seqs sequences, updating their states in place.
  *

@@ -23,7 +23,10 @@ GDN_BF16, GDN_F32 = 0, 1
 EXPORTED = ("gdn_status_string", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill",
             "gdn_decode_step", "gdn_verify_step", "gdn_channel_decay_prefill",
             "gdn_channel_decay_decode_step", "gdn_conv_prep", "gdn_conv_decode_step",
-            "gdn_conv_window_from_prefill", "gdn_gated_rmsnorm", "gdn_decode_step_with_conv")
+            "gdn_conv_window_from_prefill", "gdn_gated_rmsnorm", "gdn_decode_step_with_conv",
+            "gdn_chunk_prefill_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
 
 _lib = None
 _P = ctypes.c_void_p
@@ -53,6 +56,9 @@ def load(path: Optional[str] = None):
     lib.gdn_chunk_prefill.restype = ctypes.c_int
     lib.gdn_chunk_prefill.argtypes = [_P, _P, _P, ctypes.c_int, _P, _P, _P, _I, _I, _I, _I, _I,
                                       _I, ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.gdn_chunk_prefill_noalloc.restype = ctypes.c_int
+    lib.gdn_chunk_prefill_noalloc.argtypes = [_P, _P, _P, ctypes.c_int, _P, _P, _P, _I, _I, _I, _I,
+                                              _I, _I, ctypes.c_float, _P, _P, _P, _P]
     lib.gdn_decode_step.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [_P, _P, _P, ctypes.c_int, _P, _P, _P, _P, _I, _I, _I, _I,
                                     _I, ctypes.c_float, _P, _P]
@@ -166,6 +172,30 @@ def gdn_chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, initial_state=None,
                                   _ptr(initial_state), _ptr(final_state), _ptr(o),
                                   _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "gdn_chunk_prefill")
+    return o
+
+
+def gdn_chunk_prefill_noalloc(q, k, v, g, beta, cu_seqlens, scale, o, initial_state=None,
+                              final_state=None, stream=None):
+    """gdn_chunk_prefill with its workspace in the library's own device scratch: nothing is
+    allocated, here or in the library, so o must be given. Shapes as gdn_chunk_prefill.
+    Returns o."""
+    T, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    N = cu_seqlens.numel() - 1
+    _expect(k, (T, h_qk, d_k), q.dtype, "k")
+    _expect(v, (T, h_v, d_v), q.dtype, "v")
+    _expect(g, (T, h_v), torch.float32, "g")
+    _expect(beta, (T, h_v), torch.float32, "beta")
+    _expect(cu_seqlens, (N + 1,), torch.int32, "cu_seqlens")
+    _expect(initial_state, (N, h_v, d_v, d_k), torch.float32, "initial_state")
+    _expect(final_state, (N, h_v, d_v, d_k), torch.float32, "final_state")
+    _expect(o, (T, h_v, d_v), q.dtype, "o")
+    st = load().gdn_chunk_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g),
+                                          _ptr(beta), _ptr(cu_seqlens), N, T, h_qk, h_v, d_k, d_v,
+                                          float(scale), _ptr(initial_state), _ptr(final_state),
+                                          _ptr(o), _stream(stream))
+    _check(st, "gdn_chunk_prefill_noalloc")
     return o
 
 

@@ -51,10 +51,20 @@
 // tokens, the value tile) are read with ds_read_b64_tr_b16: within each group of 16 lanes,
 // when lane i points at row k0 + i/4, columns n0 + 4(i%4) .. +3, lane j receives rows
 // k0 .. k0+3 of column n0 + j.
+#include <atomic>
+#include <mutex>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
+
+// Device scratch of the prefill variant that allocates nothing (gdn_chunk_prefill_noalloc):
+// its workspace lives here, one copy per GPU the library runs on, held until the process
+// ends. In host code `scratch` names a host-side stand-in, not the device array: the device
+// address comes from hipGetSymbolAddress, once per device (noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 namespace {
 
 constexpr int kC = 64;          // chunk length
@@ -1008,6 +1018,32 @@ __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
 }
 
 }  // namespace
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+      // with device `dev` current: that device's copy of the array
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 size_t chunk_prefill_workspace_bytes(int total_tokens, int num_seqs, int h_qk, int h_v) {
   (void)h_qk;

@@ -139,6 +139,37 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dt
                                             workspace, s));
 }
 
+gdn_status gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
+                                     const float* g, const float* beta,
+                                     const int32_t* cu_seqlens, int32_t num_seqs,
+                                     int32_t total_tokens, int32_t h_qk, int32_t h_v, int32_t d_k,
+                                     int32_t d_v, float scale, const float* initial_state,
+                                     float* final_state, void* o, void* stream) {
+  static_assert(GDN_NOALLOC_SCRATCH_BYTES == gdn::kNoAllocScratchBytes, "header and library agree");
+  if (num_seqs < 0 || total_tokens < 0) return GDN_ERR_SHAPE;
+  const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
+  if (!cu_seqlens) return GDN_ERR_NULL;
+  if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+  if (!final_state && total_tokens == 0) return GDN_OK;   // nothing observable to do
+  if (io_dtype == GDN_BF16 &&
+      gdn_chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v, d_k, d_v) > GDN_NOALLOC_SCRATCH_BYTES)
+    return GDN_ERR_WORKSPACE;
+  GDN_TRY(check_seqlens(cu_seqlens, num_seqs, total_tokens, stream));
+  GDN_TRY(check_log_decay(g, (size_t)total_tokens * h_v, stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (io_dtype == GDN_F32)
+    return from_hip(gdn::launch_recurrent_prefill(q, k, v, false, g, beta, cu_seqlens, num_seqs,
+                                                  h_qk, h_v, scale, initial_state, final_state,
+                                                  o, s));
+  void* ws = nullptr;
+  if (gdn::noalloc_scratch(&ws) != hipSuccess) return GDN_ERR_HIP;
+  return from_hip(gdn::launch_chunk_prefill(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
+                                            h_qk, h_v, scale, initial_state, final_state, o, ws, s));
+}
+
 gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
                            const float* g, const float* beta,
                            float* state_pool, const int32_t* state_slots,

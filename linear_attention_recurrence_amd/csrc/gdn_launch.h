@@ -60,6 +60,12 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
                                 const float* s0, float* s_final, void* o, void* workspace,
                                 hipStream_t stream);
 
+// The prefill workspace of gdn_chunk_prefill_noalloc: the device address of this GPU's
+// copy of a static device array of kNoAllocScratchBytes, looked up once per device
+// (chunk_prefill.hip).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Causal depthwise conv + SiLU + q/k L2 norm + q scale (conv_prep.hip).
 hipError_t launch_conv_prep(const void* mixed, const float* w, int K, const int32_t* cu,
                             int num_seqs, int total_tokens, int h_qk, int h_v, float q_scale,

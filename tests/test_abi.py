@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
                                             "gdn_channel_decay_decode_step",
                                             "gdn_conv_prep", "gdn_conv_decode_step",
                                             "gdn_conv_window_from_prefill", "gdn_gated_rmsnorm",
-                                            "gdn_decode_step_with_conv"])
+                                            "gdn_decode_step_with_conv",
+                                            "gdn_chunk_prefill_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -116,6 +117,37 @@ def test_prefill_validation():
     assert call(ws=None) == L.GDN_ERR_WORKSPACE
     assert call(ws=P(8), wsb=1000) == L.GDN_ERR_WORKSPACE
     assert call(n=0, T=0) == L.GDN_OK
+
+
+def test_prefill_noalloc_validation():
+    """The variant that allocates nothing validates like gdn_chunk_prefill and rejects, with
+    nothing launched, sizes whose workspace would exceed its device scratch."""
+    lib, L = _lib()
+    f = lib.gdn_chunk_prefill_noalloc
+    P = _fake
+    ok = dict(q=P(1), k=P(2), v=P(3), dt=L.GDN_BF16, g=P(4), b=P(5), cu=P(6), n=1, T=100,
+              hqk=16, hv=32, dk=128, dv=128, sc=0.1, s0=None, sf=None, o=P(7), st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["dt"], a["g"], a["b"], a["cu"], a["n"], a["T"],
+                 a["hqk"], a["hv"], a["dk"], a["dv"], a["sc"], a["s0"], a["sf"], a["o"], a["st"])
+
+    assert call(cu=None) == L.GDN_ERR_NULL
+    assert call(o=None) == L.GDN_ERR_NULL
+    assert call(T=-5) == L.GDN_ERR_SHAPE
+    assert call(n=0, T=10) == L.GDN_ERR_SHAPE
+    assert call(hqk=3, hv=32) == L.GDN_ERR_SHAPE
+    assert call(dk=96) == L.GDN_ERR_UNSUPPORTED
+    assert call(dt=2) == L.GDN_ERR_UNSUPPORTED
+    assert call(n=0, T=0) == L.GDN_OK
+    # the scratch limit: one sequence of 5,120 tokens at 32 V heads fits, 5,121 does not
+    need = lambda T, n: L.gdn_chunk_prefill_workspace_bytes(T, n, 16, 32, 128, 128)
+    assert need(5120, 1) <= L.NOALLOC_SCRATCH_BYTES < need(5121, 1)
+    assert call(T=5121) == L.GDN_ERR_WORKSPACE
+    assert call(T=32768) == L.GDN_ERR_WORKSPACE
+    assert call(T=200, n=80) == L.GDN_ERR_WORKSPACE       # ceil(200 / 64) + 80 > 81 chunks
 
 
 def test_conv_prep_validation():
