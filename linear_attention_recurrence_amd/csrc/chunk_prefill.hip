@@ -135,23 +135,41 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ bf16x4 lds_tr4(const bf16* p) {
-  const bf16x4_gcc r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p));
+  const bf16x4_gcc r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(uint32_t)(uintptr_t)p);
   return __builtin_bit_cast(bf16x4, r);
 }
 
+// Two fp32 values rounded to bf16 (nearest even) and packed into one word, x in the low half.
+__device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {to_bf16(x), to_bf16(y)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // x = hi + lo for eight fp32 values (two accumulator quads), each half rounded to bf16:
-// hi = bf16(x), lo = bf16(x - hi), so hi + lo carries about 16 bits of x. Contraction stays
-// off: every kernel that calls this must round the same way.
+// hi = bf16(x), lo = bf16(x - hi), so hi + lo carries about 16 bits of x. Each pair is
+// rounded by one packed conversion and its halves widened back by a shift and a mask (three
+// instructions per value). Contraction stays off: every kernel that calls this must round
+// the same way.
 __device__ __forceinline__ void split8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
 #pragma clang fp contract(off)
+  u32x4 h, l;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16 ha = to_bf16(a[i]), hb = to_bf16(b[i]);
-    hi[i] = ha;
-    hi[4 + i] = hb;
-    lo[i] = to_bf16(a[i] - (float)ha);
-    lo[4 + i] = to_bf16(b[i] - (float)hb);
+  for (int p = 0; p < 4; ++p) {
+    const float x = p < 2 ? a[2 * p] : b[2 * p - 4];
+    const float y = p < 2 ? a[2 * p + 1] : b[2 * p - 3];
+    const uint32_t w = pk_bf16(x, y);
+    h[p] = w;
+    l[p] = pk_bf16(x - __builtin_bit_cast(float, w << 16), y - __builtin_bit_cast(float, w & 0xffff0000u));
   }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// The LDS-space pointer of a generic pointer into __shared__ memory: its low 32 bits are the
+// LDS address. (An address-space cast would test the generic pointer for null first.)
+__device__ __forceinline__ lds_void_ptr lds_addr(const void* p) {
+  return (lds_void_ptr)(uint32_t)(uintptr_t)p;
 }
 
 // ---- LDS images: unpadded rows, 16-byte pieces XOR-swizzled so that the row reads and the
@@ -214,29 +232,29 @@ __device__ int first_chunk(const int32_t* cu, int n, int lane) {
 
 // Direct global -> LDS copy of rows of a [rows][128] bf16 matrix (256-byte rows) into a
 // swizzled image, 1 KB per instruction: piece i fills image rows 4 i .. 4 i + 3. Image row r
-// comes from source row min(r, nv - 1) at `src + row * stride`: rows past the chunk end
-// repeat the last valid row and only feed results that are discarded or multiplied by zero.
-__device__ __forceinline__ void dma_rows256(const bf16* src, size_t stride, int nv, bf16* img, int i,
+// comes from source row min(r, nv - 1) at byte `r * stride` from `src`: rows past the chunk
+// end repeat the last valid row and only feed results that are discarded or multiplied by
+// zero. The source address is a uniform base plus a 32-bit lane offset.
+__device__ __forceinline__ void dma_rows256(const bf16* src, uint32_t stride, int nv, bf16* img, int i,
                                             int lane) {
   const int r = 4 * i + (lane >> 4);
-  const int slot = lane & 15;
-  const int piece = slot ^ ((r & 7) << 1) ^ ((r >> 3) & 1);
-  const int rs = min(r, nv - 1);
-  __builtin_amdgcn_global_load_lds(src + (size_t)rs * stride + piece * 8,
-                                   (lds_void_ptr)(img + 4 * i * kD), 16, 0, 0);
+  const uint32_t piece = (uint32_t)((lane & 15) ^ ((r & 7) << 1) ^ ((r >> 3) & 1));
+  const uint32_t off = __umul24((uint32_t)min(r, nv - 1), stride) + 16u * piece;
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(src) + off, lds_addr(img + 4 * i * kD),
+                                   16, 0, 0);
 }
 // A straight 1 KB copy (16 bytes per lane).
 __device__ __forceinline__ void dma_1k(const void* src, void* dst, int lane) {
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(src) + 16 * lane, (lds_void_ptr)dst, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(src) + 16 * lane, lds_addr(dst), 16, 0, 0);
 }
 // Tokens 32 i .. 32 i + 31 of a [64][16] bf16 value tile (32-byte rows; two lanes per
 // token); rows past the chunk end repeat the last valid row (T diag(beta) is zero there).
-__device__ __forceinline__ void dma_vtile(const bf16* vb, size_t v_stride, int nv, bf16* tile, int i,
+// v_stride is in bytes.
+__device__ __forceinline__ void dma_vtile(const bf16* vb, uint32_t v_stride, int nv, bf16* tile, int i,
                                           int lane) {
-  const int r = 32 * i + (lane >> 1);
-  const int row = r < nv ? r : nv - 1;
-  __builtin_amdgcn_global_load_lds(vb + (size_t)row * v_stride + 8 * (lane & 1),
-                                   (lds_void_ptr)(tile + 512 * i), 16, 0, 0);
+  const uint32_t r = (uint32_t)min(32 * i + (lane >> 1), nv - 1);
+  const uint32_t off = __umul24(r, v_stride) + 16u * (lane & 1);
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(vb) + off, lds_addr(tile + 512 * i), 16, 0, 0);
 }
 
 // Lower 16 x 16 tile t (0..9, row-major over the lower triangle) of a 64 x 64 product.
@@ -325,8 +343,9 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
   const size_t qk_stride = (size_t)a.h_qk * kD;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    dma_rows256(a.k + (size_t)t0 * qk_stride + (size_t)j * kD, qk_stride, nv, sm.K, 4 * w + i, lane);
-    if (WITH_P) dma_rows256(a.q + (size_t)t0 * qk_stride + (size_t)j * kD, qk_stride, nv, sm.r1.Q, 4 * w + i, lane);
+    dma_rows256(a.k + (size_t)t0 * qk_stride + (size_t)j * kD, (uint32_t)qk_stride * 2, nv, sm.K, 4 * w + i, lane);
+    if (WITH_P)
+      dma_rows256(a.q + (size_t)t0 * qk_stride + (size_t)j * kD, (uint32_t)qk_stride * 2, nv, sm.r1.Q, 4 * w + i, lane);
   }
   if (tid < kC) {
     float gg = 0.f, bb = 0.f;
@@ -536,61 +555,82 @@ struct ChainOps {
 };
 
 // One chunk of the chain from one state to the next, for 16 value rows (the lane's row l16
-// of the tile): S split into hi + lo, X = K S^T (tokens x rows), R = V - diag(gam) X,
-// U = T diag(beta) R, then S^T <- gam_C S^T + K^T (diag(gam_C / gam) U). Returns S's hi half
-// as the read-out's operand (Sh) and U in the accumulator layout (token tile rt: rows
-// 16 rt + 4 g4 + i of column l16).
-__device__ __forceinline__ void chain_chunk(const ChainOps& c, const LaneOffsets& lo, f32x4 (&St)[8],
-                                            bf16x8 (&Sh)[4], f32x4 (&U)[4], int lane) {
-#pragma clang fp contract(off)
-  const int g4 = lane >> 4;
-  // every operand of the chunk is read up front, so the LDS latency overlaps the products
-  bf16x8 ak[4][4], akt[8][2], th[kFrags], tl[kFrags];
+// of the tile), in three parts so that two waves can share it by key halves:
+//  chain_x      for key half kh (keys 64 kh .. 64 kh + 63, state tiles 4 kh .. 4 kh + 3):
+//               that half of S split into hi + lo and X_kh = K_kh S_kh^T (tokens x rows);
+//  chain_u      from X = X_0 + X_1: R = V - diag(gam) X, U = T diag(beta) R, and the decayed
+//               U split into hi + lo for the update;
+//  chain_update for key half kh: S_kh^T <- gam_C S_kh^T + K_kh^T (diag(gam_C / gam) U).
+// The halves of X are always summed as X_0 + X_1, so one wave doing both halves and two
+// waves doing one each give the same bits. S's hi half (Sh) is the read-out's operand; U is
+// returned in the accumulator layout (token tile rt: rows 16 rt + 4 g4 + i of column l16).
+// The parts take their LDS operands in registers (the load_* functions), so a caller can
+// issue every read of a chunk at once.
+
+// K rows of key half kh's two K-steps (A operands of X), token tiles 0..3.
+__device__ __forceinline__ void load_k_rows(const bf16* K, const LaneOffsets& lo, int kh, bf16x8 (&ak)[2][4]) {
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) ak[ks][rt] = lds8(c.K + lo.row[ks] + 2048 * rt);
+    for (int rt = 0; rt < 4; ++rt) ak[j][rt] = lds8(K + lo.row[2 * kh + j] + 2048 * rt);
+}
+// K^T operands of key half kh's four state tiles (A operands of the update).
+__device__ __forceinline__ void load_k_t(const bf16* K, const LaneOffsets& lo, int kh, bf16x8 (&akt)[4][2]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int mt = 4 * kh + m;
+    akt[m][0] = join8(lds_tr4(K + lo.k[mt]), lds_tr4(K + lo.k[mt] + 2048));
+    akt[m][1] = join8(lds_tr4(K + lo.k[mt] + 4096), lds_tr4(K + lo.k[mt] + 6144));
+  }
+}
+// The operands of chain_u: T diag(beta) hi and lo, the tile's values, gam, gam_C / gam.
+struct UOps {
+  bf16x8 th[kFrags], tl[kFrags];
   bf16x4 v4[4];
   f32x4 gam4[4], lam4[4];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    v4[rt] = lds_tr4(c.vt + lo.vt + 256 * rt);
-    gam4[rt] = *reinterpret_cast<const f32x4*>(&c.gl[16 * rt + 4 * g4]);
-    lam4[rt] = *reinterpret_cast<const f32x4*>(&c.gl[kC + 16 * rt + 4 * g4]);
-  }
-  const float gC = c.gl[kC - 1];
+};
+__device__ __forceinline__ void load_u_ops(const ChainOps& c, const LaneOffsets& lo, UOps& u, int lane) {
+  const int g4 = lane >> 4;
 #pragma unroll
   for (int f = 0; f < kFrags; ++f) {
-    th[f] = lds8(c.th + (f * 64 + lane) * 8);
-    tl[f] = lds8(c.tl + (f * 64 + lane) * 8);
+    u.th[f] = lds8(c.th + (f * 64 + lane) * 8);
+    u.tl[f] = lds8(c.tl + (f * 64 + lane) * 8);
   }
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    akt[mt][0] = join8(lds_tr4(c.K + lo.k[mt]), lds_tr4(c.K + lo.k[mt] + 2048));
-    akt[mt][1] = join8(lds_tr4(c.K + lo.k[mt] + 4096), lds_tr4(c.K + lo.k[mt] + 6144));
+  for (int rt = 0; rt < 4; ++rt) {
+    u.v4[rt] = lds_tr4(c.vt + lo.vt + 256 * rt);
+    u.gam4[rt] = *reinterpret_cast<const f32x4*>(&c.gl[16 * rt + 4 * g4]);
+    u.lam4[rt] = *reinterpret_cast<const f32x4*>(&c.gl[kC + 16 * rt + 4 * g4]);
   }
-  // S = Sh + Sl
-  bf16x8 Sl[4];
+}
+
+__device__ __forceinline__ void chain_x(const bf16x8 (&ak)[2][4], const f32x4 (&S)[4], bf16x8 (&Sh)[2],
+                                        f32x4 (&X)[4]) {
+  bf16x8 Sl[2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) split8(St[2 * ks], St[2 * ks + 1], Sh[ks], Sl[ks]);
-  // X = K S^T, low halves first
-  f32x4 X[4];
+  for (int j = 0; j < 2; ++j) split8(S[2 * j], S[2 * j + 1], Sh[j], Sl[j]);
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) X[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  for (int j = 0; j < 2; ++j)   // low halves first
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) X[rt] = mfma16x16x32(ak[ks][rt], Sl[ks], X[rt]);
+    for (int rt = 0; rt < 4; ++rt) X[rt] = mfma16x16x32(ak[j][rt], Sl[j], X[rt]);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) X[rt] = mfma16x16x32(ak[ks][rt], Sh[ks], X[rt]);
+    for (int rt = 0; rt < 4; ++rt) X[rt] = mfma16x16x32(ak[j][rt], Sh[j], X[rt]);
+}
+
+__device__ __forceinline__ void chain_u(const UOps& o, const f32x4 (&X0)[4], const f32x4 (&X1)[4],
+                                        f32x4 (&U)[4], bf16x8 (&Bh)[2], bf16x8 (&Bl)[2]) {
+#pragma clang fp contract(off)
   // R = V - diag(gam) X, then R = Rh + Rl as the B operands of the two 32-token K-steps
   f32x4 R[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) R[rt][i] = __builtin_fmaf(-gam4[rt][i], X[rt][i], (float)v4[rt][i]);
+    for (int i = 0; i < 4; ++i)
+      R[rt][i] = __builtin_fmaf(-o.gam4[rt][i], X0[rt][i] + X1[rt][i], (float)o.v4[rt][i]);
   bf16x8 Rh[2], Rl[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) split8(R[2 * ks], R[2 * ks + 1], Rh[ks], Rl[ks]);
@@ -600,26 +640,57 @@ __device__ __forceinline__ void chain_chunk(const ChainOps& c, const LaneOffsets
     f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks <= rt / 2; ++ks) {
-      u = mfma16x16x32(th[frag(rt, ks)], Rl[ks], u);
-      u = mfma16x16x32(tl[frag(rt, ks)], Rh[ks], u);
+      u = mfma16x16x32(o.th[frag(rt, ks)], Rl[ks], u);
+      u = mfma16x16x32(o.tl[frag(rt, ks)], Rh[ks], u);
     }
 #pragma unroll
-    for (int ks = 0; ks <= rt / 2; ++ks) u = mfma16x16x32(th[frag(rt, ks)], Rh[ks], u);
+    for (int ks = 0; ks <= rt / 2; ++ks) u = mfma16x16x32(o.th[frag(rt, ks)], Rh[ks], u);
     U[rt] = u;
   }
   // the decayed U as a hi + lo pair for the update
-  bf16x8 Bh[2], Bl[2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) split8(U[2 * ks] * lam4[2 * ks], U[2 * ks + 1] * lam4[2 * ks + 1], Bh[ks], Bl[ks]);
-  // S^T <- gam_C S^T + K^T (diag(gam_C / gam) U)
+  for (int ks = 0; ks < 2; ++ks)
+    split8(U[2 * ks] * o.lam4[2 * ks], U[2 * ks + 1] * o.lam4[2 * ks + 1], Bh[ks], Bl[ks]);
+}
+
+__device__ __forceinline__ void chain_update(const bf16x8 (&akt)[4][2], f32x4 (&S)[4], const bf16x8 (&Bh)[2],
+                                             const bf16x8 (&Bl)[2], float gC) {
+#pragma clang fp contract(off)
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    f32x4 s = St[mt] * gC;
-    s = mfma16x16x32(akt[mt][0], Bh[0], s);
-    s = mfma16x16x32(akt[mt][0], Bl[0], s);
-    s = mfma16x16x32(akt[mt][1], Bh[1], s);
-    St[mt] = mfma16x16x32(akt[mt][1], Bl[1], s);
+  for (int m = 0; m < 4; ++m) {
+    f32x4 s = S[m] * gC;
+    s = mfma16x16x32(akt[m][0], Bh[0], s);
+    s = mfma16x16x32(akt[m][0], Bl[0], s);
+    s = mfma16x16x32(akt[m][1], Bh[1], s);
+    S[m] = mfma16x16x32(akt[m][1], Bl[1], s);
   }
+}
+
+// The whole chunk of the chain in one wave: both key halves (S0 = keys 0..63, S1 = 64..127),
+// each part's operands read just before it.
+__device__ __forceinline__ void chain_chunk(const ChainOps& c, const LaneOffsets& lo, f32x4 (&S0)[4],
+                                            f32x4 (&S1)[4], bf16x8 (&Sh)[4], f32x4 (&U)[4], int lane) {
+  f32x4 X0[4], X1[4];
+  bf16x8 sh0[2], sh1[2], Bh[2], Bl[2];
+  {
+    bf16x8 ak[2][4];
+    load_k_rows(c.K, lo, 0, ak);
+    chain_x(ak, S0, sh0, X0);
+    load_k_rows(c.K, lo, 1, ak);
+    chain_x(ak, S1, sh1, X1);
+  }
+  Sh[0] = sh0[0]; Sh[1] = sh0[1]; Sh[2] = sh1[0]; Sh[3] = sh1[1];
+  {
+    UOps uo;
+    load_u_ops(c, lo, uo, lane);
+    chain_u(uo, X0, X1, U, Bh, Bl);
+  }
+  const float gC = c.gl[kC - 1];
+  bf16x8 akt[4][2];
+  load_k_t(c.K, lo, 0, akt);
+  chain_update(akt, S0, Bh, Bl, gC);
+  load_k_t(c.K, lo, 1, akt);
+  chain_update(akt, S1, Bh, Bl, gC);
 }
 
 // The operands one chunk of the read-out reads from LDS.
@@ -710,33 +781,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const PrefillArgs& a,
                                            nv * a.h_v * kD * 2, 0x00020000);
 }
 
-__device__ __forceinline__ void load_state(const PrefillArgs& a, int n, int h, int row0, f32x4 (&St)[8],
-                                           int lane) {
+// Key half kh of the lane's value row: S[mt] = S[row0 + l16][32 (mt' / 2) + 8 g4 + 4 (mt' % 2) + i]
+// for state tile mt' = 4 kh + mt.
+__device__ __forceinline__ void load_state(const PrefillArgs& a, int n, int h, int row0, int kh,
+                                           f32x4 (&S)[4], int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
-  const size_t off = (((size_t)n * a.h_v + h) * kD + row0 + l16) * kD;
+  const size_t off = (((size_t)n * a.h_v + h) * kD + row0 + l16) * kD + 64 * kh + 8 * g4;
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
-    St[mt] = a.s0 ? *reinterpret_cast<const f32x4*>(a.s0 + off + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1))
-                  : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < 4; ++mt)
+    S[mt] = a.s0 ? *reinterpret_cast<const f32x4*>(a.s0 + off + 32 * (mt >> 1) + 4 * (mt & 1))
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
 }
-__device__ __forceinline__ void store_state(const PrefillArgs& a, int n, int h, int row0, const f32x4 (&St)[8],
-                                            int lane) {
+__device__ __forceinline__ void store_state(const PrefillArgs& a, int n, int h, int row0, int kh,
+                                            const f32x4 (&S)[4], int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
-  const size_t off = (((size_t)n * a.h_v + h) * kD + row0 + l16) * kD;
+  const size_t off = (((size_t)n * a.h_v + h) * kD + row0 + l16) * kD + 64 * kh + 8 * g4;
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
-    *reinterpret_cast<f32x4*>(a.s_final + off + 32 * (mt >> 1) + 8 * g4 + 4 * (mt & 1)) = St[mt];
+  for (int mt = 0; mt < 4; ++mt)
+    *reinterpret_cast<f32x4*>(a.s_final + off + 32 * (mt >> 1) + 4 * (mt & 1)) = S[mt];
 }
 
 // ------------------------------------------------------------------------------------------
 // state_ro_kernel: the fewest-heads state pass (one 16-row value tile per workgroup, eight
-// workgroups per head) with the chain, the loads and the read-out on waves of their own. The
-// chain wave (wave 0) runs chain_chunk -- the dependent path from one chunk's state to the
-// next -- and hands S's hi half and U over. The read-out wave (wave 2) forms each chunk's
-// read-out during the next chunk from its own copies of Q, P^T and the decay factors, which
-// it loads itself. The loading wave (wave 1) streams K, T diag(beta), the value tile and the
-// decay factors one chunk ahead. One barrier per chunk and one at the end; the arithmetic is
-// that of the other shapes, so results agree bit for bit.
+// workgroups per head). The chain -- the dependent path from one chunk's state to the next --
+// runs on two waves, one per key half (waves 0 and 1: chain_x on their half, an exchange of
+// the halves of X through LDS, chain_u each, chain_update on their half). The read-out wave
+// (wave 3) forms each chunk's read-out during the next chunk from its own copies of Q, P^T
+// and the decay factors, which it loads itself, and S's hi half and U handed over by the
+// chain waves. The loading wave (wave 2) streams K, T diag(beta), the value tile and the
+// decay factors one chunk ahead. One workgroup barrier per chunk and one at the end; the two
+// chain waves also hand the halves of X to each other through LDS mid-chunk. The arithmetic
+// is that of the other shapes, so results agree bit for bit.
 // ------------------------------------------------------------------------------------------
 
 struct RoChainBuf {
@@ -752,25 +827,46 @@ struct RoReadBuf {
   bf16 pl[kFrags * 512];
   float gl[4 * kC];
 };
-// What the chain wave hands the read-out wave for one chunk, in lane order.
+// What the chain waves hand the read-out wave for one chunk, in lane order.
 struct Exchange {
   bf16x8 sh[4][64];
   f32x4 u[4][64];
 };
+// The two halves of X, exchanged between the two chain waves, and the handshake: ready[kh]
+// counts the chunks whose half kh is in x[kh].
+struct XHalves {
+  f32x4 x[2][4][64];
+  unsigned ready[2];
+};
 
-__device__ __forceinline__ void dma_ro_chain(const ChunkSrc& s, RoChainBuf& d, int qk_stride, int v_stride,
-                                             int lane) {
+// Wait until the other chain wave has published chunk `count - 1`'s half of X. Both chain
+// waves run the same chunks and each publishes its half before it waits for the other's, so
+// the wait always ends; the spin is capped all the same (about 2^22 polls), so a fault in
+// that reasoning could not hang the GPU.
+__device__ __forceinline__ void wait_ready(const unsigned* ready, unsigned count) {
+  for (int spin = 0; spin < (1 << 22); ++spin) {
+    if (__hip_atomic_load(ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= count) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Byte strides of the q/k and v rows.
+struct DmaStrides {
+  uint32_t qk, v;
+};
+
+__device__ __forceinline__ void dma_ro_chain(const ChunkSrc& s, RoChainBuf& d, const DmaStrides& st, int lane) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) dma_rows256(s.kb, qk_stride, s.nv, d.K, i, lane);
+  for (int i = 0; i < 16; ++i) dma_rows256(s.kb, st.qk, s.nv, d.K, i, lane);
 #pragma unroll
   for (int f = 0; f < 2 * kFrags; ++f) dma_1k(s.ws + kWsTh + f * kFragBytes, d.th + 512 * f, lane);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) dma_vtile(s.vb, v_stride, s.nv, d.vt, i, lane);
+  for (int i = 0; i < 2; ++i) dma_vtile(s.vb, st.v, s.nv, d.vt, i, lane);
   dma_1k(s.ws + kWsGam, d.gl, lane);
 }
-__device__ __forceinline__ void dma_ro_read(const ChunkSrc& s, RoReadBuf& d, int qk_stride, int lane) {
+__device__ __forceinline__ void dma_ro_read(const ChunkSrc& s, RoReadBuf& d, const DmaStrides& st, int lane) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) dma_rows256(s.qb, qk_stride, s.nv, d.Q, i, lane);
+  for (int i = 0; i < 16; ++i) dma_rows256(s.qb, st.qk, s.nv, d.Q, i, lane);
 #pragma unroll
   for (int f = 0; f < 2 * kFrags; ++f) dma_1k(s.ws + kWsPh + f * kFragBytes, d.ph + 512 * f, lane);
   dma_1k(s.ws + kWsGam, d.gl, lane);
@@ -786,13 +882,63 @@ __device__ __forceinline__ void barrier_lds_only() {
   asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(3 * kWave) void state_ro_kernel(PrefillArgs a) {
-  __shared__ RoChainBuf cb0;
-  __shared__ RoChainBuf cb1;
-  __shared__ Exchange xo0;
-  __shared__ Exchange xo1;
-  __shared__ RoReadBuf rb0;
-  __shared__ RoReadBuf rb1;
+// A chain wave of state_ro_kernel: key half KH of the state,
+// S[mt][i] = S[col0 + l16][64 KH + 32 (mt / 2) + 8 g4 + 4 (mt % 2) + i]. It takes part in the
+// workgroup barrier once per chunk, like the other waves; the halves of X pass between the
+// two chain waves through xx with its own handshake, which the other waves never wait for.
+template <int KH>
+__device__ __forceinline__ void ro_chain_wave(const PrefillArgs& a, const RoChainBuf (&cb)[2], Exchange (&xo)[2],
+                                              XHalves& xx, const LaneOffsets& lo, int n, int h, int col0,
+                                              int n_chunks, int lane) {
+  f32x4 S[4];
+  load_state(a, n, h, col0, KH, S, lane);
+  if (lane == 0) xx.ready[KH] = 0;
+  for (int ci = 0; ci < n_chunks; ++ci) {
+    const RoChainBuf& c = cb[ci & 1];
+    Exchange& x = xo[ci & 1];
+    __syncthreads();                 // the chunk's operands are in (and the flags are set up)
+    // every LDS operand of the chunk at once: the reads overlap each other and the products
+    bf16x8 ak[2][4], akt[4][2];
+    UOps uo;
+    const ChainOps ops{c.K, c.th, c.tl, c.vt, c.gl};
+    load_k_rows(c.K, lo, KH, ak);
+    load_k_t(c.K, lo, KH, akt);
+    load_u_ops(ops, lo, uo, lane);
+    const float gC = c.gl[kC - 1];
+    bf16x8 sh[2];
+    f32x4 X[4];
+    chain_x(ak, S, sh, X);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) xx.x[KH][rt][lane] = X[rt];
+    // publish: the half's stores complete before the count moves on
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+    if (lane == 0) __hip_atomic_store(&xx.ready[KH], (unsigned)ci + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) x.sh[2 * KH + jj][lane] = sh[jj];
+    wait_ready(&xx.ready[KH ^ 1], (unsigned)ci + 1);
+    f32x4 Xo[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) Xo[rt] = xx.x[KH ^ 1][rt][lane];
+    f32x4 U[4];
+    bf16x8 Bh[2], Bl[2];
+    if (KH == 0) {
+      chain_u(uo, X, Xo, U, Bh, Bl);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) x.u[rt][lane] = U[rt];
+    } else {
+      chain_u(uo, Xo, X, U, Bh, Bl);
+    }
+    chain_update(akt, S, Bh, Bl, gC);
+  }
+  __syncthreads();   // the last chunk's hand-over is visible to the read-out wave
+  if (a.s_final) store_state(a, n, h, col0, KH, S, lane);
+}
+
+__global__ __launch_bounds__(4 * kWave) void state_ro_kernel(PrefillArgs a) {
+  __shared__ RoChainBuf cb[2];
+  __shared__ Exchange xo[2];
+  __shared__ XHalves xx;
+  __shared__ RoReadBuf rb[2];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int lane = tid & 63;
@@ -818,78 +964,55 @@ __global__ __launch_bounds__(3 * kWave) void state_ro_kernel(PrefillArgs a) {
   lane_offsets(lo, g4, l16);
   auto src = [&](int ci) { return chunk_src(a, c_begin + ci, t_seq0 + ci * kC, t_seq1, h, j, col0); };
 
-  if (w == 1) {   // the loading wave: chunk ci + 1's chain operands during chunk ci
-    if (n_chunks > 0) dma_ro_chain(src(0), cb0, qk_stride, v_stride, lane);
-    for (int ci = 0; ci < n_chunks; ci += 2) {
-      __builtin_amdgcn_s_waitcnt(0);
+  DmaStrides dst;
+  dst.qk = (uint32_t)qk_stride * 2;
+  dst.v = (uint32_t)v_stride * 2;
+  if (w == 2) {   // the loading wave: chunk ci + 1's chain operands during chunk ci
+    if (n_chunks > 0) dma_ro_chain(src(0), cb[0], dst, lane);
+    for (int ci = 0; ci < n_chunks; ++ci) {
+      __builtin_amdgcn_s_waitcnt(0);   // chunk ci has landed
       __syncthreads();
-      if (ci + 1 < n_chunks) {
-        dma_ro_chain(src(ci + 1), cb1, qk_stride, v_stride, lane);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (ci + 2 < n_chunks) dma_ro_chain(src(ci + 2), cb0, qk_stride, v_stride, lane);
-      }
+      if (ci + 1 < n_chunks) dma_ro_chain(src(ci + 1), cb[(ci + 1) & 1], dst, lane);
     }
     __syncthreads();
     return;
   }
-  if (w == 2) {   // the read-out wave: chunk ci's read-out after barrier ci + 1
+  if (w == 3) {   // the read-out wave: chunk ci's read-out after the barrier of chunk ci + 1
     // chunk ci's read-out from buffer ci % 2, which then takes chunk ci + 2's operands
-    auto readout = [&](int ci, RoReadBuf& rb, const Exchange& xo) {
+    auto readout = [&](int ci) {
       const int t0 = t_seq0 + ci * kC;
+      RoReadBuf& r = rb[ci & 1];
+      const Exchange& x = xo[ci & 1];
       __builtin_amdgcn_s_waitcnt(0);   // its Q, P^T and decay factors have landed
       bf16x8 sh[4];
       f32x4 u[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sh[ks] = xo.sh[ks][lane];
+      for (int ks = 0; ks < 4; ++ks) sh[ks] = x.sh[ks][lane];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) u[rt] = xo.u[rt][lane];
-      const ReadOps ops{rb.Q, rb.ph, rb.pl, rb.gl};
+      for (int rt = 0; rt < 4; ++rt) u[rt] = x.u[rt][lane];
+      const ReadOps ops{r.Q, r.ph, r.pl, r.gl};
       readout_chunk(ops, lo, sh, u, a.scale, out_rsrc(a, t0, min(kC, t_seq1 - t0), h), v_stride * 2,
                     col0 * 2, lane);
       // every LDS read of the buffer is done before it is refilled
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
-      if (ci + 2 < n_chunks) dma_ro_read(src(ci + 2), rb, qk_stride, lane);
+      if (ci + 2 < n_chunks) dma_ro_read(src(ci + 2), r, dst, lane);
     };
-    if (n_chunks > 0) dma_ro_read(src(0), rb0, qk_stride, lane);
-    if (n_chunks > 1) dma_ro_read(src(1), rb1, qk_stride, lane);
-    for (int ci = 0; ci < n_chunks; ci += 2) {
+    if (n_chunks > 0) dma_ro_read(src(0), rb[0], dst, lane);
+    if (n_chunks > 1) dma_ro_read(src(1), rb[1], dst, lane);
+    for (int ci = 0; ci < n_chunks; ++ci) {
       barrier_lds_only();
-      if (ci >= 1) readout(ci - 1, rb1, xo1);
-      if (ci + 1 < n_chunks) {
-        barrier_lds_only();
-        readout(ci, rb0, xo0);
-      }
+      if (ci >= 1) readout(ci - 1);
     }
     barrier_lds_only();
-    if (n_chunks > 0) {
-      if ((n_chunks - 1) & 1) readout(n_chunks - 1, rb1, xo1);
-      else readout(n_chunks - 1, rb0, xo0);
-    }
+    if (n_chunks > 0) readout(n_chunks - 1);
     return;
   }
 
-  // the chain wave. St[mt][i] = S[col0 + l16][32 (mt / 2) + 8 g4 + 4 (mt % 2) + i]
-  f32x4 St[8];
-  load_state(a, n, h, col0, St, lane);
-  auto step = [&](const RoChainBuf& cb, Exchange& xo) {
-    __syncthreads();                 // the chunk's operands are in; xo was read two chunks ago
-    bf16x8 sh[4];
-    f32x4 u[4];
-    const ChainOps ops{cb.K, cb.th, cb.tl, cb.vt, cb.gl};
-    chain_chunk(ops, lo, St, sh, u, lane);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) xo.sh[ks][lane] = sh[ks];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) xo.u[rt][lane] = u[rt];
-  };
-  for (int ci = 0; ci < n_chunks; ci += 2) {
-    step(cb0, xo0);
-    if (ci + 1 < n_chunks) step(cb1, xo1);
-  }
-  __syncthreads();   // the last chunk's hand-over is visible to the read-out wave
-  if (a.s_final) store_state(a, n, h, col0, St, lane);
+  // the chain waves: wave kh holds key half kh of the state (a constant in each branch, so
+  // every register array is indexed statically)
+  if (w == 0) ro_chain_wave<0>(a, cb, xo, xx, lo, n, h, col0, n_chunks, lane);
+  else ro_chain_wave<1>(a, cb, xo, xx, lo, n, h, col0, n_chunks, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -916,22 +1039,22 @@ struct StateBuf {
 // 16 Q rows, 12 T diag(beta) fragments, 12 P^T fragments (not with FORM), the decay factors,
 // two per value tile; wave w issues the pieces p = w (mod NW).
 template <int NW, bool FORM>
-__device__ __forceinline__ void dma_chunk(const ChunkSrc& s, StateBuf<NW>& d, int qk_stride, int v_stride,
-                                          int w, int lane) {
+__device__ __forceinline__ void dma_chunk(const ChunkSrc& s, StateBuf<NW>& d, const DmaStrides& st, int w,
+                                          int lane) {
   constexpr int kP = FORM ? 0 : 2 * kFrags;
   constexpr int kTotal = 32 + 2 * kFrags + kP + 1 + 2 * NW;
 #pragma unroll
   for (int i = 0; i < (kTotal + NW - 1) / NW; ++i) {
     const int p = w + NW * i;
-    if (p < 16) dma_rows256(s.kb, qk_stride, s.nv, d.K, p, lane);
-    else if (p < 32) dma_rows256(s.qb, qk_stride, s.nv, d.Q, p - 16, lane);
+    if (p < 16) dma_rows256(s.kb, st.qk, s.nv, d.K, p, lane);
+    else if (p < 32) dma_rows256(s.qb, st.qk, s.nv, d.Q, p - 16, lane);
     else if (p < 32 + 2 * kFrags) dma_1k(s.ws + kWsTh + (p - 32) * kFragBytes, d.th + 512 * (p - 32), lane);
     else if (p < 32 + 2 * kFrags + kP)
       dma_1k(s.ws + kWsPh + (p - 32 - 2 * kFrags) * kFragBytes, d.ph + 512 * (p - 32 - 2 * kFrags), lane);
     else if (p == 32 + 2 * kFrags + kP) dma_1k(s.ws + kWsGam, d.gl, lane);
     else if (p < kTotal) {
       const int q = p - (33 + 2 * kFrags + kP);
-      dma_vtile(s.vb + 16 * (q >> 1), v_stride, s.nv, d.vt[q >> 1], q & 1, lane);
+      dma_vtile(s.vb + 16 * (q >> 1), st.v, s.nv, d.vt[q >> 1], q & 1, lane);
     }
   }
 }
@@ -992,29 +1115,36 @@ __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
   lane_offsets(lo, g4, l16);
   auto src = [&](int ci) { return chunk_src(a, c_begin + ci, t_seq0 + ci * kC, t_seq1, h, j, col_base); };
 
-  f32x4 St[8];
-  load_state(a, n, h, col0, St, lane);
+  DmaStrides dst;
+  dst.qk = (uint32_t)qk_stride * 2;
+  dst.v = (uint32_t)v_stride * 2;
+  f32x4 S0[4], S1[4];
+  load_state(a, n, h, col0, 0, S0, lane);
+  load_state(a, n, h, col0, 1, S1, lane);
   auto step = [&](int ci, StateBuf<NW>& cur, StateBuf<NW>& nxt) {
     __builtin_amdgcn_s_waitcnt(0);   // this wave's share of the chunk's loads has landed ...
     __syncthreads();                 // ... and everyone's; the other buffer is free
-    if (ci + 1 < n_chunks) dma_chunk<NW, FORM>(src(ci + 1), nxt, qk_stride, v_stride, w, lane);
+    if (ci + 1 < n_chunks) dma_chunk<NW, FORM>(src(ci + 1), nxt, dst, w, lane);
     if (FORM) form_pt<NW>(cur, a.scale, w, g4, l16, lane);
     bf16x8 sh[4];
     f32x4 u[4];
     const ChainOps ops{cur.K, cur.th, cur.tl, cur.vt[w], cur.gl};
-    chain_chunk(ops, lo, St, sh, u, lane);
+    chain_chunk(ops, lo, S0, S1, sh, u, lane);
     if (FORM) __syncthreads();       // every wave's part of P^T is in
     const int t0 = t_seq0 + ci * kC;
     const ReadOps rops{cur.Q, cur.ph, cur.pl, cur.gl};
     readout_chunk(rops, lo, sh, u, a.scale, out_rsrc(a, t0, min(kC, t_seq1 - t0), h), v_stride * 2,
                   col0 * 2, lane);
   };
-  if (n_chunks > 0) dma_chunk<NW, FORM>(src(0), buf0, qk_stride, v_stride, w, lane);
+  if (n_chunks > 0) dma_chunk<NW, FORM>(src(0), buf0, dst, w, lane);
   for (int ci = 0; ci < n_chunks; ci += 2) {
     step(ci, buf0, buf1);
     if (ci + 1 < n_chunks) step(ci + 1, buf1, buf0);
   }
-  if (a.s_final) store_state(a, n, h, col0, St, lane);
+  if (a.s_final) {
+    store_state(a, n, h, col0, 0, S0, lane);
+    store_state(a, n, h, col0, 1, S1, lane);
+  }
 }
 
 }  // namespace
@@ -1091,7 +1221,7 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
   const size_t seq_pairs = (size_t)num_seqs * h_qk;
   const size_t groups = (seq_pairs + 7) / 8 * 8 * (size_t)a.group;
   if (heads * 8 <= kStateCus) {
-    hipLaunchKernelGGL(state_ro_kernel, dim3((unsigned)(groups * 8)), dim3(3 * kWave), 0, stream, a);
+    hipLaunchKernelGGL(state_ro_kernel, dim3((unsigned)(groups * 8)), dim3(4 * kWave), 0, stream, a);
   } else if (heads * 4 <= kStateCus) {
     hipLaunchKernelGGL((state_kernel<2, false>), dim3((unsigned)(groups * 4)), dim3(2 * kWave), 0, stream, a);
   } else if (heads * 2 <= kStateCus) {
