@@ -65,6 +65,7 @@ COUNTERS = {
     "prefill_t32768": {"bytes": None, "mfma_busy": None, "sources": None},
     "prefill_t4096": {"bytes": None, "mfma_busy": None, "sources": None},
     "prefill_packed64": {"bytes": None, "mfma_busy": None, "sources": None},
+    "prefill_conv_packed64": {"bytes": None, "sources": None},
     "decode": {"bytes": None, "sources": None},
 }
 
@@ -77,7 +78,7 @@ def _sources_sha(names):
     return h.hexdigest()[:16]
 
 
-PREFILL_SOURCES = ("chunk_prefill.hip", "gdn_device.h")
+PREFILL_SOURCES = ("chunk_prefill.hip", "gdn_device.h", "conv_device.h")
 DECODE_SOURCES = ("recurrent.hip", "gdn_device.h")
 
 
@@ -405,7 +406,9 @@ def bench_epilogue(reps, warmup):
 
 def bench_frontend(reps, warmup):
     """64 packed sequences (lengths uniform in [128, 8192]): gdn_conv_prep then
-    gdn_chunk_prefill with per-sequence initial and final states."""
+    gdn_chunk_prefill with per-sequence initial and final states, and the same through
+    gdn_chunk_prefill_conv (the front end inside the prefill's loads). Returns (tokens,
+    sequences, conv ms, prefill ms, one-call ms)."""
     import torch
     import linear_attention_recurrence_amd as gdn
     import workloads
@@ -420,6 +423,8 @@ def bench_frontend(reps, warmup):
     o = torch.empty_like(v)
     fin = torch.empty_like(s0)
     ws = _workspace(T, N)
+    wsc = torch.empty(gdn.gdn_chunk_prefill_conv_workspace_bytes(T, N, H_QK, H_V, D, D), dtype=torch.uint8,
+                      device="cuda")
 
     def conv(i):
         gdn.gdn_conv_prep(mixed, w, cu, H_QK, H_V, D, D, fe.q_scale, q=q, k=k, v=v)
@@ -428,9 +433,22 @@ def bench_frontend(reps, warmup):
         gdn.gdn_chunk_prefill(q, k, v, g, b, cu, 1.0, initial_state=s0, final_state=fin, o=o,
                               workspace=ws)
 
+    def fused(i):
+        gdn.gdn_chunk_prefill_conv(mixed, w, g, b, cu, H_QK, H_V, D, D, fe.q_scale, 1.0, initial_state=s0,
+                                   final_state=fin, o=o, workspace=wsc)
+
     _, conv_ms = _timed(conv, reps, warmup)
     _, pre_ms = _timed(prefill, reps, warmup)
-    return T, N, conv_ms, pre_ms
+    _, fused_ms = _timed(fused, reps, warmup)
+    return T, N, conv_ms, pre_ms, fused_ms
+
+
+def fused_bytes(tokens: int, num_seqs: int, h_qk=H_QK, h_v=H_V) -> float:
+    """HBM bytes of the prefill with the front end inside: the mixed input (bf16), o (bf16),
+    g and beta (fp32), the initial and final states (fp32)."""
+    ch = 2 * h_qk * D + h_v * D
+    per_tok = ch * 2 + h_v * D * 2 + 2 * h_v * 4
+    return float(tokens) * per_tok + num_seqs * h_v * D * D * 4 * 2
 
 
 def bench_copy(steps, warmup, nbytes=1 << 30):
@@ -615,9 +633,10 @@ def main():
                                                "kernel": "rows_kernel<bf16, true, 8, 4>",
                                                "algorithmic_flops": cflops}}}
     if "frontend" in work:
-        T4, N4, conv_ms, pre_ms = bench_frontend(10, 2)
+        T4, N4, conv_ms, pre_ms, fused_ms = bench_frontend(10, 2)
         hbm4, mfma4 = prefill_rooflines(T4, N4, True, pre_ms, "prefill_packed64", PREFILL_KERNELS)
         cb = conv_prep_bytes(T4)
+        fb = fused_bytes(T4, N4)
         out["frontend_prefill"] = {
             "workload": "64 packed sequences, lengths uniform in [128, 8192], conv k=4 front end "
                         "then prefill with S0 and final states",
@@ -629,7 +648,16 @@ def main():
                                    "frac": cb / (conv_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                                    "kernel": "conv_prep_kernel", "kernel_ms": conv_ms,
                                    "algorithmic_bytes": cb},
-            "prefill_roofline": hbm4, "prefill_roofline_mfma": mfma4}
+            "prefill_roofline": hbm4, "prefill_roofline_mfma": mfma4,
+            "one_call": {"entry_point": "gdn_chunk_prefill_conv (front end inside the prefill's loads)",
+                         "ms_per_call": fused_ms, "tokens_per_s": T4 / (fused_ms / 1e3),
+                         "roofline": {"bound": "hbm", "achieved": fb / (fused_ms / 1e3) / 1e9,
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": fb / (fused_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                      "traffic": counter("prefill_conv_packed64", "bytes", PREFILL_SOURCES),
+                                      "kernel": "gdn_chunk_prefill_conv call: prep_kernel<false, true> + "
+                                                "state_kernel<8, true, true>",
+                                      "call_ms": fused_ms, "algorithmic_bytes": fb}}}
     if "epilogue" in work:
         nvec, ems = bench_epilogue(200, 10)
         eb = nvec * D * 2 * 3          # o and z read, out written, bf16

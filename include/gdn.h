@@ -107,6 +107,36 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dt
                              const float* initial_state, float* final_state,
                              void* o, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Prefill from the layer's projected input: the front end of gdn_conv_prep (the short causal
+ * depthwise convolution that section "01 . GatedDeltaNet(config)" of page "Qwen3-Next 80B-A3B
+ * -- The Evolving Transformer" places before the recurrence, SiLU, the L2 norm of each q and
+ * k head and q_scale) followed by gdn_chunk_prefill, in one call, bit for bit equal to those
+ * two calls.
+ *
+ *   mixed_qkv     [total_tokens][2 h_qk d_k + h_v d_v] bf16, channels q | k | v, head-major
+ *   conv_weight   [channels][conv_kernel] fp32, tap conv_kernel - 1 on the current token;
+ *                 1 <= conv_kernel <= 4
+ *   q_scale       multiplies the normalised q (the front end's scale); `scale` multiplies
+ *                 the read-out as in gdn_chunk_prefill (1 when q_scale already holds d_k^-1/2)
+ *   g, beta, cu_seqlens, states, o (bf16) as gdn_chunk_prefill
+ *   workspace     at least gdn_chunk_prefill_conv_workspace_bytes(...) bytes
+ *
+ * With more than 128 (sequence, V head) pairs the front end runs inside the prefill's own
+ * loads (q, k and v are computed into on-chip memory as each chunk is loaded and never
+ * written to device memory); with fewer, eight workgroups share each head and would repeat
+ * it, so it runs as its own pass into the workspace first (which the size query includes).
+ * Validation and errors as gdn_chunk_prefill and gdn_conv_prep.
+ */
+size_t gdn_chunk_prefill_conv_workspace_bytes(int32_t total_tokens, int32_t num_seqs,
+                                              int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v);
+gdn_status gdn_chunk_prefill_conv(const void* mixed_qkv, const float* conv_weight, int32_t conv_kernel,
+                                  float q_scale, const float* g, const float* beta,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                                  int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, float scale,
+                                  const float* initial_state, float* final_state, void* o,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of the library's own device scratch behind gdn_chunk_prefill_noalloc (per GPU). */
 #define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 

@@ -7,6 +7,7 @@ raised if it has not been built (see ``linear_attention_recurrence_amd.build``).
 
 from ._lib import (GDN_BF16, GDN_F32, GdnError, gdn_channel_decay_decode_step,
                    gdn_channel_decay_prefill, gdn_chunk_prefill, gdn_chunk_prefill_noalloc,
+                   gdn_chunk_prefill_conv, gdn_chunk_prefill_conv_workspace_bytes,
                    gdn_chunk_prefill_workspace_bytes, gdn_conv_decode_step, gdn_conv_prep,
                    gdn_conv_window_from_prefill, gdn_decode_step, gdn_decode_step_with_conv,
                    gdn_gated_rmsnorm,
@@ -14,6 +15,7 @@ from ._lib import (GDN_BF16, GDN_F32, GdnError, gdn_channel_decay_decode_step,
 
 __all__ = ["GDN_BF16", "GDN_F32", "GdnError", "gdn_channel_decay_decode_step",
            "gdn_channel_decay_prefill", "gdn_chunk_prefill", "gdn_chunk_prefill_noalloc",
+           "gdn_chunk_prefill_conv", "gdn_chunk_prefill_conv_workspace_bytes",
            "gdn_chunk_prefill_workspace_bytes", "gdn_conv_decode_step", "gdn_conv_prep",
            "gdn_conv_window_from_prefill", "gdn_decode_step", "gdn_decode_step_with_conv",
            "gdn_gated_rmsnorm",

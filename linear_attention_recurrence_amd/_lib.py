@@ -24,7 +24,8 @@ EXPORTED = ("gdn_status_string", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk
             "gdn_decode_step", "gdn_verify_step", "gdn_channel_decay_prefill",
             "gdn_channel_decay_decode_step", "gdn_conv_prep", "gdn_conv_decode_step",
             "gdn_conv_window_from_prefill", "gdn_gated_rmsnorm", "gdn_decode_step_with_conv",
-            "gdn_chunk_prefill_noalloc")
+            "gdn_chunk_prefill_noalloc", "gdn_chunk_prefill_conv_workspace_bytes",
+            "gdn_chunk_prefill_conv")
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
 
@@ -56,6 +57,11 @@ def load(path: Optional[str] = None):
     lib.gdn_chunk_prefill.restype = ctypes.c_int
     lib.gdn_chunk_prefill.argtypes = [_P, _P, _P, ctypes.c_int, _P, _P, _P, _I, _I, _I, _I, _I,
                                       _I, ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.gdn_chunk_prefill_conv_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_chunk_prefill_conv_workspace_bytes.argtypes = [_I] * 6
+    lib.gdn_chunk_prefill_conv.restype = ctypes.c_int
+    lib.gdn_chunk_prefill_conv.argtypes = [_P, _P, _I, ctypes.c_float, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                           ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.gdn_chunk_prefill_noalloc.restype = ctypes.c_int
     lib.gdn_chunk_prefill_noalloc.argtypes = [_P, _P, _P, ctypes.c_int, _P, _P, _P, _I, _I, _I, _I,
                                               _I, _I, ctypes.c_float, _P, _P, _P, _P]
@@ -172,6 +178,41 @@ def gdn_chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, initial_state=None,
                                   _ptr(initial_state), _ptr(final_state), _ptr(o),
                                   _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "gdn_chunk_prefill")
+    return o
+
+
+def gdn_chunk_prefill_conv_workspace_bytes(total_tokens, num_seqs, h_qk, h_v, d_k, d_v) -> int:
+    return int(load().gdn_chunk_prefill_conv_workspace_bytes(total_tokens, num_seqs, h_qk, h_v, d_k, d_v))
+
+
+def gdn_chunk_prefill_conv(mixed_qkv, conv_weight, g, beta, cu_seqlens, h_qk, h_v, d_k, d_v, q_scale,
+                           scale, initial_state=None, final_state=None, o=None, workspace=None,
+                           stream=None):
+    """The front end (gdn_conv_prep) and the prefill in one call, from the mixed bf16 input
+    [T][2 h_qk d_k + h_v d_v] and the conv taps [channels][K] fp32. Returns o [T][h_v][d_v] bf16."""
+    T, C = mixed_qkv.shape
+    N = cu_seqlens.numel() - 1
+    K = int(conv_weight.shape[1])
+    with _on(stream):
+        if o is None:
+            o = torch.empty((T, h_v, d_v), dtype=torch.bfloat16, device=mixed_qkv.device)
+        need = gdn_chunk_prefill_conv_workspace_bytes(T, N, h_qk, h_v, d_k, d_v)
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=mixed_qkv.device)
+    _expect(mixed_qkv, (T, 2 * h_qk * d_k + h_v * d_v), torch.bfloat16, "mixed_qkv")
+    _expect(conv_weight, (C, K), torch.float32, "conv_weight")
+    _expect(g, (T, h_v), torch.float32, "g")
+    _expect(beta, (T, h_v), torch.float32, "beta")
+    _expect(cu_seqlens, (N + 1,), torch.int32, "cu_seqlens")
+    _expect(initial_state, (N, h_v, d_v, d_k), torch.float32, "initial_state")
+    _expect(final_state, (N, h_v, d_v, d_k), torch.float32, "final_state")
+    _expect(o, (T, h_v, d_v), torch.bfloat16, "o")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().gdn_chunk_prefill_conv(_ptr(mixed_qkv), _ptr(conv_weight), K, float(q_scale), _ptr(g),
+                                       _ptr(beta), _ptr(cu_seqlens), N, T, h_qk, h_v, d_k, d_v,
+                                       float(scale), _ptr(initial_state), _ptr(final_state), _ptr(o),
+                                       _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "gdn_chunk_prefill_conv")
     return o
 
 

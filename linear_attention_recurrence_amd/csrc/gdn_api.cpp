@@ -139,6 +139,37 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dt
                                             workspace, s));
 }
 
+size_t gdn_chunk_prefill_conv_workspace_bytes(int32_t total_tokens, int32_t num_seqs, int32_t h_qk,
+                                              int32_t h_v, int32_t d_k, int32_t d_v) {
+  if (total_tokens < 0 || num_seqs <= 0 || check_common(h_qk, h_v, d_k, d_v) != GDN_OK) return 0;
+  return gdn::chunk_prefill_conv_workspace_bytes(total_tokens, num_seqs, h_qk, h_v);
+}
+
+gdn_status gdn_chunk_prefill_conv(const void* mixed_qkv, const float* conv_weight, int32_t conv_kernel,
+                                  float q_scale, const float* g, const float* beta,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                                  int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, float scale,
+                                  const float* initial_state, float* final_state, void* o,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || total_tokens < 0) return GDN_ERR_SHAPE;
+  const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  if (conv_kernel < 1) return GDN_ERR_SHAPE;
+  if (conv_kernel > 4) return GDN_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
+  if (!cu_seqlens) return GDN_ERR_NULL;
+  if (total_tokens > 0 && (!mixed_qkv || !conv_weight || !g || !beta || !o)) return GDN_ERR_NULL;
+  if (!final_state && total_tokens == 0) return GDN_OK;   // nothing observable to do
+  const size_t need = gdn_chunk_prefill_conv_workspace_bytes(total_tokens, num_seqs, h_qk, h_v, d_k, d_v);
+  if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  GDN_TRY(check_seqlens(cu_seqlens, num_seqs, total_tokens, stream));
+  GDN_TRY(check_log_decay(g, (size_t)total_tokens * h_v, stream));
+  return from_hip(gdn::launch_chunk_prefill_conv(mixed_qkv, conv_weight, conv_kernel, q_scale, g, beta,
+                                                 cu_seqlens, num_seqs, total_tokens, h_qk, h_v, scale,
+                                                 initial_state, final_state, o, workspace,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 gdn_status gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v, gdn_dtype io_dtype,
                                      const float* g, const float* beta,
                                      const int32_t* cu_seqlens, int32_t num_seqs,

@@ -31,7 +31,9 @@ def test_header_declares_the_boundary():
                                             "gdn_conv_prep", "gdn_conv_decode_step",
                                             "gdn_conv_window_from_prefill", "gdn_gated_rmsnorm",
                                             "gdn_decode_step_with_conv",
-                                            "gdn_chunk_prefill_noalloc"])
+                                            "gdn_chunk_prefill_noalloc",
+                                            "gdn_chunk_prefill_conv_workspace_bytes",
+                                            "gdn_chunk_prefill_conv"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -148,6 +150,38 @@ def test_prefill_noalloc_validation():
     assert call(T=5121) == L.GDN_ERR_WORKSPACE
     assert call(T=32768) == L.GDN_ERR_WORKSPACE
     assert call(T=200, n=80) == L.GDN_ERR_WORKSPACE       # ceil(200 / 64) + 80 > 81 chunks
+
+
+def test_prefill_conv_validation():
+    """The prefill with the front end validates like gdn_chunk_prefill and gdn_conv_prep, and
+    its workspace query adds the q, k, v pass only where the front end does not run inside."""
+    lib, L = _lib()
+    f = lib.gdn_chunk_prefill_conv
+    P = _fake
+    ok = dict(x=P(1), w=P(2), K=4, qs=0.1, g=P(4), b=P(5), cu=P(6), n=64, T=1000, hqk=16, hv=32,
+              dk=128, dv=128, sc=1.0, s0=None, sf=None, o=P(7), ws=None, wsb=0, st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["x"], a["w"], a["K"], a["qs"], a["g"], a["b"], a["cu"], a["n"], a["T"], a["hqk"],
+                 a["hv"], a["dk"], a["dv"], a["sc"], a["s0"], a["sf"], a["o"], a["ws"], a["wsb"], a["st"])
+
+    assert call(x=None) == L.GDN_ERR_NULL
+    assert call(w=None) == L.GDN_ERR_NULL
+    assert call(cu=None) == L.GDN_ERR_NULL
+    assert call(K=0) == L.GDN_ERR_SHAPE
+    assert call(K=5) == L.GDN_ERR_UNSUPPORTED
+    assert call(T=-1) == L.GDN_ERR_SHAPE
+    assert call(dk=64) == L.GDN_ERR_UNSUPPORTED
+    assert call() == L.GDN_ERR_WORKSPACE
+    assert call(ws=P(8), wsb=100) == L.GDN_ERR_WORKSPACE
+    assert call(n=0, T=0) == L.GDN_OK
+    q = lambda T, n: lib.gdn_chunk_prefill_conv_workspace_bytes(T, n, 16, 32, 128, 128)
+    p = lambda T, n: lib.gdn_chunk_prefill_workspace_bytes(T, n, 16, 32, 128, 128)
+    assert q(276989, 64) == p(276989, 64)                        # 2048 pairs: inside
+    assert q(4096, 1) == p(4096, 1) + 4096 * 8192 * 2            # 32 pairs: its own pass
+    assert q(-1, 1) == 0
 
 
 def test_conv_prep_validation():

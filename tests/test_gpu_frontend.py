@@ -232,3 +232,68 @@ def test_decode_with_conv_equals_two_calls(K, h_qk, h_v):
     assert torch.equal(pool_a, pool_b)
     if K > 1:
         assert torch.equal(win_a, win_b)
+
+
+def _two_calls_and_fused(fe):
+    """gdn_conv_prep + gdn_chunk_prefill, and gdn_chunk_prefill_conv, on the same batch."""
+    import torch
+    import linear_attention_recurrence_amd as gdn
+    cu = to_dev(fe.cu_seqlens)
+    mixed, w = to_dev(fe.mixed), to_dev(fe.conv_weight)
+    g, b = to_dev(fe.g), to_dev(fe.beta)
+    s0 = to_dev(fe.initial_state)
+    N, T = fe.num_seqs, fe.total_tokens
+    q, k, v = gdn.gdn_conv_prep(mixed, w, cu, fe.h_qk, fe.h_v, fe.d_k, fe.d_v, fe.q_scale)
+    fin2 = torch.full((N, fe.h_v, 128, 128), float("nan"), dtype=torch.float32, device="cuda")
+    o2 = gdn.gdn_chunk_prefill(q, k, v, g, b, cu, 1.0, initial_state=s0, final_state=fin2)
+    fin1 = torch.full_like(fin2, float("nan"))
+    o1 = gdn.gdn_chunk_prefill_conv(mixed, w, g, b, cu, fe.h_qk, fe.h_v, fe.d_k, fe.d_v, fe.q_scale, 1.0,
+                                    initial_state=s0, final_state=fin1)
+    torch.cuda.synchronize()
+    return (o1, fin1), (o2, fin2), (q, k, v)
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+def test_prefill_conv_many_heads_equals_two_calls(K):
+    """More than 128 (sequence, V head) pairs: the front end runs inside the prefill's loads;
+    outputs and states equal gdn_conv_prep then gdn_chunk_prefill bit for bit (sequences
+    shorter than the kernel, empty ones, whole chunks and ragged tails)."""
+    fe = workloads.make_frontend([0, 1, 3, 64, 65, 200, 130, 2], conv_kernel=K, seed=700 + K)
+    (o1, f1), (o2, f2), _ = _two_calls_and_fused(fe)
+    assert torch_equal(o1, o2) and torch_equal(f1, f2)
+
+
+def test_prefill_conv_few_heads_equals_two_calls():
+    """At most 128 pairs (here 64): the front end runs as its own pass into the workspace."""
+    fe = workloads.make_frontend([100, 300], seed=710)
+    (o1, f1), (o2, f2), _ = _two_calls_and_fused(fe)
+    assert torch_equal(o1, o2) and torch_equal(f1, f2)
+
+
+def test_config4_prefill_conv():
+    """64 packed sequences, lengths uniform in [128, 8192], conv k = 4, S0: the one-call path
+    equals the two calls bit for bit, and the recurrence on the front end's bf16 q, k, v
+    matches the oracle on three sequences (the two calls are checked on every sequence by
+    test_config4_front_end_and_prefill)."""
+    fe = workloads.config4()
+    (o1, f1), (o2, f2), (q, k, v) = _two_calls_and_fused(fe)
+    assert torch_equal(o1, o2) and torch_equal(f1, f2)
+    cu = fe.cu_seqlens
+    lens = np.diff(cu)
+    seqs = [int(np.argmin(lens)), 5, int(np.argmax(lens))]
+    x = workloads.PrefillInputs(q=bf16_bits(q), k=bf16_bits(k), v=bf16_bits(v), g=fe.g, beta=fe.beta,
+                                cu_seqlens=cu, initial_state=fe.initial_state, scale=1.0, io_dtype="bf16")
+    refp = oracle_prefill(x, seqs=seqs)
+    o_h = to_host_f64(o1)
+    f_h = to_host_f64(f1)
+    for n in seqs:
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        check_outputs(np.stack([o_h[t0:t1, h] for h in range(32)]), np.stack([refp[(n, h)][0] for h in range(32)]),
+                      "prefill_conv seq %d" % n)
+        check_state(f_h[n], np.stack([refp[(n, h)][1] for h in range(32)]), "prefill_conv seq %d" % n)
+
+
+def torch_equal(a, b):
+    """Bit-for-bit equality (a NaN anywhere fails: every output is written)."""
+    import torch
+    return bool(torch.equal(a, b))
