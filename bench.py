@@ -15,7 +15,7 @@ workload as a CPU baseline.
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps K2]
                   [--workload prefill,decode,frontend,epilogue] [--no-cpu-baseline]
-      prints one JSON line
+      prints one JSON line (prefill_t32768 or prefill_t4096 alone for one prefill workload)
   python bench.py --workload copy
       a plain 1 GiB device copy, the calibration run for hardware byte counters
   python bench.py --pmc-summary DIR
@@ -509,7 +509,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--workload", default="prefill,decode,frontend,epilogue",
-                    help="comma list of prefill, decode, frontend, epilogue, copy")
+                    help="comma list of prefill (both prefill_t32768 and prefill_t4096), decode, "
+                         "frontend, epilogue, copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", metavar="DIR")
     args = ap.parse_args()
@@ -525,7 +526,7 @@ def main():
     torch.cuda.set_device(0)
     out = {}
 
-    if "prefill" in work:
+    if "prefill" in work or "prefill_t32768" in work:
         T, wall, call_ms = bench_prefill("t32768", args.steps, args.warmup)
         hbm, mfma = prefill_rooflines(T, 1, True, call_ms, "prefill_t32768", PREFILL_KERNELS)
         out.update({
@@ -546,6 +547,7 @@ def main():
             "roofline": hbm,
             "roofline_mfma": mfma,
         })
+    if "prefill" in work or "prefill_t4096" in work:
         psteps = max(20, args.steps)
         T1, wall1, ms1 = bench_prefill("t4096", psteps, args.warmup)
         hbm1, mfma1 = prefill_rooflines(T1, 1, False, ms1, "prefill_t4096", PREFILL_KERNELS)
@@ -673,7 +675,7 @@ def main():
     if "copy" in work:
         nb, cms = bench_copy(max(5, args.steps), args.warmup)
         out["copy"] = {"bytes_each_way": nb, "ms": cms, "GBs_read_plus_write": 2 * nb / (cms / 1e3) / 1e9}
-    if "prefill" in work and not args.no_cpu_baseline:
+    if ("prefill" in work or "prefill_t32768" in work) and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 

@@ -70,7 +70,6 @@ namespace {
 
 constexpr int kC = 64;          // chunk length
 constexpr int kD = 128;         // head dim
-constexpr int kThreads = 256;
 constexpr size_t kStateCus = 256;   // compute units of the chip
 constexpr int kF32Pad = kC + 4;     // [token][token] fp32 LDS rows
 
@@ -156,8 +155,10 @@ __device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
 // x = hi + lo for eight fp32 values (two accumulator quads), each half rounded to bf16:
 // hi = bf16(x), lo = bf16(x - hi), so hi + lo carries about 16 bits of x. Each pair is
 // rounded by one packed conversion and its halves widened back by a shift and a mask (three
-// instructions per value). Contraction stays off: every kernel that calls this must round
-// the same way.
+// instructions per value). The packed word passes through an empty asm statement: seen
+// through, the shift of the pair is rewritten as a second conversion of x alone, one more
+// instruction per pair. Contraction stays off: every kernel that calls this must round the
+// same way.
 __device__ __forceinline__ void split8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
 #pragma clang fp contract(off)
   u32x4 h, l;
@@ -165,7 +166,8 @@ __device__ __forceinline__ void split8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo)
   for (int p = 0; p < 4; ++p) {
     const float x = p < 2 ? a[2 * p] : b[2 * p - 4];
     const float y = p < 2 ? a[2 * p + 1] : b[2 * p - 3];
-    const uint32_t w = pk_bf16(x, y);
+    uint32_t w = pk_bf16(x, y);
+    asm("" : "+v"(w));
     h[p] = w;
     l[p] = pk_bf16(x - __builtin_bit_cast(float, w << 16), y - __builtin_bit_cast(float, w & 0xffff0000u));
   }
@@ -386,25 +388,35 @@ __device__ __forceinline__ int pt_off(int rt, int ct, int lane) {
 }
 
 // ------------------------------------------------------------------------------------------
-// prep_kernel: one workgroup per (chunk, V head)
+// prep_kernel: one workgroup per (chunk, HP V heads of one QK head)
 // ------------------------------------------------------------------------------------------
+// The chunk's K (and Q) rows are loaded and their Gram products formed once for the HP V
+// heads that share them (two when the heads of a QK head pair up, else one); the decays,
+// A, T and the workspace blocks are per V head, four waves each for the triangular solve.
+template <bool WITH_P, bool FE, int HP>
 struct PrepSmem {
-  bf16 K[kC * kD];              // swizzled 256-byte rows
-  bf16 halo[4 * kD];            // with the front end: the raw K rows before the chunk
   union {
-    bf16 Q[kC * kD];            // loads and K Q^T only; then A with T
-    float A[kC][kF32Pad];       // A in the strict lower triangle, T transposed in the upper one
-  } r1;
-  alignas(16) float G[kC];
-  alignas(16) float beta[kC];
+    struct {
+      bf16 K[kC * kD];          // swizzled 256-byte rows
+      // Q rows (WITH_P), or with the front end the raw K rows before the chunk
+      bf16 Q[WITH_P ? kC * kD : (FE ? 4 * kD : 8)];
+    } in;
+    // per V head, once the Gram products are in registers: A in the strict lower triangle,
+    // T transposed in the upper one
+    float M[HP][kC][kF32Pad];
+  } r;
+  alignas(16) float G[HP][kC];
+  alignas(16) float beta[HP][kC];
 };
 
 // WITH_P: also K Q^T and P^T (few heads); otherwise the state pass forms P^T itself. FE: K
 // comes from the mixed input through the front end (with WITH_P = false only).
-template <bool WITH_P, bool FE>
-__global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
+template <bool WITH_P, bool FE, int HP>
+__global__ __launch_bounds__(4 * HP * kWave, HP == 1 ? 4 : 3) void prep_kernel(PrefillArgs a) {
   static_assert(!(WITH_P && FE), "the front end runs inside the many-heads prefill only");
-  __shared__ PrepSmem sm;
+  static_assert(HP == 1 || HP == 2, "one or two V heads per workgroup");
+  constexpr int NW = 4 * HP;                      // waves
+  __shared__ PrepSmem<WITH_P, FE, HP> sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int lane = tid & 63;
@@ -412,145 +424,164 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
   const int l16 = lane & 15;
 
   // workgroups of the V heads sharing one QK head sit on the same XCD (blockIdx % 8)
+  const int per = a.group / HP;               // workgroups per (chunk, QK head)
   const int bid = blockIdx.x;
-  const int grp = bid / (8 * a.group), rem = bid % (8 * a.group);
+  const int grp = bid / (8 * per), rem = bid % (8 * per);
   const int p = grp * 8 + rem % 8;            // (chunk, QK head) pair
-  const int gi = rem / 8;                     // V head within the QK group
+  const int gi = (rem / 8) * HP;              // first V head of the workgroup within the QK group
   const int c = p / a.h_qk, j = p % a.h_qk;
   if (c >= a.n_chunks_max) return;
   int n, local;
   locate_chunk(a.cu, a.num_seqs, c, lane, n, local);
   if (n < 0) return;
-  const int h = j * a.group + gi;
+  const int h0 = j * a.group + gi;            // V heads h0 .. h0 + HP - 1
   const int t0 = a.cu[n] + local * kC;
   const int nv = min(kC, a.cu[n + 1] - t0);
-  uint8_t* wsh = a.ws + ((size_t)c * a.h_v + h) * kWsHead;
+  uint8_t* const ws0 = a.ws + ((size_t)c * a.h_v + h0) * kWsHead;   // head h0 + hh: + hh kWsHead
 
   // ---- loads: K, Q rows straight into swizzled LDS images; g, beta ----
+  constexpr int kPieces = 16 / NW;            // 1 KB pieces (four rows) of each image per wave
   const size_t qk_stride = (size_t)a.h_qk * kD;
   if constexpr (FE) {   // the raw K rows of QK head j (and the halo) by direct loads
     const int ch0 = (a.h_qk + j) * kD;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dma_rows256(a.mixed + (size_t)t0 * a.C + ch0, (uint32_t)a.C * 2, nv, sm.K, 4 * w + i, lane);
-    if (w == 0 && t0 > a.cu[n]) dma_halo(a, ch0, t0, sm.halo, lane);
+    for (int i = 0; i < kPieces; ++i)
+      dma_rows256(a.mixed + (size_t)t0 * a.C + ch0, (uint32_t)a.C * 2, nv, sm.r.in.K, kPieces * w + i, lane);
+    if (w == 0 && t0 > a.cu[n]) dma_halo(a, ch0, t0, sm.r.in.Q, lane);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      dma_rows256(a.k + (size_t)t0 * qk_stride + (size_t)j * kD, (uint32_t)qk_stride * 2, nv, sm.K, 4 * w + i, lane);
+    for (int i = 0; i < kPieces; ++i) {
+      dma_rows256(a.k + (size_t)t0 * qk_stride + (size_t)j * kD, (uint32_t)qk_stride * 2, nv, sm.r.in.K,
+                  kPieces * w + i, lane);
       if (WITH_P)
-        dma_rows256(a.q + (size_t)t0 * qk_stride + (size_t)j * kD, (uint32_t)qk_stride * 2, nv, sm.r1.Q, 4 * w + i, lane);
+        dma_rows256(a.q + (size_t)t0 * qk_stride + (size_t)j * kD, (uint32_t)qk_stride * 2, nv, sm.r.in.Q,
+                    kPieces * w + i, lane);
     }
   }
-  if (tid < kC) {
+  if (tid < HP * kC) {
+    const int hh = tid / kC, r = tid % kC;
     float gg = 0.f, bb = 0.f;
-    if (tid < nv) {
-      gg = a.g[(size_t)(t0 + tid) * a.h_v + h];
-      bb = a.beta[(size_t)(t0 + tid) * a.h_v + h];
+    if (r < nv) {
+      gg = a.g[(size_t)(t0 + r) * a.h_v + h0 + hh];
+      bb = a.beta[(size_t)(t0 + r) * a.h_v + h0 + hh];
     }
-    sm.G[tid] = gg;
-    sm.beta[tid] = bb;
+    sm.G[hh][r] = gg;
+    sm.beta[hh][r] = bb;
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if constexpr (FE) {   // K rows from the front end: quarter-wave 4 w + g4 takes rows 4 (4 w + g4) .. + 3
-    const int r0 = 4 * (4 * w + g4);
+  if constexpr (FE) {   // K rows from the front end: quarter-wave 4 w + g4 takes 4 / HP rows
+    constexpr int R = 4 / HP;
+    const int r0 = R * (4 * w + g4);
     bf16x8 hist[3];
-    fe_history<true>(sm.K, sm.halo, t0 == a.cu[n], r0, l16, hist);
+    fe_history<true>(sm.r.in.K, sm.r.in.Q, t0 == a.cu[n], r0, l16, hist);
     __syncthreads();
-    fe_rows<true, 4>(a, sm.K, (a.h_qk + j) * kD, false, true, r0, l16, hist);
+    fe_rows<true, R>(a, sm.r.in.K, (a.h_qk + j) * kD, false, true, r0, l16, hist);
     __syncthreads();
   }
 
   // ---- K K^T (lower 10 tiles, for A) and, WITH_P, K Q^T (the 10 tiles with key tile <=
-  // query tile, for P^T), in registers. WITH_P: waves 0, 1 take K K^T and waves 2, 3 K Q^T,
-  // alternate tiles each; otherwise the four waves share K K^T (tiles w, w + 4, w + 8) ----
-  f32x4 acc[5];
-  const int first = WITH_P ? (w & 1) : w;
-  const int step = WITH_P ? 2 : 4;
-  const bool is_p = WITH_P && w >= 2;
+  // query tile, for P^T), in registers: WITH_P, the first half of the waves takes K K^T and
+  // the second K Q^T, tiles dealt round-robin; otherwise every wave takes K K^T tiles ----
+  constexpr int NK = WITH_P ? NW / 2 : NW;    // waves per product
+  constexpr int NT = (10 + NK - 1) / NK;      // tiles per wave, at most
+  const bool is_p = WITH_P && w >= NK;
+  const int first = WITH_P ? w % NK : w;
+  f32x4 acc[NT];
 #pragma unroll
-  for (int jj = 0; jj < 5; ++jj) {
-    const int t = first + step * jj;
+  for (int jj = 0; jj < NT; ++jj) {
+    const int t = first + NK * jj;
     if (t < 10) {
       const int rt = tile_row(t), ct = tile_col(t);
-      acc[jj] = is_p ? gram_tile(sm.K, sm.r1.Q, ct, rt, g4, l16) : gram_tile(sm.K, sm.K, rt, ct, g4, l16);
+      acc[jj] = is_p ? gram_tile(sm.r.in.K, sm.r.in.Q, ct, rt, g4, l16)
+                     : gram_tile(sm.r.in.K, sm.r.in.K, rt, ct, g4, l16);
     }
   }
-  // ---- prefix sum of log-decays (wave 0, its Gram tiles issued first) ----
-  if (w == 0) {
-    float x = sm.G[lane];
+  // ---- prefix sums of log-decays (wave hh for V head h0 + hh, its Gram tiles issued first) ----
+  if (w < HP) {
+    float x = sm.G[w][lane];
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(x, off, 64);
       if (lane >= off) x += y;
     }
     const float GC = __shfl(x, 63, 64);
-    sm.G[lane] = x;
+    sm.G[w][lane] = x;
+    uint8_t* wsh = ws0 + (size_t)w * kWsHead;
     reinterpret_cast<float*>(wsh + kWsGam)[lane] = __expf(x);
     reinterpret_cast<float*>(wsh + kWsLam)[lane] = __expf(GC - x);
     reinterpret_cast<float*>(wsh + kWsG)[lane] = x;
   }
-  __syncthreads();   // Q is consumed (its space becomes A) and G is ready
+  __syncthreads();   // K and Q are consumed (their space becomes the M's) and G is ready
 
   if (is_p) {
-    // P^T hi and lo straight to the workspace (8-byte pieces), and the two all-zero halves
-    // of fragments (rt, ks) = (0, 0) and (2, 1) (key tiles 1 and 3 above the diagonal)
-    bf16* Ph = reinterpret_cast<bf16*>(wsh + kWsPh);
-    bf16* Pl = reinterpret_cast<bf16*>(wsh + kWsPl);
+    // P^T hi and lo of every V head straight to the workspace (8-byte pieces), and the two
+    // all-zero halves of fragments (rt, ks) = (0, 0) and (2, 1) (key tiles 1 and 3 above the
+    // diagonal): wave NK + 2 hh + z zeroes half z of V head hh's
 #pragma unroll
-    for (int jj = 0; jj < 5; ++jj) {
-      const int t = first + step * jj;
-      if (t < 10) {
-        const int rt = tile_row(t), ct = tile_col(t);
-        bf16x4 hi, lo;
-        pt_tile_values(sm.G, acc[jj], rt, ct, a.scale, g4, l16, hi, lo);
-        *reinterpret_cast<bf16x4*>(Ph + pt_off(rt, ct, lane)) = hi;
-        *reinterpret_cast<bf16x4*>(Pl + pt_off(rt, ct, lane)) = lo;
+    for (int hh = 0; hh < HP; ++hh) {
+      bf16* Ph = reinterpret_cast<bf16*>(ws0 + (size_t)hh * kWsHead + kWsPh);
+      bf16* Pl = reinterpret_cast<bf16*>(ws0 + (size_t)hh * kWsHead + kWsPl);
+#pragma unroll
+      for (int jj = 0; jj < NT; ++jj) {
+        const int t = first + NK * jj;
+        if (t < 10) {
+          const int rt = tile_row(t), ct = tile_col(t);
+          bf16x4 hi, lo;
+          pt_tile_values(sm.G[hh], acc[jj], rt, ct, a.scale, g4, l16, hi, lo);
+          *reinterpret_cast<bf16x4*>(Ph + pt_off(rt, ct, lane)) = hi;
+          *reinterpret_cast<bf16x4*>(Pl + pt_off(rt, ct, lane)) = lo;
+        }
       }
     }
-    const int rz = (w - 2) * 2;   // wave 2: fragment (0, 0), wave 3: fragment (2, 1)
+    const int q = w - NK, hz = q >> 1, rz = (q & 1) * 2;
+    bf16* Ph = reinterpret_cast<bf16*>(ws0 + (size_t)hz * kWsHead + kWsPh);
+    bf16* Pl = reinterpret_cast<bf16*>(ws0 + (size_t)hz * kWsHead + kWsPl);
     *reinterpret_cast<bf16x4*>(Ph + pt_off(rz, rz + 1, lane)) = bf16x4{};
     *reinterpret_cast<bf16x4*>(Pl + pt_off(rz, rz + 1, lane)) = bf16x4{};
   } else {
-    // A = strictly-lower(beta_r Gam_rs (K K^T)_rs) into LDS; every LDS read first (the
-    // stores into A would order them)
-    f32x4 Gr[5], Br[5];
-    float Gs[5];
+    // A = strictly-lower(beta_r Gam_rs (K K^T)_rs) of every V head into LDS; each head's LDS
+    // reads first (the stores into A would order them)
 #pragma unroll
-    for (int jj = 0; jj < 5; ++jj) {
-      const int t = first + step * jj;
-      if (t < 10) {
-        const int rt = tile_row(t), ct = tile_col(t);
-        Gr[jj] = *reinterpret_cast<const f32x4*>(&sm.G[16 * rt + 4 * g4]);
-        Br[jj] = *reinterpret_cast<const f32x4*>(&sm.beta[16 * rt + 4 * g4]);
-        Gs[jj] = sm.G[16 * ct + l16];
+    for (int hh = 0; hh < HP; ++hh) {
+      f32x4 Gr[NT], Br[NT];
+      float Gs[NT];
+#pragma unroll
+      for (int jj = 0; jj < NT; ++jj) {
+        const int t = first + NK * jj;
+        if (t < 10) {
+          const int rt = tile_row(t), ct = tile_col(t);
+          Gr[jj] = *reinterpret_cast<const f32x4*>(&sm.G[hh][16 * rt + 4 * g4]);
+          Br[jj] = *reinterpret_cast<const f32x4*>(&sm.beta[hh][16 * rt + 4 * g4]);
+          Gs[jj] = sm.G[hh][16 * ct + l16];
+        }
       }
-    }
 #pragma unroll
-    for (int jj = 0; jj < 5; ++jj) {
-      const int t = first + step * jj;
-      if (t < 10) {
-        const int rt = tile_row(t), ct = tile_col(t);
-        const int s = 16 * ct + l16;
+      for (int jj = 0; jj < NT; ++jj) {
+        const int t = first + NK * jj;
+        if (t < 10) {
+          const int rt = tile_row(t), ct = tile_col(t);
+          const int s = 16 * ct + l16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * g4 + i;
-          const float decay = __expf(fminf(Gr[jj][i] - Gs[jj], 0.f));   // bounded as in pt_tile_values
-          sm.r1.A[r][s] = s < r ? Br[jj][i] * decay * acc[jj][i] : 0.f;
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rt + 4 * g4 + i;
+            const float decay = __expf(fminf(Gr[jj][i] - Gs[jj], 0.f));   // bounded as in pt_tile_values
+            sm.r.M[hh][r][s] = s < r ? Br[jj][i] * decay * acc[jj][i] : 0.f;
+          }
         }
       }
     }
   }
   __syncthreads();
 
-  // ---- T = (I + A)^-1 --------------------------------------------------------------------
+  // ---- T = (I + A)^-1 per V head: waves 4 hh .. 4 hh + 3 on V head h0 + hh ----------------
   // T is unit lower triangular and A strictly lower triangular, so they share one array: A
   // keeps the strict lower triangle and T[r][c] (r >= c) goes to the mirror position [c][r].
-  float (&M)[kC][kF32Pad] = sm.r1.A;
-  // diagonal 16 x 16 blocks: wave b inverts block b, lane = column, one row of A at a time
+  const int hh = w >> 2, wl = w & 3;
+  float (&M)[kC][kF32Pad] = sm.r.M[hh];
+  // diagonal 16 x 16 blocks: wave wl inverts block wl, lane = column, one row of A at a time
   if (lane < 16) {
-    const int b0 = 16 * w, col = lane;
+    const int b0 = 16 * wl, col = lane;
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {   // row r of the block: x_r = e_r - sum_{m < r} A_rm x_m
@@ -566,11 +597,11 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
   }
   __syncthreads();
   // off-diagonal block (i, b), i = b + d:  T_ib = -T_ii * sum_{k=b}^{i-1} A_ik T_kb,
-  // level by level on the fp32 matrix cores (wave b handles block (b + d, b))
+  // level by level on the fp32 matrix cores (wave wl handles block (wl + d, wl))
 #pragma unroll 1
   for (int d = 1; d < 4; ++d) {
-    if (w < 4 - d) {
-      const int b = w, i = b + d;
+    if (wl < 4 - d) {
+      const int b = wl, i = b + d;
       f32x4 X = {0.f, 0.f, 0.f, 0.f};
       for (int kb = b; kb < i; ++kb) {
 #pragma unroll
@@ -594,29 +625,30 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrefillArgs a) {
   }
 
   // ---- T diag(beta) as a hi + lo bf16 pair, straight to the workspace in operand order.
-  // Lane = row r; wave w takes columns s0 = 8 (w + 4 it) .. + 7, so the reads of T's
+  // Lane = row r; wave wl takes columns s0 = 8 (wl + 4 it) .. + 7, so the reads of T's
   // mirrored entries M[s][r] hit distinct banks.
+  uint8_t* wsh = ws0 + (size_t)hh * kWsHead;
   bf16* Thg = reinterpret_cast<bf16*>(wsh + kWsTh);
   bf16* Tlg = reinterpret_cast<bf16*>(wsh + kWsTl);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
-    const int r = lane, s0 = 8 * (w + 4 * it);
+    const int r = lane, s0 = 8 * (wl + 4 * it);
     if ((s0 >> 5) <= (r >> 4) / 2) {   // a stored (not all-zero) fragment
       f32x4 tv[2];
 #pragma unroll
       for (int e = 0; e < 8; ++e) tv[e >> 2][e & 3] = M[s0 + e][r];
-      const f32x4 bv[2] = {*reinterpret_cast<const f32x4*>(&sm.beta[s0]),
-                           *reinterpret_cast<const f32x4*>(&sm.beta[s0 + 4])};
+      const f32x4 bv[2] = {*reinterpret_cast<const f32x4*>(&sm.beta[hh][s0]),
+                           *reinterpret_cast<const f32x4*>(&sm.beta[hh][s0 + 4])};
 #pragma unroll
       for (int e = 0; e < 8; ++e)   // T is lower triangular; the mirror of its strict upper part holds A
         tv[e >> 2][e & 3] = (s0 + e <= r) ? tv[e >> 2][e & 3] * bv[e >> 2][e & 3] : 0.f;
       bf16x8 hv, lv;
       split8(tv[0], tv[1], hv, lv);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int off = tb_frag_off(r, s0 + 4 * hh);
-        *reinterpret_cast<bf16x4*>(Thg + off) = bf16x4{hv[4 * hh], hv[4 * hh + 1], hv[4 * hh + 2], hv[4 * hh + 3]};
-        *reinterpret_cast<bf16x4*>(Tlg + off) = bf16x4{lv[4 * hh], lv[4 * hh + 1], lv[4 * hh + 2], lv[4 * hh + 3]};
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int off = tb_frag_off(r, s0 + 4 * h2);
+        *reinterpret_cast<bf16x4*>(Thg + off) = bf16x4{hv[4 * h2], hv[4 * h2 + 1], hv[4 * h2 + 2], hv[4 * h2 + 3]};
+        *reinterpret_cast<bf16x4*>(Tlg + off) = bf16x4{lv[4 * h2], lv[4 * h2 + 1], lv[4 * h2 + 2], lv[4 * h2 + 3]};
       }
     }
   }
@@ -737,18 +769,23 @@ __device__ __forceinline__ void chain_u(const UOps& o, const f32x4 (&X0)[4], con
   bf16x8 Rh[2], Rl[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) split8(R[2 * ks], R[2 * ks + 1], Rh[ks], Rl[ks]);
-  // U = T diag(beta) R = Th Rl + Tl Rh + Th Rh (lower triangular: K-steps 0 .. rt / 2)
+  // U = T diag(beta) R = Th Rl + Tl Rh + Th Rh (lower triangular: K-steps 0 .. rt / 2). Each
+  // token tile accumulates its terms in the order Th Rl, Tl Rh per K-step, then Th Rh per
+  // K-step; the four tiles' chains are issued step by step, interleaved, so that no product
+  // waits on the one before it in its own chain.
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    f32x4 u = {0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < 4; ++rt) U[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks <= rt / 2; ++ks) {
-      u = mfma16x16x32(o.th[frag(rt, ks)], Rl[ks], u);
-      u = mfma16x16x32(o.tl[frag(rt, ks)], Rh[ks], u);
+  for (int st = 0; st < 6; ++st) {
+#pragma unroll
+    for (int rt = 3; rt >= 0; --rt) {
+      const int nk = rt / 2 + 1;            // K-steps of this tile
+      if (st >= 3 * nk) continue;
+      const int ks = st < 2 * nk ? st >> 1 : st - 2 * nk;
+      if (st >= 2 * nk) U[rt] = mfma16x16x32(o.th[frag(rt, ks)], Rh[ks], U[rt]);
+      else if (st & 1) U[rt] = mfma16x16x32(o.tl[frag(rt, ks)], Rh[ks], U[rt]);
+      else U[rt] = mfma16x16x32(o.th[frag(rt, ks)], Rl[ks], U[rt]);
     }
-#pragma unroll
-    for (int ks = 0; ks <= rt / 2; ++ks) u = mfma16x16x32(o.th[frag(rt, ks)], Rh[ks], u);
-    U[rt] = u;
   }
   // the decayed U as a hi + lo pair for the update
 #pragma unroll
@@ -944,12 +981,12 @@ struct XHalves {
 
 // Wait until the other chain wave has published chunk `count - 1`'s half of X. Both chain
 // waves run the same chunks and each publishes its half before it waits for the other's, so
-// the wait always ends; the spin is capped all the same (about 2^22 polls), so a fault in
-// that reasoning could not hang the GPU.
+// the wait always ends; the spin is capped all the same (2^22 polls, a fraction of a second),
+// so a fault in that reasoning could not hang the GPU. The poll does not sleep: the waiting
+// wave has its SIMD to itself, and each poll is one LDS read.
 __device__ __forceinline__ void wait_ready(const unsigned* ready, unsigned count) {
   for (int spin = 0; spin < (1 << 22); ++spin) {
     if (__hip_atomic_load(ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= count) return;
-    __builtin_amdgcn_s_sleep(1);
   }
 }
 
@@ -1359,10 +1396,18 @@ hipError_t launch_prefill(PrefillArgs a, int total_tokens, hipStream_t stream) {
   const bool with_p = heads * 2 <= kStateCus;
   if (FE && with_p) return hipErrorInvalidValue;
   if (total_tokens > 0) {
+    // V heads of one QK head pair up in the workgroups when their number is even
     const size_t pairs = nc * (size_t)a.h_qk;
-    const size_t prep_blocks = (pairs + 7) / 8 * 8 * (size_t)a.group;
-    if (with_p) hipLaunchKernelGGL((prep_kernel<true, false>), dim3((unsigned)prep_blocks), dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((prep_kernel<false, FE>), dim3((unsigned)prep_blocks), dim3(kThreads), 0, stream, a);
+    const int hp = a.group % 2 == 0 ? 2 : 1;
+    const size_t prep_blocks = (pairs + 7) / 8 * 8 * (size_t)(a.group / hp);
+    const dim3 grid((unsigned)prep_blocks), block(4 * hp * kWave);
+    if (with_p) {
+      if (hp == 2) hipLaunchKernelGGL((prep_kernel<true, false, 2>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((prep_kernel<true, false, 1>), grid, block, 0, stream, a);
+    } else {
+      if (hp == 2) hipLaunchKernelGGL((prep_kernel<false, FE, 2>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((prep_kernel<false, FE, 1>), grid, block, 0, stream, a);
+    }
   }
   // With few heads, eight, four or two workgroups per head spread the heads over many CUs
   // (eight with the chain, the loads and the read-out on waves of their own); once the heads
