@@ -15,7 +15,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libgdn.so")
+# GDN_LIBRARY names another build of the library to load (for instance one with the host
+# code built under the address and undefined-behaviour sanitizers).
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(_PKG, "libgdn.so")
 
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(6)
 GDN_BF16, GDN_F32 = 0, 1

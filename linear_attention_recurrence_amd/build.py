@@ -52,6 +52,35 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# The host side of the C ABI (argument checks, dispatch) under the address and undefined-
+# behaviour sanitizers, linked with the kernels' objects from the last build(). The sanitizer
+# flags reach the host compilation only. Load it with the sanitizer runtime preloaded
+# (LD_PRELOAD=<SANITIZER_RUNTIME>) and GDN_LIBRARY=<the returned path>.
+SANITIZED_LIB = os.path.join(BUILD_DIR, "libgdn_hostsan.so")
+SANITIZER_RUNTIME = "/opt/rocm/lib/llvm/lib/clang/22/lib/linux/libclang_rt.asan-x86_64.so"
+_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+        "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized() -> str:
+    kernels = [os.path.join(BUILD_DIR, s + ".o") for s in SOURCES if s.endswith(".hip")]
+    missing = [k for k in kernels if not os.path.exists(k)]
+    if missing:
+        raise RuntimeError("build() first: missing %s" % ", ".join(missing))
+    obj = os.path.join(BUILD_DIR, "gdn_api.hostsan.o")
+    cmd = [HIPCC, "-O1", "-g", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC] + _SAN + [
+        "-c", os.path.join(CSRC, "gdn_api.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for gdn_api.cpp:\n%s\n%s" % (r.stdout, r.stderr))
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-shared-libasan"] + _SAN + kernels + [
+        obj, "-o", SANITIZED_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (r.stdout, r.stderr))
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
+#include <cstring>
 #include <vector>
 #include "gdn.h"
 
@@ -89,12 +90,23 @@ gdn_status check_log_decay(const float* g, size_t count, void* stream) {
     if (gdn_st_ != GDN_OK) return gdn_st_; \
   } while (0)
 
+// The integer a caller passed for an enum argument. A C caller may pass any int, and in C++
+// loading an enum object that holds a value outside the enum's range is undefined, so the
+// bits are copied out rather than loaded as the enum.
+template <typename E>
+int enum_code(const E* e) {
+  static_assert(sizeof(E) == sizeof(int), "enum arguments are int-sized");
+  int v;
+  std::memcpy(&v, e, sizeof v);
+  return v;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* gdn_status_string(gdn_status s) {
-  switch (s) {
+  switch (enum_code(&s)) {
     case GDN_OK: return "GDN_OK";
     case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
     case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: a size is negative or inconsistent";
@@ -120,7 +132,7 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dt
   if (num_seqs < 0 || total_tokens < 0) return GDN_ERR_SHAPE;
   const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
   if (st != GDN_OK) return st;
-  if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (enum_code(&io_dtype) != GDN_BF16 && enum_code(&io_dtype) != GDN_F32) return GDN_ERR_UNSUPPORTED;
   if (num_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
   if (!cu_seqlens) return GDN_ERR_NULL;
   if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
@@ -128,7 +140,7 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dt
   GDN_TRY(check_seqlens(cu_seqlens, num_seqs, total_tokens, stream));
   GDN_TRY(check_log_decay(g, (size_t)total_tokens * h_v, stream));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (io_dtype == GDN_F32)
+  if (enum_code(&io_dtype) == GDN_F32)
     return from_hip(gdn::launch_recurrent_prefill(q, k, v, false, g, beta, cu_seqlens, num_seqs,
                                                   h_qk, h_v, scale, initial_state, final_state,
                                                   o, s));
@@ -180,18 +192,18 @@ gdn_status gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v
   if (num_seqs < 0 || total_tokens < 0) return GDN_ERR_SHAPE;
   const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
   if (st != GDN_OK) return st;
-  if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (enum_code(&io_dtype) != GDN_BF16 && enum_code(&io_dtype) != GDN_F32) return GDN_ERR_UNSUPPORTED;
   if (num_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
   if (!cu_seqlens) return GDN_ERR_NULL;
   if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
   if (!final_state && total_tokens == 0) return GDN_OK;   // nothing observable to do
-  if (io_dtype == GDN_BF16 &&
+  if (enum_code(&io_dtype) == GDN_BF16 &&
       gdn_chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v, d_k, d_v) > GDN_NOALLOC_SCRATCH_BYTES)
     return GDN_ERR_WORKSPACE;
   GDN_TRY(check_seqlens(cu_seqlens, num_seqs, total_tokens, stream));
   GDN_TRY(check_log_decay(g, (size_t)total_tokens * h_v, stream));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (io_dtype == GDN_F32)
+  if (enum_code(&io_dtype) == GDN_F32)
     return from_hip(gdn::launch_recurrent_prefill(q, k, v, false, g, beta, cu_seqlens, num_seqs,
                                                   h_qk, h_v, scale, initial_state, final_state,
                                                   o, s));
@@ -209,12 +221,12 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtyp
   if (num_seqs < 0) return GDN_ERR_SHAPE;
   const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
   if (st != GDN_OK) return st;
-  if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (enum_code(&io_dtype) != GDN_BF16 && enum_code(&io_dtype) != GDN_F32) return GDN_ERR_UNSUPPORTED;
   if (num_seqs == 0) return GDN_OK;
   if (!q || !k || !v || !g || !beta || !state_pool || !o) return GDN_ERR_NULL;
   GDN_TRY(check_slots(state_slots, num_seqs, stream));
   GDN_TRY(check_log_decay(g, (size_t)num_seqs * h_v, stream));
-  return from_hip(gdn::launch_decode(q, k, v, io_dtype == GDN_BF16, g, beta, state_pool,
+  return from_hip(gdn::launch_decode(q, k, v, enum_code(&io_dtype) == GDN_BF16, g, beta, state_pool,
                                      state_slots, num_seqs, h_qk, h_v, scale, o,
                                      static_cast<hipStream_t>(stream)));
 }
@@ -227,12 +239,12 @@ gdn_status gdn_verify_step(const void* q, const void* k, const void* v, gdn_dtyp
   if (num_seqs < 0 || num_tokens < 0) return GDN_ERR_SHAPE;
   const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
   if (st != GDN_OK) return st;
-  if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (enum_code(&io_dtype) != GDN_BF16 && enum_code(&io_dtype) != GDN_F32) return GDN_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0) return GDN_OK;
   if (!q || !k || !v || !g || !beta || !state_pool || !o) return GDN_ERR_NULL;
   GDN_TRY(check_slots(state_slots, num_seqs, stream));
   GDN_TRY(check_log_decay(g, (size_t)num_seqs * num_tokens * h_v, stream));
-  return from_hip(gdn::launch_verify(q, k, v, io_dtype == GDN_BF16, g, beta, state_pool,
+  return from_hip(gdn::launch_verify(q, k, v, enum_code(&io_dtype) == GDN_BF16, g, beta, state_pool,
                                      state_slots, snapshots, num_seqs, num_tokens, h_qk, h_v,
                                      scale, o, static_cast<hipStream_t>(stream)));
 }
@@ -246,14 +258,14 @@ gdn_status gdn_channel_decay_prefill(const void* q, const void* k, const void* v
   if (num_seqs < 0 || total_tokens < 0) return GDN_ERR_SHAPE;
   const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
   if (st != GDN_OK) return st;
-  if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (enum_code(&io_dtype) != GDN_BF16 && enum_code(&io_dtype) != GDN_F32) return GDN_ERR_UNSUPPORTED;
   if (num_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
   if (!cu_seqlens) return GDN_ERR_NULL;
   if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
   if (!final_state && total_tokens == 0) return GDN_OK;   // nothing observable to do
   GDN_TRY(check_seqlens(cu_seqlens, num_seqs, total_tokens, stream));
   GDN_TRY(check_log_decay(g, (size_t)total_tokens * h_v * d_v, stream));
-  return from_hip(gdn::launch_channel_prefill(q, k, v, io_dtype == GDN_BF16, g, beta, cu_seqlens,
+  return from_hip(gdn::launch_channel_prefill(q, k, v, enum_code(&io_dtype) == GDN_BF16, g, beta, cu_seqlens,
                                               num_seqs, h_qk, h_v, scale, initial_state,
                                               final_state, o, static_cast<hipStream_t>(stream)));
 }
@@ -266,12 +278,12 @@ gdn_status gdn_channel_decay_decode_step(const void* q, const void* k, const voi
   if (num_seqs < 0) return GDN_ERR_SHAPE;
   const gdn_status st = check_common(h_qk, h_v, d_k, d_v);
   if (st != GDN_OK) return st;
-  if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (enum_code(&io_dtype) != GDN_BF16 && enum_code(&io_dtype) != GDN_F32) return GDN_ERR_UNSUPPORTED;
   if (num_seqs == 0) return GDN_OK;
   if (!q || !k || !v || !g || !beta || !state_pool || !o) return GDN_ERR_NULL;
   GDN_TRY(check_slots(state_slots, num_seqs, stream));
   GDN_TRY(check_log_decay(g, (size_t)num_seqs * h_v * d_v, stream));
-  return from_hip(gdn::launch_channel_decode(q, k, v, io_dtype == GDN_BF16, g, beta, state_pool,
+  return from_hip(gdn::launch_channel_decode(q, k, v, enum_code(&io_dtype) == GDN_BF16, g, beta, state_pool,
                                              state_slots, num_seqs, h_qk, h_v, scale, o,
                                              static_cast<hipStream_t>(stream)));
 }
@@ -363,14 +375,14 @@ gdn_status gdn_gated_rmsnorm(const void* o, const void* z, gdn_dtype io_dtype, c
   if (rows < 0 || h_v < 1 || d_v < 1) return GDN_ERR_SHAPE;
   if (!(eps >= 0.f) || !std::isfinite(eps)) return GDN_ERR_SHAPE;
   if (d_v != 128) return GDN_ERR_UNSUPPORTED;
-  if (io_dtype != GDN_BF16 && io_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
-  if (gate != GDN_GATE_SIGMOID && gate != GDN_GATE_SILU) return GDN_ERR_UNSUPPORTED;
+  if (enum_code(&io_dtype) != GDN_BF16 && enum_code(&io_dtype) != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (enum_code(&gate) != GDN_GATE_SIGMOID && enum_code(&gate) != GDN_GATE_SILU) return GDN_ERR_UNSUPPORTED;
   const long long n_vec = (long long)rows * h_v;
   if (n_vec > (1LL << 34)) return GDN_ERR_UNSUPPORTED;
   if (rows == 0) return GDN_OK;
   if (!o || !z || !weight || !out) return GDN_ERR_NULL;
-  return from_hip(gdn::launch_gated_rmsnorm(o, z, io_dtype == GDN_BF16, weight, n_vec, eps,
-                                            gate == GDN_GATE_SILU,
+  return from_hip(gdn::launch_gated_rmsnorm(o, z, enum_code(&io_dtype) == GDN_BF16, weight, n_vec, eps,
+                                            enum_code(&gate) == GDN_GATE_SILU,
                                             out, static_cast<hipStream_t>(stream)));
 }
 
