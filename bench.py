@@ -51,22 +51,23 @@ H_QK, H_V = 16, 32
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_amd", "csrc")
 
 # Hardware counters of one call, from rocprofv3 --pmc runs of `python bench.py --workload
-# prefill,frontend,decode,copy --steps 5 --warmup 1 --decode-steps 20 --no-cpu-baseline`
-# (the commands and raw per-kernel figures are kept under profiles/):
+# prefill_t32768,frontend,decode,copy` and `--workload prefill_t4096` (with `--steps 5
+# --warmup 1 --decode-steps 20 --no-cpu-baseline`; the commands and the per-kernel figures
+# are kept in profiles/hbm_mfma_counters.md):
 #  * "bytes": HBM bytes per call, FETCH_SIZE plus WRITE_SIZE (KiB per dispatch, summed over
 #    the call's kernels) in two passes, each scaled by what the same counter reads for a
 #    plain 1 GiB device copy;
 #  * "mfma_busy": the fraction of the matrix cores' cycles spent busy over the call,
-#    sum(SQ_VALU_MFMA_BUSY_CYCLES) / (GRBM_GUI_ACTIVE x 1024 SIMDs) per kernel, weighted by
+#    sum(SQ_VALU_MFMA_BUSY_CYCLES) / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) per kernel, weighted by
 #    each kernel's share of the call's time.
 # `sources` fingerprints the kernel sources the figures were taken on: once they change,
 # the figures no longer describe the kernels and are reported as null.
 COUNTERS = {
-    "prefill_t32768": {"bytes": None, "mfma_busy": None, "sources": None},
-    "prefill_t4096": {"bytes": None, "mfma_busy": None, "sources": None},
-    "prefill_packed64": {"bytes": None, "mfma_busy": None, "sources": None},
-    "prefill_conv_packed64": {"bytes": None, "sources": None},
-    "decode": {"bytes": None, "sources": None},
+    "prefill_t32768": {"bytes": 1990589353, "mfma_busy": 0.1417, "sources": "4e0008825c5b30b2"},
+    "prefill_t4096": {"bytes": 250218012, "mfma_busy": 0.1419, "sources": "4e0008825c5b30b2"},
+    "prefill_packed64": {"bytes": 12458554831, "mfma_busy": 0.2398, "sources": "4e0008825c5b30b2"},
+    "prefill_conv_packed64": {"bytes": 12534611196, "sources": "4e0008825c5b30b2"},
+    "decode": {"bytes": 1083359601, "sources": "47d685d5456327c3"},
 }
 
 
