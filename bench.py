@@ -97,10 +97,10 @@ def counter(name, field, sources):
 # ---------------------------------------------------------------------------------------
 
 def prefill_flops(tokens: int, h_v: int = H_V) -> float:
-    """Matrix-product FLOPs of the chunked form per token and V head: five C x C x d
-    products (K K^T, Q K^T, T(beta gam)K, T(beta)V, P U) = 10 C d, and three C x d x d
-    products (W S^T, Q S^T, U^T K) = 6 d^2."""
-    return float(tokens) * h_v * (10 * C * D + 6 * D * D)
+    """Matrix-product FLOPs of the chunked form per token and V head: four C x C x d
+    products (K K^T, Q K^T, T diag(beta) R, P U) = 8 C d, and three C x d x d products
+    (K S^T, Q S^T, U^T K) = 6 d^2."""
+    return float(tokens) * h_v * (8 * C * D + 6 * D * D)
 
 
 def prefill_bytes(tokens: int, num_seqs: int, with_s0: bool, h_qk=H_QK, h_v=H_V) -> float:

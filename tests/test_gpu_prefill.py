@@ -88,10 +88,10 @@ def _sub_batch(x, first, last):
 def test_prefill_many_sequences_full_heads():
     """The state pass picks its workgroup shape from the number of (sequence, V head) pairs:
     12 sequences x 32 V heads take one workgroup of eight one-tile waves per head, which
-    forms -W and P^T on chip (prep then writes -T diag(beta gam) instead); 4 sequences take
-    two workgroups per head, 2 sequences four with helper waves, and 1 sequence eight with a
-    read-out wave, all reading -W and P^T from the workspace. The per-row arithmetic, and
-    -W and P^T themselves, are the same in all of them, so results must agree bit for bit."""
+    forms P^T on chip; 4 sequences take two workgroups per head, 2 sequences four, and 1
+    sequence eight with the chain on two waves and a read-out wave, all reading P^T from the
+    workspace. The per-row arithmetic, and P^T itself, are the same in all of them, so
+    results must agree bit for bit."""
     lens = [0, 1, 64, 65, 200, 17, 128, 0, 311, 63, 90, 5]
     x = workloads.make_prefill(lens, h_qk=16, h_v=32, with_initial_state=True, seed=13)
     o, fin = _run(x)

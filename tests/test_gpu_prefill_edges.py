@@ -9,8 +9,8 @@ is then at its worst); and all-zero key and query rows in mid-chunk. Each runs a
 64, 65 and 200 (a whole chunk, a one-token tail, several chunks with a ragged tail), with
 and without an initial state, and through every workgroup shape of the state pass, which
 the library picks from the number of (sequence, V head) pairs: 32 pairs (eight workgroups
-per head with a read-out wave), 64 (four with helper waves), 128 (two) and 160 (one
-workgroup of eight waves per head, which forms -W and P^T on chip). The same tolerances as
+per head with the chain on two waves and a read-out wave), 64 (four), 128 (two) and 160 (one
+workgroup of eight waves per head, which forms P^T on chip). The same tolerances as
 every other prefill test.
 """
 
