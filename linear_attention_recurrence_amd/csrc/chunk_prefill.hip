@@ -16,8 +16,9 @@
 // Everything that does not involve S depends on one chunk only, so the work splits in two
 // launches that share a workspace:
 //
-//  * prep_kernel, one workgroup per (chunk, V head), all chunks in parallel: K K^T (and
-//    K Q^T) on the bf16 matrix cores, the prefix sums, the unit-lower-triangular inverse T in
+//  * prep_kernel, one workgroup per (chunk, QK head) and one or two of the QK head's V heads,
+//    all chunks in parallel: K K^T (and K Q^T, formed once for the V heads that share them)
+//    on the bf16 matrix cores, the prefix sums, the unit-lower-triangular inverse T in
 //    fp32 (16 x 16 diagonal blocks by substitution, off-diagonal blocks on the fp32 matrix
 //    cores). Writes T diag(beta) and P^T, P = scale (Q K^T o Gam o lower-incl), each as a
 //    hi + lo bf16 pair in the operand order of the state pass, and gam, gam_C / gam, G.
