@@ -126,11 +126,16 @@ struct PrefillArgs {
   int num_seqs, h_qk, h_v, group, n_chunks_max;
   float scale;
   // with the front end inside the prefill (FE kernels): the mixed q | k | v input
-  // [tokens][C] bf16, the conv taps [C][conv_k] fp32 and the q scale; q, k, v are unused
+  // [tokens][C] bf16, the conv taps [C][conv_k] fp32 and the q scale. The prep writes the
+  // front end's q and k ([tokens][h_qk][128] each, in the workspace) to q_out and k_out,
+  // which the state pass then reads as q and k; v is unused (the state pass runs the front
+  // end on the v rows itself)
   const bf16* mixed;
   const float* conv_w;
   int conv_k, C;
   float q_scale;
+  bf16* q_out;
+  bf16* k_out;
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -309,10 +314,12 @@ __device__ __forceinline__ void fe_history(const bf16* base, const bf16* halo, b
 }
 
 // Rows r0 .. r0 + R - 1 converted in place, each read just before it is overwritten (only
-// this quarter-wave touches them once the history reads are done).
+// this quarter-wave touches them once the history reads are done). With gout, rows below nv
+// also go to gout + row * gstride (elements), the row's 128 channels contiguous.
 template <bool IMG, int R>
 __device__ __forceinline__ void fe_rows(const PrefillArgs& a, bf16* base, int ch0, bool is_q, bool is_k, int r0,
-                                        int l16, const bf16x8 (&hist)[3]) {
+                                        int l16, const bf16x8 (&hist)[3], bf16* gout = nullptr,
+                                        size_t gstride = 0, int nv = 0) {
   float wt[4][8];
   load_taps(a.conv_w, a.conv_k, ch0 + 8 * l16, wt);
   float h1[8], h2[8], h3[8];
@@ -329,7 +336,9 @@ __device__ __forceinline__ void fe_rows(const PrefillArgs& a, bf16* base, int ch
     float x0[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x0[e] = (float)raw[e];
-    *row = conv_token(wt, x0, h1, h2, h3, is_q, is_k, a.q_scale);
+    const bf16x8 y = conv_token(wt, x0, h1, h2, h3, is_q, is_k, a.q_scale);
+    *row = y;
+    if (gout && r0 + u < nv) *reinterpret_cast<bf16x8*>(gout + (size_t)(r0 + u) * gstride + 8 * l16) = y;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       h3[e] = a.conv_k > 3 ? h2[e] : 0.f;
@@ -399,8 +408,9 @@ struct PrepSmem {
   union {
     struct {
       bf16 K[kC * kD];          // swizzled 256-byte rows
-      // Q rows (WITH_P), or with the front end the raw K rows before the chunk
-      bf16 Q[WITH_P ? kC * kD : (FE ? 4 * kD : 8)];
+      bf16 Q[(WITH_P || FE) ? kC * kD : 8];
+      // with the front end: the raw K and Q rows before the chunk
+      bf16 halo[FE ? 2 : 1][FE ? 4 * kD : 8];
     } in;
     // per V head, once the Gram products are in registers: A in the strict lower triangle,
     // T transposed in the upper one
@@ -443,12 +453,14 @@ __global__ __launch_bounds__(4 * HP * kWave, HP == 1 ? 4 : 3) void prep_kernel(P
   // ---- loads: K, Q rows straight into swizzled LDS images; g, beta ----
   constexpr int kPieces = 16 / NW;            // 1 KB pieces (four rows) of each image per wave
   const size_t qk_stride = (size_t)a.h_qk * kD;
-  if constexpr (FE) {   // the raw K rows of QK head j (and the halo) by direct loads
-    const int ch0 = (a.h_qk + j) * kD;
+  if constexpr (FE) {   // the raw K and Q rows of QK head j (and their halos) by direct loads
+    const int chk = (a.h_qk + j) * kD, chq = j * kD;
 #pragma unroll
-    for (int i = 0; i < kPieces; ++i)
-      dma_rows256(a.mixed + (size_t)t0 * a.C + ch0, (uint32_t)a.C * 2, nv, sm.r.in.K, kPieces * w + i, lane);
-    if (w == 0 && t0 > a.cu[n]) dma_halo(a, ch0, t0, sm.r.in.Q, lane);
+    for (int i = 0; i < kPieces; ++i) {
+      dma_rows256(a.mixed + (size_t)t0 * a.C + chk, (uint32_t)a.C * 2, nv, sm.r.in.K, kPieces * w + i, lane);
+      dma_rows256(a.mixed + (size_t)t0 * a.C + chq, (uint32_t)a.C * 2, nv, sm.r.in.Q, kPieces * w + i, lane);
+    }
+    if (t0 > a.cu[n] && w < 2) dma_halo(a, w == 0 ? chk : chq, t0, sm.r.in.halo[w], lane);
   } else {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
@@ -471,13 +483,29 @@ __global__ __launch_bounds__(4 * HP * kWave, HP == 1 ? 4 : 3) void prep_kernel(P
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if constexpr (FE) {   // K rows from the front end: quarter-wave 4 w + g4 takes 4 / HP rows
+  if constexpr (FE) {
+    // K and Q rows from the front end: quarter-wave 4 w + g4 takes 4 / HP rows of each. The
+    // first workgroup of the QK head also writes them out for the state pass, so each QK
+    // head's q and k are computed once per chunk.
+    // (K, then Q, each with its own barrier: one set of history rows in registers at a time;
+    // the lane indices pass through an empty asm statement so that the addresses derived
+    // from them are formed where they are used, not kept live across the block)
     constexpr int R = 4 / HP;
-    const int r0 = R * (4 * w + g4);
+    int fg4 = g4, fl16 = l16;
+    asm volatile("" : "+v"(fg4), "+v"(fl16));
+    const int r0 = R * (4 * w + fg4);
+    const bool first = t0 == a.cu[n];
+    const size_t row0 = ((size_t)t0 * a.h_qk + j) * kD;
+    const size_t stride = (size_t)a.h_qk * kD;
     bf16x8 hist[3];
-    fe_history<true>(sm.r.in.K, sm.r.in.Q, t0 == a.cu[n], r0, l16, hist);
+    fe_history<true>(sm.r.in.K, sm.r.in.halo[0], first, r0, fl16, hist);
     __syncthreads();
-    fe_rows<true, R>(a, sm.r.in.K, (a.h_qk + j) * kD, false, true, r0, l16, hist);
+    fe_rows<true, R>(a, sm.r.in.K, (a.h_qk + j) * kD, false, true, r0, fl16, hist,
+                     gi == 0 ? a.k_out + row0 : nullptr, stride, nv);
+    fe_history<true>(sm.r.in.Q, sm.r.in.halo[1], first, r0, fl16, hist);
+    __syncthreads();
+    fe_rows<true, R>(a, sm.r.in.Q, j * kD, true, false, r0, fl16, hist, gi == 0 ? a.q_out + row0 : nullptr,
+                     stride, nv);
     __syncthreads();
   }
 
@@ -1174,36 +1202,30 @@ struct StateBuf {
   bf16 pl[kFrags * 512];
   float gl[4 * kC];          // gam, gam_C / gam, G, unused
   bf16 vt[NW][kC * 16];
-  bf16 halo[FE ? 3 : 1][FE ? 4 * kD : 8];   // with the front end: the raw q, k, v rows before the chunk
+  bf16 halo[FE ? 4 * kD : 8];   // with the front end: the raw value rows before the chunk
 };
 
 // This wave's share of the direct loads of one chunk: 1 KB pieces numbered 0 .. 16 K rows,
 // 16 Q rows, 12 T diag(beta) fragments, 12 P^T fragments (not with FORM), the decay factors,
-// two per value tile; wave w issues the pieces p = w (mod NW). With FE the K, Q and value
-// rows are the raw mixed-input rows of the heads (converted in place by fe_chunk), and three
-// more pieces load the halos.
+// two per value tile; wave w issues the pieces p = w (mod NW). With FE the value rows are
+// the head's raw mixed-input rows (converted in place by fe_chunk), and one more piece loads
+// the three raw rows before the chunk.
 template <int NW, bool FORM, bool FE>
 __device__ __forceinline__ void dma_chunk(const PrefillArgs& a, const ChunkSrc& s, StateBuf<NW, FE>& d,
-                                          const DmaStrides& st, int t0, bool first, int j, int h, int w,
-                                          int lane) {
+                                          const DmaStrides& st, int t0, bool first, int h, int w, int lane) {
   constexpr int kP = FORM ? 0 : 2 * kFrags;
-  constexpr int kTotal = 32 + 2 * kFrags + kP + 1 + 2 * NW + (FE ? 3 : 0);
-  const bf16* kb = s.kb;
-  const bf16* qb = s.qb;
+  constexpr int kTotal = 32 + 2 * kFrags + kP + 1 + 2 * NW + (FE ? 1 : 0);
   const bf16* vb = s.vb;
-  uint32_t qk = st.qk, vs = st.v;
+  uint32_t vs = st.v;
   if constexpr (FE) {
-    const bf16* row0 = a.mixed + (size_t)t0 * a.C;
-    kb = row0 + (a.h_qk + j) * kD;
-    qb = row0 + j * kD;
-    vb = row0 + (2 * a.h_qk + h) * kD;
-    qk = vs = (uint32_t)a.C * 2;
+    vb = a.mixed + (size_t)t0 * a.C + (2 * a.h_qk + h) * kD;
+    vs = (uint32_t)a.C * 2;
   }
 #pragma unroll
   for (int i = 0; i < (kTotal + NW - 1) / NW; ++i) {
     const int p = w + NW * i;
-    if (p < 16) dma_rows256(kb, qk, s.nv, d.K, p, lane);
-    else if (p < 32) dma_rows256(qb, qk, s.nv, d.Q, p - 16, lane);
+    if (p < 16) dma_rows256(s.kb, st.qk, s.nv, d.K, p, lane);
+    else if (p < 32) dma_rows256(s.qb, st.qk, s.nv, d.Q, p - 16, lane);
     else if (p < 32 + 2 * kFrags) dma_1k(s.ws + kWsTh + (p - 32) * kFragBytes, d.th + 512 * (p - 32), lane);
     else if (p < 32 + 2 * kFrags + kP)
       dma_1k(s.ws + kWsPh + (p - 32 - 2 * kFrags) * kFragBytes, d.ph + 512 * (p - 32 - 2 * kFrags), lane);
@@ -1213,37 +1235,28 @@ __device__ __forceinline__ void dma_chunk(const PrefillArgs& a, const ChunkSrc& 
       dma_vtile(vb + 16 * (q >> 1), vs, s.nv, d.vt[q >> 1], q & 1, lane);
     } else if (p < kTotal) {
       if constexpr (FE) {
-        const int m = p - (33 + 2 * kFrags + kP + 2 * NW);   // 0: q, 1: k, 2: v
-        const int ch0 = m == 0 ? j * kD : m == 1 ? (a.h_qk + j) * kD : (2 * a.h_qk + h) * kD;
-        if (!first) dma_halo(a, ch0, t0, d.halo[m], lane);
+        if (!first) dma_halo(a, (2 * a.h_qk + h) * kD, t0, d.halo, lane);
       }
     }
   }
 }
 
-// With FE, the workgroup's share of the conversion of a chunk's raw rows (landed in `d`):
-// waves 0, 1 take Q, waves 2, 3 K and waves 4, 5 the values, 8 rows per quarter-wave (whole
-// waves on one head, so no wave branches on the head's kind). Two workgroup barriers: the
-// reads of the raw rows (each quarter-wave's and the three before them) all come before any
-// row is overwritten.
+// With FE, the conversion of a chunk's raw value rows (landed in `d`): quarter-wave 4 w + g4
+// takes rows 2 (4 w + g4) and the next one. Two workgroup barriers: the reads of the three
+// rows before each quarter-wave's own all come before any row is overwritten.
 template <int NW>
-__device__ __forceinline__ void fe_chunk(const PrefillArgs& a, StateBuf<NW, true>& d, bool first, int j, int h, int w,
+__device__ __forceinline__ void fe_chunk(const PrefillArgs& a, StateBuf<NW, true>& d, bool first, int h, int w,
                                          int g4, int l16) {
   static_assert(NW == 8, "the front end inside the state pass uses eight waves");
   // The lane indices pass through an empty asm statement so that the addresses derived from
   // them are formed here each chunk: hoisted out of the chunk loop, they stay live across
   // the whole chunk and the state pass runs out of registers.
   asm volatile("" : "+v"(g4), "+v"(l16));
-  const int kind = w >> 1;                     // 0: q, 1: k, 2: v; 3: none
-  const int r0 = 8 * (4 * (w & 1) + g4);
-  const int ch0 = kind == 0 ? j * kD : kind == 1 ? (a.h_qk + j) * kD : (2 * a.h_qk + h) * kD;
-  bf16* img = kind == 0 ? d.Q : d.K;
+  const int r0 = 2 * (4 * w + g4);
   bf16x8 hist[3];
-  if (kind < 2) fe_history<true>(img, d.halo[kind], first, r0, l16, hist);
-  else if (kind == 2) fe_history<false>(d.vt[0], d.halo[2], first, r0, l16, hist);
+  fe_history<false>(d.vt[0], d.halo, first, r0, l16, hist);
   __syncthreads();
-  if (kind < 2) fe_rows<true, 8>(a, img, ch0, kind == 0, kind == 1, r0, l16, hist);
-  else if (kind == 2) fe_rows<false, 8>(a, d.vt[0], ch0, false, false, r0, l16, hist);
+  fe_rows<false, 2>(a, d.vt[0], (2 * a.h_qk + h) * kD, false, false, r0, l16, hist);
 }
 
 // With FORM, the workgroup's share of P^T for the chunk in `b` (Q, K and G in): wave w takes
@@ -1314,7 +1327,7 @@ __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
   auto step = [&](int ci, StateBuf<NW, FE>& cur, StateBuf<NW, FE>& nxt) {
     __builtin_amdgcn_s_waitcnt(0);   // this wave's share of the chunk's loads has landed ...
     __syncthreads();                 // ... and everyone's; the other buffer is free
-    if (ci + 1 < n_chunks) dma_chunk<NW, FORM, FE>(a, src(ci + 1), nxt, dst, t_seq0 + (ci + 1) * kC, false, j, h, w, lane);
+    if (ci + 1 < n_chunks) dma_chunk<NW, FORM, FE>(a, src(ci + 1), nxt, dst, t_seq0 + (ci + 1) * kC, false, h, w, lane);
     if (FORM) form_pt<NW, FE>(cur, a.scale, w, g4, l16, lane);
     bf16x8 sh[4];
     f32x4 u[4];
@@ -1329,16 +1342,16 @@ __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
       if (ci + 1 < n_chunks) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        fe_chunk<NW>(a, nxt, false, j, h, w, g4, l16);
+        fe_chunk<NW>(a, nxt, false, h, w, g4, l16);
       }
     }
   };
   if (n_chunks > 0) {
-    dma_chunk<NW, FORM, FE>(a, src(0), buf0, dst, t_seq0, true, j, h, w, lane);
+    dma_chunk<NW, FORM, FE>(a, src(0), buf0, dst, t_seq0, true, h, w, lane);
     if constexpr (FE) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      fe_chunk<NW>(a, buf0, true, j, h, w, g4, l16);
+      fe_chunk<NW>(a, buf0, true, h, w, g4, l16);
     }
   }
   for (int ci = 0; ci < n_chunks; ci += 2) {
@@ -1468,9 +1481,9 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
 }
 
 size_t chunk_prefill_conv_workspace_bytes(int total_tokens, int num_seqs, int h_qk, int h_v) {
-  size_t b = chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v);
-  if (!conv_fused(num_seqs, h_v)) b += (size_t)total_tokens * (2 * h_qk + h_v) * kD * 2;
-  return b;
+  // after the prefill's own blocks: q and k from the front end (fused), or q, k and v
+  const size_t heads = conv_fused(num_seqs, h_v) ? 2 * (size_t)h_qk : 2 * (size_t)h_qk + h_v;
+  return chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v) + (size_t)total_tokens * heads * kD * 2;
 }
 
 hipError_t launch_chunk_prefill_conv(const void* mixed, const float* conv_weight, int conv_kernel,
@@ -1500,6 +1513,11 @@ hipError_t launch_chunk_prefill_conv(const void* mixed, const float* conv_weight
   a.conv_k = conv_kernel;
   a.C = (2 * h_qk + h_v) * kD;
   a.q_scale = q_scale;
+  a.q_out = reinterpret_cast<bf16*>(static_cast<uint8_t*>(workspace) +
+                                    chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v));
+  a.k_out = a.q_out + (size_t)total_tokens * h_qk * kD;
+  a.q = a.q_out;
+  a.k = a.k_out;
   return launch_prefill<true>(a, total_tokens, stream);
 }
 
