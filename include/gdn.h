@@ -122,10 +122,9 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dt
  *   g, beta, cu_seqlens, states, o (bf16) as gdn_chunk_prefill
  *   workspace     at least gdn_chunk_prefill_conv_workspace_bytes(...) bytes
  *
- * With more than 128 (sequence, V head) pairs the front end runs inside the prefill's own
- * loads (q, k and v are computed into on-chip memory as each chunk is loaded and never
- * written to device memory); with fewer, eight workgroups share each head and would repeat
- * it, so it runs as its own pass into the workspace first (which the size query includes).
+ * The front end runs as its own pass into the workspace (q, k and v after the prefill's own
+ * blocks, which the size query includes), then the prefill reads them there: the results are
+ * bit for bit those of gdn_conv_prep followed by gdn_chunk_prefill.
  * Validation and errors as gdn_chunk_prefill and gdn_conv_prep.
  */
 size_t gdn_chunk_prefill_conv_workspace_bytes(int32_t total_tokens, int32_t num_seqs,

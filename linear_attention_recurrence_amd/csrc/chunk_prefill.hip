@@ -55,7 +55,6 @@
 #include <atomic>
 #include <mutex>
 
-#include "conv_device.h"
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -125,17 +124,6 @@ struct PrefillArgs {
   uint8_t* ws;              // per (chunk, V head) blocks
   int num_seqs, h_qk, h_v, group, n_chunks_max;
   float scale;
-  // with the front end inside the prefill (FE kernels): the mixed q | k | v input
-  // [tokens][C] bf16, the conv taps [C][conv_k] fp32 and the q scale. The prep writes the
-  // front end's q and k ([tokens][h_qk][128] each, in the workspace) to q_out and k_out,
-  // which the state pass then reads as q and k; v is unused (the state pass runs the front
-  // end on the v rows itself)
-  const bf16* mixed;
-  const float* conv_w;
-  int conv_k, C;
-  float q_scale;
-  bf16* q_out;
-  bf16* k_out;
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -272,87 +260,6 @@ __device__ __forceinline__ void dma_vtile(const bf16* vb, uint32_t v_stride, int
   __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(vb) + off, lds_addr(tile + 512 * i), 16, 0, 0);
 }
 
-// ---- The front end inside the prefill's loads (FE kernels). The raw mixed-input rows of a
-// head for a chunk are brought into LDS by the same direct loads as q, k, v rows otherwise
-// (into the very image or value tile that will hold the head's rows), with the three rows
-// before the chunk in a small halo area when the chunk is not its sequence's first; then
-// each quarter-wave reads its rows r0 .. r0 + R - 1 and the three before them (fe_read),
-// and after a barrier writes the front end's output over its own rows (fe_write). The
-// output is conv_token's -- the device function of the packed front end -- so each row is
-// bit for bit what gdn_conv_prep writes. The 16 lanes of a quarter-wave cover the head's
-// 128 channels, 8 each. Rows at or past nv repeat input row nv - 1 (the direct loads clamp
-// them), which gives finite values that only feed discarded results or products with zero.
-
-// Where a head's rows sit in LDS: a swizzled 256-byte-row image (IMG), or a [tile][64][16]
-// value tile set (channel c in tile c / 16, tiles 512 * 2 elements apart).
-template <bool IMG>
-__device__ __forceinline__ bf16* fe_at(bf16* base, int r, int l16) {
-  if constexpr (IMG) return base + sw256(r, 8 * l16);
-  else return base + (l16 >> 1) * (kC * 16) + 16 * r + 8 * (l16 & 1);
-}
-// The halo of a chunk: one 1 KB load, lanes 16 m .. 16 m + 15 reading token t0 - 3 + min(m, 2).
-__device__ __forceinline__ void dma_halo(const PrefillArgs& a, int ch0, int t0, bf16* halo, int lane) {
-  const int t = t0 - 3 + min(lane >> 4, 2);
-  const size_t off = ((size_t)t * a.C + ch0) * 2 + 16 * (lane & 15);
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(a.mixed) + off, lds_addr(halo), 16, 0, 0);
-}
-
-// The three raw rows before row r0 (zero before the sequence start; `first`: the chunk starts
-// its sequence and the halo is not loaded). Read by every quarter-wave before the barrier
-// after which rows are overwritten: they are the previous quarter-wave's last rows, or the halo.
-template <bool IMG>
-__device__ __forceinline__ void fe_history(const bf16* base, const bf16* halo, bool first, int r0, int l16,
-                                           bf16x8 (&hist)[3]) {
-#pragma unroll
-  for (int u = 0; u < 3; ++u) {
-    const int r = r0 - 3 + u;
-    const bf16* p = r >= 0 ? fe_at<IMG>(const_cast<bf16*>(base), r, l16) : halo + (3 + r) * kD + 8 * l16;
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) hist[u][e] = (first && r < 0) ? (bf16)0.f : x[e];
-  }
-}
-
-// Rows r0 .. r0 + R - 1 converted in place, each read just before it is overwritten (only
-// this quarter-wave touches them once the history reads are done). With gout, rows below nv
-// also go to gout + row * gstride (elements), the row's 128 channels contiguous.
-template <bool IMG, int R>
-__device__ __forceinline__ void fe_rows(const PrefillArgs& a, bf16* base, int ch0, bool is_q, bool is_k, int r0,
-                                        int l16, const bf16x8 (&hist)[3], bf16* gout = nullptr,
-                                        size_t gstride = 0, int nv = 0) {
-  float wt[4][8];
-  load_taps(a.conv_w, a.conv_k, ch0 + 8 * l16, wt);
-  float h1[8], h2[8], h3[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {   // inputs more than K - 1 tokens back are zero
-    h3[e] = a.conv_k > 3 ? (float)hist[0][e] : 0.f;
-    h2[e] = a.conv_k > 2 ? (float)hist[1][e] : 0.f;
-    h1[e] = a.conv_k > 1 ? (float)hist[2][e] : 0.f;
-  }
-#pragma unroll
-  for (int u = 0; u < R; ++u) {
-    bf16x8* row = reinterpret_cast<bf16x8*>(fe_at<IMG>(base, r0 + u, l16));
-    const bf16x8 raw = *row;
-    float x0[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x0[e] = (float)raw[e];
-    const bf16x8 y = conv_token(wt, x0, h1, h2, h3, is_q, is_k, a.q_scale);
-    *row = y;
-    if (gout && r0 + u < nv) *reinterpret_cast<bf16x8*>(gout + (size_t)(r0 + u) * gstride + 8 * l16) = y;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      h3[e] = a.conv_k > 3 ? h2[e] : 0.f;
-      h2[e] = a.conv_k > 2 ? h1[e] : 0.f;
-      h1[e] = a.conv_k > 1 ? x0[e] : 0.f;
-    }
-  }
-}
-
-// Row r of a swizzled 256-byte-row image, 16 bytes at channel 8 l16.
-__device__ __forceinline__ void put_row256(bf16* img, int r, int l16, bf16x8 v) {
-  *reinterpret_cast<bf16x8*>(img + sw256(r, 8 * l16)) = v;
-}
-
 // Lower 16 x 16 tile t (0..9, row-major over the lower triangle) of a 64 x 64 product.
 __device__ __forceinline__ constexpr int tile_row(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
 __device__ __forceinline__ constexpr int tile_col(int t) { return t - tile_row(t) * (tile_row(t) + 1) / 2; }
@@ -403,14 +310,12 @@ __device__ __forceinline__ int pt_off(int rt, int ct, int lane) {
 // The chunk's K (and Q) rows are loaded and their Gram products formed once for the HP V
 // heads that share them (two when the heads of a QK head pair up, else one); the decays,
 // A, T and the workspace blocks are per V head, four waves each for the triangular solve.
-template <bool WITH_P, bool FE, int HP>
+template <bool WITH_P, int HP>
 struct PrepSmem {
   union {
     struct {
       bf16 K[kC * kD];          // swizzled 256-byte rows
-      bf16 Q[(WITH_P || FE) ? kC * kD : 8];
-      // with the front end: the raw K and Q rows before the chunk
-      bf16 halo[FE ? 2 : 1][FE ? 4 * kD : 8];
+      bf16 Q[WITH_P ? kC * kD : 8];
     } in;
     // per V head, once the Gram products are in registers: A in the strict lower triangle,
     // T transposed in the upper one
@@ -420,14 +325,12 @@ struct PrepSmem {
   alignas(16) float beta[HP][kC];
 };
 
-// WITH_P: also K Q^T and P^T (few heads); otherwise the state pass forms P^T itself. FE: K
-// comes from the mixed input through the front end (with WITH_P = false only).
-template <bool WITH_P, bool FE, int HP>
+// WITH_P: also K Q^T and P^T (few heads); otherwise the state pass forms P^T itself.
+template <bool WITH_P, int HP>
 __global__ __launch_bounds__(4 * HP * kWave, HP == 1 ? 4 : 3) void prep_kernel(PrefillArgs a) {
-  static_assert(!(WITH_P && FE), "the front end runs inside the many-heads prefill only");
   static_assert(HP == 1 || HP == 2, "one or two V heads per workgroup");
   constexpr int NW = 4 * HP;                      // waves
-  __shared__ PrepSmem<WITH_P, FE, HP> sm;
+  __shared__ PrepSmem<WITH_P, HP> sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int lane = tid & 63;
@@ -453,23 +356,13 @@ __global__ __launch_bounds__(4 * HP * kWave, HP == 1 ? 4 : 3) void prep_kernel(P
   // ---- loads: K, Q rows straight into swizzled LDS images; g, beta ----
   constexpr int kPieces = 16 / NW;            // 1 KB pieces (four rows) of each image per wave
   const size_t qk_stride = (size_t)a.h_qk * kD;
-  if constexpr (FE) {   // the raw K and Q rows of QK head j (and their halos) by direct loads
-    const int chk = (a.h_qk + j) * kD, chq = j * kD;
 #pragma unroll
-    for (int i = 0; i < kPieces; ++i) {
-      dma_rows256(a.mixed + (size_t)t0 * a.C + chk, (uint32_t)a.C * 2, nv, sm.r.in.K, kPieces * w + i, lane);
-      dma_rows256(a.mixed + (size_t)t0 * a.C + chq, (uint32_t)a.C * 2, nv, sm.r.in.Q, kPieces * w + i, lane);
-    }
-    if (t0 > a.cu[n] && w < 2) dma_halo(a, w == 0 ? chk : chq, t0, sm.r.in.halo[w], lane);
-  } else {
-#pragma unroll
-    for (int i = 0; i < kPieces; ++i) {
-      dma_rows256(a.k + (size_t)t0 * qk_stride + (size_t)j * kD, (uint32_t)qk_stride * 2, nv, sm.r.in.K,
+  for (int i = 0; i < kPieces; ++i) {
+    dma_rows256(a.k + (size_t)t0 * qk_stride + (size_t)j * kD, (uint32_t)qk_stride * 2, nv, sm.r.in.K,
+                kPieces * w + i, lane);
+    if (WITH_P)
+      dma_rows256(a.q + (size_t)t0 * qk_stride + (size_t)j * kD, (uint32_t)qk_stride * 2, nv, sm.r.in.Q,
                   kPieces * w + i, lane);
-      if (WITH_P)
-        dma_rows256(a.q + (size_t)t0 * qk_stride + (size_t)j * kD, (uint32_t)qk_stride * 2, nv, sm.r.in.Q,
-                    kPieces * w + i, lane);
-    }
   }
   if (tid < HP * kC) {
     const int hh = tid / kC, r = tid % kC;
@@ -483,31 +376,6 @@ __global__ __launch_bounds__(4 * HP * kWave, HP == 1 ? 4 : 3) void prep_kernel(P
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if constexpr (FE) {
-    // K and Q rows from the front end: quarter-wave 4 w + g4 takes 4 / HP rows of each. The
-    // first workgroup of the QK head also writes them out for the state pass, so each QK
-    // head's q and k are computed once per chunk.
-    // (K, then Q, each with its own barrier: one set of history rows in registers at a time;
-    // the lane indices pass through an empty asm statement so that the addresses derived
-    // from them are formed where they are used, not kept live across the block)
-    constexpr int R = 4 / HP;
-    int fg4 = g4, fl16 = l16;
-    asm volatile("" : "+v"(fg4), "+v"(fl16));
-    const int r0 = R * (4 * w + fg4);
-    const bool first = t0 == a.cu[n];
-    const size_t row0 = ((size_t)t0 * a.h_qk + j) * kD;
-    const size_t stride = (size_t)a.h_qk * kD;
-    bf16x8 hist[3];
-    fe_history<true>(sm.r.in.K, sm.r.in.halo[0], first, r0, fl16, hist);
-    __syncthreads();
-    fe_rows<true, R>(a, sm.r.in.K, (a.h_qk + j) * kD, false, true, r0, fl16, hist,
-                     gi == 0 ? a.k_out + row0 : nullptr, stride, nv);
-    fe_history<true>(sm.r.in.Q, sm.r.in.halo[1], first, r0, fl16, hist);
-    __syncthreads();
-    fe_rows<true, R>(a, sm.r.in.Q, j * kD, true, false, r0, fl16, hist, gi == 0 ? a.q_out + row0 : nullptr,
-                     stride, nv);
-    __syncthreads();
-  }
 
   // ---- K K^T (lower 10 tiles, for A) and, WITH_P, K Q^T (the 10 tiles with key tile <=
   // query tile, for P^T), in registers: WITH_P, the first half of the waves takes K K^T and
@@ -1192,7 +1060,7 @@ __global__ __launch_bounds__(4 * kWave) void state_ro_kernel(PrefillArgs a) {
 // operand order and roundings, and prep writes none: P^T stays off HBM.
 // ------------------------------------------------------------------------------------------
 
-template <int NW, bool FE>
+template <int NW>
 struct StateBuf {
   bf16 K[kC * kD];
   bf16 Q[kC * kD];
@@ -1202,25 +1070,16 @@ struct StateBuf {
   bf16 pl[kFrags * 512];
   float gl[4 * kC];          // gam, gam_C / gam, G, unused
   bf16 vt[NW][kC * 16];
-  bf16 halo[FE ? 4 * kD : 8];   // with the front end: the raw value rows before the chunk
 };
 
 // This wave's share of the direct loads of one chunk: 1 KB pieces numbered 0 .. 16 K rows,
 // 16 Q rows, 12 T diag(beta) fragments, 12 P^T fragments (not with FORM), the decay factors,
-// two per value tile; wave w issues the pieces p = w (mod NW). With FE the value rows are
-// the head's raw mixed-input rows (converted in place by fe_chunk), and one more piece loads
-// the three raw rows before the chunk.
-template <int NW, bool FORM, bool FE>
-__device__ __forceinline__ void dma_chunk(const PrefillArgs& a, const ChunkSrc& s, StateBuf<NW, FE>& d,
-                                          const DmaStrides& st, int t0, bool first, int h, int w, int lane) {
+// two per value tile; wave w issues the pieces p = w (mod NW).
+template <int NW, bool FORM>
+__device__ __forceinline__ void dma_chunk(const ChunkSrc& s, StateBuf<NW>& d, const DmaStrides& st, int w,
+                                          int lane) {
   constexpr int kP = FORM ? 0 : 2 * kFrags;
-  constexpr int kTotal = 32 + 2 * kFrags + kP + 1 + 2 * NW + (FE ? 1 : 0);
-  const bf16* vb = s.vb;
-  uint32_t vs = st.v;
-  if constexpr (FE) {
-    vb = a.mixed + (size_t)t0 * a.C + (2 * a.h_qk + h) * kD;
-    vs = (uint32_t)a.C * 2;
-  }
+  constexpr int kTotal = 32 + 2 * kFrags + kP + 1 + 2 * NW;
 #pragma unroll
   for (int i = 0; i < (kTotal + NW - 1) / NW; ++i) {
     const int p = w + NW * i;
@@ -1230,39 +1089,17 @@ __device__ __forceinline__ void dma_chunk(const PrefillArgs& a, const ChunkSrc& 
     else if (p < 32 + 2 * kFrags + kP)
       dma_1k(s.ws + kWsPh + (p - 32 - 2 * kFrags) * kFragBytes, d.ph + 512 * (p - 32 - 2 * kFrags), lane);
     else if (p == 32 + 2 * kFrags + kP) dma_1k(s.ws + kWsGam, d.gl, lane);
-    else if (p < 33 + 2 * kFrags + kP + 2 * NW) {
+    else if (p < kTotal) {
       const int q = p - (33 + 2 * kFrags + kP);
-      dma_vtile(vb + 16 * (q >> 1), vs, s.nv, d.vt[q >> 1], q & 1, lane);
-    } else if (p < kTotal) {
-      if constexpr (FE) {
-        if (!first) dma_halo(a, (2 * a.h_qk + h) * kD, t0, d.halo, lane);
-      }
+      dma_vtile(s.vb + 16 * (q >> 1), st.v, s.nv, d.vt[q >> 1], q & 1, lane);
     }
   }
 }
 
-// With FE, the conversion of a chunk's raw value rows (landed in `d`): quarter-wave 4 w + g4
-// takes rows 2 (4 w + g4) and the next one. Two workgroup barriers: the reads of the three
-// rows before each quarter-wave's own all come before any row is overwritten.
-template <int NW>
-__device__ __forceinline__ void fe_chunk(const PrefillArgs& a, StateBuf<NW, true>& d, bool first, int h, int w,
-                                         int g4, int l16) {
-  static_assert(NW == 8, "the front end inside the state pass uses eight waves");
-  // The lane indices pass through an empty asm statement so that the addresses derived from
-  // them are formed here each chunk: hoisted out of the chunk loop, they stay live across
-  // the whole chunk and the state pass runs out of registers.
-  asm volatile("" : "+v"(g4), "+v"(l16));
-  const int r0 = 2 * (4 * w + g4);
-  bf16x8 hist[3];
-  fe_history<false>(d.vt[0], d.halo, first, r0, l16, hist);
-  __syncthreads();
-  fe_rows<false, 2>(a, d.vt[0], (2 * a.h_qk + h) * kD, false, false, r0, l16, hist);
-}
-
 // With FORM, the workgroup's share of P^T for the chunk in `b` (Q, K and G in): wave w takes
 // tiles w, w + NW, ... of the 10 (key tile <= query tile), and the two all-zero halves.
-template <int NW, bool FE>
-__device__ __forceinline__ void form_pt(StateBuf<NW, FE>& b, float scale, int w, int g4, int l16, int lane) {
+template <int NW>
+__device__ __forceinline__ void form_pt(StateBuf<NW>& b, float scale, int w, int g4, int l16, int lane) {
 #pragma unroll
   for (int jt = 0; jt < (10 + NW - 1) / NW; ++jt) {
     const int t = w + NW * jt;
@@ -1284,13 +1121,10 @@ __device__ __forceinline__ void form_pt(StateBuf<NW, FE>& b, float scale, int w,
   }
 }
 
-// FE (with NW = 8 and FORM only): Q, K and the value tiles come from the front end inside
-// the pass, computed for the next chunk at the end of each chunk (fe_chunk).
-template <int NW, bool FORM, bool FE>
+template <int NW, bool FORM>
 __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
-  static_assert(!FE || (NW == 8 && FORM), "the front end runs inside the many-heads shape only");
-  __shared__ StateBuf<NW, FE> buf0;
-  __shared__ StateBuf<NW, FE> buf1;
+  __shared__ StateBuf<NW> buf0;
+  __shared__ StateBuf<NW> buf1;
   constexpr int kBlocks = 8 / NW;      // workgroups per (sequence, V head)
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
@@ -1324,36 +1158,22 @@ __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
   f32x4 S0[4], S1[4];
   load_state(a, n, h, col0, 0, S0, lane);
   load_state(a, n, h, col0, 1, S1, lane);
-  auto step = [&](int ci, StateBuf<NW, FE>& cur, StateBuf<NW, FE>& nxt) {
+  auto step = [&](int ci, StateBuf<NW>& cur, StateBuf<NW>& nxt) {
     __builtin_amdgcn_s_waitcnt(0);   // this wave's share of the chunk's loads has landed ...
     __syncthreads();                 // ... and everyone's; the other buffer is free
-    if (ci + 1 < n_chunks) dma_chunk<NW, FORM, FE>(a, src(ci + 1), nxt, dst, t_seq0 + (ci + 1) * kC, false, h, w, lane);
-    if (FORM) form_pt<NW, FE>(cur, a.scale, w, g4, l16, lane);
+    if (ci + 1 < n_chunks) dma_chunk<NW, FORM>(src(ci + 1), nxt, dst, w, lane);
+    if (FORM) form_pt<NW>(cur, a.scale, w, g4, l16, lane);
     bf16x8 sh[4];
     f32x4 u[4];
     const ChainOps ops{cur.K, cur.th, cur.tl, cur.vt[w], cur.gl};
     chain_chunk(ops, lo, S0, S1, sh, u, lane);
-    const int t0 = t_seq0 + ci * kC;
     if (FORM) __syncthreads();       // every wave's part of P^T is in
+    const int t0 = t_seq0 + ci * kC;
     const ReadOps rops{cur.Q, cur.ph, cur.pl, cur.gl};
     readout_chunk(rops, lo, sh, u, a.scale, out_rsrc(a, t0, min(kC, t_seq1 - t0), h), v_stride * 2,
                   col0 * 2, lane);
-    if constexpr (FE) {   // the next chunk's rows from its raw rows, landed during this chunk
-      if (ci + 1 < n_chunks) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        fe_chunk<NW>(a, nxt, false, h, w, g4, l16);
-      }
-    }
   };
-  if (n_chunks > 0) {
-    dma_chunk<NW, FORM, FE>(a, src(0), buf0, dst, t_seq0, true, h, w, lane);
-    if constexpr (FE) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      fe_chunk<NW>(a, buf0, true, h, w, g4, l16);
-    }
-  }
+  if (n_chunks > 0) dma_chunk<NW, FORM>(src(0), buf0, dst, w, lane);
   for (int ci = 0; ci < n_chunks; ci += 2) {
     step(ci, buf0, buf1);
     if (ci + 1 < n_chunks) step(ci + 1, buf1, buf0);
@@ -1399,16 +1219,13 @@ size_t chunk_prefill_workspace_bytes(int total_tokens, int num_seqs, int h_qk, i
 
 namespace {
 
-// The two launches of a chunked prefill; with FE (many heads only) the front end runs
-// inside them, reading a.mixed.
-template <bool FE>
+// The two launches of a chunked prefill.
 hipError_t launch_prefill(PrefillArgs a, int total_tokens, hipStream_t stream) {
   // With up to 128 (sequence, V head) pairs the state pass reads P^T from the workspace;
   // beyond, one workgroup per head forms it on chip.
   const size_t nc = (size_t)a.n_chunks_max;
   const size_t heads = (size_t)a.num_seqs * a.h_v;
   const bool with_p = heads * 2 <= kStateCus;
-  if (FE && with_p) return hipErrorInvalidValue;
   if (total_tokens > 0) {
     // V heads of one QK head pair up in the workgroups when their number is even
     const size_t pairs = nc * (size_t)a.h_qk;
@@ -1416,11 +1233,11 @@ hipError_t launch_prefill(PrefillArgs a, int total_tokens, hipStream_t stream) {
     const size_t prep_blocks = (pairs + 7) / 8 * 8 * (size_t)(a.group / hp);
     const dim3 grid((unsigned)prep_blocks), block(4 * hp * kWave);
     if (with_p) {
-      if (hp == 2) hipLaunchKernelGGL((prep_kernel<true, false, 2>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((prep_kernel<true, false, 1>), grid, block, 0, stream, a);
+      if (hp == 2) hipLaunchKernelGGL((prep_kernel<true, 2>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((prep_kernel<true, 1>), grid, block, 0, stream, a);
     } else {
-      if (hp == 2) hipLaunchKernelGGL((prep_kernel<false, FE, 2>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((prep_kernel<false, FE, 1>), grid, block, 0, stream, a);
+      if (hp == 2) hipLaunchKernelGGL((prep_kernel<false, 2>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((prep_kernel<false, 1>), grid, block, 0, stream, a);
     }
   }
   // With few heads, eight, four or two workgroups per head spread the heads over many CUs
@@ -1429,14 +1246,14 @@ hipError_t launch_prefill(PrefillArgs a, int total_tokens, hipStream_t stream) {
   // the operand traffic every workgroup repeats, and forms P^T itself.
   const size_t seq_pairs = (size_t)a.num_seqs * a.h_qk;
   const size_t groups = (seq_pairs + 7) / 8 * 8 * (size_t)a.group;
-  if (!FE && heads * 8 <= kStateCus) {
+  if (heads * 8 <= kStateCus) {
     hipLaunchKernelGGL(state_ro_kernel, dim3((unsigned)(groups * 8)), dim3(4 * kWave), 0, stream, a);
-  } else if (!FE && heads * 4 <= kStateCus) {
-    hipLaunchKernelGGL((state_kernel<2, false, false>), dim3((unsigned)(groups * 4)), dim3(2 * kWave), 0, stream, a);
-  } else if (!FE && heads * 2 <= kStateCus) {
-    hipLaunchKernelGGL((state_kernel<4, false, false>), dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
+  } else if (heads * 4 <= kStateCus) {
+    hipLaunchKernelGGL((state_kernel<2, false>), dim3((unsigned)(groups * 4)), dim3(2 * kWave), 0, stream, a);
+  } else if (heads * 2 <= kStateCus) {
+    hipLaunchKernelGGL((state_kernel<4, false>), dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((state_kernel<8, true, FE>), dim3((unsigned)groups), dim3(8 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((state_kernel<8, true>), dim3((unsigned)groups), dim3(8 * kWave), 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -1461,10 +1278,6 @@ PrefillArgs prefill_args(const float* g, const float* beta, const int32_t* cu_se
   return a;
 }
 
-// Whether gdn_chunk_prefill_conv runs the front end inside the prefill (many heads) or as
-// its own pass into the workspace.
-bool conv_fused(int num_seqs, int h_v) { return (size_t)num_seqs * h_v * 2 > kStateCus; }
-
 }  // namespace
 
 hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
@@ -1477,13 +1290,17 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
   a.q = static_cast<const bf16*>(q);
   a.k = static_cast<const bf16*>(k);
   a.v = static_cast<const bf16*>(v);
-  return launch_prefill<false>(a, total_tokens, stream);
+  return launch_prefill(a, total_tokens, stream);
 }
 
+// The front end and the prefill in one call: the front end's q, k and v go to the workspace,
+// after the prefill's own blocks, and the prefill reads them there. (Two forms that ran the
+// front end inside the prefill's loads instead were measured slower: the conversion then
+// lands on the latency-bound prefill kernels at low occupancy, where the standalone pass
+// spreads it over the whole chip.)
 size_t chunk_prefill_conv_workspace_bytes(int total_tokens, int num_seqs, int h_qk, int h_v) {
-  // after the prefill's own blocks: q and k from the front end (fused), or q, k and v
-  const size_t heads = conv_fused(num_seqs, h_v) ? 2 * (size_t)h_qk : 2 * (size_t)h_qk + h_v;
-  return chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v) + (size_t)total_tokens * heads * kD * 2;
+  return chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v) +
+         (size_t)total_tokens * (2 * h_qk + h_v) * kD * 2;
 }
 
 hipError_t launch_chunk_prefill_conv(const void* mixed, const float* conv_weight, int conv_kernel,
@@ -1491,34 +1308,17 @@ hipError_t launch_chunk_prefill_conv(const void* mixed, const float* conv_weight
                                      const int32_t* cu_seqlens, int num_seqs, int total_tokens,
                                      int h_qk, int h_v, float scale, const float* s0, float* s_final,
                                      void* o, void* workspace, hipStream_t stream) {
-  if (!conv_fused(num_seqs, h_v)) {
-    // few heads: the front end as its own pass, q, k, v after the prefill's own workspace
-    uint8_t* qkv = static_cast<uint8_t*>(workspace) +
-                   chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v);
-    bf16* q = reinterpret_cast<bf16*>(qkv);
-    bf16* k = q + (size_t)total_tokens * h_qk * kD;
-    bf16* v = k + (size_t)total_tokens * h_qk * kD;
-    if (total_tokens > 0) {
-      const hipError_t e = launch_conv_prep(mixed, conv_weight, conv_kernel, cu_seqlens, num_seqs, total_tokens,
-                                            h_qk, h_v, q_scale, q, k, v, stream);
-      if (e != hipSuccess) return e;
-    }
-    return launch_chunk_prefill(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, h_qk, h_v, scale, s0,
-                                s_final, o, workspace, stream);
+  uint8_t* qkv = static_cast<uint8_t*>(workspace) + chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v);
+  bf16* q = reinterpret_cast<bf16*>(qkv);
+  bf16* k = q + (size_t)total_tokens * h_qk * kD;
+  bf16* v = k + (size_t)total_tokens * h_qk * kD;
+  if (total_tokens > 0) {
+    const hipError_t e = launch_conv_prep(mixed, conv_weight, conv_kernel, cu_seqlens, num_seqs, total_tokens, h_qk,
+                                          h_v, q_scale, q, k, v, stream);
+    if (e != hipSuccess) return e;
   }
-  PrefillArgs a = prefill_args(g, beta, cu_seqlens, num_seqs, total_tokens, h_qk, h_v, scale, s0,
-                               s_final, o, workspace);
-  a.mixed = static_cast<const bf16*>(mixed);
-  a.conv_w = conv_weight;
-  a.conv_k = conv_kernel;
-  a.C = (2 * h_qk + h_v) * kD;
-  a.q_scale = q_scale;
-  a.q_out = reinterpret_cast<bf16*>(static_cast<uint8_t*>(workspace) +
-                                    chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v));
-  a.k_out = a.q_out + (size_t)total_tokens * h_qk * kD;
-  a.q = a.q_out;
-  a.k = a.k_out;
-  return launch_prefill<true>(a, total_tokens, stream);
+  return launch_chunk_prefill(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, h_qk, h_v, scale, s0, s_final,
+                              o, workspace, stream);
 }
 
 }  // namespace gdn

@@ -61,9 +61,8 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
                                 hipStream_t stream);
 
 // The chunked prefill with the front end in front of it (chunk_prefill.hip): from the mixed
-// q | k | v input and the conv taps. With many heads (num_seqs * h_v > 128) the front end
-// runs inside the prefill's loads; otherwise as its own pass into the workspace, whose size
-// the query includes.
+// q | k | v input and the conv taps. The front end runs as its own pass into the workspace
+// (whose size the query includes), then the prefill.
 size_t chunk_prefill_conv_workspace_bytes(int total_tokens, int num_seqs, int h_qk, int h_v);
 hipError_t launch_chunk_prefill_conv(const void* mixed, const float* conv_weight, int conv_kernel,
                                      float q_scale, const float* g, const float* beta,

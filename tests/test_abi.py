@@ -179,8 +179,8 @@ def test_prefill_conv_validation():
     assert call(n=0, T=0) == L.GDN_OK
     q = lambda T, n: lib.gdn_chunk_prefill_conv_workspace_bytes(T, n, 16, 32, 128, 128)
     p = lambda T, n: lib.gdn_chunk_prefill_workspace_bytes(T, n, 16, 32, 128, 128)
-    assert q(276989, 64) == p(276989, 64) + 276989 * 4096 * 2   # 2048 pairs: q, k staged
-    assert q(4096, 1) == p(4096, 1) + 4096 * 8192 * 2            # 32 pairs: its own pass
+    assert q(276989, 64) == p(276989, 64) + 276989 * 8192 * 2   # q, k and v after the blocks
+    assert q(4096, 1) == p(4096, 1) + 4096 * 8192 * 2
     assert q(-1, 1) == 0
 
 
