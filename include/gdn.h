@@ -73,7 +73,10 @@ const char* gdn_status_string(gdn_status s);
  * every 64-token chunk, 25600 bytes per V head (decay factors, and T diag(beta) =
  * (I + A)^-1 diag(beta) and the masked and decayed Q K^T each as a hi + lo bf16 pair),
  * sized for ceil(total_tokens / 64) + num_seqs chunks so no host read of cu_seqlens is
- * needed.
+ * needed. With at most 32 (sequence, V head) pairs the call instead runs in segments of 64
+ * chunks per sequence whenever that needs less: num_seqs * (64 * h_v * 25600 + h_v * d_v *
+ * d_k * 4) bytes (one segment's blocks and the states between segments), whatever the
+ * lengths -- 54.5 MB for one sequence at 32 V heads.
  * Returns 0 for invalid sizes. The contents are scratch: nothing persists between calls,
  * and calls sharing a workspace must not overlap.
  */
@@ -149,8 +152,10 @@ gdn_status gdn_chunk_prefill_conv(const void* mixed_qkv, const float* conv_weigh
  * routine); the caller still owns q, k, v, g, beta, cu_seqlens, the states and o.
  *
  * Limit: sizes for which gdn_chunk_prefill_workspace_bytes(...) exceeds
- * GDN_NOALLOC_SCRATCH_BYTES return GDN_ERR_WORKSPACE with nothing launched (with 32 V heads:
- * ceil(total_tokens / 64) + num_seqs <= 81, e.g. one sequence of up to 5,120 tokens);
+ * GDN_NOALLOC_SCRATCH_BYTES return GDN_ERR_WORKSPACE with nothing launched. One sequence at
+ * 32 V heads (or any batch of up to 32 (sequence, V head) pairs needing at most the
+ * scratch in segments) has no length limit; larger batches at 32 V heads need
+ * ceil(total_tokens / 64) + num_seqs <= 81, e.g. two sequences of up to 2,560 tokens.
  * GDN_F32 needs no workspace and has no limit.
  *
  * Sharing: every call on one GPU uses that GPU's one array, which keeps whatever the last

@@ -124,6 +124,12 @@ struct PrefillArgs {
   uint8_t* ws;              // per (chunk, V head) blocks
   int num_seqs, h_qk, h_v, group, n_chunks_max;
   float scale;
+  // a segmented call (seg_len > 0, fewest-heads shape only): the launches cover chunks
+  // seg_lo .. seg_lo + seg_len - 1 of every sequence, chunk seg_lo + i of sequence n in
+  // workspace slot n seg_len + i; the state between segments waits in `carry`
+  // ([num_seqs][h_v][d_v][d_k] fp32, in the workspace)
+  int seg_lo, seg_len;
+  float* carry;
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -343,11 +349,17 @@ __global__ __launch_bounds__(4 * HP * kWave, HP == 1 ? 4 : 3) void prep_kernel(P
   const int grp = bid / (8 * per), rem = bid % (8 * per);
   const int p = grp * 8 + rem % 8;            // (chunk, QK head) pair
   const int gi = (rem / 8) * HP;              // first V head of the workgroup within the QK group
-  const int c = p / a.h_qk, j = p % a.h_qk;
+  const int c = p / a.h_qk, j = p % a.h_qk;    // c: the workspace slot
   if (c >= a.n_chunks_max) return;
   int n, local;
-  locate_chunk(a.cu, a.num_seqs, c, lane, n, local);
-  if (n < 0) return;
+  if (a.seg_len) {   // slot n seg_len + i: chunk seg_lo + i of sequence n
+    n = c / a.seg_len;
+    local = a.seg_lo + c % a.seg_len;
+    if (n >= a.num_seqs || local >= seq_chunks(a.cu, n)) return;
+  } else {
+    locate_chunk(a.cu, a.num_seqs, c, lane, n, local);
+    if (n < 0) return;
+  }
   const int h0 = j * a.group + gi;            // V heads h0 .. h0 + HP - 1
   const int t0 = a.cu[n] + local * kC;
   const int nv = min(kC, a.cu[n + 1] - t0);
@@ -820,22 +832,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const PrefillArgs& a,
 
 // Key half kh of the lane's value row: S[mt] = S[row0 + l16][32 (mt' / 2) + 8 g4 + 4 (mt' % 2) + i]
 // for state tile mt' = 4 kh + mt.
-__device__ __forceinline__ void load_state(const PrefillArgs& a, int n, int h, int row0, int kh,
+__device__ __forceinline__ void load_state(const PrefillArgs& a, const float* src, int n, int h, int row0, int kh,
                                            f32x4 (&S)[4], int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
   const size_t off = (((size_t)n * a.h_v + h) * kD + row0 + l16) * kD + 64 * kh + 8 * g4;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
-    S[mt] = a.s0 ? *reinterpret_cast<const f32x4*>(a.s0 + off + 32 * (mt >> 1) + 4 * (mt & 1))
-                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    S[mt] = src ? *reinterpret_cast<const f32x4*>(src + off + 32 * (mt >> 1) + 4 * (mt & 1))
+                : f32x4{0.f, 0.f, 0.f, 0.f};
 }
-__device__ __forceinline__ void store_state(const PrefillArgs& a, int n, int h, int row0, int kh,
+__device__ __forceinline__ void load_state(const PrefillArgs& a, int n, int h, int row0, int kh, f32x4 (&S)[4],
+                                           int lane) {
+  load_state(a, a.s0, n, h, row0, kh, S, lane);
+}
+__device__ __forceinline__ void store_state(const PrefillArgs& a, float* dst, int n, int h, int row0, int kh,
                                             const f32x4 (&S)[4], int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
   const size_t off = (((size_t)n * a.h_v + h) * kD + row0 + l16) * kD + 64 * kh + 8 * g4;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
-    *reinterpret_cast<f32x4*>(a.s_final + off + 32 * (mt >> 1) + 4 * (mt & 1)) = S[mt];
+    *reinterpret_cast<f32x4*>(dst + off + 32 * (mt >> 1) + 4 * (mt & 1)) = S[mt];
+}
+__device__ __forceinline__ void store_state(const PrefillArgs& a, int n, int h, int row0, int kh,
+                                            const f32x4 (&S)[4], int lane) {
+  store_state(a, a.s_final, n, h, row0, kh, S, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -926,9 +946,9 @@ __device__ __forceinline__ void barrier_lds_only() {
 template <int KH>
 __device__ __forceinline__ void ro_chain_wave(const PrefillArgs& a, const RoChainBuf (&cb)[2], Exchange (&xo)[2],
                                               XHalves& xx, const LaneOffsets& lo, int n, int h, int col0,
-                                              int n_chunks, int lane) {
+                                              int n_chunks, const float* s_in, float* s_out, int lane) {
   f32x4 S[4];
-  load_state(a, n, h, col0, KH, S, lane);
+  load_state(a, s_in, n, h, col0, KH, S, lane);
   if (lane == 0) xx.ready[KH] = 0;
   for (int ci = 0; ci < n_chunks; ++ci) {
     const RoChainBuf& c = cb[ci & 1];
@@ -968,7 +988,7 @@ __device__ __forceinline__ void ro_chain_wave(const PrefillArgs& a, const RoChai
     chain_update(akt, S, Bh, Bl, gC);
   }
   __syncthreads();   // the last chunk's hand-over is visible to the read-out wave
-  if (a.s_final) store_state(a, n, h, col0, KH, S, lane);
+  if (s_out) store_state(a, s_out, n, h, col0, KH, S, lane);
 }
 
 __global__ __launch_bounds__(4 * kWave) void state_ro_kernel(PrefillArgs a) {
@@ -993,13 +1013,21 @@ __global__ __launch_bounds__(4 * kWave) void state_ro_kernel(PrefillArgs a) {
   const int h = j * a.group + sub / 8;
   const int col0 = (sub % 8) * 16;            // the workgroup's value rows
   const int t_seq0 = a.cu[n], t_seq1 = a.cu[n + 1];
-  const int n_chunks = (t_seq1 - t_seq0 + kC - 1) / kC;
-  const int c_begin = first_chunk(a.cu, n, lane);
+  const int seq_chunks_n = (t_seq1 - t_seq0 + kC - 1) / kC;
+  // this launch's chunks of the sequence: all of them, or those of the segment
+  const int seg_lo = a.seg_len ? a.seg_lo : 0;
+  const int n_chunks = a.seg_len ? max(0, min(a.seg_len, seq_chunks_n - seg_lo)) : seq_chunks_n;
+  if (seg_lo > 0 && n_chunks == 0) return;   // the sequence ended in an earlier segment
+  const int c_begin = a.seg_len ? n * a.seg_len : first_chunk(a.cu, n, lane);
+  // state in and out: the caller's, or the carry between segments
+  const float* s_in = seg_lo == 0 ? a.s0 : a.carry;
+  float* s_out = seg_lo + n_chunks == seq_chunks_n ? a.s_final : a.carry;
+  const int t_lo = t_seq0 + seg_lo * kC;
   const int qk_stride = a.h_qk * kD;
   const int v_stride = a.h_v * kD;
   LaneOffsets lo;
   lane_offsets(lo, g4, l16);
-  auto src = [&](int ci) { return chunk_src(a, c_begin + ci, t_seq0 + ci * kC, t_seq1, h, j, col0); };
+  auto src = [&](int ci) { return chunk_src(a, c_begin + ci, t_lo + ci * kC, t_seq1, h, j, col0); };
 
   DmaStrides dst;
   dst.qk = (uint32_t)qk_stride * 2;
@@ -1017,7 +1045,7 @@ __global__ __launch_bounds__(4 * kWave) void state_ro_kernel(PrefillArgs a) {
   if (w == 3) {   // the read-out wave: chunk ci's read-out after the barrier of chunk ci + 1
     // chunk ci's read-out from buffer ci % 2, which then takes chunk ci + 2's operands
     auto readout = [&](int ci) {
-      const int t0 = t_seq0 + ci * kC;
+      const int t0 = t_lo + ci * kC;
       RoReadBuf& r = rb[ci & 1];
       const Exchange& x = xo[ci & 1];
       __builtin_amdgcn_s_waitcnt(0);   // its Q, P^T and decay factors have landed
@@ -1048,8 +1076,8 @@ __global__ __launch_bounds__(4 * kWave) void state_ro_kernel(PrefillArgs a) {
 
   // the chain waves: wave kh holds key half kh of the state (a constant in each branch, so
   // every register array is indexed statically)
-  if (w == 0) ro_chain_wave<0>(a, cb, xo, xx, lo, n, h, col0, n_chunks, lane);
-  else ro_chain_wave<1>(a, cb, xo, xx, lo, n, h, col0, n_chunks, lane);
+  if (w == 0) ro_chain_wave<0>(a, cb, xo, xx, lo, n, h, col0, n_chunks, s_in, s_out, lane);
+  else ro_chain_wave<1>(a, cb, xo, xx, lo, n, h, col0, n_chunks, s_in, s_out, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1212,8 +1240,28 @@ hipError_t noalloc_scratch(void** ptr) {
   return hipSuccess;
 }
 
+namespace {
+
+// The fewest-heads shape (up to 32 (sequence, V head) pairs) can run in segments of
+// kSegChunks chunks per sequence, a prep launch and a state-pass launch each, so that its
+// workspace holds one segment's blocks and the states between segments, whatever the
+// sequence lengths. It does when that is smaller than the whole call's blocks.
+constexpr int kSegChunks = 64;
+
+size_t segmented_workspace_bytes(int num_seqs, int h_v) {
+  return ((size_t)num_seqs * kSegChunks * h_v) * kWsHead + (size_t)num_seqs * h_v * kD * kD * 4;
+}
+
+bool prefill_segmented(int total_tokens, int num_seqs, int h_v) {
+  const size_t whole = max_chunks(total_tokens, num_seqs) * (size_t)h_v * kWsHead;
+  return (size_t)num_seqs * h_v * 8 <= kStateCus && segmented_workspace_bytes(num_seqs, h_v) < whole;
+}
+
+}  // namespace
+
 size_t chunk_prefill_workspace_bytes(int total_tokens, int num_seqs, int h_qk, int h_v) {
   (void)h_qk;
+  if (prefill_segmented(total_tokens, num_seqs, h_v)) return segmented_workspace_bytes(num_seqs, h_v);
   return max_chunks(total_tokens, num_seqs) * (size_t)h_v * kWsHead;
 }
 
@@ -1290,7 +1338,19 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, con
   a.q = static_cast<const bf16*>(q);
   a.k = static_cast<const bf16*>(k);
   a.v = static_cast<const bf16*>(v);
-  return launch_prefill(a, total_tokens, stream);
+  if (!prefill_segmented(total_tokens, num_seqs, h_v)) return launch_prefill(a, total_tokens, stream);
+  // segments of kSegChunks chunks of every sequence; as many as the longest possible
+  // sequence (all the tokens in one) needs (a segment past a sequence's end does nothing)
+  a.seg_len = kSegChunks;
+  a.n_chunks_max = num_seqs * kSegChunks;
+  a.carry = reinterpret_cast<float*>(a.ws + (size_t)num_seqs * kSegChunks * h_v * kWsHead);
+  const int n_seg = max(1, ((total_tokens + kC - 1) / kC + kSegChunks - 1) / kSegChunks);
+  for (int s = 0; s < n_seg; ++s) {
+    a.seg_lo = s * kSegChunks;
+    const hipError_t e = launch_prefill(a, total_tokens, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // The front end and the prefill in one call: the front end's q, k and v go to the workspace,

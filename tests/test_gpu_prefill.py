@@ -202,6 +202,38 @@ def test_config2_all_heads():
     _compare(x, o, fin, label="config2 all 32 heads")
 
 
+def test_prefill_segmented_equals_other_shape():
+    """With up to 32 (sequence, V head) pairs a call whose workspace would exceed one segment's
+    runs in segments of 64 chunks per sequence (a prep and a state-pass launch each, the state
+    between them in the workspace). One sequence of 9,000 tokens at 32 V heads (141 chunks,
+    three segments) equals, bit for bit, the same sequence run inside a batch of two (64 pairs:
+    another state-pass shape, no segments), and the oracle on every head."""
+    xb = workloads.make_prefill([9000, 70], h_qk=16, h_v=32, with_initial_state=True, seed=41)
+    ob, fb = _run(xb)
+    x = _sub_batch(xb, 0, 1)
+    o, fin = _run(x)
+    np.testing.assert_array_equal(o, ob[:9000])
+    np.testing.assert_array_equal(fin[0], fb[0])
+    _compare(x, o, fin, label="segmented T=9000")
+
+
+def test_prefill_segmented_varlen():
+    """Segments over several sequences (4 QK / 8 V heads: three sequences are 24 pairs) of
+    4200, 0 and 12000 tokens (66, 0 and 188 chunks): the first ends in the second segment,
+    the empty one returns its initial state, the third runs three segments and the fourth
+    has no work. Against the oracle; the state written over the initial one in place and
+    a call without a final state give the same outputs."""
+    x = workloads.make_prefill([4200, 0, 12000], h_qk=4, h_v=8, with_initial_state=True, seed=42)
+    o, fin = _run(x)
+    _compare(x, o, fin, label="segmented varlen")
+    np.testing.assert_array_equal(fin[1], x.initial_state[1].astype(np.float64))
+    o2, fin2 = _run(x, alias=True)
+    np.testing.assert_array_equal(o2, o)
+    np.testing.assert_array_equal(fin2, fin)
+    o3, _ = _run(x, with_final=False)
+    np.testing.assert_array_equal(o3, o)
+
+
 def test_prefill_on_side_stream_equals_current_stream():
     """A call launched on a stream other than torch's current one, with the binding
     allocating o and the workspace: the allocations belong to that stream, so work queued

@@ -3,8 +3,8 @@ against gdn_chunk_prefill, through the C ABI (GPU).
 
 Two calls in a row on the scratch -- the second smaller, so it runs over what the first left
 there -- each equal bit for bit to gdn_chunk_prefill with a caller workspace (the same
-kernels), and the first within the parity bars of the fp64 oracle. A size beyond the scratch
-is rejected with nothing written.
+kernels), and the first within the parity bars of the fp64 oracle; a long sequence, which
+runs in segments; a size beyond the scratch is rejected with nothing written.
 """
 
 import numpy as np
@@ -39,7 +39,7 @@ def _both(x):
 
 
 def test_noalloc_equals_prefill_two_calls():
-    # first call: one sequence of 5,000 tokens, 32 V heads (near the scratch limit)
+    # first call: one sequence of 5,000 tokens, 32 V heads (two segments)
     x1 = workloads.make_prefill([5000], with_initial_state=True, seed=901)
     (o_ref, f_ref), (o_na, f_na) = _both(x1)
     np.testing.assert_array_equal(o_na, o_ref)
@@ -55,12 +55,23 @@ def test_noalloc_equals_prefill_two_calls():
     np.testing.assert_array_equal(f_na2, f_ref2)
 
 
+def test_noalloc_long_sequence_in_segments():
+    """One sequence of 32,768 tokens at 32 V heads runs in segments whose workspace fits the
+    scratch: equal bit for bit to gdn_chunk_prefill."""
+    x = workloads.make_prefill([32768], with_initial_state=True, seed=904)
+    (o_ref, f_ref), (o_na, f_na) = _both(x)
+    np.testing.assert_array_equal(o_na, o_ref)
+    np.testing.assert_array_equal(f_na, f_ref)
+
+
 def test_noalloc_rejects_sizes_beyond_the_scratch():
+    """Two sequences at 32 V heads (64 pairs: no segments) of 2,600 tokens each need
+    84 blocks of 32 x 25,600 bytes, more than the 64 MiB scratch."""
     import torch
     import linear_attention_recurrence_amd as gdn
-    x = workloads.make_prefill([5121], h_qk=16, h_v=32, seed=903)
+    x = workloads.make_prefill([2600, 2600], h_qk=16, h_v=32, seed=903)
     d = prefill_to_dev(x)
-    o = torch.full((5121, 32, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    o = torch.full((5200, 32, 128), 3.0, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(gdn.GdnError) as e:
         gdn.gdn_chunk_prefill_noalloc(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"],
                                       x.scale, o)
