@@ -103,10 +103,12 @@ def counter(name, field, sources):
 # ---------------------------------------------------------------------------------------
 
 def prefill_flops(tokens: int, h_v: int = H_V) -> float:
-    """Matrix-product FLOPs of the chunked form per token and V head: four C x C x d
-    products (K K^T, Q K^T, T diag(beta) R, P U) = 8 C d, and three C x d x d products
-    (K S^T, Q S^T, U^T K) = 6 d^2."""
-    return float(tokens) * h_v * (8 * C * D + 6 * D * D)
+    """Matrix-product FLOPs of the chunked form per token and V head, as derived from the
+    update: five C x C x d products (K K^T, Q K^T, T diag(beta gam) K, T diag(beta) V, P U)
+    = 10 C d, and three C x d x d products (W S^T, Q S^T, U^T K) = 6 d^2: 180,224 at C = 64,
+    d = 128. (The kernels apply T to the residual V - diag(gam) K S^T instead, one C x C x d
+    product fewer, 8 C d + 6 d^2; the figure here is the method's, not the kernels'.)"""
+    return float(tokens) * h_v * (10 * C * D + 6 * D * D)
 
 
 def prefill_bytes(tokens: int, num_seqs: int, with_s0: bool, h_qk=H_QK, h_v=H_V) -> float:
