@@ -140,8 +140,12 @@ __device__ __forceinline__ bf16x8 lds8(const bf16* p) { return *reinterpret_cast
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// Transposing LDS read (ds_read_b64_tr_b16). The address-space cast keeps the pointer's
+// origin (a __shared__ array) visible to the compiler: from a bare integer address it would
+// assume the read may touch bytes that a direct global -> LDS load in flight is writing,
+// and make the read wait for every such load.
 __device__ __forceinline__ bf16x4 lds_tr4(const bf16* p) {
-  const bf16x4_gcc r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(uint32_t)(uintptr_t)p);
+  const bf16x4_gcc r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)p);
   return __builtin_bit_cast(bf16x4, r);
 }
 
@@ -705,14 +709,17 @@ __device__ __forceinline__ void chain_u(const UOps& o, const f32x4 (&X0)[4], con
 __device__ __forceinline__ void chain_update(const bf16x8 (&akt)[4][2], f32x4 (&S)[4], const bf16x8 (&Bh)[2],
                                              const bf16x8 (&Bl)[2], float gC) {
 #pragma clang fp contract(off)
+  // each tile: gam_C S, then the four products in this order; the tiles' chains interleaved
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    f32x4 s = S[m] * gC;
-    s = mfma16x16x32(akt[m][0], Bh[0], s);
-    s = mfma16x16x32(akt[m][0], Bl[0], s);
-    s = mfma16x16x32(akt[m][1], Bh[1], s);
-    S[m] = mfma16x16x32(akt[m][1], Bl[1], s);
-  }
+  for (int m = 0; m < 4; ++m) S[m] = S[m] * gC;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) S[m] = mfma16x16x32(akt[m][0], Bh[0], S[m]);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) S[m] = mfma16x16x32(akt[m][0], Bl[0], S[m]);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) S[m] = mfma16x16x32(akt[m][1], Bh[1], S[m]);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) S[m] = mfma16x16x32(akt[m][1], Bl[1], S[m]);
 }
 
 // The whole chunk of the chain in one wave: both key halves (S0 = keys 0..63, S1 = 64..127),
@@ -1195,7 +1202,7 @@ __global__ __launch_bounds__(NW * kWave) void state_kernel(PrefillArgs a) {
     f32x4 u[4];
     const ChainOps ops{cur.K, cur.th, cur.tl, cur.vt[w], cur.gl};
     chain_chunk(ops, lo, S0, S1, sh, u, lane);
-    if (FORM) __syncthreads();       // every wave's part of P^T is in
+    if (FORM) barrier_lds_only();    // every wave's part of P^T is in (the next chunk's loads may still fly)
     const int t0 = t_seq0 + ci * kC;
     const ReadOps rops{cur.Q, cur.ph, cur.pl, cur.gl};
     readout_chunk(rops, lo, sh, u, a.scale, out_rsrc(a, t0, min(kC, t_seq1 - t0), h), v_stride * 2,
