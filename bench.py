@@ -64,11 +64,11 @@ CSRC = os.path.join(ROOT, "linear_attention_recurrence_amd", "csrc")
 # `sources` fingerprints the kernel sources the figures were taken on: once they change,
 # the figures no longer describe the kernels and are reported as null.
 COUNTERS = {
-    "prefill_t32768": {"bytes": 1990589353, "mfma_busy": 0.1417, "sources": "e771e3cf933c17be"},
-    "prefill_t4096": {"bytes": 250218012, "mfma_busy": 0.1419, "sources": "e771e3cf933c17be"},
-    "prefill_packed64": {"bytes": None, "mfma_busy": None, "sources": None},
-    "prefill_conv_packed64": {"bytes": None, "sources": None},
-    "decode": {"bytes": 1083359601, "sources": "1cbcbd1979d4176c"},
+    "prefill_t32768": {"bytes": 2018450644, "mfma_busy": 0.1423, "sources": "1f913db54679a9dc"},
+    "prefill_t4096": {"bytes": 250252792, "mfma_busy": 0.1433, "sources": "1f913db54679a9dc"},
+    "prefill_packed64": {"bytes": 12458540374, "mfma_busy": 0.2522, "sources": "1f913db54679a9dc"},
+    "prefill_conv_packed64": {"bytes": 21649815087, "sources": "488c5df19ffeab60"},
+    "decode": {"bytes": 1083357157, "sources": "1cbcbd1979d4176c"},
 }
 
 
@@ -86,6 +86,7 @@ def _sources_sha(names):
 
 
 PREFILL_SOURCES = ("chunk_prefill.hip", "gdn_device.h")
+PREFILL_CONV_SOURCES = ("chunk_prefill.hip", "conv_prep.hip", "conv_device.h", "gdn_device.h")
 DECODE_SOURCES = ("recurrent.hip", "gdn_device.h")
 
 
@@ -665,7 +666,7 @@ def main():
                          "roofline": {"bound": "hbm", "achieved": fb / (fused_ms / 1e3) / 1e9,
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": fb / (fused_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                                      "traffic": counter("prefill_conv_packed64", "bytes", PREFILL_SOURCES),
+                                      "traffic": counter("prefill_conv_packed64", "bytes", PREFILL_CONV_SOURCES),
                                       "kernel": "gdn_chunk_prefill_conv call: conv_prep_kernel + "
                                                 "prep_kernel<false, 2> + state_kernel<8, true>",
                                       "call_ms": fused_ms, "algorithmic_bytes": fb}}}
