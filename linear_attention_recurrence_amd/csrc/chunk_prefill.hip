@@ -498,9 +498,12 @@ __global__ __launch_bounds__(4 * HP * kWave, HP == 1 ? 4 : 3) void prep_kernel(P
   // keeps the strict lower triangle and T[r][c] (r >= c) goes to the mirror position [c][r].
   const int hh = w >> 2, wl = w & 3;
   float (&M)[kC][kF32Pad] = sm.r.M[hh];
-  // diagonal 16 x 16 blocks: wave wl inverts block wl, lane = column, one row of A at a time
-  if (lane < 16) {
-    const int b0 = 16 * wl, col = lane;
+  // diagonal 16 x 16 blocks: the head's first wave inverts all four, 16 lanes per block
+  // (block lane / 16, lane = column), one row of A at a time; the other waves wait at the
+  // barrier (their lanes would run the same dependent chain, so the SIMDs issue a quarter
+  // of the instructions this way)
+  if (wl == 0) {
+    const int b0 = 16 * (lane >> 4), col = lane & 15;
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {   // row r of the block: x_r = e_r - sum_{m < r} A_rm x_m
