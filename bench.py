@@ -556,6 +556,10 @@ def main():
                        "global_batch": 1, "seq_len": T, "parallelism": "none (1 GPU)"},
             "roofline": hbm,
             "roofline_mfma": mfma,
+            # context only: the whole-model claim the pages make, which names no hardware and
+            # measures a different thing than this mixer's tokens/s
+            "pages_claim": "whole Qwen3-Next model: about 10x the inference throughput of "
+                           "Qwen3-32B at contexts beyond 32K tokens; no hardware named",
         })
     if "prefill" in work or "prefill_t4096" in work:
         psteps = max(20, args.steps)
