@@ -1099,8 +1099,8 @@ __global__ __launch_bounds__(4 * kWave) void state_ro_kernel(PrefillArgs a) {
 // ------------------------------------------------------------------------------------------
 // state_kernel<NW, FORM>: NW waves of one 16-row value tile each per workgroup, each wave
 // running both the chain and the read-out of its rows, so 8 / NW workgroups per (sequence,
-// V head), placed on one XCD. With FORM (one workgroup per head, once the heads fill the
-// chip) the workgroup forms P^T itself from the chunk's Q, K and G, with prep's products,
+// V head), placed on one XCD. With FORM (one workgroup per head, once the heads outnumber
+// the CUs) the workgroup forms P^T itself from the chunk's Q, K and G, with prep's products,
 // operand order and roundings, and prep writes none: P^T stays off HBM.
 // ------------------------------------------------------------------------------------------
 
@@ -1285,11 +1285,12 @@ namespace {
 
 // The two launches of a chunked prefill.
 hipError_t launch_prefill(PrefillArgs a, int total_tokens, hipStream_t stream) {
-  // With up to 128 (sequence, V head) pairs the state pass reads P^T from the workspace;
-  // beyond, one workgroup per head forms it on chip.
+  // With up to one (sequence, V head) pair per CU the state pass reads P^T from the
+  // workspace; beyond, one workgroup per head forms it on chip (no P^T traffic; with every
+  // CU busy that costs less than reading it).
   const size_t nc = (size_t)a.n_chunks_max;
   const size_t heads = (size_t)a.num_seqs * a.h_v;
-  const bool with_p = heads * 2 <= kStateCus;
+  const bool with_p = heads <= kStateCus;
   if (total_tokens > 0) {
     // V heads of one QK head pair up in the workgroups when their number is even
     const size_t pairs = nc * (size_t)a.h_qk;
@@ -1305,9 +1306,9 @@ hipError_t launch_prefill(PrefillArgs a, int total_tokens, hipStream_t stream) {
     }
   }
   // With few heads, eight, four or two workgroups per head spread the heads over many CUs
-  // (eight with the chain, the loads and the read-out on waves of their own); once the heads
-  // fill the chip, one 8-wave workgroup per head (two waves per SIMD to hide latency) avoids
-  // the operand traffic every workgroup repeats, and forms P^T itself.
+  // (eight with the chain, the loads and the read-out on waves of their own); beyond, one
+  // 8-wave workgroup per head (two waves per SIMD to hide latency) avoids the operand traffic
+  // every workgroup repeats, and once the heads outnumber the CUs it forms P^T itself.
   const size_t seq_pairs = (size_t)a.num_seqs * a.h_qk;
   const size_t groups = (seq_pairs + 7) / 8 * 8 * (size_t)a.group;
   if (heads * 8 <= kStateCus) {
@@ -1316,6 +1317,8 @@ hipError_t launch_prefill(PrefillArgs a, int total_tokens, hipStream_t stream) {
     hipLaunchKernelGGL((state_kernel<2, false>), dim3((unsigned)(groups * 4)), dim3(2 * kWave), 0, stream, a);
   } else if (heads * 2 <= kStateCus) {
     hipLaunchKernelGGL((state_kernel<4, false>), dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
+  } else if (heads <= kStateCus) {
+    hipLaunchKernelGGL((state_kernel<8, false>), dim3((unsigned)groups), dim3(8 * kWave), 0, stream, a);
   } else {
     hipLaunchKernelGGL((state_kernel<8, true>), dim3((unsigned)groups), dim3(8 * kWave), 0, stream, a);
   }

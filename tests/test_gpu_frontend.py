@@ -255,9 +255,10 @@ def _two_calls_and_fused(fe):
 
 @pytest.mark.parametrize("K", [1, 2, 3, 4])
 def test_prefill_conv_many_heads_equals_two_calls(K):
-    """More than 128 (sequence, V head) pairs (the one-workgroup-per-head state pass): outputs
-    and states equal gdn_conv_prep then gdn_chunk_prefill bit for bit (sequences shorter than
-    the kernel, empty ones, whole chunks and ragged tails)."""
+    """More than 128 (sequence, V head) pairs (the one-workgroup-per-head state pass; here 256,
+    reading P^T from the workspace): outputs and states equal gdn_conv_prep then
+    gdn_chunk_prefill bit for bit (sequences shorter than the kernel, empty ones, whole chunks
+    and ragged tails)."""
     fe = workloads.make_frontend([0, 1, 3, 64, 65, 200, 130, 2], conv_kernel=K, seed=700 + K)
     (o1, f1), (o2, f2), _ = _two_calls_and_fused(fe)
     assert torch_equal(o1, o2) and torch_equal(f1, f2)

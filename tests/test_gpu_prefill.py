@@ -88,15 +88,16 @@ def _sub_batch(x, first, last):
 def test_prefill_many_sequences_full_heads():
     """The state pass picks its workgroup shape from the number of (sequence, V head) pairs:
     12 sequences x 32 V heads take one workgroup of eight one-tile waves per head, which
-    forms P^T on chip; 4 sequences take two workgroups per head, 2 sequences four, and 1
-    sequence eight with the chain on two waves and a read-out wave, all reading P^T from the
-    workspace. The per-row arithmetic, and P^T itself, are the same in all of them, so
-    results must agree bit for bit."""
+    forms P^T on chip; 6 sequences take the same workgroup reading P^T from the workspace;
+    4 sequences take two workgroups per head, 2 sequences four, and 1 sequence eight with
+    the chain on two waves and a read-out wave, all reading P^T from the workspace. The
+    per-row arithmetic, and P^T itself, are the same in all of them, so results must agree
+    bit for bit."""
     lens = [0, 1, 64, 65, 200, 17, 128, 0, 311, 63, 90, 5]
     x = workloads.make_prefill(lens, h_qk=16, h_v=32, with_initial_state=True, seed=13)
     o, fin = _run(x)
     _compare(x, o, fin, label="12 seqs, 32 V heads")
-    for first, last in ((4, 8), (8, 10), (4, 5), (8, 9)):
+    for first, last in ((2, 8), (4, 8), (8, 10), (4, 5), (8, 9)):
         ob, fb = _run(_sub_batch(x, first, last))
         t0, t1 = int(x.cu_seqlens[first]), int(x.cu_seqlens[last])
         np.testing.assert_array_equal(ob, o[t0:t1])
