@@ -1258,10 +1258,11 @@ hipError_t noalloc_scratch(void** ptr) {
 
 namespace {
 
-// The fewest-heads shape (up to 32 (sequence, V head) pairs) can run in segments of
-// kSegChunks chunks per sequence, a prep launch and a state-pass launch each, so that its
-// workspace holds one segment's blocks and the states between segments, whatever the
-// sequence lengths. It does when that is smaller than the whole call's blocks.
+// With up to 32 (sequence, V head) pairs (one round of its workgroups), the fewest-heads
+// shape can run in segments of kSegChunks chunks per sequence, a prep launch and a
+// state-pass launch each, so that its workspace holds one segment's blocks and the states
+// between segments, whatever the sequence lengths. It does when that is smaller than the
+// whole call's blocks.
 constexpr int kSegChunks = 64;
 
 size_t segmented_workspace_bytes(int num_seqs, int h_v) {
@@ -1305,16 +1306,17 @@ hipError_t launch_prefill(PrefillArgs a, int total_tokens, hipStream_t stream) {
       else hipLaunchKernelGGL((prep_kernel<false, 1>), grid, block, 0, stream, a);
     }
   }
-  // With few heads, eight, four or two workgroups per head spread the heads over many CUs
-  // (eight with the chain, the loads and the read-out on waves of their own); beyond, one
-  // 8-wave workgroup per head (two waves per SIMD to hide latency) avoids the operand traffic
-  // every workgroup repeats, and once the heads outnumber the CUs it forms P^T itself.
+  // With few heads, eight or two workgroups per head spread the heads over many CUs: eight,
+  // with the chain, the loads and the read-out on waves of their own, up to two rounds of
+  // workgroups (64 pairs; its chunk step is so much shorter that two rounds of it beat one
+  // round of a shape whose waves run the whole chunk alone); two up to 128 pairs. Beyond,
+  // one 8-wave workgroup per head (two waves per SIMD to hide latency) avoids the operand
+  // traffic every workgroup repeats, and once the heads outnumber the CUs it forms P^T
+  // itself.
   const size_t seq_pairs = (size_t)a.num_seqs * a.h_qk;
   const size_t groups = (seq_pairs + 7) / 8 * 8 * (size_t)a.group;
-  if (heads * 8 <= kStateCus) {
+  if (heads * 8 <= 2 * kStateCus) {
     hipLaunchKernelGGL(state_ro_kernel, dim3((unsigned)(groups * 8)), dim3(4 * kWave), 0, stream, a);
-  } else if (heads * 4 <= kStateCus) {
-    hipLaunchKernelGGL((state_kernel<2, false>), dim3((unsigned)(groups * 4)), dim3(2 * kWave), 0, stream, a);
   } else if (heads * 2 <= kStateCus) {
     hipLaunchKernelGGL((state_kernel<4, false>), dim3((unsigned)(groups * 2)), dim3(4 * kWave), 0, stream, a);
   } else if (heads <= kStateCus) {

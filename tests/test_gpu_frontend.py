@@ -265,7 +265,8 @@ def test_prefill_conv_many_heads_equals_two_calls(K):
 
 
 def test_prefill_conv_few_heads_equals_two_calls():
-    """At most 128 pairs (here 64, four workgroups per head): equal to the two calls."""
+    """At most 128 pairs (here 64: eight workgroups per head in two rounds): equal to the two
+    calls."""
     fe = workloads.make_frontend([100, 300], seed=710)
     (o1, f1), (o2, f2), _ = _two_calls_and_fused(fe)
     assert torch_equal(o1, o2) and torch_equal(f1, f2)

@@ -89,10 +89,10 @@ def test_prefill_many_sequences_full_heads():
     """The state pass picks its workgroup shape from the number of (sequence, V head) pairs:
     12 sequences x 32 V heads take one workgroup of eight one-tile waves per head, which
     forms P^T on chip; 6 sequences take the same workgroup reading P^T from the workspace;
-    4 sequences take two workgroups per head, 2 sequences four, and 1 sequence eight with
-    the chain on two waves and a read-out wave, all reading P^T from the workspace. The
-    per-row arithmetic, and P^T itself, are the same in all of them, so results must agree
-    bit for bit."""
+    4 sequences take two workgroups per head; 2 sequences and 1 take eight, with the chain
+    on two waves and a read-out wave (two rounds of workgroups at 2 sequences), all reading
+    P^T from the workspace. The per-row arithmetic, and P^T itself, are the same in all of
+    them, so results must agree bit for bit."""
     lens = [0, 1, 64, 65, 200, 17, 128, 0, 311, 63, 90, 5]
     x = workloads.make_prefill(lens, h_qk=16, h_v=32, with_initial_state=True, seed=13)
     o, fin = _run(x)
@@ -207,9 +207,9 @@ def test_prefill_segmented_equals_other_shape():
     """With up to 32 (sequence, V head) pairs a call whose workspace would exceed one segment's
     runs in segments of 64 chunks per sequence (a prep and a state-pass launch each, the state
     between them in the workspace). One sequence of 9,000 tokens at 32 V heads (141 chunks,
-    three segments) equals, bit for bit, the same sequence run inside a batch of two (64 pairs:
-    another state-pass shape, no segments), and the oracle on every head."""
-    xb = workloads.make_prefill([9000, 70], h_qk=16, h_v=32, with_initial_state=True, seed=41)
+    three segments) equals, bit for bit, the same sequence run inside a batch of three (96
+    pairs: another state-pass shape, no segments), and the oracle on every head."""
+    xb = workloads.make_prefill([9000, 70, 33], h_qk=16, h_v=32, with_initial_state=True, seed=41)
     ob, fb = _run(xb)
     x = _sub_batch(xb, 0, 1)
     o, fin = _run(x)

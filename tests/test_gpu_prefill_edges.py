@@ -9,9 +9,9 @@ is then at its worst); and all-zero key and query rows in mid-chunk. Each runs a
 64, 65 and 200 (a whole chunk, a one-token tail, several chunks with a ragged tail), with
 and without an initial state, and through every workgroup shape of the state pass, which
 the library picks from the number of (sequence, V head) pairs: 32 pairs (eight workgroups
-per head with the chain on two waves and a read-out wave), 64 (four), 128 (two), 160 (one
-workgroup of eight waves per head) and 288 (the same, forming P^T on chip). The same
-tolerances as every other prefill test.
+per head with the chain on two waves and a read-out wave), 64 (the same in two rounds of
+workgroups), 128 (two workgroups per head), 160 (one workgroup of eight waves per head) and
+288 (the same, forming P^T on chip). The same tolerances as every other prefill test.
 """
 
 import numpy as np
@@ -23,7 +23,7 @@ from tests._util import check_outputs, check_state, oracle_prefill, prefill_to_d
 pytestmark = pytest.mark.gpu
 
 # number of sequences of the 16 QK / 32 V head shape -> the state pass's workgroup shape
-SHAPES = {"ro_32pairs": 1, "dw_64pairs": 2, "wg2_128pairs": 4, "wg1_160pairs": 5, "form_288pairs": 9}
+SHAPES = {"ro_32pairs": 1, "ro_64pairs": 2, "wg2_128pairs": 4, "wg1_160pairs": 5, "form_288pairs": 9}
 
 
 def _run(x):
