@@ -73,10 +73,10 @@ const char* gdn_status_string(gdn_status s);
  * every 64-token chunk, 25600 bytes per V head (decay factors, and T diag(beta) =
  * (I + A)^-1 diag(beta) and the masked and decayed Q K^T each as a hi + lo bf16 pair),
  * sized for ceil(total_tokens / 64) + num_seqs chunks so no host read of cu_seqlens is
- * needed. With at most 32 (sequence, V head) pairs the call instead runs in segments of 64
+ * needed. With at most 64 (sequence, V head) pairs the call instead runs in segments of 64
  * chunks per sequence whenever that needs less: num_seqs * (64 * h_v * 25600 + h_v * d_v *
  * d_k * 4) bytes (one segment's blocks and the states between segments), whatever the
- * lengths -- 54.5 MB for one sequence at 32 V heads.
+ * lengths -- 54.5 MB for one sequence at 32 V heads, 109 MB for two.
  * Returns 0 for invalid sizes. The contents are scratch: nothing persists between calls,
  * and calls sharing a workspace must not overlap.
  */

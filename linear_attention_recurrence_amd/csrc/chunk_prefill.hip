@@ -1258,11 +1258,10 @@ hipError_t noalloc_scratch(void** ptr) {
 
 namespace {
 
-// With up to 32 (sequence, V head) pairs (one round of its workgroups), the fewest-heads
-// shape can run in segments of kSegChunks chunks per sequence, a prep launch and a
-// state-pass launch each, so that its workspace holds one segment's blocks and the states
-// between segments, whatever the sequence lengths. It does when that is smaller than the
-// whole call's blocks.
+// The fewest-heads shape (up to 64 (sequence, V head) pairs) can run in segments of
+// kSegChunks chunks per sequence, a prep launch and a state-pass launch each, so that its
+// workspace holds one segment's blocks and the states between segments, whatever the
+// sequence lengths. It does when that is smaller than the whole call's blocks.
 constexpr int kSegChunks = 64;
 
 size_t segmented_workspace_bytes(int num_seqs, int h_v) {
@@ -1271,7 +1270,7 @@ size_t segmented_workspace_bytes(int num_seqs, int h_v) {
 
 bool prefill_segmented(int total_tokens, int num_seqs, int h_v) {
   const size_t whole = max_chunks(total_tokens, num_seqs) * (size_t)h_v * kWsHead;
-  return (size_t)num_seqs * h_v * 8 <= kStateCus && segmented_workspace_bytes(num_seqs, h_v) < whole;
+  return (size_t)num_seqs * h_v * 8 <= 2 * kStateCus && segmented_workspace_bytes(num_seqs, h_v) < whole;
 }
 
 }  // namespace

@@ -52,15 +52,16 @@ def test_status_strings():
 
 def test_workspace_query():
     """The documented size: per chunk 25600 B per V head, for ceil(T / 64) + N chunks; with at
-    most 32 (sequence, V head) pairs, the segmented size N (64 h_v 25600 + h_v 128^2 4) when
+    most 64 (sequence, V head) pairs, the segmented size N (64 h_v 25600 + h_v 128^2 4) when
     that is smaller, independent of T."""
     lib, _ = _lib()
     for T, N, h_qk, h_v in ((4096, 1, 16, 32), (32768, 1, 16, 32), (10 ** 6, 1, 16, 32), (276989, 64, 16, 32),
                             (0, 3, 16, 32), (65, 2, 16, 32), (4224, 1, 16, 32), (4160, 1, 16, 32),
-                            (16200, 3, 4, 8), (5000, 4, 4, 8)):
+                            (16200, 3, 4, 8), (5000, 4, 4, 8), (20000, 2, 16, 32), (20000, 3, 16, 32),
+                            (60000, 8, 4, 8), (60000, 9, 4, 8)):
         whole = (-(-T // 64) + N) * h_v * 25600
         seg = N * (64 * h_v * 25600 + h_v * 128 * 128 * 4)
-        expect = seg if N * h_v <= 32 and seg < whole else whole
+        expect = seg if N * h_v <= 64 and seg < whole else whole
         assert lib.gdn_chunk_prefill_workspace_bytes(T, N, h_qk, h_v, 128, 128) == expect
     assert lib.gdn_chunk_prefill_workspace_bytes(32768, 1, 16, 32, 128, 128) == 54_525_952
     assert lib.gdn_chunk_prefill_workspace_bytes(4096, 1, 16, 32, 128, 128) == 65 * 32 * 25600
@@ -152,7 +153,8 @@ def test_prefill_noalloc_validation():
     assert call(dt=2) == L.GDN_ERR_UNSUPPORTED
     assert call(n=0, T=0) == L.GDN_OK
     # the scratch limit: one sequence at 32 V heads runs in segments whatever its length;
-    # two sequences (64 pairs, no segments) fit up to ceil(T / 64) + 2 = 81 chunks
+    # two sequences (64 pairs) hold the whole call's blocks while those are fewer than two
+    # segments' (104 MiB), and fit up to ceil(T / 64) + 2 = 81 chunks
     need = lambda T, n: L.gdn_chunk_prefill_workspace_bytes(T, n, 16, 32, 128, 128)
     assert need(10 ** 7, 1) <= L.NOALLOC_SCRATCH_BYTES
     assert need(5056, 2) <= L.NOALLOC_SCRATCH_BYTES < need(5057, 2)

@@ -218,6 +218,20 @@ def test_prefill_segmented_equals_other_shape():
     _compare(x, o, fin, label="segmented T=9000")
 
 
+def test_prefill_segmented_two_rounds():
+    """Segments with 64 pairs (two sequences at 32 V heads: the fewest-heads shape in two
+    rounds of workgroups) of 9,000 and 5,000 tokens (141 and 79 chunks: three and two
+    segments): equal, bit for bit, to the same sequences inside a batch of three (96 pairs:
+    another shape, no segments), and the oracle on every head."""
+    xb = workloads.make_prefill([9000, 5000, 33], h_qk=16, h_v=32, with_initial_state=True, seed=43)
+    ob, fb = _run(xb)
+    x = _sub_batch(xb, 0, 2)
+    o, fin = _run(x)
+    np.testing.assert_array_equal(o, ob[:14000])
+    np.testing.assert_array_equal(fin, fb[:2])
+    _compare(x, o, fin, label="segmented 64 pairs")
+
+
 def test_prefill_segmented_varlen():
     """Segments over several sequences (4 QK / 8 V heads: three sequences are 24 pairs) of
     4200, 0 and 12000 tokens (66, 0 and 188 chunks): the first ends in the second segment,

@@ -65,8 +65,9 @@ def test_noalloc_long_sequence_in_segments():
 
 
 def test_noalloc_rejects_sizes_beyond_the_scratch():
-    """Two sequences at 32 V heads (64 pairs: no segments) of 2,600 tokens each need
-    84 blocks of 32 x 25,600 bytes, more than the 64 MiB scratch."""
+    """Two sequences at 32 V heads (64 pairs) of 2,600 tokens each need 84 blocks of 32 x
+    25,600 bytes (fewer than two segments' 104 MiB, so no segments), more than the 64 MiB
+    scratch."""
     import torch
     import linear_attention_recurrence_amd as gdn
     x = workloads.make_prefill([2600, 2600], h_qk=16, h_v=32, seed=903)
