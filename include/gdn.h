@@ -153,9 +153,10 @@ gdn_status gdn_chunk_prefill_conv(const void* mixed_qkv, const float* conv_weigh
  *
  * Limit: sizes for which gdn_chunk_prefill_workspace_bytes(...) exceeds
  * GDN_NOALLOC_SCRATCH_BYTES return GDN_ERR_WORKSPACE with nothing launched. One sequence at
- * 32 V heads (or any batch of up to 32 (sequence, V head) pairs needing at most the
- * scratch in segments) has no length limit; larger batches at 32 V heads need
- * ceil(total_tokens / 64) + num_seqs <= 81, e.g. two sequences of up to 2,560 tokens.
+ * 32 V heads (or any batch of up to 64 (sequence, V head) pairs needing at most the
+ * scratch in segments, i.e. up to 39 pairs) has no length limit; larger batches at 32 V
+ * heads need ceil(total_tokens / 64) + num_seqs <= 81, e.g. two sequences of 2,528 tokens
+ * each.
  * GDN_F32 needs no workspace and has no limit.
  *
  * Sharing: every call on one GPU uses that GPU's one array, which keeps whatever the last
