@@ -113,6 +113,20 @@ def test_prefill_head_groupings(h_qk, h_v):
     _compare(x, o, fin, label="h_qk=%d h_v=%d" % (h_qk, h_v))
 
 
+@pytest.mark.parametrize("h_qk,h_v,n", [(1, 1, 33), (1, 1, 65), (1, 1, 129), (1, 1, 257),
+                                         (1, 2, 17), (1, 2, 33), (1, 2, 65), (1, 2, 129)])
+def test_prefill_shape_boundaries(h_qk, h_v, n):
+    """(sequence, V head) pair counts just past each change of the state pass's workgroup
+    shape (33, 65, 129 and 257 pairs, or 34, 66, 130 and 258), with 1 and 2 V heads per QK
+    head, so the workgroup grids end in part-filled groups of eight QK heads: every head of
+    sequences of 0 to 150 tokens against the oracle, with initial and final states."""
+    rng = np.random.default_rng(1000 + 10 * h_v + n)
+    lens = [int(v) for v in rng.integers(0, 151, n)]
+    x = workloads.make_prefill(lens, h_qk=h_qk, h_v=h_v, with_initial_state=True, seed=2000 + n)
+    o, fin = _run(x)
+    _compare(x, o, fin, label="%d pairs" % (n * h_v))
+
+
 def test_prefill_all_sequences_empty():
     """Zero tokens: every final state is its initial state, and nothing else is written."""
     x = workloads.make_prefill([0, 0, 0], h_qk=2, h_v=4, with_initial_state=True, seed=21)
