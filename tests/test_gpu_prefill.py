@@ -246,6 +246,22 @@ def test_prefill_segmented_two_rounds():
     _compare(x, o, fin, label="segmented 64 pairs")
 
 
+def test_prefill_segmented_many_small_heads():
+    """Segments with 40 pairs (20 sequences of 3,000 to 6,000 tokens, 1 QK / 2 V heads: two
+    rounds of workgroups, the last group of eight QK heads part-filled), sequences ending in
+    different segments: every head against the oracle, and the same sequences in a batch
+    with one more (the whole call at once, no segments) bit for bit."""
+    rng = np.random.default_rng(44)
+    lens = [int(v) for v in rng.integers(3000, 6001, 20)]
+    x = workloads.make_prefill(lens + [33] * 13, h_qk=1, h_v=2, with_initial_state=True, seed=45)
+    ob, fb = _run(x)            # 66 pairs: no segments
+    xs = _sub_batch(x, 0, 20)   # 40 pairs: segments
+    o, fin = _run(xs)
+    np.testing.assert_array_equal(o, ob[:xs.total_tokens])
+    np.testing.assert_array_equal(fin, fb[:20])
+    _compare(xs, o, fin, label="segmented 40 pairs")
+
+
 def test_prefill_segmented_varlen():
     """Segments over several sequences (4 QK / 8 V heads: three sequences are 24 pairs) of
     4200, 0 and 12000 tokens (66, 0 and 188 chunks): the first ends in the second segment,
