@@ -4,7 +4,8 @@ against gdn_chunk_prefill, through the C ABI (GPU).
 Two calls in a row on the scratch -- the second smaller, so it runs over what the first left
 there -- each equal bit for bit to gdn_chunk_prefill with a caller workspace (the same
 kernels), and the first within the parity bars of the fp64 oracle; a long sequence, which
-runs in segments; a size beyond the scratch is rejected with nothing written.
+runs in segments; a batch that fits only in segments, in two rounds of workgroups; a size
+beyond the scratch is rejected with nothing written.
 """
 
 import numpy as np
@@ -59,6 +60,16 @@ def test_noalloc_long_sequence_in_segments():
     """One sequence of 32,768 tokens at 32 V heads runs in segments whose workspace fits the
     scratch: equal bit for bit to gdn_chunk_prefill."""
     x = workloads.make_prefill([32768], with_initial_state=True, seed=904)
+    (o_ref, f_ref), (o_na, f_na) = _both(x)
+    np.testing.assert_array_equal(o_na, o_ref)
+    np.testing.assert_array_equal(f_na, f_ref)
+
+
+def test_noalloc_segments_in_two_rounds():
+    """35 sequences of 5,000 tokens at 1 QK / 1 V head (35 pairs: two rounds of state-pass
+    workgroups): the whole call's blocks (70.9 MB) would exceed the scratch, the segments'
+    (59.6 MB) fit, so the call runs in segments; equal bit for bit to gdn_chunk_prefill."""
+    x = workloads.make_prefill([5000] * 35, h_qk=1, h_v=1, with_initial_state=True, seed=905)
     (o_ref, f_ref), (o_na, f_na) = _both(x)
     np.testing.assert_array_equal(o_na, o_ref)
     np.testing.assert_array_equal(f_na, f_ref)
