@@ -67,7 +67,7 @@ COUNTERS = {
     "prefill_t32768": {"bytes": 2019260415, "mfma_busy": 0.1429, "sources": "35dd743ffc4a9a31"},
     "prefill_t4096": {"bytes": 250360062, "mfma_busy": 0.1426, "sources": "35dd743ffc4a9a31"},
     "prefill_packed64": {"bytes": 12458608103, "mfma_busy": 0.2553, "sources": "35dd743ffc4a9a31"},
-    "prefill_conv_packed64": {"bytes": 21649736857, "sources": "ec4b1aa13a18e5ce"},
+    "prefill_conv_packed64": {"bytes": 22514032759, "sources": "fd794bc2c643059f"},
     "decode": {"bytes": 1083356788, "sources": "1cbcbd1979d4176c"},
 }
 
