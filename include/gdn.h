@@ -76,7 +76,8 @@ const char* gdn_status_string(gdn_status s);
  * needed. With at most 64 (sequence, V head) pairs the call instead runs in segments of 64
  * chunks per sequence whenever that needs less: num_seqs * (64 * h_v * 25600 + h_v * d_v *
  * d_k * 4) bytes (one segment's blocks and the states between segments), whatever the
- * lengths -- 54.5 MB for one sequence at 32 V heads, 109 MB for two.
+ * lengths -- 54.5 MB for one sequence at 32 V heads, 109 MB for two. With total_tokens = 0
+ * (every sequence empty) no workspace is needed: 0, and workspace may be NULL.
  * Returns 0 for invalid sizes. The contents are scratch: nothing persists between calls,
  * and calls sharing a workspace must not overlap.
  */

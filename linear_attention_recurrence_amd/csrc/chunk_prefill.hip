@@ -1277,6 +1277,9 @@ bool prefill_segmented(int total_tokens, int num_seqs, int h_v) {
 
 size_t chunk_prefill_workspace_bytes(int total_tokens, int num_seqs, int h_qk, int h_v) {
   (void)h_qk;
+  // with no tokens there are no chunks: no prep launch, and the state pass only copies each
+  // initial state to its final state without touching the workspace
+  if (total_tokens == 0) return 0;
   if (prefill_segmented(total_tokens, num_seqs, h_v)) return segmented_workspace_bytes(num_seqs, h_v);
   return max_chunks(total_tokens, num_seqs) * (size_t)h_v * kWsHead;
 }

@@ -145,7 +145,7 @@ gdn_status gdn_chunk_prefill(const void* q, const void* k, const void* v, gdn_dt
                                                   h_qk, h_v, scale, initial_state, final_state,
                                                   o, s));
   const size_t need = gdn_chunk_prefill_workspace_bytes(total_tokens, num_seqs, h_qk, h_v, d_k, d_v);
-  if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
   return from_hip(gdn::launch_chunk_prefill(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
                                             h_qk, h_v, scale, initial_state, final_state, o,
                                             workspace, s));
@@ -173,7 +173,7 @@ gdn_status gdn_chunk_prefill_conv(const void* mixed_qkv, const float* conv_weigh
   if (total_tokens > 0 && (!mixed_qkv || !conv_weight || !g || !beta || !o)) return GDN_ERR_NULL;
   if (!final_state && total_tokens == 0) return GDN_OK;   // nothing observable to do
   const size_t need = gdn_chunk_prefill_conv_workspace_bytes(total_tokens, num_seqs, h_qk, h_v, d_k, d_v);
-  if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
   GDN_TRY(check_seqlens(cu_seqlens, num_seqs, total_tokens, stream));
   GDN_TRY(check_log_decay(g, (size_t)total_tokens * h_v, stream));
   return from_hip(gdn::launch_chunk_prefill_conv(mixed_qkv, conv_weight, conv_kernel, q_scale, g, beta,

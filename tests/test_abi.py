@@ -53,7 +53,7 @@ def test_status_strings():
 def test_workspace_query():
     """The documented size: per chunk 25600 B per V head, for ceil(T / 64) + N chunks; with at
     most 64 (sequence, V head) pairs, the segmented size N (64 h_v 25600 + h_v 128^2 4) when
-    that is smaller, independent of T."""
+    that is smaller, independent of T; none (0) with no tokens."""
     lib, _ = _lib()
     for T, N, h_qk, h_v in ((4096, 1, 16, 32), (32768, 1, 16, 32), (10 ** 6, 1, 16, 32), (276989, 64, 16, 32),
                             (0, 3, 16, 32), (65, 2, 16, 32), (4224, 1, 16, 32), (4160, 1, 16, 32),
@@ -62,6 +62,8 @@ def test_workspace_query():
         whole = (-(-T // 64) + N) * h_v * 25600
         seg = N * (64 * h_v * 25600 + h_v * 128 * 128 * 4)
         expect = seg if N * h_v <= 64 and seg < whole else whole
+        if T == 0:
+            expect = 0   # no chunks: the call only copies initial to final states
         assert lib.gdn_chunk_prefill_workspace_bytes(T, N, h_qk, h_v, 128, 128) == expect
     assert lib.gdn_chunk_prefill_workspace_bytes(32768, 1, 16, 32, 128, 128) == 54_525_952
     assert lib.gdn_chunk_prefill_workspace_bytes(4096, 1, 16, 32, 128, 128) == 65 * 32 * 25600
@@ -192,6 +194,7 @@ def test_prefill_conv_validation():
     assert q(276989, 64) == p(276989, 64) + 276989 * 8192 * 2   # q, k and v after the blocks
     assert q(4096, 1) == p(4096, 1) + 4096 * 8192 * 2
     assert q(-1, 1) == 0
+    assert q(0, 3) == 0 and p(0, 3) == 0
 
 
 def test_conv_prep_validation():
